@@ -1,0 +1,61 @@
+"""H2O-style running-score eviction (oracle side).
+
+[tokendh] section "历史太长,会撑爆什么": H2O keeps a continuously accumulated
+table of attention scores and physically deletes entries from memory.
+[tokendh] section "把边界划在'生命周期'上": at every decode step it first
+updates the accumulated scores and then decides what to delete.
+
+Readings taken where the pages are silent:
+  * one table per (batch, KV head): a slot's score grows by the softmax weight
+    every query head of the group gives it at this step;
+  * step order: the new token is written into the free slot, attention runs
+    over every occupied slot (the new one included), the scores are
+    accumulated (the new token starts from 0), and then, if more than
+    heavy + recent slots are occupied, exactly one is evicted;
+  * the recent window protects the newest `recent` positions
+    (position > cur_pos - recent); among the rest the lowest score goes,
+    ties to the lower position;
+  * the evicted slot is freed (position -1, score 0) and receives the next token.
+"""
+import numpy as np
+
+from .attention import unit_attention
+from .selection import argmin_lower
+
+
+def h2o_accumulate_evict(logits, lse, slot_pos, acc, n_slots, cur_pos, new_slot, heavy, recent):
+    """One unit.  logits [G][>=n_slots] and lse [G] from attention over slots [0, n_slots);
+    slot_pos [cap] int (-1 free), acc [cap] float64; new_slot = slot holding cur_pos.
+    Returns (slot_pos', acc', evicted slot or -1)."""
+    slot_pos = np.array(slot_pos, np.int64)
+    acc = np.array(acc, np.float64)
+    slot_pos[new_slot] = cur_pos
+    acc[new_slot] = 0.0
+    n = int(n_slots)
+    occupied = slot_pos[:n] >= 0
+    p = np.exp(np.asarray(logits, np.float64)[:, :n] - np.asarray(lse, np.float64)[:, None])   # [G][n]
+    acc[:n] += np.where(occupied, p.sum(axis=0), 0.0)
+    if int((slot_pos >= 0).sum()) <= heavy + recent:
+        return slot_pos, acc, -1
+    cand = np.zeros(slot_pos.shape[0], bool)
+    cand[:n] = occupied & (slot_pos[:n] <= cur_pos - recent)
+    ev = argmin_lower(acc, slot_pos, cand)
+    if ev >= 0:
+        slot_pos[ev] = -1
+        acc[ev] = 0.0
+    return slot_pos, acc, ev
+
+
+def h2o_step(Kslots, Vslots, slot_pos, acc, n_slots, free_slot, qg, k_new, v_new, cur_pos,
+             heavy, recent, scale):
+    """One decode step of one unit.  Kslots [cap][D], Vslots [cap][Dv] are updated in place.
+    free_slot: slot to write the new token into (-1: append at n_slots).
+    Returns (out [G][Dv], lse [G], slot_pos', acc', n_slots', evicted)."""
+    slot = free_slot if free_slot >= 0 else n_slots
+    if free_slot < 0:
+        n_slots += 1
+    Kslots[slot] = k_new
+    Vslots[slot] = v_new
+    out, lse, logits = unit_attention(qg, Kslots[:n_slots], Vslots[:n_slots], scale)
+    slot_pos, acc, ev = h2o_accumulate_evict(logits, lse, slot_pos, acc, n_slots, cur_pos, slot, heavy, recent)
+    return out, lse, slot_pos, acc, n_slots, ev
