@@ -1,0 +1,215 @@
+/* se.h -- C ABI of the MI355X (gfx950) sparse-decode library (libse.so).
+ *
+ * Decode-time sparse attention over a KV cache whose kept positions each
+ * method chooses.  The SparseEngine pages describe the contract this follows:
+ *   - tokendh.com news f00df0ef4a (SparseEngine explainer), section
+ *     "把边界划在'生命周期'上": each method owns a cache manager that creates,
+ *     updates and frees its own KV representation at lifecycle hooks, and an
+ *     AttentionView turns whatever the method keeps into the one format the
+ *     attention computation reads;
+ *   - ai-feeds.com digest "SparseEngine：稀疏优先推理引擎", section 方法 /
+ *     关键模块: the view exposes the selected positions uniformly so that the
+ *     attention kernel does not change per method.
+ * Here the cache manager's state is caller-owned device buffers, the update /
+ * evict hooks are se_page_meta_update, se_snapkv_score_compact and
+ * se_h2o_accumulate_evict, the view producers are se_quest_select and
+ * se_omnikv_topk, and the attention backend is se_sparse_decode_attn.
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument except the se_cache descriptor is DEVICE memory
+ *     owned by the caller.  The library never allocates or frees memory, keeps
+ *     no state between calls and never synchronizes: all work is enqueued on
+ *     `stream` (a hipStream_t; 0 is the null stream).
+ *   - Arguments are validated on the host before anything is enqueued.  On an
+ *     error the call returns a negative se_status, nothing is enqueued and the
+ *     outputs are untouched.  SE_ERR_HIP reports a failed kernel launch.
+ *   - Layouts are row-major and dense.  A "unit" is one (batch row, KV head).
+ *     q is [B][Hq][d_k]; K is [B][Hkv][capacity][d_k]; V is
+ *     [B][Hkv][capacity][d_v]; query head h reads KV head h / (Hq / Hkv).
+ *     For a latent (MLA) cache Hkv = 1 and V is not a separate buffer: the
+ *     value of a slot is the first d_v elements of its K row.
+ *   - seq_len is int32 [B]: slots [0, seq_len[b]) of every unit of batch row b
+ *     are valid.
+ *   - Device-side conditions that depend on data (a view longer than the
+ *     candidates, an append past capacity) are clamped, not reported.
+ *   - NaN or Inf inputs are undefined behaviour (not checked).
+ *   - Calls are reentrant; calls that write the same buffers must be ordered
+ *     by the caller (same stream or events).
+ */
+#ifndef SE_H
+#define SE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SE_ABI_VERSION 1
+
+typedef enum {
+  SE_OK = 0,
+  SE_ERR_NULL = -1,        /* a required pointer is NULL */
+  SE_ERR_SHAPE = -2,       /* inconsistent or unsupported sizes */
+  SE_ERR_DTYPE = -3,       /* unsupported element type */
+  SE_ERR_ALIGN = -4,       /* a device pointer is not 16-byte aligned */
+  SE_ERR_BUDGET = -5,      /* a budget / window / k argument out of range */
+  SE_ERR_WORKSPACE = -6,   /* workspace missing or smaller than se_workspace_bytes() */
+  SE_ERR_UNSUPPORTED = -7, /* valid but not implemented combination */
+  SE_ERR_HIP = -8          /* a HIP launch failed */
+} se_status;
+
+typedef enum { SE_F32 = 0, SE_BF16 = 1 } se_dtype;
+
+/* Host-side description of one layer's cache.  Element type `dtype` applies to
+ * q, K, V, new rows and page metadata; scores, outputs and logits are float. */
+typedef struct {
+  int32_t batch;        /* B */
+  int32_t n_q_heads;    /* Hq, a multiple of n_kv_heads, Hq / Hkv <= 64 */
+  int32_t n_kv_heads;   /* Hkv (1 for a latent cache) */
+  int32_t d_k;          /* key width: 64, 128 or 576 */
+  int32_t d_v;          /* value width: equals d_k, or 512 for a latent cache */
+  int32_t capacity;     /* slots per unit */
+  int32_t dtype;        /* se_dtype */
+  int32_t latent;       /* nonzero: V is K[..., :d_v] (MLA-style latent cache) */
+} se_cache;
+
+/* Operation ids for se_workspace_bytes. */
+typedef enum {
+  SE_OP_QUEST = 1,      /* a0 = page_size, a1 = top_pages */
+  SE_OP_ATTN = 2,       /* a0 = view_cap * granularity (slots per unit), a1 = num_splits (0 = auto) */
+  SE_OP_SNAPKV = 3,     /* a0 = prompt_len, a1 = window */
+  SE_OP_OMNIKV = 4      /* a0 = logit_cap, a1 = top_k */
+} se_op;
+
+/* Append one decode token's K/V row to every unit (helper of the hooks: the
+ * step loop needs no framework compute kernel).
+ *   k_new [B][Hkv][d_k], v_new [B][Hkv][d_v] (ignored for a latent cache).
+ *   slot: NULL, or int32 [B][Hkv].  Where slot is NULL or slot[b][0] < 0 the
+ *   row goes to slot seq_len[b] and seq_len[b] is incremented; otherwise row
+ *   (b, h) is written into slot[b][h] and seq_len is unchanged (a slot freed
+ *   by eviction).  A write at or past capacity is dropped. */
+se_status se_kv_append(const se_cache* c, void* k, void* v, const void* k_new, const void* v_new,
+                       const int32_t* slot, int32_t* seq_len, hipStream_t stream);
+
+/* Quest summary index.  tokendh.com explainer, section "历史太长,会撑爆什么":
+ * dynamic-sparse methods keep the full history plus a per-page summary index.
+ * Here the index is the elementwise min and max of K over each page's valid
+ * tokens: kmin, kmax [B][Hkv][ceil(capacity / page_size)][d_k], dtype of K
+ * (min and max are exact).  first_page >= 0 rebuilds pages
+ * [first_page, ceil(seq_len[b] / page_size)); first_page = -1 rebuilds only
+ * the page holding slot seq_len[b] - 1 (the decode-step update).  Pages past
+ * seq_len are not written. */
+se_status se_page_meta_update(const se_cache* c, const void* k, void* kmin, void* kmax,
+                              const int32_t* seq_len, int32_t page_size, int32_t first_page,
+                              hipStream_t stream);
+
+/* Quest page selection.  tokendh.com explainer, section "历史太长,会撑爆什么"
+ * (Quest picks pages dynamically from the query) and Netics blog
+ * "SparseEngine 统一接入十五种稀疏注意力", section "SparseEngine 围绕 KV cache
+ * 构建了什么" (page-selection methods choose KV pages per query).
+ * Score of page p for query head h: sum_d max(q_hd * kmin_pd, q_hd * kmax_pd)
+ * (an upper bound of q_h . k over the page), accumulated in fp32; the score of
+ * a page for a KV head is the max over the heads of its group.  The view is
+ * the top_pages best valid pages (ties to the lower page), ascending:
+ *   view_idx int32 [B][Hkv][top_pages] (entries past view_len are -1),
+ *   view_len int32 [B][Hkv] = min(top_pages, ceil(seq_len[b] / page_size)),
+ *   page_score: NULL or float [B][Hkv][ceil(capacity / page_size)] (-inf for
+ *   pages past seq_len).
+ * ws: device workspace of se_workspace_bytes(SE_OP_QUEST, c, page_size, top_pages) bytes. */
+se_status se_quest_select(const se_cache* c, const void* q, const void* kmin, const void* kmax,
+                          const int32_t* seq_len, int32_t page_size, int32_t top_pages,
+                          int32_t* view_idx, int32_t* view_len, float* page_score,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Split-K flash decode over an AttentionView (tokendh.com explainer, section
+ * "把边界划在'生命周期'上"; ai-feeds digest, section 方法 / 关键模块).
+ *   view_idx: NULL = every slot below seq_len[b]; else int32 [B][Hkv][view_cap],
+ *   entry e of unit u covering slots [view_idx*g, view_idx*g + g) with
+ *   g = granularity (page size for page views, 1 for token views); only the
+ *   first view_len[b][h] entries are read and slots >= seq_len[b] are skipped.
+ *   out float [B][Hq][d_v] = softmax(scale * q . k) . v over the view (0 for an
+ *   empty view); lse: NULL or float [B][Hq] natural-log sum of exp(scale q.k)
+ *   (-inf for an empty view); logits: NULL or float [B][Hq][logit_cap], the
+ *   scaled logit of view slot i (entry * g + offset) at index i, -inf where the
+ *   slot holds no valid token (indices >= view_cap * g are not written).
+ *   num_splits: 0 chooses the split-K factor; otherwise the number of chunks
+ *   each unit's view is cut into (results agree to rounding for any value).
+ *   ws: se_workspace_bytes(SE_OP_ATTN, c, view_cap * g, num_splits) bytes. */
+se_status se_sparse_decode_attn(const se_cache* c, const void* q, const void* k, const void* v,
+                                const int32_t* seq_len, const int32_t* view_idx,
+                                const int32_t* view_len, int32_t view_cap, int32_t granularity,
+                                float scale, float* out, float* lse, float* logits,
+                                int32_t logit_cap, int32_t num_splits,
+                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* SnapKV prefill-end eviction.  tokendh.com explainer, section
+ * "把边界划在'生命周期'上": the method looks at how the last few prompt tokens
+ * attend over the history, keeps the important part and physically deletes
+ * the rest.  Every batch row has prompt_len valid slots.
+ *   q_obs [B][Hq][window][d_k]: queries of prompt positions L - window + i.
+ *   vote[j] (j < L - window) = sum over the group's heads and the window rows
+ *   of the causal softmax weight the row gives key j (each row's softmax runs
+ *   over keys 0 .. its own position); pooled = max-pool(vote, pool_kernel,
+ *   stride 1, out-of-range ignored); kept = the budget - window best pooled
+ *   positions (ties to the lower position) plus the window, ascending; with
+ *   budget >= prompt_len every position is kept.
+ *   kept_pos int32 [B][Hkv][budget] (-1 past min(budget, L)); k_out / v_out
+ *   [B][Hkv][out->capacity][d] receive the kept rows in that order (bit copies);
+ *   votes: NULL or float [B][Hkv][L - window]; out_seq_len: NULL or int32 [B]
+ *   set to min(budget, L).  `out` describes k_out / v_out (same heads, widths,
+ *   dtype; capacity >= min(budget, L)).
+ *   ws: se_workspace_bytes(SE_OP_SNAPKV, c, prompt_len, window) bytes. */
+se_status se_snapkv_score_compact(const se_cache* c, const void* q_obs, const void* k, const void* v,
+                                  int32_t prompt_len, int32_t window, int32_t pool_kernel,
+                                  int32_t budget, float scale, const se_cache* out, void* k_out,
+                                  void* v_out, int32_t* kept_pos, float* votes,
+                                  int32_t* out_seq_len, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
+/* H2O accumulate-then-evict step.  tokendh.com explainer, sections
+ * "历史太长,会撑爆什么" (a continuously accumulated score table plus physical
+ * deletion) and "把边界划在'生命周期'上" (scores updated every decode step,
+ * then the victim chosen).
+ *   logits float [B][Hq][logit_cap], lse float [B][Hq]: from
+ *   se_sparse_decode_attn over every slot below seq_len[b] (identity view).
+ *   slot_pos int32 [B][Hkv][capacity] (token position held by a slot, -1 =
+ *   free); acc float [B][Hkv][capacity] (accumulated score).
+ *   evict_slot int32 [B][Hkv], in/out: on entry the slot that received the
+ *   token at cur_pos (-1: it was appended at seq_len[b] - 1); on exit the
+ *   evicted slot or -1.
+ *   Per unit: the new slot gets position cur_pos and score 0; every occupied
+ *   slot below seq_len[b] adds the sum over the group's heads of
+ *   exp(logit - lse); if more than heavy + recent slots are occupied, the
+ *   lowest-scoring slot with position <= cur_pos - recent (ties to the lower
+ *   position) is freed (position -1, score 0). */
+se_status se_h2o_accumulate_evict(const se_cache* c, const float* logits, const float* lse,
+                                  int32_t logit_cap, const int32_t* seq_len, int32_t* slot_pos,
+                                  float* acc, int32_t cur_pos, int32_t heavy_budget,
+                                  int32_t recent_window, int32_t* evict_slot, hipStream_t stream);
+
+/* OmniKV filter-layer top-k.  tokendh.com explainer, section
+ * "把边界划在'生命周期'上": some layers judge which history matters and later
+ * layers reuse that judgement.
+ *   score[j] = sum over the group's heads of exp(logit_hj - lse_h) for
+ *   j < seq_len[b] (logits / lse from a full-view se_sparse_decode_attn);
+ *   view_idx int32 [B][Hkv][top_k]: the top_k best slots (ties to the lower
+ *   slot), ascending, -1 padded; view_len int32 [B][Hkv] = min(top_k, seq_len[b]);
+ *   scores: NULL or float [B][Hkv][logit_cap].
+ *   ws: se_workspace_bytes(SE_OP_OMNIKV, c, logit_cap, top_k) bytes. */
+se_status se_omnikv_topk(const se_cache* c, const float* logits, const float* lse, int32_t logit_cap,
+                         const int32_t* seq_len, int32_t top_k, int32_t* view_idx,
+                         int32_t* view_len, float* scores, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/* Workspace bytes an operation needs for cache `c` (0 if none). */
+size_t se_workspace_bytes(int32_t op, const se_cache* c, int32_t a0, int32_t a1);
+const char* se_status_string(int32_t status);
+int32_t se_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SE_H */

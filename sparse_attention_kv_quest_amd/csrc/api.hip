@@ -1,0 +1,212 @@
+// C ABI of libse: host-side validation, then dispatch to the launchers.
+// Nothing is enqueued unless every argument checks out.
+#include "se_internal.hpp"
+#include <stdio.h>
+#include <stdlib.h>
+
+using namespace se;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool trace_on() {
+  static int on = -1;
+  if (on < 0) {
+    const char* e = getenv("SE_TRACE");
+    on = (e && e[0] && e[0] != '0') ? 1 : 0;
+  }
+  return on == 1;
+}
+
+#define SE_TRACE_CALL(...)                                  \
+  do {                                                      \
+    if (trace_on()) { fprintf(stderr, "[se] " __VA_ARGS__); fputc('\n', stderr); } \
+  } while (0)
+
+se_status check_cache(const se_cache* c) {
+  if (c == nullptr) return SE_ERR_NULL;
+  if (c->dtype != SE_F32 && c->dtype != SE_BF16) return SE_ERR_DTYPE;
+  if (c->batch <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->capacity <= 0) return SE_ERR_SHAPE;
+  if (c->n_q_heads % c->n_kv_heads != 0) return SE_ERR_SHAPE;
+  if (c->n_q_heads / c->n_kv_heads > 64) return SE_ERR_SHAPE;
+  if (c->d_k != 64 && c->d_k != 128 && c->d_k != 576) return SE_ERR_SHAPE;
+  if (c->latent) {
+    if (c->n_kv_heads != 1 || c->d_v <= 0 || c->d_v > c->d_k || c->d_v % 8 != 0) return SE_ERR_SHAPE;
+  } else if (c->d_v != c->d_k) {
+    return SE_ERR_SHAPE;
+  }
+  return SE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t se_abi_version(void) { return SE_ABI_VERSION; }
+
+const char* se_status_string(int32_t st) {
+  switch (st) {
+    case SE_OK: return "ok";
+    case SE_ERR_NULL: return "null pointer";
+    case SE_ERR_SHAPE: return "bad shape";
+    case SE_ERR_DTYPE: return "unsupported dtype";
+    case SE_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case SE_ERR_BUDGET: return "budget / window / k out of range";
+    case SE_ERR_WORKSPACE: return "workspace too small";
+    case SE_ERR_UNSUPPORTED: return "unsupported combination";
+    case SE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t se_workspace_bytes(int32_t op, const se_cache* c, int32_t a0, int32_t a1) {
+  if (check_cache(c) != SE_OK) return 0;
+  switch (op) {
+    case SE_OP_QUEST: return a0 > 0 ? quest_ws_bytes(*c, a0, a1) : 0;
+    case SE_OP_ATTN: return attn_ws_bytes(*c, a0 > 0 ? a0 : c->capacity, a1);
+    case SE_OP_SNAPKV: return (a0 > a1 && a1 > 0) ? snapkv_ws_bytes(*c, a0, a1) : 0;
+    case SE_OP_OMNIKV: return a0 > 0 ? omnikv_ws_bytes(*c, a0, a1) : 0;
+    default: return 0;
+  }
+}
+
+se_status se_kv_append(const se_cache* c, void* k, void* v, const void* k_new, const void* v_new,
+                       const int32_t* slot, int32_t* seq_len, hipStream_t stream) {
+  se_status st = check_cache(c);
+  if (st != SE_OK) return st;
+  if (!k || !k_new || !seq_len || (!c->latent && (!v || !v_new))) return SE_ERR_NULL;
+  if (!aligned16(k) || !aligned16(k_new) || (!c->latent && (!aligned16(v) || !aligned16(v_new))))
+    return SE_ERR_ALIGN;
+  SE_TRACE_CALL("kv_append B=%d Hkv=%d d_k=%d cap=%d slot=%p", c->batch, c->n_kv_heads, c->d_k, c->capacity,
+                (const void*)slot);
+  return launch_kv_append(*c, k, v, k_new, v_new, slot, seq_len, stream);
+}
+
+se_status se_page_meta_update(const se_cache* c, const void* k, void* kmin, void* kmax,
+                              const int32_t* seq_len, int32_t page_size, int32_t first_page,
+                              hipStream_t stream) {
+  se_status st = check_cache(c);
+  if (st != SE_OK) return st;
+  if (!k || !kmin || !kmax || !seq_len) return SE_ERR_NULL;
+  if (!aligned16(k) || !aligned16(kmin) || !aligned16(kmax)) return SE_ERR_ALIGN;
+  if (page_size <= 0 || page_size > c->capacity || first_page < -1) return SE_ERR_SHAPE;
+  SE_TRACE_CALL("page_meta B=%d Hkv=%d d_k=%d P=%d first=%d", c->batch, c->n_kv_heads, c->d_k, page_size,
+                first_page);
+  return launch_page_meta(*c, k, kmin, kmax, seq_len, page_size, first_page, stream);
+}
+
+se_status se_quest_select(const se_cache* c, const void* q, const void* kmin, const void* kmax,
+                          const int32_t* seq_len, int32_t page_size, int32_t top_pages,
+                          int32_t* view_idx, int32_t* view_len, float* page_score,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  se_status st = check_cache(c);
+  if (st != SE_OK) return st;
+  if (!q || !kmin || !kmax || !seq_len || !view_idx || !view_len) return SE_ERR_NULL;
+  if (!aligned16(q) || !aligned16(kmin) || !aligned16(kmax)) return SE_ERR_ALIGN;
+  if (page_size <= 0 || page_size > c->capacity) return SE_ERR_SHAPE;
+  if (top_pages < 1) return SE_ERR_BUDGET;
+  if (!page_score) {
+    const size_t need = quest_ws_bytes(*c, page_size, top_pages);
+    if (!ws || ws_bytes < need) return SE_ERR_WORKSPACE;
+  }
+  SE_TRACE_CALL("quest_select B=%d Hq=%d Hkv=%d d_k=%d P=%d k=%d", c->batch, c->n_q_heads, c->n_kv_heads,
+                c->d_k, page_size, top_pages);
+  return launch_quest(*c, q, kmin, kmax, seq_len, page_size, top_pages, view_idx, view_len, page_score, ws,
+                      stream);
+}
+
+se_status se_sparse_decode_attn(const se_cache* c, const void* q, const void* k, const void* v,
+                                const int32_t* seq_len, const int32_t* view_idx,
+                                const int32_t* view_len, int32_t view_cap, int32_t granularity,
+                                float scale, float* out, float* lse, float* logits,
+                                int32_t logit_cap, int32_t num_splits,
+                                void* ws, size_t ws_bytes, hipStream_t stream) {
+  se_status st = check_cache(c);
+  if (st != SE_OK) return st;
+  if (!q || !k || !seq_len || !out || (!c->latent && !v)) return SE_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || (!c->latent && !aligned16(v))) return SE_ERR_ALIGN;
+  if (view_idx) {
+    if (!view_len) return SE_ERR_NULL;
+    if (view_cap <= 0 || granularity <= 0) return SE_ERR_SHAPE;
+    if (int64_t(view_cap) * granularity > (int64_t(1) << 30)) return SE_ERR_SHAPE;
+  }
+  if (logits && logit_cap <= 0) return SE_ERR_SHAPE;
+  if (num_splits < 0 || num_splits > 4096) return SE_ERR_SHAPE;
+  if (!(scale > 0.f) || !(scale < 1e30f)) return SE_ERR_SHAPE;
+  const int slots = view_idx ? view_cap * granularity : c->capacity;
+  const size_t need = attn_ws_bytes(*c, slots, num_splits);
+  if (!ws || ws_bytes < need) return SE_ERR_WORKSPACE;
+  SE_TRACE_CALL("sparse_decode_attn B=%d Hq=%d Hkv=%d d_k=%d d_v=%d view=%s cap=%d g=%d splits=%d logits=%d",
+                c->batch, c->n_q_heads, c->n_kv_heads, c->d_k, c->d_v, view_idx ? "idx" : "identity",
+                view_cap, granularity, num_splits, logits ? logit_cap : 0);
+  return launch_attn(*c, q, k, v, seq_len, view_idx, view_len, view_cap, granularity, scale, out, lse, logits,
+                     logit_cap, num_splits, ws, stream);
+}
+
+se_status se_snapkv_score_compact(const se_cache* c, const void* q_obs, const void* k, const void* v,
+                                  int32_t prompt_len, int32_t window, int32_t pool_kernel,
+                                  int32_t budget, float scale, const se_cache* out, void* k_out,
+                                  void* v_out, int32_t* kept_pos, float* votes,
+                                  int32_t* out_seq_len, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  se_status st = check_cache(c);
+  if (st != SE_OK) return st;
+  st = check_cache(out);
+  if (st != SE_OK) return st;
+  if (!q_obs || !k || !k_out || !kept_pos || (!c->latent && (!v || !v_out))) return SE_ERR_NULL;
+  if (!aligned16(q_obs) || !aligned16(k) || !aligned16(k_out) ||
+      (!c->latent && (!aligned16(v) || !aligned16(v_out))))
+    return SE_ERR_ALIGN;
+  if (c->latent) return SE_ERR_UNSUPPORTED;
+  if (out->batch != c->batch || out->n_q_heads != c->n_q_heads || out->n_kv_heads != c->n_kv_heads ||
+      out->d_k != c->d_k || out->d_v != c->d_v || out->dtype != c->dtype || out->latent != c->latent)
+    return SE_ERR_SHAPE;
+  if (prompt_len <= 0 || prompt_len > c->capacity) return SE_ERR_SHAPE;
+  if (window < 1 || window >= prompt_len) return SE_ERR_BUDGET;
+  if (pool_kernel < 1 || pool_kernel % 2 == 0) return SE_ERR_BUDGET;
+  if (budget < window) return SE_ERR_BUDGET;
+  if (out->capacity < std::min(budget, prompt_len)) return SE_ERR_BUDGET;
+  if (!(scale > 0.f) || !(scale < 1e30f)) return SE_ERR_SHAPE;
+  const size_t need = snapkv_ws_bytes(*c, prompt_len, window);
+  if (!ws || ws_bytes < need) return SE_ERR_WORKSPACE;
+  SE_TRACE_CALL("snapkv_score_compact B=%d Hq=%d Hkv=%d L=%d W=%d pool=%d budget=%d", c->batch, c->n_q_heads,
+                c->n_kv_heads, prompt_len, window, pool_kernel, budget);
+  return launch_snapkv(*c, q_obs, k, v, prompt_len, window, pool_kernel, budget, scale, *out, k_out, v_out,
+                       kept_pos, votes, out_seq_len, ws, stream);
+}
+
+se_status se_h2o_accumulate_evict(const se_cache* c, const float* logits, const float* lse,
+                                  int32_t logit_cap, const int32_t* seq_len, int32_t* slot_pos,
+                                  float* acc, int32_t cur_pos, int32_t heavy_budget,
+                                  int32_t recent_window, int32_t* evict_slot, hipStream_t stream) {
+  se_status st = check_cache(c);
+  if (st != SE_OK) return st;
+  if (!logits || !lse || !seq_len || !slot_pos || !acc || !evict_slot) return SE_ERR_NULL;
+  if (logit_cap <= 0 || logit_cap < c->capacity) return SE_ERR_SHAPE;
+  if (heavy_budget < 0 || recent_window < 0) return SE_ERR_BUDGET;
+  if (int64_t(heavy_budget) + recent_window + 1 > c->capacity) return SE_ERR_BUDGET;
+  if (cur_pos < 0) return SE_ERR_SHAPE;
+  SE_TRACE_CALL("h2o_accumulate_evict B=%d Hq=%d Hkv=%d cap=%d pos=%d heavy=%d recent=%d", c->batch,
+                c->n_q_heads, c->n_kv_heads, c->capacity, cur_pos, heavy_budget, recent_window);
+  return launch_h2o(*c, logits, lse, logit_cap, seq_len, slot_pos, acc, cur_pos, heavy_budget, recent_window,
+                    evict_slot, stream);
+}
+
+se_status se_omnikv_topk(const se_cache* c, const float* logits, const float* lse, int32_t logit_cap,
+                         const int32_t* seq_len, int32_t top_k, int32_t* view_idx,
+                         int32_t* view_len, float* scores, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  se_status st = check_cache(c);
+  if (st != SE_OK) return st;
+  if (!logits || !lse || !seq_len || !view_idx || !view_len) return SE_ERR_NULL;
+  if (logit_cap <= 0) return SE_ERR_SHAPE;
+  if (top_k < 1 || top_k > logit_cap) return SE_ERR_BUDGET;
+  const size_t need = omnikv_ws_bytes(*c, logit_cap, top_k);
+  if (need > 0 && (!ws || ws_bytes < need)) return SE_ERR_WORKSPACE;
+  SE_TRACE_CALL("omnikv_topk B=%d Hq=%d Hkv=%d cap=%d k=%d", c->batch, c->n_q_heads, c->n_kv_heads, logit_cap,
+                top_k);
+  return launch_omnikv(*c, logits, lse, logit_cap, seq_len, top_k, view_idx, view_len, scores, ws, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,212 @@
+// Split-K flash decode over an AttentionView: the vector-ALU kernel (any
+// element type, key width <= 576, value width <= 512, group <= 64) and the
+// split combine.  The bf16 GQA fast path (MFMA) lives in attn_mfma.hip.
+//
+// tokendh.com explainer, section "把边界划在'生命周期'上", and the ai-feeds
+// digest, section 方法 / 关键模块: every method's kept positions reach attention
+// through one view format, so one kernel serves all of them.  A view entry
+// names `gran` consecutive cache slots; slots past seq_len are skipped.
+#include "se_internal.hpp"
+#include "attn_common.hpp"
+
+namespace se {
+
+constexpr int VT = 16;  // slots per tile in the vector kernel
+
+template <typename T, int MAXR>
+__global__ __launch_bounds__(256) void attn_vector_kernel(AttnArgs a) {
+  extern __shared__ float smem[];
+  const int G = a.G, Dk = a.Dk, Dv = a.Dv;
+  float* qs = smem;                    // [G][Dk]
+  float* kt = qs + G * Dk;             // [VT][Dk]
+  float* vt = kt + VT * Dk;            // [VT][Dv] (unused for latent caches)
+  float* pt = vt + (a.latent ? 0 : VT * Dv);  // [G][VT]
+  float* ms = pt + G * VT;             // [G] running max
+  float* ls = ms + G;                  // [G] running sum
+  float* al = ls + G;                  // [G] rescale of this tile
+  int* tok = (int*)(al + G);           // [VT]
+
+  const int unit = blockIdx.y, split = blockIdx.x;
+  const int b = unit / a.Hkv, kvh = unit % a.Hkv;
+  const int n_slots = view_slot_count(a, unit, b);
+  const int chunk = (n_slots + a.splits - 1) / a.splits;
+  const int s0 = min(n_slots, split * chunk), s1 = min(n_slots, s0 + chunk);
+
+  const T* qg = (const T*)a.q + (size_t(b) * a.Hq + size_t(kvh) * G) * Dk;
+  for (int i = threadIdx.x; i < G * Dk; i += 256) qs[i] = to_f32(qg[i]);
+  for (int h = threadIdx.x; h < G; h += 256) { ms[h] = -INFINITY; ls[h] = 0.f; }
+  const int R = (G * Dv + 255) / 256;
+  float acc[MAXR];
+#pragma unroll
+  for (int r = 0; r < MAXR; ++r) acc[r] = 0.f;
+  const T* ku = (const T*)a.k + size_t(unit) * a.cap * a.k_stride;
+  const T* vu = a.latent ? ku : (const T*)a.v + size_t(unit) * a.cap * a.v_stride;
+  const int vstride = a.latent ? a.k_stride : a.v_stride;
+  __syncthreads();
+
+  for (int t0 = s0; t0 < s1; t0 += VT) {
+    const int nt = min(VT, s1 - t0);
+    if (threadIdx.x < VT) tok[threadIdx.x] = threadIdx.x < nt ? view_token(a, unit, b, t0 + threadIdx.x) : -1;
+    __syncthreads();
+    for (int i = threadIdx.x; i < VT * Dk; i += 256) {
+      const int j = i / Dk, d = i % Dk, t = tok[j];
+      kt[i] = t >= 0 ? to_f32(ku[size_t(t) * a.k_stride + d]) : 0.f;
+    }
+    if (!a.latent)
+      for (int i = threadIdx.x; i < VT * Dv; i += 256) {
+        const int j = i / Dv, d = i % Dv, t = tok[j];
+        vt[i] = t >= 0 ? to_f32(vu[size_t(t) * vstride + d]) : 0.f;
+      }
+    __syncthreads();
+    // logits of (slot j, head h)
+    for (int i = threadIdx.x; i < G * VT; i += 256) {
+      const int h = i / VT, j = i % VT;
+      float lg = -INFINITY;
+      if (tok[j] >= 0) {
+        float dot = 0.f;
+        for (int d = 0; d < Dk; ++d) dot += qs[h * Dk + d] * kt[j * Dk + d];
+        lg = dot * a.scale;
+      }
+      if (a.logits != nullptr && j < nt && t0 + j < a.logit_cap)
+        a.logits[(size_t(b) * a.Hq + size_t(kvh) * G + h) * a.logit_cap + t0 + j] = lg;
+      pt[i] = lg;
+    }
+    __syncthreads();
+    // online softmax bookkeeping, one thread per head
+    for (int h = threadIdx.x; h < G; h += 256) {
+      float mt = -INFINITY;
+      for (int j = 0; j < VT; ++j) mt = fmaxf(mt, pt[h * VT + j]);
+      const float mo = ms[h], mn = fmaxf(mo, mt);
+      float alpha = 1.f, sum = 0.f;
+      if (mn != -INFINITY) {
+        alpha = exp2f((mo - mn) * LOG2E);
+        for (int j = 0; j < VT; ++j) {
+          float p = exp2f((pt[h * VT + j] - mn) * LOG2E);
+          pt[h * VT + j] = p;
+          sum += p;
+        }
+      } else {
+        for (int j = 0; j < VT; ++j) pt[h * VT + j] = 0.f;
+      }
+      ms[h] = mn;
+      ls[h] = ls[h] * alpha + sum;
+      al[h] = alpha;
+    }
+    __syncthreads();
+    const float* vsrc = a.latent ? kt : vt;
+    const int vs = a.latent ? Dk : Dv;
+#pragma unroll
+    for (int r = 0; r < MAXR; ++r) {
+      const int pair = threadIdx.x + 256 * r;
+      if (r < R && pair < G * Dv) {
+        const int h = pair / Dv, d = pair % Dv;
+        float o = acc[r] * al[h];
+        for (int j = 0; j < VT; ++j) o += pt[h * VT + j] * vsrc[j * vs + d];
+        acc[r] = o;
+      }
+    }
+    __syncthreads();
+  }
+  // partial results of this split
+  float* pml = a.part_ml + (size_t(unit) * a.splits + split) * G * 2;
+  float* po = a.part_o + (size_t(unit) * a.splits + split) * G * Dv;
+  for (int h = threadIdx.x; h < G; h += 256) { pml[2 * h] = ms[h]; pml[2 * h + 1] = ls[h]; }
+#pragma unroll
+  for (int r = 0; r < MAXR; ++r) {
+    const int pair = threadIdx.x + 256 * r;
+    if (r < R && pair < G * Dv) po[pair] = acc[r];
+  }
+}
+
+// One block per (unit, head of the group): merge the split partials by log-sum-exp.
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  const int unit = blockIdx.y, h = blockIdx.x;
+  const int G = a.G, Dv = a.Dv, S = a.splits;
+  const int b = unit / a.Hkv, kvh = unit % a.Hkv;
+  const float* pml = a.part_ml + size_t(unit) * S * G * 2;
+  const float* po = a.part_o + size_t(unit) * S * G * Dv;
+  float m = -INFINITY;
+  for (int s = 0; s < S; ++s) m = fmaxf(m, pml[(s * G + h) * 2]);
+  float l = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float ms = pml[(s * G + h) * 2];
+    if (ms != -INFINITY) l += pml[(s * G + h) * 2 + 1] * exp2f((ms - m) * LOG2E);
+  }
+  const size_t row = size_t(b) * a.Hq + size_t(kvh) * G + h;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  for (int d = threadIdx.x; d < Dv; d += blockDim.x) {
+    float o = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const float ms = pml[(s * G + h) * 2];
+      if (ms != -INFINITY) o += po[(size_t(s) * G + h) * Dv + d] * exp2f((ms - m) * LOG2E);
+    }
+    a.out[row * Dv + d] = o * inv;
+  }
+  if (threadIdx.x == 0 && a.lse != nullptr) a.lse[row] = l > 0.f ? m + logf(l) : -INFINITY;
+}
+
+int attn_auto_splits(const se_cache& c, int slots) {
+  const int units = c.batch * c.n_kv_heads;
+  int s = ceil_div(1024, units);
+  s = std::max(1, std::min(s, ceil_div(slots, 64)));
+  return std::min(s, 256);
+}
+
+size_t attn_ws_bytes(const se_cache& c, int slots, int num_splits) {
+  const int S = num_splits > 0 ? num_splits : attn_auto_splits(c, slots);
+  const size_t units = size_t(c.batch) * c.n_kv_heads, G = c.n_q_heads / c.n_kv_heads;
+  return units * S * G * (2 + size_t(c.d_v)) * sizeof(float);
+}
+
+se_status launch_attn_vector(const AttnArgs& a, hipStream_t s) {
+  const int units = a.B * a.Hkv;
+  const size_t lds = (size_t(a.G) * a.Dk + VT * a.Dk + (a.latent ? 0 : VT * a.Dv) + a.G * VT + 3 * a.G) *
+                         sizeof(float) + VT * sizeof(int);
+  if (lds > 160 * 1024) return SE_ERR_UNSUPPORTED;
+  const int R = (a.G * a.Dv + 255) / 256;
+  dim3 grid(a.splits, units);
+#define SE_LAUNCH_VEC(TT, RR)                                                                       \
+  do {                                                                                            \
+    if (lds > 64 * 1024)                                                                          \
+      hipFuncSetAttribute((const void*)attn_vector_kernel<TT, RR>,                                \
+                          hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));                  \
+    hipLaunchKernelGGL((attn_vector_kernel<TT, RR>), grid, dim3(256), lds, s, a);                  \
+  } while (0)
+  if (a.dtype == SE_F32) {
+    if (R <= 4) SE_LAUNCH_VEC(float, 4);
+    else if (R <= 16) SE_LAUNCH_VEC(float, 16);
+    else if (R <= 64) SE_LAUNCH_VEC(float, 64);
+    else return SE_ERR_UNSUPPORTED;
+  } else {
+    if (R <= 4) SE_LAUNCH_VEC(bf16_t, 4);
+    else if (R <= 16) SE_LAUNCH_VEC(bf16_t, 16);
+    else if (R <= 64) SE_LAUNCH_VEC(bf16_t, 64);
+    else return SE_ERR_UNSUPPORTED;
+  }
+#undef SE_LAUNCH_VEC
+  return launch_status();
+}
+
+se_status launch_attn_combine(const AttnArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(a.G, a.B * a.Hkv), dim3(a.Dv >= 256 ? 256 : 128), 0, s, a);
+  return launch_status();
+}
+
+se_status launch_attn(const se_cache& c, const void* q, const void* k, const void* v,
+                      const int32_t* seq_len, const int32_t* view_idx, const int32_t* view_len,
+                      int view_cap, int granularity, float scale, float* out, float* lse,
+                      float* logits, int logit_cap, int num_splits, void* ws, hipStream_t s) {
+  AttnArgs a = make_attn_args(c, q, k, v, seq_len, view_idx, view_len, view_cap, granularity, scale, out,
+                              lse, logits, logit_cap);
+  const int slots = view_idx ? view_cap * granularity : c.capacity;
+  a.splits = num_splits > 0 ? num_splits : attn_auto_splits(c, slots);
+  a.part_ml = (float*)ws;
+  a.part_o = a.part_ml + size_t(a.B) * a.Hkv * a.splits * a.G * 2;
+  se_status st = SE_ERR_UNSUPPORTED;
+  if (attn_mfma_supported(a)) st = launch_attn_mfma(a, s);
+  if (st == SE_ERR_UNSUPPORTED) st = launch_attn_vector(a, s);
+  if (st != SE_OK) return st;
+  return launch_attn_combine(a, s);
+}
+
+}  // namespace se

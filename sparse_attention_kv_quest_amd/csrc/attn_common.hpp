@@ -1,0 +1,58 @@
+// Shared description of one attention launch and the view -> slot mapping.
+#pragma once
+#include "se_internal.hpp"
+
+namespace se {
+
+constexpr float LOG2E = 1.4426950408889634f;
+
+struct AttnArgs {
+  const void* q; const void* k; const void* v;
+  const int32_t* seq_len; const int32_t* view_idx; const int32_t* view_len;
+  float* out; float* lse; float* logits;
+  float* part_ml;   // [units][splits][G][2]: running max, running sum
+  float* part_o;    // [units][splits][G][Dv]: unnormalised output
+  float scale;
+  int B, Hq, Hkv, G, Dk, Dv, cap, latent, dtype;
+  int k_stride, v_stride;  // elements per K / V row
+  int view_cap, gran, logit_cap, splits;
+};
+
+// Number of view slots of a unit: view entries times granularity, or seq_len for the identity view.
+__device__ __forceinline__ int view_slot_count(const AttnArgs& a, int unit, int b) {
+  if (a.view_idx == nullptr) return min(a.seq_len[b], a.cap);
+  return min(a.view_len[unit], a.view_cap) * a.gran;
+}
+
+// Cache slot read by view slot `s` of a unit, or -1 if it holds no valid token.
+__device__ __forceinline__ int view_token(const AttnArgs& a, int unit, int b, int s) {
+  const int len = min(a.seq_len[b], a.cap);
+  if (a.view_idx == nullptr) return s < len ? s : -1;
+  const int e = s / a.gran, o = s - e * a.gran;
+  const int page = a.view_idx[size_t(unit) * a.view_cap + e];
+  if (page < 0) return -1;
+  const int64_t t = int64_t(page) * a.gran + o;
+  return t < len ? int(t) : -1;
+}
+
+inline AttnArgs make_attn_args(const se_cache& c, const void* q, const void* k, const void* v,
+                               const int32_t* seq_len, const int32_t* view_idx, const int32_t* view_len,
+                               int view_cap, int gran, float scale, float* out, float* lse, float* logits,
+                               int logit_cap) {
+  AttnArgs a{};
+  a.q = q; a.k = k; a.v = c.latent ? k : v;
+  a.seq_len = seq_len; a.view_idx = view_idx; a.view_len = view_len;
+  a.out = out; a.lse = lse; a.logits = logits;
+  a.scale = scale;
+  a.B = c.batch; a.Hq = c.n_q_heads; a.Hkv = c.n_kv_heads; a.G = c.n_q_heads / c.n_kv_heads;
+  a.Dk = c.d_k; a.Dv = c.d_v; a.cap = c.capacity; a.latent = c.latent; a.dtype = c.dtype;
+  a.k_stride = c.d_k; a.v_stride = c.latent ? c.d_k : c.d_v;
+  a.view_cap = view_idx ? view_cap : 0; a.gran = view_idx ? gran : 1;
+  a.logit_cap = logits ? logit_cap : 0;
+  return a;
+}
+
+bool attn_mfma_supported(const AttnArgs& a);
+se_status launch_attn_mfma(const AttnArgs& a, hipStream_t s);
+
+}  // namespace se

@@ -45,11 +45,12 @@ def rng_for(*words: int) -> np.random.Generator:
 
 
 def quantize_(x: np.ndarray) -> np.ndarray:
-    """In place: x -> clip(round(32 x), -255, 255) / 32 (float32, exact)."""
+    """In place: x -> clip(round(32 x), -255, 255) / 32 (float32, exact, no negative zero)."""
     np.multiply(x, GRID, out=x)
     np.rint(x, out=x)
     np.clip(x, -CLIP, CLIP, out=x)
     np.multiply(x, 1.0 / GRID, out=x)
+    np.add(x, 0.0, out=x)          # -0.0 -> +0.0
     return x
 
 
