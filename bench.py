@@ -38,6 +38,7 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--splits", type=int, default=0, help="split-K factor of the attention (0 = library choice)")
     return ap.parse_args()
 
 
@@ -92,7 +93,7 @@ def main():
     layers = [Layer(se, cfg, c, K0, V0, 977 * i, torch) for i in range(args.layers)]
     del K0, V0
     ws_q = se.workspace(se.SE_OP_QUEST, c, P, k)
-    ws_a = se.workspace(se.SE_OP_ATTN, c, k * P, 0)
+    ws_a = se.workspace(se.SE_OP_ATTN, c, k * P, args.splits)
     lse = torch.empty((B, Hq), device="cuda")
     torch.cuda.synchronize()
     log(f"caches ready in {time.time() - t0:.1f}s")
@@ -102,11 +103,11 @@ def main():
         se.se_page_meta_update(c, L.k, L.kmin, L.kmax, L.seq, P, -1)
         se.se_quest_select(c, q, L.kmin, L.kmax, L.seq, P, k, L.view, L.vlen, None, ws_q)
         se.se_sparse_decode_attn(c, q, L.k, L.v, L.seq, L.view, L.vlen, k, P, cfg.softmax_scale, L.out, lse,
-                                 ws=ws_a)
+                                 num_splits=args.splits, ws=ws_a)
 
     def attn_only(L):
         se.se_sparse_decode_attn(c, q, L.k, L.v, L.seq, L.view, L.vlen, k, P, cfg.softmax_scale, L.out, lse,
-                                 ws=ws_a)
+                                 num_splits=args.splits, ws=ws_a)
 
     nL = args.layers
     use_graph = not args.no_graph
@@ -188,7 +189,7 @@ def main():
         "dtype": "bf16", "data": "synthetic (seeded grid-quantised N(0,1), 8 planted pages per KV head)",
         "config": {"workload": "quest_32k", "batch": B, "q_heads": Hq, "kv_heads": H, "head_dim": D,
                    "context": cfg.context, "page_size": P, "top_pages": k, "layers_rotated": nL,
-                   "graph": use_graph},
+                   "graph": use_graph, "attn_splits": args.splits},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "se_sparse_decode_attn (split-K main + combine)", "us_per_launch": round(us_attn, 3),

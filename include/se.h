@@ -136,7 +136,8 @@ se_status se_quest_select(const se_cache* c, const void* q, const void* kmin, co
  *   scaled logit of view slot i (entry * g + offset) at index i, -inf where the
  *   slot holds no valid token (indices >= view_cap * g are not written).
  *   num_splits: 0 chooses the split-K factor; otherwise the number of chunks
- *   each unit's view is cut into (results agree to rounding for any value).
+ *   (1..256) each unit's view is cut into (results agree to rounding for any
+ *   value).
  *   ws: se_workspace_bytes(SE_OP_ATTN, c, view_cap * g, num_splits) bytes. */
 se_status se_sparse_decode_attn(const se_cache* c, const void* q, const void* k, const void* v,
                                 const int32_t* seq_len, const int32_t* view_idx,

@@ -132,7 +132,7 @@ se_status se_sparse_decode_attn(const se_cache* c, const void* q, const void* k,
     if (int64_t(view_cap) * granularity > (int64_t(1) << 30)) return SE_ERR_SHAPE;
   }
   if (logits && logit_cap <= 0) return SE_ERR_SHAPE;
-  if (num_splits < 0 || num_splits > 4096) return SE_ERR_SHAPE;
+  if (num_splits < 0 || num_splits > 256) return SE_ERR_SHAPE;
   if (!(scale > 0.f) || !(scale < 1e30f)) return SE_ERR_SHAPE;
   const int slots = view_idx ? view_cap * granularity : c->capacity;
   const size_t need = attn_ws_bytes(*c, slots, num_splits);

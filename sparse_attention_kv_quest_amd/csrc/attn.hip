@@ -118,38 +118,59 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(AttnArgs a) {
   }
 }
 
-// One block per (unit, head of the group): merge the split partials by log-sum-exp.
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+// One block per (head of the group, unit): merge the split partials by log-sum-exp.
+// The per-split weights exp(m_s - M) are formed once in LDS; the output pass then
+// streams the partial outputs with independent loads.
+constexpr int COMBINE_MAX_SPLITS = 256;
+
+__global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
+  __shared__ float f_s[COMBINE_MAX_SPLITS];
+  __shared__ float red[2];
   const int unit = blockIdx.y, h = blockIdx.x;
   const int G = a.G, Dv = a.Dv, S = a.splits;
   const int b = unit / a.Hkv, kvh = unit % a.Hkv;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const float* pml = a.part_ml + size_t(unit) * S * G * 2;
   const float* po = a.part_o + size_t(unit) * S * G * Dv;
-  float m = -INFINITY;
-  for (int s = 0; s < S; ++s) m = fmaxf(m, pml[(s * G + h) * 2]);
-  float l = 0.f;
-  for (int s = 0; s < S; ++s) {
+  float mloc = -INFINITY;
+  for (int s = threadIdx.x; s < S; s += 128) {
     const float ms = pml[(s * G + h) * 2];
-    if (ms != -INFINITY) l += pml[(s * G + h) * 2 + 1] * exp2f((ms - m) * LOG2E);
+    f_s[s] = ms;
+    mloc = fmaxf(mloc, ms);
   }
+  mloc = wave_max(mloc);
+  if (lane == 0) red[w] = mloc;
+  __syncthreads();
+  const float M = fmaxf(red[0], red[1]);
+  __syncthreads();
+  float lloc = 0.f;
+  for (int s = threadIdx.x; s < S; s += 128) {
+    const float ms = f_s[s];
+    const float f = (ms != -INFINITY) ? exp2f((ms - M) * LOG2E) : 0.f;
+    f_s[s] = f;
+    lloc += f * pml[(s * G + h) * 2 + 1];
+  }
+  lloc = wave_sum(lloc);
+  if (lane == 0) red[w] = lloc;
+  __syncthreads();
+  const float L = red[0] + red[1];
   const size_t row = size_t(b) * a.Hq + size_t(kvh) * G + h;
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  for (int d = threadIdx.x; d < Dv; d += blockDim.x) {
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  for (int d = threadIdx.x; d < Dv; d += 128) {
     float o = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float ms = pml[(s * G + h) * 2];
-      if (ms != -INFINITY) o += po[(size_t(s) * G + h) * Dv + d] * exp2f((ms - m) * LOG2E);
-    }
+#pragma unroll 8
+    for (int s = 0; s < S; ++s) o += f_s[s] * po[(size_t(s) * G + h) * Dv + d];
     a.out[row * Dv + d] = o * inv;
   }
-  if (threadIdx.x == 0 && a.lse != nullptr) a.lse[row] = l > 0.f ? m + logf(l) : -INFINITY;
+  if (threadIdx.x == 0 && a.lse != nullptr) a.lse[row] = L > 0.f ? M + logf(L) : -INFINITY;
 }
 
 int attn_auto_splits(const se_cache& c, int slots) {
   const int units = c.batch * c.n_kv_heads;
+  if (attn_mfma_eligible(c)) return attn_mfma_auto_splits(units, slots);
   int s = ceil_div(1024, units);
   s = std::max(1, std::min(s, ceil_div(slots, 64)));
-  return std::min(s, 256);
+  return std::min(s, COMBINE_MAX_SPLITS);
 }
 
 size_t attn_ws_bytes(const se_cache& c, int slots, int num_splits) {
@@ -188,7 +209,7 @@ se_status launch_attn_vector(const AttnArgs& a, hipStream_t s) {
 }
 
 se_status launch_attn_combine(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(a.G, a.B * a.Hkv), dim3(a.Dv >= 256 ? 256 : 128), 0, s, a);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(a.G, a.B * a.Hkv), dim3(128), 0, s, a);
   return launch_status();
 }
 

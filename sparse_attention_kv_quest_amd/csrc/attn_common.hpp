@@ -15,7 +15,7 @@ struct AttnArgs {
   float scale;
   int B, Hq, Hkv, G, Dk, Dv, cap, latent, dtype;
   int k_stride, v_stride;  // elements per K / V row
-  int view_cap, gran, logit_cap, splits;
+  int view_cap, gran, gshift, logit_cap, splits;   // gshift = log2(gran) or -1
 };
 
 // Number of view slots of a unit: view entries times granularity, or seq_len for the identity view.
@@ -48,11 +48,20 @@ inline AttnArgs make_attn_args(const se_cache& c, const void* q, const void* k, 
   a.Dk = c.d_k; a.Dv = c.d_v; a.cap = c.capacity; a.latent = c.latent; a.dtype = c.dtype;
   a.k_stride = c.d_k; a.v_stride = c.latent ? c.d_k : c.d_v;
   a.view_cap = view_idx ? view_cap : 0; a.gran = view_idx ? gran : 1;
+  a.gshift = -1;
+  for (int sh = 0; sh < 31; ++sh)
+    if ((1 << sh) == a.gran) { a.gshift = sh; break; }
   a.logit_cap = logits ? logit_cap : 0;
   return a;
 }
 
 bool attn_mfma_supported(const AttnArgs& a);
+int attn_mfma_auto_splits(int units, int slots);
 se_status launch_attn_mfma(const AttnArgs& a, hipStream_t s);
+
+inline bool attn_mfma_eligible(const se_cache& c) {
+  return c.dtype == SE_BF16 && !c.latent && (c.d_k == 128 || c.d_k == 64) && c.d_v == c.d_k &&
+         c.n_q_heads / c.n_kv_heads <= 16;
+}
 
 }  // namespace se

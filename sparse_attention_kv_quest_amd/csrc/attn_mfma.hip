@@ -1,9 +1,385 @@
-// bf16 GQA decode attention on MFMA (placeholder until the kernel lands).
+// bf16 GQA split-K decode attention on MFMA (gfx950, v_mfma_f32_16x16x32_bf16).
+//
+// The G query heads of a KV head share every K/V row they read, so both
+// products of decode attention are small dense contractions:
+//   S^T[token][head] = K[token][:] . Q[head][:]      (A = K rows, B = Q^T)
+//   O^T[dim][head]  += V^T[dim][token] . P^T[token][head]
+// Heads are padded to 16 columns.  K rows go straight from HBM into the MFMA
+// A-operand registers (per load instruction, 16 rows x 64 contiguous bytes);
+// V rows are transposed through a wave-private LDS tile so that every lane
+// holds eight tokens of one dimension.  Softmax runs in fp32; P enters the
+// second product as a bf16 hi + lo pair, so the rounding of P costs ~2^-17
+// relative.
+//
+// Work split: a block of 4 waves owns a contiguous chunk of one unit's view
+// slots (split-K).  Each wave walks every fourth 32-slot tile of the chunk
+// with the next tile's K/V loads in flight while it computes the current one
+// (registers double-buffered: two waves per SIMD for d 128, or one wave per
+// SIMD with two tiles in flight), so HBM sees a continuous stream.  The view
+// entries of the chunk are cached in LDS first, so a token lookup never waits
+// on the loads in flight.  The running max of a head is
+// only moved (and the output rescaled) when a tile's max exceeds it by more
+// than 2^8, which keeps the accumulators untouched on almost every tile; the
+// shift cancels in the final normalisation.  The four waves merge their
+// (max, sum, output) in LDS and the block writes one partial; the combine
+// kernel merges the splits.
 #include "attn_common.hpp"
+#include "mfma_util.hpp"
 
 namespace se {
 
-bool attn_mfma_supported(const AttnArgs&) { return false; }
-se_status launch_attn_mfma(const AttnArgs&, hipStream_t) { return SE_ERR_UNSUPPORTED; }
+constexpr int MF_TS = 32;         // view slots per wave tile
+constexpr int MF_WAVES = 4;
+constexpr int MF_VCACHE = 2048;   // view entries cached in LDS per block
+constexpr float MF_RESCALE_MARGIN = 8.f;   // log2 units
+
+template <int D>
+struct MfTile {
+  u32x4 k0[D / 32], k1[D / 32];   // K rows of slots base + c16 and base + 16 + c16
+  u32x4 v[D / 64][4];             // V rows of slots base + 4 (lane & 7) + r, 8-dim chunks
+  int tk0, tk1;
+};
+
+struct MfCtx {
+  const uint16_t* ku;
+  const uint16_t* vu;
+  const int32_t* vglob;  // view entries in global memory (used when they do not fit the LDS cache)
+  int e0, len, s1, gshift;
+  bool identity;
+};
+
+__shared__ int32_t mf_vcache[MF_VCACHE];
+
+// Cache slot read by view slot s, or -1 (power-of-two granularity 1 << gshift).
+// VC: the view entries come from the LDS cache.
+template <bool VC>
+__device__ __forceinline__ int mf_token(const MfCtx& x, int s) {
+  int t;
+  if (x.identity) {
+    t = s;
+  } else {
+    const int e = s >> x.gshift;
+    const int page = (s < x.s1) ? (VC ? mf_vcache[e - x.e0] : x.vglob[e]) : -1;
+    t = page < 0 ? -1 : (page << x.gshift) + (s & ((1 << x.gshift) - 1));
+  }
+  return (s < x.s1 && t >= 0 && t < x.len) ? t : -1;
+}
+
+template <int D, bool VC>
+__device__ __forceinline__ void mf_load(const MfCtx& x, int base, int lane, MfTile<D>& T) {
+  constexpr int NKS = D / 32, VPASS = D / 64;
+  const int g = lane >> 4, c16 = lane & 15, qa = lane & 7;
+  T.tk0 = mf_token<VC>(x, base + c16);
+  T.tk1 = mf_token<VC>(x, base + 16 + c16);
+  int vtok[4];
+  const int sq = base + 4 * qa;
+  if (x.identity || x.gshift >= 2) {   // a 4-aligned slot quad stays inside one view entry
+    const int t0 = mf_token<VC>(x, sq);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vtok[r] = (t0 >= 0 && sq + r < x.s1 && t0 + r < x.len) ? t0 + r : -1;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vtok[r] = mf_token<VC>(x, sq + r);
+  }
+  // Loads are unconditional: a slot without a token reads the unit's row 0, which is
+  // finite data; its K is masked through the logits and its weight p is 0.  Keeping
+  // the loads unconditional keeps the compiler's wait counters exact across the
+  // prefetch.  Offsets stay 32-bit within the unit.
+  const uint32_t r0 = uint32_t(max(T.tk0, 0)) * D + 8 * g, r1 = uint32_t(max(T.tk1, 0)) * D + 8 * g;
+#pragma unroll
+  for (int c = 0; c < NKS; ++c) {
+    T.k0[c] = ld16(x.ku + r0 + 32 * c);
+    T.k1[c] = ld16(x.ku + r1 + 32 * c);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t rv = uint32_t(max(vtok[r], 0)) * D + 8 * (lane >> 3);
+#pragma unroll
+    for (int p = 0; p < VPASS; ++p) T.v[p][r] = ld16(x.vu + rv + 64 * p);
+  }
+}
+
+template <int D>
+struct MfState {
+  f32x4 o[D / 16];
+  float m2, lsum;
+};
+
+template <int D>
+__device__ __forceinline__ void mf_compute(const AttnArgs& a, const MfCtx& x, int base, int lane, const u32x4* qv,
+                                           float sc2, float* lg_row, uint16_t* vt, const MfTile<D>& T,
+                                           MfState<D>& st) {
+  constexpr int NKS = D / 32, NDB = D / 16, VPASS = D / 64, PITCH = MF_TS + 4;
+  const int g = lane >> 4, c16 = lane & 15, qa = lane & 7;
+  // ---- S^T = K Q^T for the two 16-slot blocks
+  f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < NKS; ++c) {
+    sa = mfma_bf16_16x16x32(T.k0[c], qv[c], sa);
+    sb = mfma_bf16_16x16x32(T.k1[c], qv[c], sb);
+  }
+  const uint64_t va = __ballot(T.tk0 >= 0), vb = __ballot(T.tk1 >= 0);
+  float sv[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool oka = (va >> (4 * g + i)) & 1, okb = (vb >> (4 * g + i)) & 1;
+    sv[i] = oka ? sa[i] * sc2 : -INFINITY;
+    sv[4 + i] = okb ? sb[i] * sc2 : -INFINITY;
+  }
+  if (lg_row != nullptr) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool oka = (va >> (4 * g + i)) & 1, okb = (vb >> (4 * g + i)) & 1;
+      const int sla = base + 4 * g + i, slb = base + 16 + 4 * g + i;
+      if (sla < x.s1 && sla < a.logit_cap) lg_row[sla] = oka ? sa[i] * a.scale : -INFINITY;
+      if (slb < x.s1 && slb < a.logit_cap) lg_row[slb] = okb ? sb[i] * a.scale : -INFINITY;
+    }
+  }
+  // ---- online softmax; head c16 lives in lanes c16, c16+16, c16+32, c16+48
+  float tmax = sv[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, sv[i]);
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+  // move the running max only when this tile exceeds it by more than the margin
+  const bool grow = tmax > st.m2 + MF_RESCALE_MARGIN;
+  if (__ballot(grow) != 0) {
+    const float mnew = grow ? tmax : st.m2;
+    const float alpha = (grow && st.m2 != -INFINITY) ? exp2f(st.m2 - mnew) : 1.f;
+    st.lsum *= alpha;
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) st.o[i] *= alpha;
+    st.m2 = mnew;
+  }
+  // while no valid slot has been seen the max stays -inf and every logit is -inf
+  const float mref = st.m2 == -INFINITY ? 0.f : st.m2;
+  float p[8];
+  float psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    p[i] = exp2f(sv[i] - mref);   // 0 for masked slots; at most 2^8 otherwise
+    psum += p[i];
+  }
+  st.lsum += psum;
+  // P as the B operand, split into bf16 hi + lo
+  u32x4 ph, pl;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t h = pack_bf16(p[2 * j], p[2 * j + 1]);
+    ph[j] = h;
+    pl[j] = pack_bf16(p[2 * j] - bf16x2_lo_f32(h), p[2 * j + 1] - bf16x2_hi_f32(h));
+  }
+  // ---- V quads -> transposed LDS tile: row = dim, 32 tokens per row
+#pragma unroll
+  for (int pp = 0; pp < VPASS; ++pp) {
+    const int ch = (lane >> 3) + 8 * pp;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t w0 = T.v[pp][0][m], w1 = T.v[pp][1][m], w2 = T.v[pp][2][m], w3 = T.v[pp][3][m];
+      uint2 lo, hi;
+      lo.x = lo16_pair(w0, w1);
+      lo.y = lo16_pair(w2, w3);
+      hi.x = hi16_pair(w0, w1);
+      hi.y = hi16_pair(w2, w3);
+      *reinterpret_cast<uint2*>(vt + (8 * ch + 2 * m) * PITCH + 4 * qa) = lo;
+      *reinterpret_cast<uint2*>(vt + (8 * ch + 2 * m + 1) * PITCH + 4 * qa) = hi;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // ---- O^T += V^T P^T
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const uint16_t* row = vt + (16 * db + c16) * PITCH;
+    const uint2 x0 = *reinterpret_cast<const uint2*>(row + 4 * g);
+    const uint2 x1 = *reinterpret_cast<const uint2*>(row + 16 + 4 * g);
+    const u32x4 av = {x0.x, x0.y, x1.x, x1.y};
+    st.o[db] = mfma_bf16_16x16x32(av, ph, st.o[db]);
+    st.o[db] = mfma_bf16_16x16x32(av, pl, st.o[db]);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int D, bool VC, int OCC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void attn_mfma_kernel(AttnArgs a) {
+  constexpr int PITCH = MF_TS + 4;          // u16 per transposed V row (72 bytes)
+  constexpr int NDB = D / 16;
+  constexpr int NKS = D / 32;
+  static_assert(D == 64 || D == 128, "head width");
+  __shared__ __align__(16) uint16_t vt_lds[MF_WAVES][D * PITCH];
+  __shared__ float red_m[MF_WAVES][16], red_l[MF_WAVES][16];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int unit = blockIdx.y, split = blockIdx.x;
+  const int b = unit / a.Hkv, kvh = unit % a.Hkv;
+  const int G = a.G;
+  // A page / token view is chunked by its capacity, so the block can fetch its view
+  // entries right away; slots past the view's length are masked.  The identity view
+  // is chunked by seq_len.
+  const bool identity = a.view_idx == nullptr;
+  const int len = min(a.seq_len[b], a.cap);
+  const int n_slots = identity ? len : a.view_cap * a.gran;
+  const int s_valid = identity ? len : min(a.view_len[unit], a.view_cap) * a.gran;
+  int chunk = (n_slots + a.splits - 1) / a.splits;
+  chunk = (chunk + MF_TS - 1) / MF_TS * MF_TS;
+  const int s0 = min(n_slots, split * chunk), s1 = min(n_slots, s0 + chunk);
+
+  MfCtx x;
+  x.ku = (const uint16_t*)a.k + size_t(unit) * a.cap * D;
+  x.vu = (const uint16_t*)a.v + size_t(unit) * a.cap * D;
+  x.len = len;
+  x.s1 = min(s1, s_valid);
+  x.gshift = a.gshift;
+  x.identity = identity;
+  x.e0 = 0;
+  x.vglob = nullptr;
+  if (!x.identity) {
+    const int32_t* vrow = a.view_idx + size_t(unit) * a.view_cap;
+    x.vglob = vrow;
+    if (VC) {
+      const int e0 = s0 >> a.gshift, e1 = s1 > s0 ? ((s1 - 1) >> a.gshift) + 1 : e0;
+      for (int e = e0 + threadIdx.x; e < e1; e += 256) mf_vcache[e - e0] = vrow[e];
+      x.e0 = e0;
+    }
+  }
+
+  // Q as the B operand: lane holds head c16, dims 32c + 8g .. 32c + 8g + 7 of k-step c
+  u32x4 qv[NKS];
+  if (c16 < G) {
+    const uint16_t* qp = (const uint16_t*)a.q + (size_t(b) * a.Hq + size_t(kvh) * G + c16) * D + 8 * g;
+#pragma unroll
+    for (int c = 0; c < NKS; ++c) qv[c] = ld16(qp + 32 * c);
+  } else {
+#pragma unroll
+    for (int c = 0; c < NKS; ++c) qv[c] = u32x4{0, 0, 0, 0};
+  }
+  __syncthreads();   // view cache ready
+
+  const float sc2 = a.scale * LOG2E;
+  MfState<D> st;
+  st.m2 = -INFINITY;
+  st.lsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) st.o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint16_t* vt = vt_lds[w];
+  float* lg_row = (a.logits != nullptr && c16 < G)
+                      ? a.logits + (size_t(b) * a.Hq + size_t(kvh) * G + c16) * a.logit_cap
+                      : nullptr;
+
+  // This wave's tiles are w, w + 4, ...  The prefetch of the next tile is issued
+  // unconditionally (a tile past the chunk has no tokens and reads row 0), so the
+  // loop body is straight-line code and the compiler keeps exact wait counts:
+  // computing tile i waits only for tile i's loads, not for tile i + 1's.
+  const int ntiles = (s1 - s0 + MF_TS - 1) / MF_TS;
+  const int nmine = w < ntiles ? (ntiles - w + MF_WAVES - 1) / MF_WAVES : 0;
+  constexpr int STEP = MF_WAVES * MF_TS;   // slots between this wave's consecutive tiles
+  if (OCC == 1) {
+    MfTile<D> T0, T1, T2;                  // two tiles in flight while a third is computed
+    if (nmine > 0) {
+      const int first = s0 + w * MF_TS;
+      mf_load<D, VC>(x, first, lane, T0);
+      mf_load<D, VC>(x, first + STEP, lane, T1);
+      for (int i = 0; i < nmine; i += 3) {
+        const int b0 = first + i * STEP;
+        mf_load<D, VC>(x, b0 + 2 * STEP, lane, T2);
+        mf_compute<D>(a, x, b0, lane, qv, sc2, lg_row, vt, T0, st);
+        if (i + 1 >= nmine) break;
+        mf_load<D, VC>(x, b0 + 3 * STEP, lane, T0);
+        mf_compute<D>(a, x, b0 + STEP, lane, qv, sc2, lg_row, vt, T1, st);
+        if (i + 2 >= nmine) break;
+        mf_load<D, VC>(x, b0 + 4 * STEP, lane, T1);
+        mf_compute<D>(a, x, b0 + 2 * STEP, lane, qv, sc2, lg_row, vt, T2, st);
+      }
+    }
+  } else {
+    MfTile<D> T0, T1;                      // one tile in flight while the other is computed
+    if (nmine > 0) {
+      const int first = s0 + w * MF_TS;
+      mf_load<D, VC>(x, first, lane, T0);
+      for (int i = 0; i < nmine; i += 2) {
+        const int b0 = first + i * STEP;
+        mf_load<D, VC>(x, b0 + STEP, lane, T1);
+        mf_compute<D>(a, x, b0, lane, qv, sc2, lg_row, vt, T0, st);
+        if (i + 1 >= nmine) break;
+        mf_load<D, VC>(x, b0 + 2 * STEP, lane, T0);
+        mf_compute<D>(a, x, b0 + STEP, lane, qv, sc2, lg_row, vt, T1, st);
+      }
+    }
+  }
+
+  // ---- merge the four waves of the block
+  float lsum = st.lsum;
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  __syncthreads();
+  float* red_o = reinterpret_cast<float*>(&vt_lds[0][0]);   // [MF_WAVES][D][16] fp32 (fits in the V tiles)
+  static_assert(MF_WAVES * D * 16 * sizeof(float) <= sizeof(vt_lds), "reduction buffer");
+  if (g == 0) { red_m[w][c16] = st.m2; red_l[w][c16] = lsum; }
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red_o[(w * D + 16 * db + 4 * g + i) * 16 + c16] = st.o[db][i];
+  __syncthreads();
+  float* pml = a.part_ml + (size_t(unit) * a.splits + split) * G * 2;
+  float* po = a.part_o + (size_t(unit) * a.splits + split) * G * D;
+  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    const int h = idx / D, d = idx % D;
+    float M = red_m[0][h];
+#pragma unroll
+    for (int ww = 1; ww < MF_WAVES; ++ww) M = fmaxf(M, red_m[ww][h]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int ww = 0; ww < MF_WAVES; ++ww) {
+        const float mw = red_m[ww][h];
+        if (mw != -INFINITY) {
+          const float f = exp2f(mw - M);
+          L += f * red_l[ww][h];
+          O += f * red_o[(ww * D + d) * 16 + h];
+        }
+      }
+    }
+    po[h * D + d] = O;
+    if (d == 0) {
+      pml[2 * h] = M == -INFINITY ? -INFINITY : M * 0.6931471805599453f;
+      pml[2 * h + 1] = L;
+    }
+  }
+}
+
+bool attn_mfma_supported(const AttnArgs& a) {
+  return a.dtype == SE_BF16 && !a.latent && (a.Dk == 128 || a.Dk == 64) && a.Dv == a.Dk && a.G <= 16 &&
+         (a.view_idx == nullptr || a.gshift >= 0) && a.cap <= (1 << 30) / a.Dk;
+}
+
+// One block per CU when the units alone do not fill the chip.
+int attn_mfma_auto_splits(int units, int slots) {
+  const int target_blocks = 256;
+  int s = (target_blocks + units - 1) / units;
+  s = std::max(1, std::min(s, (slots + 4 * MF_TS - 1) / (4 * MF_TS)));
+  return std::min(s, 256);
+}
+
+se_status launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
+  dim3 grid(a.splits, a.B * a.Hkv);
+  // entries one block reads: its chunk of slots divided by the granularity (+2 for straddled entries)
+  const int slots = a.view_idx ? a.view_cap * a.gran : 0;
+  int chunk = (slots + a.splits - 1) / a.splits;
+  chunk = (chunk + MF_TS - 1) / MF_TS * MF_TS;
+  const bool vc = a.view_idx != nullptr && chunk / a.gran + 2 <= MF_VCACHE;
+#define SE_MF_LAUNCH(DD, VV, OO) hipLaunchKernelGGL((attn_mfma_kernel<DD, VV, OO>), grid, dim3(256), 0, s, a)
+  if (a.Dk == 128) {
+    if (vc) SE_MF_LAUNCH(128, true, 2); else SE_MF_LAUNCH(128, false, 2);
+  } else {
+    if (vc) SE_MF_LAUNCH(64, true, 1); else SE_MF_LAUNCH(64, false, 1);
+  }
+#undef SE_MF_LAUNCH
+  return launch_status();
+}
 
 }  // namespace se

@@ -7,15 +7,20 @@
 // q+ = max(q, 0), q- = min(q, 0); a KV head's page score is the max over the
 // heads of its group.  The view is the top pages (ties to the lower page),
 // in ascending page order.
+//
+// bf16 caches score on MFMA: the bound of every (page, head) pair is one dense
+// contraction S^T = [max | min] . [q+ | q-]^T over 2 d_k terms, whose partial
+// sums are exact in fp32 for the grid-valued inputs the tests use.  fp32 caches
+// use the vector kernel.
 #include "se_internal.hpp"
+#include "mfma_util.hpp"
 
 namespace se {
 
-constexpr int QUEST_TOPK_LDS = 8192;  // page scores held in LDS by the top-k kernel
+constexpr int QUEST_TOPK_LDS = 8192;  // page scores held in LDS by the block top-k kernel
 
-// ------------------------------------------------------------------ vector scoring (any dtype / width)
+// ------------------------------------------------------------------ vector scoring (fp32 / fallback)
 // grid: (page blocks, units); block 256 threads = PPB pages x G heads (G <= 64).
-// q of the group is staged in LDS as fp32 split into q+ and q-.
 template <typename T>
 __global__ __launch_bounds__(256) void quest_score_vector_kernel(
     const T* __restrict__ q, const T* __restrict__ kmin, const T* __restrict__ kmax,
@@ -57,16 +62,103 @@ __global__ __launch_bounds__(256) void quest_score_vector_kernel(
   }
 }
 
+// ------------------------------------------------------------------ MFMA scoring (bf16)
+// grid: (page groups, units); 4 waves, each scoring BPW blocks of 16 pages.  Every
+// metadata load of a wave is issued up front, before q is staged in LDS.
+// A operand of k-step s: lane (g, c) reads dims 32s + 8g .. 32s + 8g + 7 of page c.s max (then min) row;
+// B operand: q+ (then q-) of head c (+16 per head block), the same dims, staged in
+// LDS in lane order.  Result lane (g, c): pages 4g..4g+3, head c.
+template <int D, int HB, int BPW>
+__global__ __launch_bounds__(256) void quest_score_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kmin, const uint16_t* __restrict__ kmax,
+    const int32_t* __restrict__ seq_len, float* __restrict__ score, int Hkv, int G, int P, int ncp, int cap) {
+  constexpr int NKS = D / 32;
+  __shared__ u32x4 qb[2 * NKS][HB][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
+  const int unit = blockIdx.y, b = unit / Hkv, kvh = unit % Hkv;
+  const int npages = min((min(seq_len[b], cap) + P - 1) / P, ncp);
+  // issue the metadata loads of every block first: they do not depend on q
+  u32x4 amx[BPW][NKS], amn[BPW][NKS];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    // unconditional loads (pages past the last valid one read page 0; their scores are
+    // masked below) keep the wait counters exact
+    const int pg = ((blockIdx.x * 4 + w) * BPW + i) * 16 + c16;
+    const bool ok = pg < npages;
+    const uint16_t* mxp = kmax + (size_t(unit) * ncp + (ok ? pg : 0)) * D + 8 * g;
+    const uint16_t* mnp = kmin + (size_t(unit) * ncp + (ok ? pg : 0)) * D + 8 * g;
+#pragma unroll
+    for (int c = 0; c < NKS; ++c) {
+      amx[i][c] = ld16(mxp + 32 * c);
+      amn[i][c] = ld16(mnp + 32 * c);
+    }
+  }
+  const uint16_t* qg = q + (size_t(b) * Hkv * G + size_t(kvh) * G) * D;
+  for (int idx = threadIdx.x; idx < 2 * NKS * HB * 64; idx += 256) {
+    const int ln = idx & 63, hb = (idx >> 6) % HB, s = idx / (64 * HB);
+    const bool neg = s >= NKS;
+    const int c = neg ? s - NKS : s;
+    const int head = 16 * hb + (ln & 15), gg = ln >> 4;
+    u32x4 x = {0, 0, 0, 0};
+    if (head < G) {
+      x = ld16(qg + size_t(head) * D + 32 * c + 8 * gg);
+      // q- keeps the halves whose sign bit is set, q+ the others
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t sgn = ((x[j] >> 15) & 1u) * 0xffffu | ((x[j] >> 31) & 1u) * 0xffff0000u;
+        x[j] &= neg ? sgn : ~sgn;
+      }
+    }
+    qb[s][hb][ln] = x;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int p0 = ((blockIdx.x * 4 + w) * BPW + i) * 16;
+    if (p0 >= ncp) break;
+    float best[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if (p0 < npages) {
+      f32x4 acc[HB];
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NKS; ++c)
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma_bf16_16x16x32(amx[i][c], qb[c][hb][lane], acc[hb]);
+#pragma unroll
+      for (int c = 0; c < NKS; ++c)
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma_bf16_16x16x32(amn[i][c], qb[NKS + c][hb][lane], acc[hb]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = -INFINITY;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+          if (16 * hb + c16 < G) v = fmaxf(v, acc[hb][r]);
+        for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+        best[r] = (p0 + 4 * g + r < npages) ? v : -INFINITY;
+      }
+    }
+    if (c16 == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int page = p0 + 4 * g + r;
+        if (page < ncp) score[size_t(unit) * ncp + page] = best[r];
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ top-k pages
-// One block per unit: page scores -> ascending view of the best top_pages valid pages.
+// One block per unit: page scores (staged in LDS when they fit) -> ascending view.
 template <int BLOCK>
-__global__ __launch_bounds__(BLOCK) void quest_topk_kernel(
+__global__ __launch_bounds__(BLOCK) void quest_topk_block_kernel(
     const float* __restrict__ score, const int32_t* __restrict__ seq_len, int32_t* __restrict__ view_idx,
-    int32_t* __restrict__ view_len, int Hkv, int P, int n_cap_pages, int top_pages) {
+    int32_t* __restrict__ view_len, int Hkv, int P, int n_cap_pages, int cap, int top_pages) {
   __shared__ float s_lds[QUEST_TOPK_LDS];
   __shared__ TopkShared sh;
   const int unit = blockIdx.x, b = unit / Hkv;
-  const int n = min((seq_len[b] + P - 1) / P, n_cap_pages);
+  const int n = min((min(seq_len[b], cap) + P - 1) / P, n_cap_pages);
   const float* su = score + size_t(unit) * n_cap_pages;
   int32_t* out = view_idx + size_t(unit) * top_pages;
   int kk;
@@ -84,26 +176,49 @@ size_t quest_ws_bytes(const se_cache& c, int page_size, int /*top_pages*/) {
   return size_t(c.batch) * c.n_kv_heads * ceil_div(c.capacity, page_size) * sizeof(float);
 }
 
+template <int D, int HB>
+static void launch_score_mfma(const se_cache& c, const void* q, const void* kmin, const void* kmax,
+                              const int32_t* seq_len, float* score, int P, int ncp, hipStream_t s) {
+  const int units = c.batch * c.n_kv_heads, G = c.n_q_heads / c.n_kv_heads;
+  constexpr int BPW = D >= 512 ? 1 : 2;
+  dim3 grid(ceil_div(ncp, 64 * BPW), units);
+  hipLaunchKernelGGL((quest_score_mfma_kernel<D, HB, BPW>), grid, dim3(256), 0, s, (const uint16_t*)q,
+                     (const uint16_t*)kmin, (const uint16_t*)kmax, seq_len, score, c.n_kv_heads, G, P, ncp,
+                     c.capacity);
+}
+
 se_status launch_quest(const se_cache& c, const void* q, const void* kmin, const void* kmax,
                        const int32_t* seq_len, int page_size, int top_pages, int32_t* view_idx,
                        int32_t* view_len, float* page_score, void* ws, hipStream_t s) {
   const int units = c.batch * c.n_kv_heads, G = c.n_q_heads / c.n_kv_heads;
   const int ncp = ceil_div(c.capacity, page_size);
   float* score = page_score ? page_score : (float*)ws;
-  const int ppb = 256 / G;
-  dim3 grid(ceil_div(ncp, ppb), units);
-  const size_t lds = (size_t(2) * G * c.d_k + 256) * sizeof(float);
-  if (c.dtype == SE_F32)
-    hipLaunchKernelGGL(quest_score_vector_kernel<float>, grid, dim3(256), lds, s, (const float*)q,
-                       (const float*)kmin, (const float*)kmax, seq_len, score, c.n_kv_heads, G, c.d_k,
-                       page_size, ncp);
-  else
-    hipLaunchKernelGGL(quest_score_vector_kernel<bf16_t>, grid, dim3(256), lds, s, (const bf16_t*)q,
-                       (const bf16_t*)kmin, (const bf16_t*)kmax, seq_len, score, c.n_kv_heads, G, c.d_k,
-                       page_size, ncp);
+  bool done = false;
+  if (c.dtype == SE_BF16) {
+    done = true;
+    if (c.d_k == 128 && G <= 16) launch_score_mfma<128, 1>(c, q, kmin, kmax, seq_len, score, page_size, ncp, s);
+    else if (c.d_k == 128 && G <= 32) launch_score_mfma<128, 2>(c, q, kmin, kmax, seq_len, score, page_size, ncp, s);
+    else if (c.d_k == 64 && G <= 16) launch_score_mfma<64, 1>(c, q, kmin, kmax, seq_len, score, page_size, ncp, s);
+    else if (c.d_k == 576 && G <= 32) launch_score_mfma<576, 2>(c, q, kmin, kmax, seq_len, score, page_size, ncp, s);
+    else done = false;
+  }
+  if (!done) {
+    const int ppb = 256 / G;
+    dim3 grid(ceil_div(ncp, ppb), units);
+    const size_t lds = (size_t(2) * G * c.d_k + 256) * sizeof(float);
+    if (lds > 64 * 1024) return SE_ERR_UNSUPPORTED;
+    if (c.dtype == SE_F32)
+      hipLaunchKernelGGL(quest_score_vector_kernel<float>, grid, dim3(256), lds, s, (const float*)q,
+                         (const float*)kmin, (const float*)kmax, seq_len, score, c.n_kv_heads, G, c.d_k,
+                         page_size, ncp);
+    else
+      hipLaunchKernelGGL(quest_score_vector_kernel<bf16_t>, grid, dim3(256), lds, s, (const bf16_t*)q,
+                         (const bf16_t*)kmin, (const bf16_t*)kmax, seq_len, score, c.n_kv_heads, G, c.d_k,
+                         page_size, ncp);
+  }
   if (hipGetLastError() != hipSuccess) return SE_ERR_HIP;
-  hipLaunchKernelGGL(quest_topk_kernel<256>, dim3(units), dim3(256), 0, s, score, seq_len, view_idx,
-                     view_len, c.n_kv_heads, page_size, ncp, top_pages);
+  hipLaunchKernelGGL(quest_topk_block_kernel<256>, dim3(units), dim3(256), 0, s, score, seq_len, view_idx,
+                     view_len, c.n_kv_heads, page_size, ncp, c.capacity, top_pages);
   return launch_status();
 }
 

@@ -79,69 +79,101 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
 }
 
 // ------------------------------------------------------------------ block top-k
-// Exact top-k by unique 64-bit key (radix select, 8-bit digits, most significant
-// first), then an order-preserving compaction: the chosen indices come out in
-// ascending index order.  `score(i)` gives the float score of candidate i < n;
-// ties go to the lower index.  Writes out[0..min(k,n)) and pads out[.. k) with -1.
+// Exact top-k by unique 64-bit key, then an order-preserving compaction: the
+// chosen indices come out in ascending index order.  `score(i)` gives the float
+// score of candidate i < n; ties go to the lower index.  Writes out[0..min(k,n))
+// and pads out[.. k) with -1.
+//
+// Radix select: the bits every candidate shares are skipped (one OR / AND
+// reduction), then 8-bit digits are resolved most significant first.  The
+// digit histogram is kept in 8 LDS copies (one per thread % 8) so that a skewed
+// digit does not serialise the atomics; the search stops as soon as one digit
+// bucket holds exactly the keys still to choose.
+constexpr int TOPK_HCOPIES = 8;
 struct TopkShared {
-  uint32_t hist[256];
-  uint64_t prefix;
-  int remaining;
-  int done;
+  uint32_t hist[TOPK_HCOPIES][256];
+  uint64_t red_or[16], red_and[16];
+  int digit, rem, cnt;
   int scan_tmp[16];
 };
 
 template <int BLOCK, class ScoreFn>
 __device__ int block_topk_ascending(ScoreFn score, int n, int k, int32_t* out, TopkShared& sh) {
-  const int tid = threadIdx.x;
+  constexpr int NW = BLOCK / WAVE;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   const int kk = k < n ? k : n;
+  // contiguous candidate range of this thread (keeps the compaction order-preserving)
+  const int per = (n + BLOCK - 1) / BLOCK;
+  const int lo = min(n, tid * per), hi = min(n, lo + per);
   uint64_t threshold = 0;  // select keys >= threshold
   if (kk > 0 && kk < n) {
-    if (tid == 0) { sh.prefix = 0; sh.remaining = kk; sh.done = 0; }
-    for (int shift = 56; shift >= 0; shift -= 8) {
-      for (int i = tid; i < 256; i += BLOCK) sh.hist[i] = 0;
+    uint64_t kor = 0, kand = ~0ull;
+    for (int i = lo; i < hi; ++i) {
+      const uint64_t key = key_desc_score_asc_index(score(i), uint32_t(i));
+      kor |= key;
+      kand &= key;
+    }
+    for (int o = WAVE / 2; o > 0; o >>= 1) {
+      kor |= __shfl_xor(kor, o, WAVE);
+      kand &= __shfl_xor(kand, o, WAVE);
+    }
+    if (lane == 0) { sh.red_or[w] = kor; sh.red_and[w] = kand; }
+    __syncthreads();
+    kor = 0; kand = ~0ull;
+    for (int i = 0; i < NW; ++i) { kor |= sh.red_or[i]; kand &= sh.red_and[i]; }
+    const int top = 63 - __clzll((long long)(kor ^ kand));   // highest differing bit (keys are unique)
+    uint64_t mask = top == 63 ? 0ull : (~0ull << (top + 1));
+    uint64_t prefix = kand & mask;
+    int remaining = kk;
+    const int cp = tid & (TOPK_HCOPIES - 1);
+    for (int hb = top; hb >= 0; hb -= 8) {
+      const int shift = hb >= 7 ? hb - 7 : 0;
+      const uint32_t dmask = (1u << (hb - shift + 1)) - 1u;
+      for (int j = tid; j < TOPK_HCOPIES * 256; j += BLOCK) (&sh.hist[0][0])[j] = 0;
       __syncthreads();
-      const uint64_t prefix = sh.prefix;
-      const uint64_t mask = shift == 56 ? 0ull : (~0ull << (shift + 8));
-      for (int i = tid; i < n; i += BLOCK) {
-        uint64_t key = key_desc_score_asc_index(score(i), uint32_t(i));
-        if ((key & mask) == (prefix & mask)) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+      for (int i = lo; i < hi; ++i) {
+        const uint64_t key = key_desc_score_asc_index(score(i), uint32_t(i));
+        if ((key & mask) == prefix) atomicAdd(&sh.hist[cp][uint32_t(key >> shift) & dmask], 1u);
       }
       __syncthreads();
       if (tid < WAVE) {
-        // lane owns digits [4*lane, 4*lane+4); find the digit holding the remaining-th largest.
-        uint32_t c[4];
-        int own = 0;
-        for (int j = 0; j < 4; ++j) { c[j] = sh.hist[4 * tid + j]; own += int(c[j]); }
-        // count of keys with a larger digit than this lane's block: suffix sum over higher lanes
-        int incl = own;
+        // lane owns digits 4*lane .. 4*lane+3
+        int c4[4], own = 0;
+        for (int j = 0; j < 4; ++j) {
+          int s = 0;
+          for (int c = 0; c < TOPK_HCOPIES; ++c) s += int(sh.hist[c][4 * tid + j]);
+          c4[j] = s;
+          own += s;
+        }
+        int incl = own;   // keys whose digit lies in this lane's block or above
         for (int o = 1; o < WAVE; o <<= 1) {
-          int t = __shfl_down(incl, o, WAVE);
+          const int t = __shfl_down(incl, o, WAVE);
           if (tid + o < WAVE) incl += t;
         }
-        int above = incl - own;  // keys in digits >= 4*(lane+1)
-        const int rem = sh.remaining;
-        if (above < rem && rem <= incl) {
+        const int above = incl - own;
+        if (above < remaining && remaining <= incl) {
           int acc = above;
           for (int j = 3; j >= 0; --j) {
-            if (acc + int(c[j]) >= rem) {
-              sh.prefix = prefix | (uint64_t(4 * tid + j) << shift);
-              sh.remaining = rem - acc;
-              sh.done = (int(c[j]) == rem - acc);
+            if (acc + c4[j] >= remaining) {
+              sh.digit = 4 * tid + j;
+              sh.rem = remaining - acc;
+              sh.cnt = c4[j];
               break;
             }
-            acc += int(c[j]);
+            acc += c4[j];
           }
         }
       }
       __syncthreads();
-      if (sh.done) break;
+      const int fd = sh.digit, frem = sh.rem, fcnt = sh.cnt;
+      __syncthreads();
+      prefix |= uint64_t(uint32_t(fd)) << shift;
+      mask |= uint64_t(dmask) << shift;
+      remaining = frem;
+      if (fcnt == frem) break;   // the whole digit bucket is selected
     }
-    threshold = sh.prefix;
+    threshold = prefix;
   }
-  // order-preserving compaction over contiguous index ranges per thread
-  const int per = (n + BLOCK - 1) / BLOCK;
-  const int lo = tid * per, hi = min(n, lo + per);
   int cnt = 0;
   if (kk > 0)
     for (int i = lo; i < hi; ++i) cnt += key_desc_score_asc_index(score(i), uint32_t(i)) >= threshold;
@@ -156,6 +188,7 @@ __device__ int block_topk_ascending(ScoreFn score, int n, int k, int32_t* out, T
   for (int i = kk + tid; i < k; i += BLOCK) out[i] = -1;
   return kk;
 }
+
 
 // ------------------------------------------------------------------ launch helpers
 inline se_status launch_status() {
