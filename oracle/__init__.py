@@ -25,7 +25,7 @@ library routines, closed forms, invariants and brute force.  Fidelity to the
 *original* Quest, SnapKV, H2O and OmniKV papers beyond what the pages state is
 parity unpinned (see `UNPINNED` below).
 """
-from .selection import top_k_ascending, argmin_lower  # noqa: F401
+from .selection import top_k_ascending, argmin_lower, boundary_gap, argmin_gap  # noqa: F401
 from .quest import page_meta, quest_bounds, quest_select  # noqa: F401
 from .attention import view_tokens, decode_attention, unit_attention  # noqa: F401
 from .snapkv import snapkv_votes, snapkv_pool, snapkv_keep, snapkv_compact  # noqa: F401

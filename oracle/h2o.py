@@ -20,13 +20,14 @@ Readings taken where the pages are silent:
 import numpy as np
 
 from .attention import unit_attention
-from .selection import argmin_lower
+from .selection import argmin_gap, argmin_lower
 
 
-def h2o_accumulate_evict(logits, lse, slot_pos, acc, n_slots, cur_pos, new_slot, heavy, recent):
+def h2o_accumulate_evict(logits, lse, slot_pos, acc, n_slots, cur_pos, new_slot, heavy, recent, gap_out=None):
     """One unit.  logits [G][>=n_slots] and lse [G] from attention over slots [0, n_slots);
     slot_pos [cap] int (-1 free), acc [cap] float64; new_slot = slot holding cur_pos.
-    Returns (slot_pos', acc', evicted slot or -1)."""
+    Returns (slot_pos', acc', evicted slot or -1).  If gap_out is a list, the relative
+    gap of the eviction decision (argmin_gap) is appended to it."""
     slot_pos = np.array(slot_pos, np.int64)
     acc = np.array(acc, np.float64)
     slot_pos[new_slot] = cur_pos
@@ -40,6 +41,8 @@ def h2o_accumulate_evict(logits, lse, slot_pos, acc, n_slots, cur_pos, new_slot,
     cand = np.zeros(slot_pos.shape[0], bool)
     cand[:n] = occupied & (slot_pos[:n] <= cur_pos - recent)
     ev = argmin_lower(acc, slot_pos, cand)
+    if gap_out is not None:
+        gap_out.append(argmin_gap(acc, cand))
     if ev >= 0:
         slot_pos[ev] = -1
         acc[ev] = 0.0
@@ -47,7 +50,7 @@ def h2o_accumulate_evict(logits, lse, slot_pos, acc, n_slots, cur_pos, new_slot,
 
 
 def h2o_step(Kslots, Vslots, slot_pos, acc, n_slots, free_slot, qg, k_new, v_new, cur_pos,
-             heavy, recent, scale):
+             heavy, recent, scale, gap_out=None):
     """One decode step of one unit.  Kslots [cap][D], Vslots [cap][Dv] are updated in place.
     free_slot: slot to write the new token into (-1: append at n_slots).
     Returns (out [G][Dv], lse [G], slot_pos', acc', n_slots', evicted)."""
@@ -57,5 +60,6 @@ def h2o_step(Kslots, Vslots, slot_pos, acc, n_slots, free_slot, qg, k_new, v_new
     Kslots[slot] = k_new
     Vslots[slot] = v_new
     out, lse, logits = unit_attention(qg, Kslots[:n_slots], Vslots[:n_slots], scale)
-    slot_pos, acc, ev = h2o_accumulate_evict(logits, lse, slot_pos, acc, n_slots, cur_pos, slot, heavy, recent)
+    slot_pos, acc, ev = h2o_accumulate_evict(logits, lse, slot_pos, acc, n_slots, cur_pos, slot, heavy, recent,
+                                             gap_out)
     return out, lse, slot_pos, acc, n_slots, ev

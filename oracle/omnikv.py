@@ -16,7 +16,7 @@ Readings taken where the pages are silent:
 import numpy as np
 
 from .attention import unit_attention
-from .selection import top_k_ascending
+from .selection import boundary_gap, top_k_ascending
 
 
 def omnikv_scores(logits, lse, n):
@@ -44,10 +44,11 @@ def omnikv_layer_views(n_layers, filters):
     return plan
 
 
-def unit_sweep(q_layers, K_layers, V_layers, n, filters, top_k, scale, layers=None):
+def unit_sweep(q_layers, K_layers, V_layers, n, filters, top_k, scale, layers=None, gaps=None):
     """One unit, one decode step through a layer stack.
     q_layers[l] [G][D]; K_layers[l] [>=n][D]; V_layers[l] [>=n][Dv].
-    Returns (outs {layer: [G][Dv]}, views {filter layer: ascending ids})."""
+    Returns (outs {layer: [G][Dv]}, views {filter layer: ascending ids}).  If `gaps` is
+    a dict, the relative top-k boundary gap of each filter layer is stored in it."""
     plan = omnikv_layer_views(len(q_layers), filters)
     views, outs = {}, {}
     want = set(range(len(q_layers))) if layers is None else set(layers)
@@ -66,5 +67,7 @@ def unit_sweep(q_layers, K_layers, V_layers, n, filters, top_k, scale, layers=No
         out, lse, logits = unit_attention(q_layers[layer], Kt, Vt, scale)
         if mode == "filter":
             views[layer] = omnikv_select(logits, lse, n, top_k)
+            if gaps is not None:
+                gaps[layer] = boundary_gap(omnikv_scores(logits, lse, n), top_k)
         outs[layer] = out
     return outs, views

@@ -34,3 +34,37 @@ def argmin_lower(score, key_for_ties, valid):
         return -1
     order = np.lexsort((np.asarray(key_for_ties)[cand], s[cand]))
     return int(cand[order[0]])
+
+
+def boundary_gap(score, k, valid=None):
+    """Relative distance, at the top-k boundary, between the k-th best score and the
+    nearest different score across the boundary (inf when every candidate or none is
+    kept).  When equal scores straddle the boundary, the distance to the nearest
+    different score on either side.  Used to keep generated inputs clear of
+    near-ties that float32 rounding could reorder."""
+    s = np.asarray(score, dtype=np.float64)
+    if valid is not None:
+        s = s[np.asarray(valid, bool)]
+    n = s.shape[0]
+    if k <= 0 or k >= n:
+        return np.inf
+    srt = np.sort(s)[::-1]
+    kth, nxt = srt[k - 1], srt[k]
+    if kth != nxt:
+        return float((kth - nxt) / abs(kth))
+    gap = np.inf
+    above, below = srt[srt > kth], srt[srt < kth]
+    if above.size:
+        gap = min(gap, float((above.min() - kth) / abs(kth)))
+    if below.size:
+        gap = min(gap, float((kth - below.max()) / abs(kth)))
+    return gap
+
+
+def argmin_gap(score, valid):
+    """Relative distance between the smallest candidate score and the next different one."""
+    s = np.sort(np.asarray(score, dtype=np.float64)[np.asarray(valid, bool)])
+    if s.size < 2:
+        return np.inf
+    d = s[s > s[0]]
+    return float((d[0] - s[0]) / abs(s[0])) if d.size else np.inf

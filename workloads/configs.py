@@ -36,6 +36,9 @@ class WorkloadConfig:
     scale: float = 0.0         # softmax scale; 0 means 1/sqrt(d_k)
     planted_pages: int = 0     # Quest workload: pages whose keys lean towards the query direction
     planted_region_pages: int = 0
+    snap_peaks: int = 0        # SnapKV workload: planted key positions (a ladder of vote levels)
+    snap_peak_spacing: int = 0
+    snap_peak_levels: int = 0
     extra: dict = field(default_factory=dict)
 
     @property
@@ -69,7 +72,7 @@ CONFIGS = {
     2: WorkloadConfig(
         cfg_id=2, name="snapkv_128k", dtype="bf16", batch=8, n_q_heads=32, n_kv_heads=4,
         d_k=128, d_v=128, context=131072, snap_window=32, snap_pool=7, snap_budget=8192,
-        decode_steps=128),
+        decode_steps=128, snap_peaks=1280, snap_peak_spacing=100, snap_peak_levels=40),
     # H2O (1024 heavy + 256 recent) and OmniKV (48 layers, filters 2/8/16, top-2048) at 16K.
     3: WorkloadConfig(
         cfg_id=3, name="h2o_omnikv_16k", dtype="bf16", batch=64, n_q_heads=32, n_kv_heads=4,

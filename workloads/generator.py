@@ -99,8 +99,34 @@ def unit_kv(cfg: WorkloadConfig, layer: int, unit: int, length: Optional[int] = 
             if (p + 1) * P <= L:
                 rows = 0.8 * u[None, :] + 0.2 * noise[i]
                 k[p * P:(p + 1) * P] = quantize_(rows.astype(np.float32))
+    if cfg.snap_peaks:
+        for pos, key in zip(*_snap_peaks(cfg, layer, unit)):
+            if pos < L:
+                k[pos] = key
     v = None if cfg.latent else unit_rows(cfg, layer, T_V, unit, L, cfg.d_v)
     return k, v
+
+
+def _snap_direction(cfg: WorkloadConfig, layer: int, unit: int) -> np.ndarray:
+    return rng_for(cfg.cfg_id, layer, T_DIR, unit).standard_normal(cfg.d_k, dtype=np.float32)
+
+
+def _snap_peaks(cfg: WorkloadConfig, layer: int, unit: int):
+    """Planted SnapKV keys of one unit: (positions, rows).  Peak j sits at position
+    48 + spacing * j and its key is a_l * sign(u) with level l = j mod levels and
+    a_l = 2 + l / 32 (exact grid values), u being the unit's query direction.  With
+    the window queries drawn around u, the peaks' votes form a ladder of distinct
+    levels far above the random keys, so the kept set's boundary falls between
+    well-separated vote levels."""
+    sgn = np.where(_snap_direction(cfg, layer, unit) >= 0, 1.0, -1.0).astype(np.float32)
+    j = np.arange(cfg.snap_peaks)
+    pos = 48 + cfg.snap_peak_spacing * j
+    a = (2.0 + (j % cfg.snap_peak_levels) / 32.0).astype(np.float32)
+    return pos, a[:, None] * sgn[None, :]
+
+
+def snap_peak_positions(cfg: WorkloadConfig) -> np.ndarray:
+    return 48 + cfg.snap_peak_spacing * np.arange(cfg.snap_peaks)
 
 
 def cache_kv(cfg: WorkloadConfig, layer: int, capacity: int, length: Optional[int] = None,
@@ -154,8 +180,14 @@ def decode_kv_new(cfg: WorkloadConfig, layer: int, step: int):
 # ---------------------------------------------------------------- SnapKV
 
 def unit_obs_queries(cfg: WorkloadConfig, layer: int, unit: int, attempt: int = 0) -> np.ndarray:
-    """[G][window][d_k]: queries of the last `window` prompt tokens for the G heads of one KV head."""
-    return grid_normal((cfg.cfg_id, layer, T_QOBS, unit, attempt), (cfg.group, cfg.snap_window, cfg.d_k))
+    """[G][window][d_k]: queries of the last `window` prompt tokens for the G heads of one KV head.
+    With planted peaks the queries are u + 0.5 eps around the unit's direction u."""
+    shape = (cfg.group, cfg.snap_window, cfg.d_k)
+    if cfg.snap_peaks:
+        u = _snap_direction(cfg, layer, unit)
+        eps = rng_for(cfg.cfg_id, layer, T_QOBS, unit, attempt).standard_normal(shape, dtype=np.float32)
+        return quantize_((u + 0.5 * eps).astype(np.float32))
+    return grid_normal((cfg.cfg_id, layer, T_QOBS, unit, attempt), shape)
 
 
 def obs_queries(cfg: WorkloadConfig, layer: int, attempts: Optional[Attempts] = None) -> np.ndarray:
