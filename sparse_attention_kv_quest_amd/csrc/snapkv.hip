@@ -1,15 +1,334 @@
-// SnapKV prefill-end eviction (placeholder until the kernels land).
+// SnapKV prefill-end eviction: observation-window votes, max-pool, top-k, compaction.
+//
+// tokendh.com explainer, section "把边界划在'生命周期'上": at its hook SnapKV
+// looks at how the last few prompt tokens attend over the history, keeps the
+// important part and physically deletes the rest.  Here the window rows are
+// the G x W queries (head h, window index i) at positions L - W + i; row r's
+// softmax runs causally over keys 0 .. L - W + i; a history key's vote is the
+// sum of the rows' weights on it; votes are max-pooled (odd width, stride 1);
+// the best budget - W pooled positions (ties to the lower position) and the
+// window are kept, ascending, and their K / V rows are copied out.
+//
+// The window scores are a dense contraction (G x W rows share every key), so
+// bf16 caches score them on MFMA in two passes over K: pass A forms each row's
+// log-sum-exp (split over key chunks, then merged), pass B sums the softmax
+// weights per key.  fp32 caches use vector kernels.
 #include "se_internal.hpp"
+#include "mfma_util.hpp"
 
 namespace se {
 
-size_t snapkv_ws_bytes(const se_cache& c, int prompt_len, int window) {
-  return size_t(c.batch) * c.n_kv_heads * (prompt_len - window) * sizeof(float);
+constexpr float SK_LOG2E = 1.4426950408889634f;
+constexpr int SK_CHUNK = 1024;        // keys per block in the MFMA passes
+constexpr float SK_MARGIN = 8.f;      // lazy running-max margin (log2 units)
+constexpr int SK_TOPK_BLOCK = 1024;
+
+struct SnapArgs {
+  const void* q; const void* k; const void* v;
+  void* k_out; void* v_out;
+  int32_t* kept; float* votes; float* pooled; float* part; float* lse2; int32_t* out_len;
+  int B, Hq, Hkv, G, D, cap, out_cap, L, W, R, pool, budget, nchunks, dtype;
+  float sc2;   // scale * log2(e)
+};
+
+// ------------------------------------------------------------------ MFMA passes (bf16)
+// grid (chunks, units); 4 waves, each owning NRB 16-row blocks of the R = 64 * NRB rows.
+// S^T[key][row] = K[key] . Q[row]: A = 16 key rows (lane: key c16, dims 32c + 8g..),
+// B = Q^T of one 16-row block (lane: row c16, same dims); lane (g, c16) then holds
+// keys 4g..4g+3 of row c16.
+template <int D, int NRB, bool PASS_B>
+__global__ __launch_bounds__(256) void snap_mfma_kernel(SnapArgs a) {
+  constexpr int NKS = D / 32;
+  __shared__ float vsum[4][SK_CHUNK / 16][16];   // pass B: per-wave key sums of each 16-key block
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
+  const int unit = blockIdx.y, chunk = blockIdx.x;
+  const int b = unit / a.Hkv, kvh = unit % a.Hkv;
+  const int n_hist = a.L - a.W;
+  const int kend = PASS_B ? n_hist : a.L;          // pass B scores history keys only
+  const int k0 = chunk * SK_CHUNK, k1 = min(kend, k0 + SK_CHUNK);
+  const uint16_t* ku = (const uint16_t*)a.k + size_t(unit) * a.cap * D;
+  const uint16_t* qu = (const uint16_t*)a.q + (size_t(b) * a.Hq + size_t(kvh) * a.G) * a.W * D;
+  // Q operand of this wave's row blocks
+  u32x4 qv[NRB][NKS];
+  int rowpos[NRB];
+  float lse2[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int row = (w * NRB + rb) * 16 + c16;
+    rowpos[rb] = a.L - a.W + row % a.W;
+#pragma unroll
+    for (int c = 0; c < NKS; ++c) qv[rb][c] = ld16(qu + size_t(row) * D + 32 * c + 8 * g);
+    lse2[rb] = PASS_B ? a.lse2[size_t(unit) * a.R + row] : 0.f;
+  }
+  float m[NRB], l[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) { m[rb] = -INFINITY; l[rb] = 0.f; }
+
+  const int nblk = (k1 - k0 + 15) / 16;
+  u32x4 kc[NKS], kn[NKS];
+  auto load = [&](int blk, u32x4* dst) {
+    const int key = k0 + blk * 16 + c16;
+    const uint32_t off = uint32_t(min(max(key, 0), a.cap - 1)) * D + 8 * g;   // clamped: masked below
+#pragma unroll
+    for (int c = 0; c < NKS; ++c) dst[c] = ld16(ku + off + 32 * c);
+  };
+  if (nblk > 0) load(0, kc);
+  for (int blk = 0; blk < nblk; ++blk) {
+    load(blk + 1 < nblk ? blk + 1 : blk, kn);
+    const int kb = k0 + blk * 16;
+    float kvals[NRB][4];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NKS; ++c) s = mfma_bf16_16x16x32(kc[c], qv[rb][c], s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = kb + 4 * g + i;
+        const bool ok = key < k1 && key <= rowpos[rb];
+        kvals[rb][i] = ok ? s[i] * a.sc2 : -INFINITY;
+      }
+    }
+    if (!PASS_B) {
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        const float bm = fmaxf(fmaxf(kvals[rb][0], kvals[rb][1]), fmaxf(kvals[rb][2], kvals[rb][3]));
+        if (bm > m[rb] + SK_MARGIN) {
+          l[rb] *= (m[rb] == -INFINITY) ? 0.f : exp2f(m[rb] - bm);
+          m[rb] = bm;
+        }
+        const float mref = m[rb] == -INFINITY ? 0.f : m[rb];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) l[rb] += exp2f(kvals[rb][i] - mref);
+      }
+    } else {
+      float ks[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float t = 0.f;
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) t += exp2f(kvals[rb][i] - lse2[rb]);
+        for (int o = 1; o < 16; o <<= 1) t += __shfl_xor(t, o, 64);   // over the 16 rows of the lane group
+        ks[i] = t;
+      }
+      if (c16 == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vsum[w][blk][4 * g + i] = ks[i];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < NKS; ++c) kc[c] = kn[c];
+  }
+  if (!PASS_B) {
+    // merge the 4 lanes of each row (g = 0..3), then write the chunk's partial
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      float mm = m[rb];
+      mm = fmaxf(mm, __shfl_xor(mm, 16, 64));
+      mm = fmaxf(mm, __shfl_xor(mm, 32, 64));
+      float ll = (m[rb] == -INFINITY) ? 0.f : l[rb] * exp2f(m[rb] - mm);
+      ll += __shfl_xor(ll, 16, 64);
+      ll += __shfl_xor(ll, 32, 64);
+      if (g == 0) {
+        const int row = (w * NRB + rb) * 16 + c16;
+        float* p = a.part + ((size_t(unit) * a.nchunks + chunk) * a.R + row) * 2;
+        p[0] = mm;
+        p[1] = ll;
+      }
+    }
+  } else {
+    __syncthreads();
+    for (int j = threadIdx.x; j < k1 - k0; j += 256) {
+      const float t = vsum[0][j / 16][j % 16] + vsum[1][j / 16][j % 16] + vsum[2][j / 16][j % 16] +
+                      vsum[3][j / 16][j % 16];
+      a.votes[size_t(unit) * n_hist + k0 + j] = t;
+    }
+  }
 }
 
-se_status launch_snapkv(const se_cache&, const void*, const void*, const void*, int, int, int, int, float,
-                        const se_cache&, void*, void*, int32_t*, float*, int32_t*, void*, hipStream_t) {
-  return SE_ERR_UNSUPPORTED;
+// One thread per (unit, row): merge the chunk partials into the row's log2-sum-exp2.
+__global__ void snap_lse_merge_kernel(SnapArgs a) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= a.B * a.Hkv * a.R) return;
+  const int unit = idx / a.R, row = idx % a.R;
+  float M = -INFINITY;
+  for (int c = 0; c < a.nchunks; ++c) M = fmaxf(M, a.part[((size_t(unit) * a.nchunks + c) * a.R + row) * 2]);
+  float S = 0.f;
+  for (int c = 0; c < a.nchunks; ++c) {
+    const float* p = a.part + ((size_t(unit) * a.nchunks + c) * a.R + row) * 2;
+    if (p[0] != -INFINITY) S += p[1] * exp2f(p[0] - M);
+  }
+  a.lse2[idx] = M + log2f(S);
+}
+
+// ------------------------------------------------------------------ vector passes (any dtype)
+template <typename T>
+__global__ __launch_bounds__(256) void snap_vec_lse_kernel(SnapArgs a) {
+  extern __shared__ float qrow[];   // [D]
+  __shared__ float rm[4], rl[4];
+  const int row = blockIdx.x, unit = blockIdx.y;
+  const int b = unit / a.Hkv, kvh = unit % a.Hkv, D = a.D;
+  const T* qu = (const T*)a.q + ((size_t(b) * a.Hq + size_t(kvh) * a.G) * a.W + row) * D;
+  const T* ku = (const T*)a.k + size_t(unit) * a.cap * D;
+  for (int d = threadIdx.x; d < D; d += 256) qrow[d] = to_f32(qu[d]);
+  __syncthreads();
+  const int pos = a.L - a.W + row % a.W;
+  float m = -INFINITY, l = 0.f;
+  for (int j = threadIdx.x; j <= pos; j += 256) {
+    float dot = 0.f;
+    for (int d = 0; d < D; ++d) dot += qrow[d] * to_f32(ku[size_t(j) * D + d]);
+    const float s = dot * a.sc2;
+    if (s > m) { l = l * exp2f(m - s); m = s; }
+    l += exp2f(s - m);
+  }
+  const float mw = wave_max(m);
+  l = (m == -INFINITY) ? 0.f : l * exp2f(m - mw);
+  l = wave_sum(l);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) { rm[w] = mw; rl[w] = l; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float M = fmaxf(fmaxf(rm[0], rm[1]), fmaxf(rm[2], rm[3])), S = 0.f;
+    for (int i = 0; i < 4; ++i)
+      if (rm[i] != -INFINITY) S += rl[i] * exp2f(rm[i] - M);
+    a.lse2[size_t(unit) * a.R + row] = M + log2f(S);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void snap_vec_vote_kernel(SnapArgs a) {
+  extern __shared__ float qs[];   // [R][D]
+  const int unit = blockIdx.y, b = unit / a.Hkv, kvh = unit % a.Hkv, D = a.D;
+  const T* qu = (const T*)a.q + (size_t(b) * a.Hq + size_t(kvh) * a.G) * a.W * D;
+  const T* ku = (const T*)a.k + size_t(unit) * a.cap * D;
+  for (int i = threadIdx.x; i < a.R * D; i += 256) qs[i] = to_f32(qu[i]);
+  __syncthreads();
+  const int n_hist = a.L - a.W;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= n_hist) return;
+  float vote = 0.f;
+  for (int r = 0; r < a.R; ++r) {
+    float dot = 0.f;
+    for (int d = 0; d < D; ++d) dot += qs[r * D + d] * to_f32(ku[size_t(j) * D + d]);
+    vote += exp2f(dot * a.sc2 - a.lse2[size_t(unit) * a.R + r]);
+  }
+  a.votes[size_t(unit) * n_hist + j] = vote;
+}
+
+// ------------------------------------------------------------------ pool, select, gather
+__global__ void snap_pool_kernel(SnapArgs a) {
+  const int unit = blockIdx.y, n = a.L - a.W;
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n) return;
+  const int r = a.pool / 2;
+  const float* v = a.votes + size_t(unit) * n;
+  float mx = -INFINITY;
+  for (int d = max(0, j - r); d <= min(n - 1, j + r); ++d) mx = fmaxf(mx, v[d]);
+  a.pooled[size_t(unit) * n + j] = mx;
+}
+
+__global__ __launch_bounds__(SK_TOPK_BLOCK) void snap_select_kernel(SnapArgs a) {
+  __shared__ TopkShared sh;
+  const int unit = blockIdx.x, n = a.L - a.W;
+  const float* pooled = a.pooled + size_t(unit) * n;
+  int32_t* kept = a.kept + size_t(unit) * a.budget;
+  const int k = a.budget - a.W;
+  const int kk = block_topk_ascending<SK_TOPK_BLOCK>([&](int i) { return pooled[i]; }, n, k, kept, sh);
+  __syncthreads();   // the top-k pads kept[kk .. k) with -1 before the window is written there
+  // the window follows the chosen history positions; everything past them is -1
+  for (int i = threadIdx.x; i < a.W; i += SK_TOPK_BLOCK) kept[kk + i] = n + i;
+  for (int i = kk + a.W + threadIdx.x; i < a.budget; i += SK_TOPK_BLOCK) kept[i] = -1;
+  if (threadIdx.x == 0 && unit % a.Hkv == 0 && a.out_len != nullptr) a.out_len[unit / a.Hkv] = kk + a.W;
+}
+
+// grid (row groups, units): copies kept rows of K and V (16-byte words).
+__global__ __launch_bounds__(256) void snap_gather_kernel(SnapArgs a, int row_words) {
+  const int unit = blockIdx.y;
+  const int kept_n = min(a.budget, a.L);
+  const int32_t* kept = a.kept + size_t(unit) * a.budget;
+  const u32x4* ks = (const u32x4*)a.k + size_t(unit) * a.cap * row_words;
+  const u32x4* vs = (const u32x4*)a.v + size_t(unit) * a.cap * row_words;
+  u32x4* kd = (u32x4*)a.k_out + size_t(unit) * a.out_cap * row_words;
+  u32x4* vd = (u32x4*)a.v_out + size_t(unit) * a.out_cap * row_words;
+  const int rows_per_block = 256 / row_words;
+  const int i = blockIdx.x * rows_per_block + threadIdx.x / row_words, wd = threadIdx.x % row_words;
+  if (threadIdx.x >= rows_per_block * row_words || i >= kept_n) return;
+  const int src = kept[i];
+  if (src < 0 || src >= a.cap) return;
+  kd[size_t(i) * row_words + wd] = ks[size_t(src) * row_words + wd];
+  vd[size_t(i) * row_words + wd] = vs[size_t(src) * row_words + wd];
+}
+
+// ------------------------------------------------------------------ host
+static bool snap_mfma_ok(const se_cache& c, int W) {
+  const int R = (c.n_q_heads / c.n_kv_heads) * W;
+  return c.dtype == SE_BF16 && (c.d_k == 128 || c.d_k == 64) && R % 64 == 0 && R <= 256;
+}
+
+static int snap_chunks(int L) { return ceil_div(L, SK_CHUNK); }
+
+size_t snapkv_ws_bytes(const se_cache& c, int prompt_len, int window) {
+  const size_t units = size_t(c.batch) * c.n_kv_heads, R = size_t(c.n_q_heads / c.n_kv_heads) * window;
+  const size_t n = size_t(prompt_len - window);
+  return units * (size_t(snap_chunks(prompt_len)) * R * 2 + R + 2 * n) * sizeof(float);
+}
+
+se_status launch_snapkv(const se_cache& c, const void* q_obs, const void* k, const void* v, int prompt_len,
+                        int window, int pool_kernel, int budget, float scale, const se_cache& out, void* k_out,
+                        void* v_out, int32_t* kept_pos, float* votes, int32_t* out_seq_len, void* ws,
+                        hipStream_t s) {
+  SnapArgs a{};
+  a.q = q_obs; a.k = k; a.v = v; a.k_out = k_out; a.v_out = v_out;
+  a.B = c.batch; a.Hq = c.n_q_heads; a.Hkv = c.n_kv_heads; a.G = c.n_q_heads / c.n_kv_heads; a.D = c.d_k;
+  a.cap = c.capacity; a.out_cap = out.capacity; a.L = prompt_len; a.W = window; a.R = a.G * window;
+  a.pool = pool_kernel; a.budget = budget; a.nchunks = snap_chunks(prompt_len); a.dtype = c.dtype;
+  a.sc2 = scale * SK_LOG2E;
+  const size_t units = size_t(a.B) * a.Hkv, n = size_t(prompt_len - window);
+  float* wsf = (float*)ws;
+  a.part = wsf;
+  a.lse2 = a.part + units * a.nchunks * a.R * 2;
+  a.pooled = a.lse2 + units * a.R;
+  a.votes = votes ? votes : a.pooled + units * n;
+  a.kept = kept_pos;
+  a.out_len = out_seq_len;
+  const dim3 vgrid(ceil_div(int(n), 256), int(units));
+  if (snap_mfma_ok(c, window)) {
+    const int nrb = a.R / 64;
+    const dim3 ga(a.nchunks, int(units)), gb(ceil_div(int(n), SK_CHUNK), int(units));
+#define SK_LAUNCH(DD, NN)                                                                          \
+  do {                                                                                             \
+    hipLaunchKernelGGL((snap_mfma_kernel<DD, NN, false>), ga, dim3(256), 0, s, a);                 \
+    hipLaunchKernelGGL(snap_lse_merge_kernel, dim3(ceil_div(int(units) * a.R, 256)), dim3(256), 0, s, a); \
+    hipLaunchKernelGGL((snap_mfma_kernel<DD, NN, true>), gb, dim3(256), 0, s, a);                  \
+  } while (0)
+    if (c.d_k == 128) {
+      if (nrb == 1) SK_LAUNCH(128, 1); else if (nrb == 2) SK_LAUNCH(128, 2);
+      else if (nrb == 3) SK_LAUNCH(128, 3); else SK_LAUNCH(128, 4);
+    } else {
+      if (nrb == 1) SK_LAUNCH(64, 1); else if (nrb == 2) SK_LAUNCH(64, 2);
+      else if (nrb == 3) SK_LAUNCH(64, 3); else SK_LAUNCH(64, 4);
+    }
+#undef SK_LAUNCH
+  } else {
+    const size_t lds = size_t(a.R) * a.D * sizeof(float);
+    if (lds > 64 * 1024) return SE_ERR_UNSUPPORTED;
+    if (c.dtype == SE_F32) {
+      hipLaunchKernelGGL(snap_vec_lse_kernel<float>, dim3(a.R, int(units)), dim3(256), a.D * sizeof(float), s, a);
+      hipLaunchKernelGGL(snap_vec_vote_kernel<float>, vgrid, dim3(256), lds, s, a);
+    } else {
+      hipLaunchKernelGGL(snap_vec_lse_kernel<bf16_t>, dim3(a.R, int(units)), dim3(256), a.D * sizeof(float), s, a);
+      hipLaunchKernelGGL(snap_vec_vote_kernel<bf16_t>, vgrid, dim3(256), lds, s, a);
+    }
+  }
+  if (hipGetLastError() != hipSuccess) return SE_ERR_HIP;
+  hipLaunchKernelGGL(snap_pool_kernel, vgrid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(snap_select_kernel, dim3(int(units)), dim3(SK_TOPK_BLOCK), 0, s, a);
+  const int esz = c.dtype == SE_F32 ? 4 : 2;
+  const int row_words = c.d_k * esz / 16;
+  const int rows_per_block = 256 / row_words;
+  hipLaunchKernelGGL(snap_gather_kernel, dim3(ceil_div(std::min(budget, prompt_len), rows_per_block), int(units)),
+                     dim3(256), 0, s, a, row_words);
+  return launch_status();
 }
 
 }  // namespace se

@@ -1,0 +1,103 @@
+"""GPU parity of se_snapkv_score_compact (window votes, max-pool, top-k, compaction)
+against the CPU oracle, through the C ABI."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import boundary_gap
+from oracle import snapkv as osnap
+from tests.gpu_util import banner, dev, host
+from tests.sampled_units import SNAP_UNITS
+from workloads import generator as gen
+from workloads import get_config
+
+pytestmark = pytest.mark.gpu
+
+ATTEMPTS = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "attempts.json")))
+GAP = ATTEMPTS["gap"]
+
+
+def attempts_of(name):
+    return {tuple(int(x) for x in k.split(",")): v for k, v in ATTEMPTS.get(name, {}).items()}
+
+
+def run_snap(se, cfg, units, attempts, cap=None, budget=None, check_gap=True):
+    B, H, Hq, D = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.d_k
+    L, W, pool = cfg.context, cfg.snap_window, cfg.snap_pool
+    budget = cfg.snap_budget if budget is None else budget
+    cap = L if cap is None else cap
+    dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    K, V = gen.cache_kv(cfg, 0, cap, length=L)
+    qo = gen.obs_queries(cfg, 0, attempts)
+    c = se.cache(B, Hq, H, D, D, cap, cfg.dtype)
+    nkeep = min(budget, L)
+    oc = se.cache(B, Hq, H, D, D, nkeep + 3, cfg.dtype)
+    k_out = torch.zeros((B, H, nkeep + 3, D), dtype=dt, device="cuda")
+    v_out = torch.zeros_like(k_out)
+    kept = torch.zeros((B, H, budget), dtype=torch.int32, device="cuda")
+    votes = torch.zeros((B, H, L - W), device="cuda")
+    olen = torch.zeros((B,), dtype=torch.int32, device="cuda")
+    ws = se.workspace(se.SE_OP_SNAPKV, c, L, W)
+    se.se_snapkv_score_compact(c, dev(qo, dt), dev(K, dt), dev(V, dt), L, W, pool, budget, cfg.softmax_scale, oc,
+                               k_out, v_out, kept, votes, olen, ws)
+    torch.cuda.synchronize()
+    g_kept, g_votes, g_k, g_v = host(kept), host(votes), host(k_out), host(v_out)
+    assert np.all(host(olen) == nkeep)
+    G = cfg.group
+    for u in units:
+        b, h = divmod(u, H)
+        ref_votes = osnap.unit_votes(qo[b, h * G:(h + 1) * G], K[b, h], L, W, cfg.softmax_scale)
+        pooled = osnap.snapkv_pool(ref_votes, pool)
+        if check_gap and budget < L:
+            assert boundary_gap(pooled, budget - W) >= GAP, f"unit {u}: generated input has a near-tie"
+        ref_kept = osnap.snapkv_keep(pooled, L, W, budget)
+        np.testing.assert_allclose(g_votes[b, h], ref_votes, rtol=1e-4, atol=1e-30, err_msg=f"unit {u} votes")
+        np.testing.assert_array_equal(g_kept[b, h, :nkeep], ref_kept, err_msg=f"unit {u} kept")
+        assert np.all(g_kept[b, h, nkeep:] == -1)
+        np.testing.assert_array_equal(g_k[b, h, :nkeep], K[b, h][ref_kept])
+        np.testing.assert_array_equal(g_v[b, h, :nkeep], V[b, h][ref_kept])
+    return g_kept
+
+
+def test_snapkv_tiny_f32_all_units(se):
+    cfg = get_config(0)
+    banner("snapkv tiny f32")
+    run_snap(se, cfg, range(cfg.units), attempts_of("snapkv_tiny"), cap=cfg.context + 5)
+
+
+def mid_config():
+    # bf16, MFMA path (G * W = 64 rows), a scaled-down vote ladder keeps the boundary clear
+    return get_config(2, batch=2, context=4096, snap_window=8, snap_budget=400, snap_peaks=100,
+                      snap_peak_spacing=40, snap_peak_levels=10)
+
+
+def test_snapkv_bf16_mfma_mid(se):
+    cfg = mid_config()
+    banner("snapkv bf16 mid")
+    run_snap(se, cfg, range(cfg.units), {})
+
+
+def test_snapkv_bf16_rows_128_and_256(se):
+    for W in (16, 32):
+        cfg = get_config(2, batch=1, context=3000, snap_window=W, snap_budget=300, snap_peaks=60,
+                          snap_peak_spacing=40, snap_peak_levels=8)
+        banner(f"snapkv bf16 rows {cfg.group * W}")
+        run_snap(se, cfg, range(cfg.units), {})
+
+
+def test_snapkv_budget_covers_prompt_and_window_only(se):
+    cfg = get_config(0, context=300)
+    banner("snapkv edges")
+    kept = run_snap(se, cfg, range(cfg.units), {}, budget=400, check_gap=False)
+    assert np.all(kept[:, :, :300] == np.arange(300))
+    kept = run_snap(se, cfg, range(cfg.units), {}, budget=cfg.snap_window, check_gap=False)
+    assert np.all(kept[:, :, :cfg.snap_window] == np.arange(300 - cfg.snap_window, 300))
+
+
+def test_snapkv_128k_sampled_units(se):
+    cfg = get_config(2)
+    banner("snapkv 128K: 8 x 4 units, 131072 -> 8192")
+    run_snap(se, cfg, SNAP_UNITS, attempts_of("snapkv_128k"))
