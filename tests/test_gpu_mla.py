@@ -1,0 +1,69 @@
+"""GPU parity of the MLA latent path: 64-token latent pages, Quest top-k over
+576-wide keys shared by 32 heads, attention with V = the first 512 latent columns."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import quest as oquest
+from tests.gpu_util import TOL, banner, dev, host, zeros
+from workloads import generator as gen
+from workloads import get_config
+
+pytestmark = pytest.mark.gpu
+
+
+def run_mla(se, cfg, units, steps=1):
+    B, Hq, D, Dv, P, k = cfg.batch, cfg.n_q_heads, cfg.d_k, cfg.d_v, cfg.page_size, cfg.top_pages
+    cap = cfg.context + steps
+    C, _ = gen.cache_kv(cfg, 0, cap)                       # [B][1][cap][576]
+    c = se.cache(B, Hq, 1, D, Dv, cap, "bf16", latent=True)
+    cd = dev(C, torch.bfloat16)
+    seq = torch.full((B,), cfg.context, dtype=torch.int32, device="cuda")
+    ncp = (cap + P - 1) // P
+    kmin = torch.zeros((B, 1, ncp, D), dtype=torch.bfloat16, device="cuda")
+    kmax = torch.zeros_like(kmin)
+    view = torch.zeros((B, 1, k), dtype=torch.int32, device="cuda")
+    vlen = torch.zeros((B, 1), dtype=torch.int32, device="cuda")
+    score = torch.zeros((B, 1, ncp), device="cuda")
+    out, lse = zeros((B, Hq, Dv)), zeros((B, Hq))
+    ws_q = se.workspace(se.SE_OP_QUEST, c, P, k)
+    ws_a = se.workspace(se.SE_OP_ATTN, c, k * P, 0)
+    se.se_page_meta_update(c, cd, kmin, kmax, seq, P, 0)
+    for s in range(steps):
+        q = gen.decode_query(cfg, 0, s)                     # [B][32][576]
+        kn, _ = gen.decode_kv_new(cfg, 0, s)
+        C[:, :, cfg.context + s] = kn
+        se.se_kv_append(c, cd, None, dev(kn, torch.bfloat16), None, None, seq)
+        se.se_page_meta_update(c, cd, kmin, kmax, seq, P, -1)
+        qd = dev(q, torch.bfloat16)
+        se.se_quest_select(c, qd, kmin, kmax, seq, P, k, view, vlen, score, ws_q)
+        se.se_sparse_decode_attn(c, qd, cd, None, seq, view, vlen, k, P, cfg.softmax_scale, out, lse, ws=ws_a)
+    torch.cuda.synchronize()
+    L = cfg.context + steps
+    g = {n: host(t) for n, t in (("kmin", kmin), ("kmax", kmax), ("view", view), ("vlen", vlen), ("score", score),
+                                 ("out", out), ("lse", lse))}
+    for b in units:
+        Cb = C[b:b + 1]
+        mn, mx = oquest.page_meta(Cb, [L], P)
+        npv = oquest.n_pages(L, P)
+        np.testing.assert_array_equal(g["kmin"][b, 0, :npv], mn[0, 0, :npv])
+        np.testing.assert_array_equal(g["kmax"][b, 0, :npv], mx[0, 0, :npv])
+        rv, rl, S = oquest.quest_select(q[b:b + 1], mn, mx, [L], P, k)
+        np.testing.assert_array_equal(g["score"][b, 0, :npv], S[0, 0, :npv].astype(np.float32))
+        np.testing.assert_array_equal(g["view"][b, 0], rv[0, 0])
+        ro, rlse, _ = oracle.decode_attention(q[b:b + 1], Cb, None, [L], cfg.softmax_scale, rv, rl, P, latent_dv=Dv)
+        np.testing.assert_allclose(g["out"][b], ro[0], rtol=0, atol=TOL["bf16"])
+        np.testing.assert_allclose(g["lse"][b], rlse[0], rtol=0, atol=TOL["bf16"])
+
+
+def test_mla_small_all_units(se):
+    cfg = get_config(4, batch=3, context=3000, top_pages=8)
+    banner("mla small")
+    run_mla(se, cfg, range(cfg.batch), steps=3)
+
+
+def test_mla_128k_sampled_units(se):
+    cfg = get_config(4)
+    banner("mla 128K: 32 x 131072 latent rows, top-64 pages")
+    run_mla(se, cfg, (0, 19, 31))
