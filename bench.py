@@ -1,22 +1,35 @@
 """Decode-step throughput of the sparse-decode path on one MI355X.
 
-A step is one decode token for every batch row through one layer of the
-Quest path on the 32K workload (16 x 32q/4kv x d128, pages of 16, top-128
-pages): append the new K/V row, rebuild the last page's min/max, score and
-select pages, and run split-K decode attention over the selected pages.
-Steps rotate over --layers distinct layer caches so that each step's working
-set has left the 256 MB Infinity Cache before it is read again.  Inputs are
-resident in HBM before timing starts.
+Headline: the Quest path on the 32K workload (16 x 32q/4kv x d128, pages of 16,
+top-128 pages).  A step is one decode token for every batch row through one
+layer: append the new K/V row, rebuild the last page's min/max, score and
+select pages, and run split-K decode attention over the selected pages.  Steps
+rotate over --layers distinct layer caches so that each step's working set has
+left the 256 MB Infinity Cache before it is read again.  Inputs are resident in
+HBM before timing starts; steps are replayed from HIP graphs.
 
-Prints one JSON line (tokens/s per layer-step, achieved HBM GB/s of the
-attention kernel against the 8 TB/s peak, and the CPU oracle timed on a
-bounded sample of the same step as a baseline).
+The other workloads are timed the same way and reported under "workloads":
+  snapkv_128k  prefill-end SnapKV eviction of a 131072-token prompt to 8192
+               tokens (timed per call), then decode steps over the compacted
+               cache (append + attention);
+  h2o_16k      H2O decode steps (append into the freed slot, attention with
+               logits, accumulate + evict) over 1024 heavy + 256 recent slots;
+  omnikv_16k   48-layer OmniKV sweeps (dense layers 0-1, filter layers 2/8/16
+               with top-2048 selection, 43 layers over the reused views);
+  mla_128k     MLA latent Quest steps at 131072 tokens (576-wide latent rows,
+               pages of 64, top-64 pages, 32 heads).
+
+Prints one JSON line: tokens/s per layer-step of the headline, achieved HBM
+GB/s of its attention call against the 8 TB/s peak, per-workload figures, and
+the CPU oracle timed on a bounded sample of the headline step as a baseline.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -26,6 +39,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+ALL_WORKLOADS = ("quest_32k", "snapkv_128k", "h2o_16k", "omnikv_16k", "mla_128k")
 
 
 def parse():
@@ -34,11 +49,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--layers", type=int, default=8, help="distinct layer caches rotated through")
-    ap.add_argument("--attn-reps", type=int, default=20, help="graph replays for the attention-kernel timing")
+    ap.add_argument("--attn-reps", type=int, default=20, help="graph replays for the attention-call timing")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--splits", type=int, default=0, help="split-K factor of the attention (0 = library choice)")
+    ap.add_argument("--workloads", default=",".join(ALL_WORKLOADS),
+                    help="comma-separated subset of " + ",".join(ALL_WORKLOADS))
     return ap.parse_args()
 
 
@@ -46,7 +63,81 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-class Layer:
+# ---------------------------------------------------------------- timing helpers
+
+class Timer:
+    """Captures a list of launches into one HIP graph (or replays them eagerly) and
+    times replays with events on the stream the launches run on."""
+
+    def __init__(self, torch, fn, use_graph):
+        self.torch, self.fn, self.use_graph = torch, fn, use_graph
+        self.stream = torch.cuda.Stream()
+        if use_graph:
+            self.graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(self.graph, stream=self.stream):
+                fn()
+            torch.cuda.synchronize()
+
+    def ms_per_replay(self, reps):
+        torch = self.torch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(self.stream):
+            e0.record(self.stream)
+            for _ in range(reps):
+                if self.use_graph:
+                    self.graph.replay()
+                else:
+                    self.fn()
+            e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+
+def dev_grid(torch, shape, seed, dtype):
+    """Seeded grid values on the device: round(32 x) / 32 clipped to +-255/32 with
+    x ~ N(0, 1), the distribution of the host generator (torch's Philox stream)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    x = torch.randn(shape, generator=g, device="cuda", dtype=torch.float32)
+    x.mul_(32.0).round_().clamp_(-255.0, 255.0).div_(32.0)
+    return x.to(dtype)
+
+
+def free(torch):
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def sha16(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counter_traffic(summary, kernels, source):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None when
+    the kernel source has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", summary)
+    src = os.path.join(ROOT, "sparse_attention_kv_quest_amd", "csrc", source)
+    if not (os.path.exists(path) and os.path.exists(src)):
+        return None
+    text = open(path).read()
+    m = re.search(r"sha256\[:16\] at measurement: " + re.escape(source) + r" ([0-9a-f]{16})", text)
+    if not m or m.group(1) != sha16(src):
+        return None
+    total = 0.0
+    for k in kernels:
+        m = re.search(re.escape(k) + r": scaled HBM traffic per launch = ([0-9.]+) MiB read \+ ([0-9.]+) MiB written",
+                      text)
+        if not m:
+            return None
+        total += (float(m.group(1)) + float(m.group(2))) * (1 << 20)
+    return int(total)
+
+
+# ---------------------------------------------------------------- headline: Quest 32K
+
+class QuestLayer:
     """Device buffers of one layer: K, V, page metadata, view, outputs."""
 
     def __init__(self, se, cfg, c, K0, V0, shift, torch):
@@ -63,24 +154,17 @@ class Layer:
         se.se_page_meta_update(c, self.k, self.kmin, self.kmax, self.seq, P, 0)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py measures one GPU: the path has no multi-GPU mode; run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
-    import torch
-    import sparse_attention_kv_quest_amd as se
+def run_quest(se, torch, args):
     from workloads import generator as gen
     from workloads import get_config
 
-    se.load()
     cfg = get_config(1)
     B, H, Hq, D, P, k = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.d_k, cfg.page_size, cfg.top_pages
-    steps_per_layer = -(-(args.warmup + args.steps) // args.layers) + 2
+    nL = args.layers
+    steps_per_layer = -(-(args.warmup + args.steps) // nL) + args.attn_reps + 4
     cap = cfg.context + steps_per_layer
     c = se.cache(B, Hq, H, D, D, cap, "bf16")
-    log(f"workload quest_32k: B={B} Hq={Hq} Hkv={H} D={D} ctx={cfg.context} P={P} top={k} cap={cap} "
-        f"layers={args.layers}")
+    log(f"quest_32k: B={B} Hq={Hq} Hkv={H} D={D} ctx={cfg.context} P={P} top={k} cap={cap} layers={nL}")
     t0 = time.time()
     K, V = gen.cache_kv(cfg, 0, cap)
     K0 = torch.from_numpy(K).to("cuda", torch.bfloat16)
@@ -90,13 +174,13 @@ def main():
     kn, vn = gen.decode_kv_new(cfg, 0, 0)
     kn = torch.from_numpy(kn).to("cuda", torch.bfloat16)
     vn = torch.from_numpy(vn).to("cuda", torch.bfloat16)
-    layers = [Layer(se, cfg, c, K0, V0, 977 * i, torch) for i in range(args.layers)]
+    layers = [QuestLayer(se, cfg, c, K0, V0, 977 * i, torch) for i in range(nL)]
     del K0, V0
     ws_q = se.workspace(se.SE_OP_QUEST, c, P, k)
     ws_a = se.workspace(se.SE_OP_ATTN, c, k * P, args.splits)
     lse = torch.empty((B, Hq), device="cuda")
     torch.cuda.synchronize()
-    log(f"caches ready in {time.time() - t0:.1f}s")
+    log(f"quest_32k: caches ready in {time.time() - t0:.1f}s")
     # a plain 256 MiB device copy of known size: counter-based traffic figures are
     # scaled by what the counters report for it
     calib = torch.empty(128 << 20, dtype=torch.bfloat16, device="cuda")
@@ -115,63 +199,18 @@ def main():
         se.se_sparse_decode_attn(c, q, L.k, L.v, L.seq, L.view, L.vlen, k, P, cfg.softmax_scale, L.out, lse,
                                  num_splits=args.splits, ws=ws_a)
 
-    nL = args.layers
     use_graph = not args.no_graph
-    # warm-up (eager), also compiles nothing: the kernels are prebuilt
     for i in range(args.warmup):
         step(layers[i % nL])
     torch.cuda.synchronize()
+    t_step = Timer(torch, lambda: [step(L) for L in layers], use_graph)
+    t_attn = Timer(torch, lambda: [attn_only(L) for L in layers], use_graph)
+    reps = max(1, args.steps // nL)
+    n_steps = reps * nL
+    ms_step = t_step.ms_per_replay(reps) / nL
+    us_attn = t_attn.ms_per_replay(args.attn_reps) * 1e3 / nL
 
-    if use_graph:
-        s = torch.cuda.Stream()
-        g_step = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_step, stream=s):
-            for L in layers:
-                step(L)
-        g_attn = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_attn, stream=s):
-            for L in layers:
-                attn_only(L)
-        torch.cuda.synchronize()
-
-    # ---- timed whole steps
-    reps = max(1, args.steps // nL) if use_graph else args.steps
-    n_steps = reps * nL if use_graph else args.steps
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    if use_graph:
-        with torch.cuda.stream(s):
-            e0.record(s)
-            for _ in range(reps):
-                g_step.replay()
-            e1.record(s)
-    else:
-        e0.record()
-        for i in range(n_steps):
-            step(layers[i % nL])
-        e1.record()
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / n_steps
-
-    # ---- attention kernel alone (same views), for the roofline
-    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    if use_graph:
-        with torch.cuda.stream(s):
-            a0.record(s)
-            for _ in range(args.attn_reps):
-                g_attn.replay()
-            a1.record(s)
-        n_attn = args.attn_reps * nL
-    else:
-        a0.record()
-        for i in range(args.attn_reps * nL):
-            attn_only(layers[i % nL])
-        a1.record()
-        n_attn = args.attn_reps * nL
-    torch.cuda.synchronize()
-    us_attn = a0.elapsed_time(a1) * 1e3 / n_attn
-
-    # algorithmic bytes of one attention launch: K and V rows of the selected tokens,
+    # algorithmic bytes of one attention call: K and V rows of the selected tokens,
     # plus q, the views and the fp32 outputs
     seq_h = layers[0].seq.cpu().numpy()
     vlen_h = layers[0].vlen.cpu().numpy()
@@ -183,32 +222,343 @@ def main():
             toks += int(np.minimum(P, np.maximum(0, seq_h[b] - pages * P)).sum())
     attn_bytes = toks * D * 2 * 2 + B * Hq * D * 2 + B * H * k * 4 + B * Hq * (D + 1) * 4
     achieved = attn_bytes / (us_attn * 1e-6) / 1e9
-
-    tok_s = B / (ms_step * 1e-3)
-    result = {
-        "metric": "sparse decode tokens/s per layer-step (Quest, 32K ctx) + achieved HBM GB/s of the attention kernel",
-        "value": round(tok_s, 1),
-        "unit": "tokens/s",
-        "n_gpus": 1, "steps": n_steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic (seeded grid-quantised N(0,1), 8 planted pages per KV head)",
-        "config": {"workload": "quest_32k", "batch": B, "q_heads": Hq, "kv_heads": H, "head_dim": D,
-                   "context": cfg.context, "page_size": P, "top_pages": k, "layers_rotated": nL,
-                   "graph": use_graph, "attn_splits": args.splits},
+    traffic = counter_traffic("quest_32k_hbm_counters.txt", ("attn_mfma_kernel", "attn_combine_kernel"),
+                              "attn_mfma.hip")
+    del layers
+    free(torch)
+    return cfg, {
+        "tokens_per_s": B / (ms_step * 1e-3), "ms_per_step": ms_step, "steps": n_steps,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "se_sparse_decode_attn (split-K main + combine)", "us_per_launch": round(us_attn, 3),
                      "bytes_per_launch": attn_bytes},
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+
+
+# ---------------------------------------------------------------- SnapKV 128K
+
+def run_snapkv(se, torch, args):
+    from workloads import get_config
+
+    cfg = get_config(2)
+    B, H, Hq, D = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.d_k
+    L, W, pool, budget = cfg.context, cfg.snap_window, cfg.snap_pool, cfg.snap_budget
+    nL = args.layers
+    steps = max(nL, args.steps // 2 // nL * nL)
+    cap_out = budget + (steps // nL + 4)
+    log(f"snapkv_128k: B={B} Hq={Hq} Hkv={H} D={D} prompt={L} W={W} pool={pool} budget={budget}")
+    c = se.cache(B, Hq, H, D, D, L, "bf16")
+    oc = se.cache(B, Hq, H, D, D, cap_out, "bf16")
+    K = dev_grid(torch, (B, H, L, D), 21, torch.bfloat16)
+    V = dev_grid(torch, (B, H, L, D), 22, torch.bfloat16)
+    qo = dev_grid(torch, (B, Hq, W, D), 23, torch.bfloat16)
+    k_out = torch.zeros((B, H, cap_out, D), dtype=torch.bfloat16, device="cuda")
+    v_out = torch.zeros_like(k_out)
+    kept = torch.empty((B, H, budget), dtype=torch.int32, device="cuda")
+    olen = torch.empty((B,), dtype=torch.int32, device="cuda")
+    ws = se.workspace(se.SE_OP_SNAPKV, c, L, W)
+
+    def compact():
+        se.se_snapkv_score_compact(c, qo, K, V, L, W, pool, budget, cfg.softmax_scale, oc, k_out, v_out, kept,
+                                   None, olen, ws)
+
+    compact()
+    torch.cuda.synchronize()
+    t_c = Timer(torch, compact, not args.no_graph)
+    ms_compact = t_c.ms_per_replay(3)
+    # algorithmic bytes: two passes over the prompt's keys, the kept rows read and written
+    compact_bytes = 2 * B * H * L * D * 2 + 2 * 2 * B * H * budget * D * 2
+    compact_flops = 2 * 2 * B * Hq * W * L * D   # q.k in both passes
+    del K, V, t_c
+    free(torch)
+
+    # decode over the compacted cache: nL copies (identity view over seq_len rows)
+    lay = []
+    for i in range(nL):
+        lay.append(dict(k=torch.roll(k_out, shifts=i, dims=2).contiguous(),
+                        v=torch.roll(v_out, shifts=i, dims=2).contiguous(), seq=olen.clone(),
+                        out=torch.empty((B, Hq, D), device="cuda")))
+    q = dev_grid(torch, (B, Hq, D), 24, torch.bfloat16)
+    kn = dev_grid(torch, (B, H, D), 25, torch.bfloat16)
+    vn = dev_grid(torch, (B, H, D), 26, torch.bfloat16)
+    lse = torch.empty((B, Hq), device="cuda")
+    ws_a = se.workspace(se.SE_OP_ATTN, oc, cap_out, 0)
+
+    def step(Ly):
+        se.se_kv_append(oc, Ly["k"], Ly["v"], kn, vn, None, Ly["seq"])
+        se.se_sparse_decode_attn(oc, q, Ly["k"], Ly["v"], Ly["seq"], None, None, 0, 1, cfg.softmax_scale,
+                                 Ly["out"], lse, ws=ws_a)
+
+    def attn(Ly):
+        se.se_sparse_decode_attn(oc, q, Ly["k"], Ly["v"], Ly["seq"], None, None, 0, 1, cfg.softmax_scale,
+                                 Ly["out"], lse, ws=ws_a)
+
+    step(lay[0])
+    t_s = Timer(torch, lambda: [step(Ly) for Ly in lay], not args.no_graph)
+    t_a = Timer(torch, lambda: [attn(Ly) for Ly in lay], not args.no_graph)
+    ms_step = t_s.ms_per_replay(steps // nL) / nL
+    us_attn = t_a.ms_per_replay(4) * 1e3 / nL
+    toks = int(lay[0]["seq"].sum().item()) * H
+    attn_bytes = toks * D * 2 * 2 + B * Hq * D * 2 + B * Hq * (D + 1) * 4
+    del lay, k_out, v_out, t_s, t_a
+    free(torch)
+    return {
+        "workload": "snapkv_128k", "batch": B, "prompt": L, "budget": budget, "window": W, "pool": pool,
+        "compaction": {"ms_per_call": round(ms_compact, 4),
+                       "prompt_tokens_per_s": round(B * L / (ms_compact * 1e-3), 1),
+                       "algorithmic_GBps": round(compact_bytes / (ms_compact * 1e-3) / 1e9, 1),
+                       "score_TFLOPs": round(compact_flops / (ms_compact * 1e-3) / 1e12, 1)},
+        "decode": {"tokens_per_s": round(B / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 5), "steps": steps,
+                   "attn_us": round(us_attn, 3), "attn_GBps": round(attn_bytes / (us_attn * 1e-6) / 1e9, 1),
+                   "attn_frac_of_peak": round(attn_bytes / (us_attn * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+
+
+# ---------------------------------------------------------------- H2O 16K
+
+def run_h2o(se, torch, args):
+    from workloads import generator as gen
+    from workloads import get_config
+
+    cfg = get_config(3)
+    B, H, Hq, D, G = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.d_k, cfg.group
+    heavy, recent = cfg.h2o_heavy, cfg.h2o_recent
+    cap = heavy + recent + 1
+    nL = args.layers
+    steps = max(nL, args.steps // nL * nL)
+    log(f"h2o_16k: B={B} Hq={Hq} Hkv={H} D={D} ctx={cfg.context} heavy={heavy} recent={recent}")
+    c = se.cache(B, Hq, H, D, D, cap, "bf16")
+    pos = np.empty((B, H, cap), np.int32)
+    acc = np.empty((B, H, cap), np.float32)
+    for u in range(B * H):
+        pos[u // H, u % H], acc[u // H, u % H] = gen.h2o_initial_state(cfg, 0, u)
+    pos_d = torch.from_numpy(pos).cuda()
+    acc_d = torch.from_numpy(acc).cuda()
+    lay = []
+    for i in range(nL):
+        lay.append(dict(k=dev_grid(torch, (B, H, cap, D), 31 + 2 * i, torch.bfloat16),
+                        v=dev_grid(torch, (B, H, cap, D), 32 + 2 * i, torch.bfloat16),
+                        pos=pos_d.clone(), acc=acc_d.clone(),
+                        seq=torch.full((B,), cap, dtype=torch.int32, device="cuda"),
+                        evict=torch.full((B, H), cap - 1, dtype=torch.int32, device="cuda"),
+                        out=torch.empty((B, Hq, D), device="cuda"), cur=cfg.context + i))
+    q = dev_grid(torch, (B, Hq, D), 30, torch.bfloat16)
+    kn = dev_grid(torch, (B, H, D), 29, torch.bfloat16)
+    vn = dev_grid(torch, (B, H, D), 28, torch.bfloat16)
+    lse = torch.empty((B, Hq), device="cuda")
+    logits = torch.empty((B, Hq, cap), device="cuda")
+    ws_a = se.workspace(se.SE_OP_ATTN, c, cap, 0)
+
+    # each captured layer slot runs at its own position; replays repeat the same work
+    def step(Ly):
+        se.se_kv_append(c, Ly["k"], Ly["v"], kn, vn, Ly["evict"], Ly["seq"])
+        se.se_sparse_decode_attn(c, q, Ly["k"], Ly["v"], Ly["seq"], None, None, 0, 1, cfg.softmax_scale, Ly["out"],
+                                 lse, logits, cap, 0, ws_a)
+        se.se_h2o_accumulate_evict(c, logits, lse, cap, Ly["seq"], Ly["pos"], Ly["acc"], Ly["cur"], heavy, recent,
+                                   Ly["evict"])
+
+    for Ly in lay:
+        step(Ly)
+    t_s = Timer(torch, lambda: [step(Ly) for Ly in lay], not args.no_graph)
+    ms_step = t_s.ms_per_replay(steps // nL) / nL
+    step_bytes = B * H * cap * (2 * D * 2 + 2 * G * 4 + 4 * 3) + B * Hq * D * (2 + 4)
+    del lay, t_s
+    free(torch)
+    return {"workload": "h2o_16k", "batch": B, "heavy": heavy, "recent": recent,
+            "tokens_per_s": round(B / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 5), "steps": steps,
+            "step_algorithmic_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1)}
+
+
+# ---------------------------------------------------------------- OmniKV 16K, 48 layers
+
+def omni_plan(n_layers, filters):
+    """(mode, source filter layer) per layer: dense before the first filter layer,
+    'filter' at a filter layer, else 'sparse' over the nearest filter layer below."""
+    plan = []
+    for layer in range(n_layers):
+        if layer in filters:
+            plan.append(("filter", layer))
+        else:
+            below = [f for f in filters if f < layer]
+            plan.append(("sparse", max(below)) if below else ("dense", -1))
+    return plan
+
+
+def run_omnikv(se, torch, args):
+    from workloads import get_config
+
+    cfg = get_config(3)
+    B, H, Hq, D = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.d_k
+    NL, filters, top = cfg.omni_layers, cfg.omni_filters, cfg.omni_top_k
+    sweeps = max(4, args.steps // 8)
+    cap = cfg.context + sweeps + 8
+    log(f"omnikv_16k: B={B} Hq={Hq} Hkv={H} D={D} ctx={cfg.context} layers={NL} filters={filters} top={top}")
+    c = se.cache(B, Hq, H, D, D, cap, "bf16")
+    plan = omni_plan(NL, filters)
+    ks, vs, seqs = [], [], []
+    for layer in range(NL):
+        ks.append(dev_grid(torch, (B, H, cap, D), 1000 + 2 * layer, torch.bfloat16))
+        vs.append(dev_grid(torch, (B, H, cap, D), 1001 + 2 * layer, torch.bfloat16))
+        seqs.append(torch.full((B,), cfg.context, dtype=torch.int32, device="cuda"))
+    views = {f: torch.empty((B, H, top), dtype=torch.int32, device="cuda") for f in filters}
+    vlens = {f: torch.empty((B, H), dtype=torch.int32, device="cuda") for f in filters}
+    qs = [dev_grid(torch, (B, Hq, D), 2000 + layer, torch.bfloat16) for layer in range(NL)]
+    kn = dev_grid(torch, (B, H, D), 2100, torch.bfloat16)
+    vn = dev_grid(torch, (B, H, D), 2101, torch.bfloat16)
+    out = torch.empty((B, Hq, D), device="cuda")
+    lse = torch.empty((B, Hq), device="cuda")
+    logits = torch.empty((B, Hq, cap), device="cuda")
+    ws_dense = se.workspace(se.SE_OP_ATTN, c, cap, 0)
+    ws_sparse = se.workspace(se.SE_OP_ATTN, c, top, 0)
+    ws_topk = se.workspace(se.SE_OP_OMNIKV, c, cap, top)
+
+    def sweep():
+        for layer, (mode, src) in enumerate(plan):
+            se.se_kv_append(c, ks[layer], vs[layer], kn, vn, None, seqs[layer])
+            if mode == "sparse":
+                se.se_sparse_decode_attn(c, qs[layer], ks[layer], vs[layer], seqs[layer], views[src], vlens[src], top,
+                                         1, cfg.softmax_scale, out, lse, ws=ws_sparse)
+            elif mode == "dense":
+                se.se_sparse_decode_attn(c, qs[layer], ks[layer], vs[layer], seqs[layer], None, None, 0, 1,
+                                         cfg.softmax_scale, out, lse, ws=ws_dense)
+            else:
+                se.se_sparse_decode_attn(c, qs[layer], ks[layer], vs[layer], seqs[layer], None, None, 0, 1,
+                                         cfg.softmax_scale, out, lse, logits, cap, 0, ws_dense)
+                se.se_omnikv_topk(c, logits, lse, cap, seqs[layer], top, views[layer], vlens[layer], None, ws_topk)
+
+    sweep()
+    t_s = Timer(torch, sweep, not args.no_graph)
+    ms_sweep = t_s.ms_per_replay(sweeps - 2)
+    n = cfg.context + sweeps
+    n_dense = sum(1 for m, _ in plan if m != "sparse")
+    n_sparse = NL - n_dense
+    sweep_bytes = B * H * (n_dense * n * D * 4 + n_sparse * top * D * 4) + len(filters) * B * Hq * n * 4 * 2
+    del ks, vs, t_s, logits
+    free(torch)
+    return {"workload": "omnikv_16k", "batch": B, "layers": NL, "filters": list(filters), "top_k": top,
+            "tokens_per_s_per_48_layer_step": round(B / (ms_sweep * 1e-3), 1),
+            "ms_per_48_layer_step": round(ms_sweep, 4), "ms_per_layer": round(ms_sweep / NL, 5),
+            "sweeps": sweeps - 2, "sweep_algorithmic_GBps": round(sweep_bytes / (ms_sweep * 1e-3) / 1e9, 1)}
+
+
+# ---------------------------------------------------------------- MLA 128K
+
+def run_mla(se, torch, args):
+    from workloads import get_config
+
+    cfg = get_config(4)
+    B, Hq, D, Dv, P, k = cfg.batch, cfg.n_q_heads, cfg.d_k, cfg.d_v, cfg.page_size, cfg.top_pages
+    nL = args.layers
+    steps = max(nL, args.steps // 2 // nL * nL)
+    cap = cfg.context + steps // nL + 4
+    log(f"mla_128k: B={B} heads={Hq} latent={D} (V {Dv}) ctx={cfg.context} P={P} top={k} layers={nL}")
+    c = se.cache(B, Hq, 1, D, Dv, cap, "bf16", latent=True)
+    ncp = (cap + P - 1) // P
+    lay = []
+    for i in range(nL):
+        Ly = dict(c=torch.empty((B, 1, cap, D), dtype=torch.bfloat16, device="cuda"),
+                  seq=torch.full((B,), cfg.context, dtype=torch.int32, device="cuda"),
+                  kmin=torch.empty((B, 1, ncp, D), dtype=torch.bfloat16, device="cuda"),
+                  view=torch.empty((B, 1, k), dtype=torch.int32, device="cuda"),
+                  vlen=torch.empty((B, 1), dtype=torch.int32, device="cuda"),
+                  out=torch.empty((B, Hq, Dv), device="cuda"))
+        Ly["kmax"] = torch.empty_like(Ly["kmin"])
+        for b in range(B):
+            Ly["c"][b] = dev_grid(torch, (1, cap, D), 3000 + 64 * i + b, torch.bfloat16)
+        se.se_page_meta_update(c, Ly["c"], Ly["kmin"], Ly["kmax"], Ly["seq"], P, 0)
+        lay.append(Ly)
+    q = dev_grid(torch, (B, Hq, D), 3900, torch.bfloat16)
+    kn = dev_grid(torch, (B, 1, D), 3901, torch.bfloat16)
+    lse = torch.empty((B, Hq), device="cuda")
+    ws_q = se.workspace(se.SE_OP_QUEST, c, P, k)
+    ws_a = se.workspace(se.SE_OP_ATTN, c, k * P, 0)
+
+    def step(Ly):
+        se.se_kv_append(c, Ly["c"], None, kn, None, None, Ly["seq"])
+        se.se_page_meta_update(c, Ly["c"], Ly["kmin"], Ly["kmax"], Ly["seq"], P, -1)
+        se.se_quest_select(c, q, Ly["kmin"], Ly["kmax"], Ly["seq"], P, k, Ly["view"], Ly["vlen"], None, ws_q)
+        se.se_sparse_decode_attn(c, q, Ly["c"], None, Ly["seq"], Ly["view"], Ly["vlen"], k, P, cfg.softmax_scale,
+                                 Ly["out"], lse, ws=ws_a)
+
+    def attn(Ly):
+        se.se_sparse_decode_attn(c, q, Ly["c"], None, Ly["seq"], Ly["view"], Ly["vlen"], k, P, cfg.softmax_scale,
+                                 Ly["out"], lse, ws=ws_a)
+
+    step(lay[0])
+    t_s = Timer(torch, lambda: [step(Ly) for Ly in lay], not args.no_graph)
+    t_a = Timer(torch, lambda: [attn(Ly) for Ly in lay], not args.no_graph)
+    ms_step = t_s.ms_per_replay(steps // nL) / nL
+    us_attn = t_a.ms_per_replay(4) * 1e3 / nL
+    seq_h = lay[0]["seq"].cpu().numpy()
+    vlen_h, view_h = lay[0]["vlen"].cpu().numpy(), lay[0]["view"].cpu().numpy()
+    toks = 0
+    for b in range(B):
+        pages = view_h[b, 0, :vlen_h[b, 0]]
+        toks += int(np.minimum(P, np.maximum(0, seq_h[b] - pages * P)).sum())
+    attn_bytes = toks * D * 2 + B * Hq * D * 2 + B * k * 4 + B * Hq * (Dv + 1) * 4
+    attn_flops = 2 * Hq * toks * (D + Dv)
+    del lay, t_s, t_a
+    free(torch)
+    gbps = attn_bytes / (us_attn * 1e-6) / 1e9
+    tfl = attn_flops / (us_attn * 1e-6) / 1e12
+    return {"workload": "mla_128k", "batch": B, "heads": Hq, "latent": D, "d_v": Dv, "context": cfg.context,
+            "page_size": P, "top_pages": k,
+            "tokens_per_s": round(B / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 5), "steps": steps,
+            "attn_us": round(us_attn, 3), "attn_GBps": round(gbps, 1), "attn_frac_of_hbm_peak": round(gbps / HBM_PEAK_GBS, 4),
+            "attn_TFLOPs": round(tfl, 1), "attn_frac_of_mfma_peak": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
+# ---------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the path has no multi-GPU mode; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    wanted = [w.strip() for w in args.workloads.split(",") if w.strip()]
+    bad = [w for w in wanted if w not in ALL_WORKLOADS]
+    if bad:
+        print(f"unknown workloads {bad}; choose from {ALL_WORKLOADS}", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import sparse_attention_kv_quest_amd as se
+
+    se.load()
+    result = {
+        "metric": "sparse decode tokens/s per layer-step (Quest, 32K ctx) + achieved HBM GB/s of the attention kernel",
+        "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": 0, "warmup": args.warmup, "ms_per_step": None,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded grid-quantised N(0,1); Quest: 8 planted pages per KV head)",
+    }
+    extra = {}
+    if "quest_32k" in wanted:
+        cfg, r = run_quest(se, torch, args)
+        result.update({"value": round(r["tokens_per_s"], 1), "steps": r["steps"],
+                       "ms_per_step": round(r["ms_per_step"], 5)})
+        result["config"] = {"workload": "quest_32k", "batch": cfg.batch, "q_heads": cfg.n_q_heads,
+                            "kv_heads": cfg.n_kv_heads, "head_dim": cfg.d_k, "context": cfg.context,
+                            "page_size": cfg.page_size, "top_pages": cfg.top_pages, "layers_rotated": args.layers,
+                            "graph": not args.no_graph, "attn_splits": args.splits}
+        result["roofline"] = r["roofline"]
+        log(f"quest_32k: {r['ms_per_step'] * 1e3:.2f} us/step, attention {r['roofline']['us_per_launch']} us")
+    else:
+        result["config"] = {"workload": "none (headline skipped)"}
+    runners = {"snapkv_128k": run_snapkv, "h2o_16k": run_h2o, "omnikv_16k": run_omnikv, "mla_128k": run_mla}
+    for w in wanted:
+        if w in runners:
+            extra[w] = runners[w](se, torch, args)
+            log(f"{w}: {json.dumps(extra[w])}")
+    if extra:
+        result["workloads"] = extra
+    if "quest_32k" in wanted and not args.no_cpu_baseline:
+        from workloads import get_config
+        result["cpu_baseline"] = cpu_baseline(get_config(1), args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
 def cpu_baseline(cfg, budget_s):
-    """The CPU oracle, single-threaded, on a bounded sample of the same decode step:
-    per unit, page metadata, the Quest page view and the attention over it."""
+    """The CPU oracle, single-threaded, on a bounded sample of the headline decode
+    step: per unit, page metadata, the Quest page view and the attention over it."""
     from threadpoolctl import threadpool_limits
     import oracle
     from oracle import quest as oquest

@@ -1,6 +1,7 @@
 // Split-K flash decode over an AttentionView: the vector-ALU kernel (any
 // element type, key width <= 576, value width <= 512, group <= 64) and the
-// split combine.  The bf16 GQA fast path (MFMA) lives in attn_mfma.hip.
+// split combine.  The bf16 MFMA paths live in attn_mfma.hip (GQA) and
+// attn_mla.hip (576-wide latent rows).
 //
 // tokendh.com explainer, section "把边界划在'生命周期'上", and the ai-feeds
 // digest, section 方法 / 关键模块: every method's kept positions reach attention
@@ -168,6 +169,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
 int attn_auto_splits(const se_cache& c, int slots) {
   const int units = c.batch * c.n_kv_heads;
   if (attn_mfma_eligible(c)) return attn_mfma_auto_splits(units, slots);
+  if (attn_mla_eligible(c)) return attn_mla_auto_splits(units, c.n_q_heads / c.n_kv_heads, slots);
   int s = ceil_div(1024, units);
   s = std::max(1, std::min(s, ceil_div(slots, 64)));
   return std::min(s, COMBINE_MAX_SPLITS);
@@ -225,6 +227,7 @@ se_status launch_attn(const se_cache& c, const void* q, const void* k, const voi
   a.part_o = a.part_ml + size_t(a.B) * a.Hkv * a.splits * a.G * 2;
   se_status st = SE_ERR_UNSUPPORTED;
   if (attn_mfma_supported(a)) st = launch_attn_mfma(a, s);
+  else if (attn_mla_supported(a)) st = launch_attn_mla(a, s);
   if (st == SE_ERR_UNSUPPORTED) st = launch_attn_vector(a, s);
   if (st != SE_OK) return st;
   return launch_attn_combine(a, s);

@@ -56,12 +56,19 @@ inline AttnArgs make_attn_args(const se_cache& c, const void* q, const void* k, 
 }
 
 bool attn_mfma_supported(const AttnArgs& a);
+bool attn_mla_supported(const AttnArgs& a);
+int attn_mla_auto_splits(int units, int G, int slots);
+se_status launch_attn_mla(const AttnArgs& a, hipStream_t s);
 int attn_mfma_auto_splits(int units, int slots);
 se_status launch_attn_mfma(const AttnArgs& a, hipStream_t s);
 
 inline bool attn_mfma_eligible(const se_cache& c) {
   return c.dtype == SE_BF16 && !c.latent && (c.d_k == 128 || c.d_k == 64) && c.d_v == c.d_k &&
          c.n_q_heads / c.n_kv_heads <= 16;
+}
+
+inline bool attn_mla_eligible(const se_cache& c) {
+  return c.dtype == SE_BF16 && c.latent && c.d_k == 576 && c.d_v == 512 && c.n_q_heads / c.n_kv_heads <= 64;
 }
 
 }  // namespace se
