@@ -222,15 +222,14 @@ def run_quest(se, torch, args):
             toks += int(np.minimum(P, np.maximum(0, seq_h[b] - pages * P)).sum())
     attn_bytes = toks * D * 2 * 2 + B * Hq * D * 2 + B * H * k * 4 + B * Hq * (D + 1) * 4
     achieved = attn_bytes / (us_attn * 1e-6) / 1e9
-    traffic = counter_traffic("quest_32k_hbm_counters.txt", ("attn_mfma_kernel", "attn_combine_kernel"),
-                              "attn_mfma.hip")
+    traffic = counter_traffic("quest_32k_hbm_counters.txt", ("attn_mfma_kernel",), "attn_mfma.hip")
     del layers
     free(torch)
     return cfg, {
         "tokens_per_s": B / (ms_step * 1e-3), "ms_per_step": ms_step, "steps": n_steps,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "se_sparse_decode_attn (split-K main + combine)", "us_per_launch": round(us_attn, 3),
+                     "kernel": "attn_mfma_kernel (se_sparse_decode_attn: split-K, splits merged in-kernel)", "us_per_launch": round(us_attn, 3),
                      "bytes_per_launch": attn_bytes},
     }
 

@@ -17,9 +17,16 @@
  *
  * Conventions shared by every call
  *   - Every pointer argument except the se_cache descriptor is DEVICE memory
- *     owned by the caller.  The library never allocates or frees memory, keeps
- *     no state between calls and never synchronizes: all work is enqueued on
- *     `stream` (a hipStream_t; 0 is the null stream).
+ *     owned by the caller.  The library never allocates or frees memory and
+ *     never synchronizes: all work is enqueued on `stream` (a hipStream_t; 0
+ *     is the null stream).
+ *   - Workspaces (`ws`, se_workspace_bytes() bytes) are caller-owned scratch.
+ *     Their leading bytes hold completion counters that let the last block of
+ *     a split computation finish it inside the same launch: a workspace must
+ *     be zero-filled once before its first use (se_workspace_init) and every
+ *     call leaves those counters zero again, so one workspace serves any
+ *     sequence of calls, including graph replays.  Calls that share a
+ *     workspace must not run concurrently.
  *   - Arguments are validated on the host before anything is enqueued.  On an
  *     error the call returns a negative se_status, nothing is enqueued and the
  *     outputs are untouched.  SE_ERR_HIP reports a failed kernel launch.
@@ -47,7 +54,7 @@
 extern "C" {
 #endif
 
-#define SE_ABI_VERSION 1
+#define SE_ABI_VERSION 2
 
 typedef enum {
   SE_OK = 0,
@@ -207,6 +214,11 @@ se_status se_omnikv_topk(const se_cache* c, const float* logits, const float* ls
 
 /* Workspace bytes an operation needs for cache `c` (0 if none). */
 size_t se_workspace_bytes(int32_t op, const se_cache* c, int32_t a0, int32_t a1);
+
+/* Zero-fill `bytes` bytes of a workspace on `stream` with a fill kernel (no
+ * memset node, so the call may be captured into a graph).  ws must be
+ * 16-byte aligned unless bytes == 0. */
+se_status se_workspace_init(void* ws, size_t bytes, hipStream_t stream);
 const char* se_status_string(int32_t status);
 int32_t se_abi_version(void);
 

@@ -22,7 +22,7 @@ STATUS = {0: "SE_OK", -1: "SE_ERR_NULL", -2: "SE_ERR_SHAPE", -3: "SE_ERR_DTYPE",
 
 EXPORTS = ("se_kv_append", "se_page_meta_update", "se_quest_select", "se_sparse_decode_attn",
            "se_snapkv_score_compact", "se_h2o_accumulate_evict", "se_omnikv_topk",
-           "se_workspace_bytes", "se_status_string", "se_abi_version")
+           "se_workspace_bytes", "se_workspace_init", "se_status_string", "se_abi_version")
 
 
 class SeError(RuntimeError):
@@ -64,6 +64,8 @@ def load(path: str = LIB_PATH):
         f = getattr(lib, name)
         f.argtypes = args
         f.restype = ctypes.c_int32
+    lib.se_workspace_init.argtypes = [_P, _SZ, _P]
+    lib.se_workspace_init.restype = ctypes.c_int32
     lib.se_workspace_bytes.argtypes = [_I32, _C, _I32, _I32]
     lib.se_workspace_bytes.restype = _SZ
     lib.se_status_string.argtypes = [_I32]
@@ -120,10 +122,18 @@ def se_workspace_bytes(op: int, c: se_cache, a0: int, a1: int) -> int:
 
 
 def workspace(op: int, c: se_cache, a0: int, a1: int, device="cuda"):
-    """A device byte buffer of se_workspace_bytes(op, c, a0, a1) bytes (at least 256)."""
+    """A zero-filled device byte buffer of se_workspace_bytes(op, c, a0, a1) bytes (at
+    least 256): workspaces start zero-filled and every call leaves their counters zero."""
     import torch
     n = max(256, se_workspace_bytes(op, c, a0, a1))
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    se_workspace_init(ws)
+    return ws
+
+
+def se_workspace_init(ws, nbytes=None, stream=None):
+    n = _nbytes(ws) if nbytes is None else int(nbytes)
+    _check("se_workspace_init", load().se_workspace_init(_ptr(ws), n, _stream(stream)))
 
 
 def se_kv_append(c, k, v, k_new, v_new, slot, seq_len, stream=None):

@@ -71,6 +71,14 @@ size_t se_workspace_bytes(int32_t op, const se_cache* c, int32_t a0, int32_t a1)
   }
 }
 
+se_status se_workspace_init(void* ws, size_t bytes, hipStream_t stream) {
+  SE_TRACE_CALL("workspace_init bytes=%zu", bytes);
+  if (bytes == 0) return SE_OK;
+  if (!ws) return SE_ERR_NULL;
+  if (!aligned16(ws)) return SE_ERR_ALIGN;
+  return launch_zero_fill(ws, bytes, stream);
+}
+
 se_status se_kv_append(const se_cache* c, void* k, void* v, const void* k_new, const void* v_new,
                        const int32_t* slot, int32_t* seq_len, hipStream_t stream) {
   se_status st = check_cache(c);

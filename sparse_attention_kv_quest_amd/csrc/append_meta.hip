@@ -8,6 +8,22 @@
 
 namespace se {
 
+// Zero fill of a workspace: 16-byte stores, then the trailing bytes.
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint4* __restrict__ p, size_t n16, uint8_t* __restrict__ tail,
+                                                        int ntail) {
+  const size_t stride = size_t(gridDim.x) * blockDim.x;
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride) p[i] = make_uint4(0, 0, 0, 0);
+  if (blockIdx.x == 0 && int(threadIdx.x) < ntail) tail[threadIdx.x] = 0;
+}
+
+se_status launch_zero_fill(void* p, size_t bytes, hipStream_t s) {
+  const size_t n16 = bytes / 16;
+  const int ntail = int(bytes - n16 * 16);
+  const int grid = int(std::max<size_t>(1, std::min<size_t>(1024, (n16 + 255) / 256)));
+  hipLaunchKernelGGL(zero_fill_kernel, dim3(grid), dim3(256), 0, s, (uint4*)p, n16, (uint8_t*)p + n16 * 16, ntail);
+  return launch_status();
+}
+
 // One block per batch row: copies the new row of every KV head, then bumps seq_len.
 __global__ __launch_bounds__(256) void kv_append_kernel(
     uint32_t* __restrict__ k, uint32_t* __restrict__ v, const uint32_t* __restrict__ k_new,

@@ -1,7 +1,8 @@
 // Split-K flash decode over an AttentionView: the vector-ALU kernel (any
-// element type, key width <= 576, value width <= 512, group <= 64) and the
-// split combine.  The bf16 MFMA paths live in attn_mfma.hip (GQA) and
-// attn_mla.hip (576-wide latent rows).
+// element type, key width <= 576, value width <= 512, group <= 64), the
+// workspace layout and the dispatch.  The bf16 MFMA paths live in
+// attn_mfma.hip (GQA) and attn_mla.hip (576-wide latent rows); every kernel
+// merges its own splits (the block finishing a unit's last split does it).
 //
 // tokendh.com explainer, section "把边界划在'生命周期'上", and the ai-feeds
 // digest, section 方法 / 关键模块: every method's kept positions reach attention
@@ -108,24 +109,35 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(AttnArgs a) {
     }
     __syncthreads();
   }
-  // partial results of this split
+  if (a.splits == 1) {
+    const size_t row0 = size_t(b) * a.Hq + size_t(kvh) * G;
+#pragma unroll
+    for (int r = 0; r < MAXR; ++r) {
+      const int pair = threadIdx.x + 256 * r;
+      if (r < R && pair < G * Dv) attn_write_final(a, row0 + pair / Dv, pair % Dv, ms[pair / Dv], ls[pair / Dv], acc[r]);
+    }
+    return;
+  }
+  // partial results of this split; the block finishing the unit's last split merges them
   float* pml = a.part_ml + (size_t(unit) * a.splits + split) * G * 2;
   float* po = a.part_o + (size_t(unit) * a.splits + split) * G * Dv;
-  for (int h = threadIdx.x; h < G; h += 256) { pml[2 * h] = ms[h]; pml[2 * h + 1] = ls[h]; }
+  for (int h = threadIdx.x; h < G; h += 256) { st_part(a, pml + 2 * h, ms[h]); st_part(a, pml + 2 * h + 1, ls[h]); }
 #pragma unroll
   for (int r = 0; r < MAXR; ++r) {
     const int pair = threadIdx.x + 256 * r;
-    if (r < R && pair < G * Dv) po[pair] = acc[r];
+    if (r < R && pair < G * Dv) st_part(a, po + pair, acc[r]);
   }
+  if (!a.fused) return;
+  int* ctr = a.counters + unit * ATTN_MAX_HG;
+  if (attn_split_done(ctr, a.splits)) attn_merge_splits<256>(a, unit, 0, G, ctr, smem);
 }
 
-// One block per (head of the group, unit): merge the split partials by log-sum-exp.
+// One block per (head of the group, unit): merge the split partials by log-sum-exp
+// (used when a unit's partials are too large for one block to merge them quickly).
 // The per-split weights exp(m_s - M) are formed once in LDS; the output pass then
 // streams the partial outputs with independent loads.
-constexpr int COMBINE_MAX_SPLITS = 256;
-
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
-  __shared__ float f_s[COMBINE_MAX_SPLITS];
+  __shared__ float f_s[ATTN_MAX_SPLITS];
   __shared__ float red[2];
   const int unit = blockIdx.y, h = blockIdx.x;
   const int G = a.G, Dv = a.Dv, S = a.splits;
@@ -172,26 +184,33 @@ int attn_auto_splits(const se_cache& c, int slots) {
   if (attn_mla_eligible(c)) return attn_mla_auto_splits(units, c.n_q_heads / c.n_kv_heads, slots);
   int s = ceil_div(1024, units);
   s = std::max(1, std::min(s, ceil_div(slots, 64)));
-  return std::min(s, COMBINE_MAX_SPLITS);
+  return std::min(s, ATTN_MAX_SPLITS);
+}
+
+// Workspace: ticket counters (zero between calls), then the split partials.
+size_t attn_counter_bytes(const se_cache& c) {
+  return (size_t(c.batch) * c.n_kv_heads * ATTN_MAX_HG * sizeof(int) + 255) / 256 * 256;
 }
 
 size_t attn_ws_bytes(const se_cache& c, int slots, int num_splits) {
   const int S = num_splits > 0 ? num_splits : attn_auto_splits(c, slots);
   const size_t units = size_t(c.batch) * c.n_kv_heads, G = c.n_q_heads / c.n_kv_heads;
-  return units * S * G * (2 + size_t(c.d_v)) * sizeof(float);
+  return attn_counter_bytes(c) + units * S * G * (2 + size_t(c.d_v)) * sizeof(float);
 }
 
 se_status launch_attn_vector(const AttnArgs& a, hipStream_t s) {
   const int units = a.B * a.Hkv;
-  const size_t lds = (size_t(a.G) * a.Dk + VT * a.Dk + (a.latent ? 0 : VT * a.Dv) + a.G * VT + 3 * a.G) *
-                         sizeof(float) + VT * sizeof(int);
+  const size_t lds_main = (size_t(a.G) * a.Dk + VT * a.Dk + (a.latent ? 0 : VT * a.Dv) + a.G * VT + 3 * a.G) *
+                             sizeof(float) + VT * sizeof(int);
+  const size_t lds_merge = (size_t(2) * a.splits * a.G + a.G) * sizeof(float);   // reuses the same LDS afterwards
+  const size_t lds = std::max(lds_main, lds_merge);
   if (lds > 160 * 1024) return SE_ERR_UNSUPPORTED;
   const int R = (a.G * a.Dv + 255) / 256;
   dim3 grid(a.splits, units);
 #define SE_LAUNCH_VEC(TT, RR)                                                                       \
   do {                                                                                            \
     if (lds > 64 * 1024)                                                                          \
-      hipFuncSetAttribute((const void*)attn_vector_kernel<TT, RR>,                                \
+      (void)hipFuncSetAttribute((const void*)attn_vector_kernel<TT, RR>,                          \
                           hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));                  \
     hipLaunchKernelGGL((attn_vector_kernel<TT, RR>), grid, dim3(256), lds, s, a);                  \
   } while (0)
@@ -210,11 +229,6 @@ se_status launch_attn_vector(const AttnArgs& a, hipStream_t s) {
   return launch_status();
 }
 
-se_status launch_attn_combine(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(a.G, a.B * a.Hkv), dim3(128), 0, s, a);
-  return launch_status();
-}
-
 se_status launch_attn(const se_cache& c, const void* q, const void* k, const void* v,
                       const int32_t* seq_len, const int32_t* view_idx, const int32_t* view_len,
                       int view_cap, int granularity, float scale, float* out, float* lse,
@@ -223,14 +237,19 @@ se_status launch_attn(const se_cache& c, const void* q, const void* k, const voi
                               lse, logits, logit_cap);
   const int slots = view_idx ? view_cap * granularity : c.capacity;
   a.splits = num_splits > 0 ? num_splits : attn_auto_splits(c, slots);
-  a.part_ml = (float*)ws;
+  a.counters = (int*)ws;
+  a.part_ml = (float*)((char*)ws + attn_counter_bytes(c));
   a.part_o = a.part_ml + size_t(a.B) * a.Hkv * a.splits * a.G * 2;
+  // one block merges a unit's splits when their partials are small; large ones
+  // (MLA: 32 heads x 512 columns per split) go to the combine kernel
+  a.fused = a.splits > 1 && size_t(a.splits) * std::min(a.G, 32) * a.Dv * sizeof(float) <= ATTN_FUSED_MERGE_BYTES;
   se_status st = SE_ERR_UNSUPPORTED;
   if (attn_mfma_supported(a)) st = launch_attn_mfma(a, s);
   else if (attn_mla_supported(a)) st = launch_attn_mla(a, s);
   if (st == SE_ERR_UNSUPPORTED) st = launch_attn_vector(a, s);
-  if (st != SE_OK) return st;
-  return launch_attn_combine(a, s);
+  if (st != SE_OK || a.splits == 1 || a.fused) return st;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(a.G, a.B * a.Hkv), dim3(128), 0, s, a);
+  return launch_status();
 }
 
 }  // namespace se

@@ -5,6 +5,9 @@
 namespace se {
 
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr int ATTN_MAX_HG = 2;          // head groups of one unit launched as separate blocks (MLA, G <= 64)
+constexpr int ATTN_MAX_SPLITS = 256;
+constexpr size_t ATTN_FUSED_MERGE_BYTES = 64 << 10;   // partial output bytes per unit merged in-kernel
 
 struct AttnArgs {
   const void* q; const void* k; const void* v;
@@ -12,6 +15,8 @@ struct AttnArgs {
   float* out; float* lse; float* logits;
   float* part_ml;   // [units][splits][G][2]: running max, running sum
   float* part_o;    // [units][splits][G][Dv]: unnormalised output
+  int* counters;    // [units][ATTN_MAX_HG] split completion tickets, zero between calls
+  int fused;        // splits > 1 and the last block of a unit merges them (else the combine kernel)
   float scale;
   int B, Hq, Hkv, G, Dk, Dv, cap, latent, dtype;
   int k_stride, v_stride;  // elements per K / V row
@@ -53,6 +58,123 @@ inline AttnArgs make_attn_args(const se_cache& c, const void* q, const void* k, 
     if ((1 << sh) == a.gran) { a.gshift = sh; break; }
   a.logit_cap = logits ? logit_cap : 0;
   return a;
+}
+
+// ------------------------------------------------------------------ split-K completion
+// Every block of a split-K launch stores its partial (max, sum, output) and then
+// takes a ticket on its (unit, head group) counter; the block that takes the
+// last ticket merges all partials by log-sum-exp and resets the counter, so the
+// workspace is zero again when the launch ends.
+//
+// The blocks of one unit run on different XCDs, whose L2 caches are not
+// coherent with each other.  Device-scope fences would write back or
+// invalidate a whole L2 per block, which stalls every block streaming through
+// that XCD.  Instead the partials are written and read only with relaxed
+// device-scope atomic accesses (sc1 stores that write through to the coherence
+// point, sc1 loads that read from it); a writer waits for its stores to
+// complete before it takes its ticket, and the merging block issues its loads
+// only after its ticket shows every split done.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Partial store: a device-scope write-through store when the launch merges in-kernel,
+// a plain store when the combine kernel (a later launch) reads it.
+__device__ __forceinline__ void st_part(const AttnArgs& a, float* p, float v) {
+  if (a.fused) st_dev(p, v); else *p = v;
+}
+
+__device__ __forceinline__ bool attn_split_done(int* ctr, int splits) {
+  __shared__ int s_last;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);     // this thread's partial stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == splits - 1;
+  __syncthreads();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  return s_last != 0;
+}
+
+// Merge the splits of heads [h0, h0 + nh) of one unit into out / lse (natural-log
+// lse) and reset the unit's ticket counter.  `lds` holds >= 2 * splits * nh + nh
+// floats.  The per-split weights exp(m_s - M) are formed once per (split, head);
+// the output pass then issues its independent loads back to back.
+template <int NT>
+__device__ void attn_merge_splits(const AttnArgs& a, int unit, int h0, int nh, int* ctr, float* lds) {
+  const int S = a.splits, G = a.G, Dv = a.Dv;
+  const int b = unit / a.Hkv, kvh = unit % a.Hkv;
+  const float* pml = a.part_ml + size_t(unit) * S * G * 2;
+  const float* po = a.part_o + size_t(unit) * S * G * Dv;
+  float* wm = lds;              // [S][nh] running max, then weight
+  float* wl = lds + S * nh;     // [S][nh] running sum
+  float* inv = wl + S * nh;     // [nh] 1 / L
+  for (int i = threadIdx.x; i < S * nh; i += NT) {
+    const int s = i / nh, hl = i - s * nh;
+    const float m = ld_dev(pml + (s * G + h0 + hl) * 2);
+    const float l = ld_dev(pml + (s * G + h0 + hl) * 2 + 1);
+    wm[i] = m;
+    wl[i] = l;
+  }
+  __syncthreads();
+  const size_t row0 = size_t(b) * a.Hq + size_t(kvh) * G + h0;
+  for (int hl = threadIdx.x; hl < nh; hl += NT) {
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, wm[s * nh + hl]);
+    float L = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const float m = wm[s * nh + hl];
+      const float f = (m != -INFINITY) ? exp2f((m - M) * LOG2E) : 0.f;
+      wm[s * nh + hl] = f;
+      L += f * wl[s * nh + hl];
+    }
+    inv[hl] = L > 0.f ? 1.f / L : 0.f;
+    if (a.lse != nullptr) a.lse[row0 + hl] = L > 0.f ? M + logf(L) : -INFINITY;
+  }
+  __syncthreads();
+  // outputs in groups of OU per thread, splits in batches of SU: all OU x SU loads of a
+  // batch are issued before the first is used (a split past S repeats split S - 1 with weight 0)
+  constexpr int SU = 8, OU = 4;
+  const int total = nh * Dv;
+  for (int base = threadIdx.x; base < total; base += NT * OU) {
+    int hl[OU];
+    const float* src[OU];
+#pragma unroll
+    for (int u = 0; u < OU; ++u) {
+      const int idx = min(base + u * NT, total - 1);
+      hl[u] = idx / Dv;
+      src[u] = po + size_t(h0 + hl[u]) * Dv + (idx - hl[u] * Dv);
+    }
+    float O[OU];
+#pragma unroll
+    for (int u = 0; u < OU; ++u) O[u] = 0.f;
+    for (int s0 = 0; s0 < S; s0 += SU) {
+      float x[SU][OU];
+#pragma unroll
+      for (int j = 0; j < SU; ++j)
+#pragma unroll
+        for (int u = 0; u < OU; ++u) x[j][u] = ld_dev(src[u] + size_t(min(s0 + j, S - 1)) * G * Dv);
+#pragma unroll
+      for (int j = 0; j < SU; ++j)
+#pragma unroll
+        for (int u = 0; u < OU; ++u) O[u] += (s0 + j < S ? wm[(s0 + j) * nh + hl[u]] : 0.f) * x[j][u];
+    }
+#pragma unroll
+    for (int u = 0; u < OU; ++u) {
+      const int idx = base + u * NT;
+      if (idx < total) a.out[(row0 + hl[u]) * Dv + (idx - hl[u] * Dv)] = O[u] * inv[hl[u]];
+    }
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Final output of a unit handled by one block (splits == 1): out = O / L, lse = M + log L.
+__device__ __forceinline__ void attn_write_final(const AttnArgs& a, size_t row, int d, float M, float L, float O) {
+  a.out[row * a.Dv + d] = L > 0.f ? O * (1.f / L) : 0.f;
+  if (d == 0 && a.lse != nullptr) a.lse[row] = L > 0.f ? M + logf(L) : -INFINITY;
 }
 
 bool attn_mfma_supported(const AttnArgs& a);

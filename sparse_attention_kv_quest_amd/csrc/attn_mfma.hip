@@ -21,8 +21,8 @@
 // only moved (and the output rescaled) when a tile's max exceeds it by more
 // than 2^8, which keeps the accumulators untouched on almost every tile; the
 // shift cancels in the final normalisation.  The four waves merge their
-// (max, sum, output) in LDS and the block writes one partial; the combine
-// kernel merges the splits.
+// (max, sum, output) in LDS and the block writes one partial; the block that
+// finishes a unit's last split merges the splits, so a call is one launch.
 #include "attn_common.hpp"
 #include "mfma_util.hpp"
 
@@ -210,7 +210,10 @@ void attn_mfma_kernel(AttnArgs a) {
   constexpr int NDB = D / 16;
   constexpr int NKS = D / 32;
   static_assert(D == 64 || D == 128, "head width");
-  __shared__ __align__(16) uint16_t vt_lds[MF_WAVES][D * PITCH];
+  // V tiles; afterwards the wave merge and the split merge reuse the same LDS
+  constexpr int MERGE_U16 = (2 * (2 * ATTN_MAX_SPLITS * 16 + 16) + MF_WAVES - 1) / MF_WAVES;
+  constexpr int VT_U16 = D * PITCH > MERGE_U16 ? D * PITCH : MERGE_U16;
+  __shared__ __align__(16) uint16_t vt_lds[MF_WAVES][VT_U16];
   __shared__ float red_m[MF_WAVES][16], red_l[MF_WAVES][16];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -266,7 +269,7 @@ void attn_mfma_kernel(AttnArgs a) {
   st.lsum = 0.f;
 #pragma unroll
   for (int i = 0; i < NDB; ++i) st.o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  uint16_t* vt = vt_lds[w];
+  uint16_t* vt = vt_lds[w];   // row pitch PITCH, D rows
   float* lg_row = (a.logits != nullptr && c16 < G)
                       ? a.logits + (size_t(b) * a.Hq + size_t(kvh) * G + c16) * a.logit_cap
                       : nullptr;
@@ -327,6 +330,7 @@ void attn_mfma_kernel(AttnArgs a) {
   __syncthreads();
   float* pml = a.part_ml + (size_t(unit) * a.splits + split) * G * 2;
   float* po = a.part_o + (size_t(unit) * a.splits + split) * G * D;
+  const bool single = a.splits == 1;
   for (int idx = threadIdx.x; idx < G * D; idx += 256) {
     const int h = idx / D, d = idx % D;
     float M = red_m[0][h];
@@ -344,11 +348,21 @@ void attn_mfma_kernel(AttnArgs a) {
         }
       }
     }
-    po[h * D + d] = O;
-    if (d == 0) {
-      pml[2 * h] = M == -INFINITY ? -INFINITY : M * 0.6931471805599453f;
-      pml[2 * h + 1] = L;
+    const float Mn = M == -INFINITY ? -INFINITY : M * 0.6931471805599453f;   // log2 -> natural units
+    if (single) {
+      attn_write_final(a, size_t(b) * a.Hq + size_t(kvh) * G + h, d, Mn, L, O);
+    } else {
+      st_part(a, po + h * D + d, O);
+      if (d == 0) {
+        st_part(a, pml + 2 * h, Mn);
+        st_part(a, pml + 2 * h + 1, L);
+      }
     }
+  }
+  if (a.fused) {
+    int* ctr = a.counters + unit * ATTN_MAX_HG;
+    static_assert(2 * ATTN_MAX_SPLITS * 16 + 16 <= int(sizeof(vt_lds) / sizeof(float)), "merge scratch");
+    if (attn_split_done(ctr, a.splits)) attn_merge_splits<256>(a, unit, 0, G, ctr, red_o);
   }
 }
 

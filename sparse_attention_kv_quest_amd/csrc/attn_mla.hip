@@ -20,7 +20,8 @@
 // slots as bf16 hi + lo pairs that every wave then reads as the B operand.
 // The next tile's K loads are issued as soon as the scores are formed and its
 // V loads as soon as the transposes are done, so a tile of rows is always in
-// flight.  Partial (max, sum, output) per split go to the combine kernel.
+// flight.  Each split stores a partial (max, sum, output), which the combine
+// kernel merges (or, for small partials, the block finishing the last split).
 #include "attn_common.hpp"
 #include "mfma_util.hpp"
 
@@ -298,12 +299,32 @@ __global__ __launch_bounds__(ML_THREADS) void attn_mla_kernel(AttnArgs a) {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   float* pml = a.part_ml + (size_t(unit) * a.splits + split) * G * 2;
   float* po = a.part_o + (size_t(unit) * a.splits + split) * G * ML_DV;
+  const bool single = a.splits == 1;
+  const size_t row0 = size_t(b) * a.Hq + size_t(kvh) * G;
   // 32 heads x 64 dims of this wave: 16 float4 per head row, 512 float4 per wave
   for (int idx = lane; idx < 16 * NHB * 16; idx += 64) {
     const int hl = idx >> 4, d4 = idx & 15, h = h0 + hl;
     if (h < G) {
       const float* src = ob + hl * ML_OB_PITCH + 4 * d4;
-      *reinterpret_cast<float4*>(po + size_t(h) * ML_DV + ML_DW * w + 4 * d4) = make_float4(src[0], src[1], src[2], src[3]);
+      float4 v = make_float4(src[0], src[1], src[2], src[3]);
+      if (single) {
+        float L = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < ML_WAVES; ++ww) L += wsum[ww][hl];
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        v = make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
+        *reinterpret_cast<float4*>(a.out + (row0 + h) * ML_DV + ML_DW * w + 4 * d4) = v;
+      } else {
+        float* dst = po + size_t(h) * ML_DV + ML_DW * w + 4 * d4;
+        if (a.fused) {
+          st_dev(dst, v.x);
+          st_dev(dst + 1, v.y);
+          st_dev(dst + 2, v.z);
+          st_dev(dst + 3, v.w);
+        } else {
+          *reinterpret_cast<float4*>(dst) = v;
+        }
+      }
     }
   }
   if (w == 0 && lane < 16 * NHB) {
@@ -313,8 +334,21 @@ __global__ __launch_bounds__(ML_THREADS) void attn_mla_kernel(AttnArgs a) {
 #pragma unroll
       for (int ww = 0; ww < ML_WAVES; ++ww) L += wsum[ww][lane];
       const float M = (lane >> 4) ? m2[NHB - 1] : m2[0];   // lanes 0..15: head block 0, 16..31: block 1
-      pml[2 * h] = (M == -INFINITY) ? -INFINITY : M * 0.6931471805599453f;
-      pml[2 * h + 1] = L;
+      const float Mn = (M == -INFINITY) ? -INFINITY : M * 0.6931471805599453f;
+      if (single) {
+        if (a.lse != nullptr) a.lse[row0 + h] = L > 0.f ? Mn + logf(L) : -INFINITY;
+      } else {
+        st_part(a, pml + 2 * h, Mn);
+        st_part(a, pml + 2 * h + 1, L);
+      }
+    }
+  }
+  if (a.fused) {
+    int* ctr = a.counters + unit * ATTN_MAX_HG + hg;
+    static_assert(2 * ATTN_MAX_SPLITS * 32 + 32 <= ML_LDS_BYTES / 4, "merge scratch");
+    if (attn_split_done(ctr, a.splits)) {
+      __syncthreads();   // every wave has stored its slice of the output transpose
+      attn_merge_splits<ML_THREADS>(a, unit, h0, min(32, G - h0), ctr, reinterpret_cast<float*>(lds));
     }
   }
 }

@@ -132,7 +132,7 @@ se_status launch_omnikv(const se_cache& c, const float* logits, const float* lse
   const int G = c.n_q_heads / c.n_kv_heads, units = c.batch * c.n_kv_heads;
   if (logit_cap <= OMNI_LDS) {
     const size_t lds = size_t(logit_cap) * sizeof(float);
-    hipFuncSetAttribute((const void*)omnikv_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+    (void)hipFuncSetAttribute((const void*)omnikv_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                         int(OMNI_LDS * sizeof(float)));
     hipLaunchKernelGGL(omnikv_kernel<true>, dim3(units), dim3(OMNI_BLOCK), lds, s, logits, lse, logit_cap,
                        seq_len, view_idx, view_len, scores, (float*)nullptr, c.n_kv_heads, G, top_k);

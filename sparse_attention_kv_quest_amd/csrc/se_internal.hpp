@@ -197,6 +197,7 @@ inline se_status launch_status() {
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // ------------------------------------------------------------------ launchers (host)
+se_status launch_zero_fill(void* p, size_t bytes, hipStream_t s);
 se_status launch_kv_append(const se_cache& c, void* k, void* v, const void* k_new, const void* v_new,
                            const int32_t* slot, int32_t* seq_len, hipStream_t s);
 se_status launch_page_meta(const se_cache& c, const void* k, void* kmin, void* kmax,

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert se.se_abi_version() == 1
+    assert se.se_abi_version() == 2
     assert se.se_status_string(0) == "ok"
     assert se.se_status_string(-6) == "workspace too small"
     assert se.se_status_string(123) == "unknown status"
@@ -43,10 +43,17 @@ def test_workspace_sizes(lib):
     c = se.cache(16, 32, 4, 128, 128, 32832, "bf16")
     assert se.se_workspace_bytes(se.SE_OP_QUEST, c, 16, 128) == 16 * 4 * 2052 * 4
     n = se.se_workspace_bytes(se.SE_OP_ATTN, c, 2048, 8)
-    assert n == 16 * 4 * 8 * 8 * (128 + 2) * 4
+    counters = 512          # 64 units x 2 head groups x int32, rounded up to 256 bytes
+    assert n == counters + 16 * 4 * 8 * 8 * (128 + 2) * 4
     assert se.se_workspace_bytes(se.SE_OP_ATTN, c, 2048, 0) > 0
     bad = se.cache(16, 30, 4, 128, 128, 32832, "bf16")
     assert se.se_workspace_bytes(se.SE_OP_ATTN, bad, 2048, 8) == 0
+
+
+def test_workspace_init_validation(lib):
+    assert lib.se_workspace_init(None, 0, None) == 0                  # nothing to do, nothing launched
+    assert lib.se_workspace_init(None, 256, None) == -1               # SE_ERR_NULL
+    assert lib.se_workspace_init(0x10008, 256, None) == -4            # SE_ERR_ALIGN
 
 
 FAKE = 0x10000     # an aligned, never dereferenced address: validation fails before any launch

@@ -116,3 +116,32 @@ def test_results_are_deterministic(se):
     b = run_attn(se, c, qd, kd, vd, seq, scale=0.1, logit_cap=333)
     for x, y in zip(a, b):
         np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("name", ["bf16_d128_g8", "f32_d64_g4", "bf16_mla"])
+def test_workspace_counters_return_to_zero(se, name):
+    """The split tickets at the head of the workspace are zero after every call, so
+    one workspace serves repeated calls with any split count, whichever merge path
+    (in-kernel or combine kernel) the split count selects."""
+    cfg = CFGS[name]
+    banner(f"workspace reuse {name}")
+    cap = 700 if cfg.latent else 333
+    lens = [cap - 5 * i for i in range(cfg.batch)]
+    c, K, V, q, kd, vd, qd, seq = make(se, cfg, cap, lens)
+    ws = se.workspace(se.SE_OP_ATTN, c, cap, 100)
+    ro, rl, _ = oracle.decode_attention(q, K, V, lens, 0.1, latent_dv=cfg.d_v if cfg.latent else None)
+    first = None
+    # small split counts merge inside the kernel, large ones in the combine kernel
+    for splits in (7, 3, 1, 100, 40, 7):
+        out, lse = zeros((cfg.batch, cfg.n_q_heads, cfg.d_v)), zeros((cfg.batch, cfg.n_q_heads))
+        se.se_sparse_decode_attn(c, qd, kd, vd if vd is not None else kd, seq, None, None, 0, 1, 0.1, out, lse,
+                                 None, 0, splits, ws)
+        torch.cuda.synchronize()
+        assert int(ws[:256].count_nonzero()) == 0
+        np.testing.assert_allclose(host(out), ro, rtol=0, atol=TOL[cfg.dtype])
+        np.testing.assert_allclose(host(lse), rl, rtol=0, atol=TOL[cfg.dtype])
+        if splits == 7:
+            if first is None:
+                first = host(out)
+            else:
+                np.testing.assert_array_equal(host(out), first)

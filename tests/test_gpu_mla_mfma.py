@@ -49,7 +49,7 @@ def check(got, ref, lens_or_counts, logit_cap):
 
 
 @pytest.mark.parametrize("heads", [16, 32, 48, 64])
-@pytest.mark.parametrize("splits", [0, 1, 3])
+@pytest.mark.parametrize("splits", [0, 1, 2, 3])
 def test_mla_identity_view_head_groups(se, heads, splits):
     banner(f"mla mfma identity heads={heads} splits={splits}")
     cap = 777
