@@ -62,42 +62,16 @@ inline AttnArgs make_attn_args(const se_cache& c, const void* q, const void* k, 
 
 // ------------------------------------------------------------------ split-K completion
 // Every block of a split-K launch stores its partial (max, sum, output) and then
-// takes a ticket on its (unit, head group) counter; the block that takes the
-// last ticket merges all partials by log-sum-exp and resets the counter, so the
-// workspace is zero again when the launch ends.
-//
-// The blocks of one unit run on different XCDs, whose L2 caches are not
-// coherent with each other.  Device-scope fences would write back or
-// invalidate a whole L2 per block, which stalls every block streaming through
-// that XCD.  Instead the partials are written and read only with relaxed
-// device-scope atomic accesses (sc1 stores that write through to the coherence
-// point, sc1 loads that read from it); a writer waits for its stores to
-// complete before it takes its ticket, and the merging block issues its loads
-// only after its ticket shows every split done.
-__device__ __forceinline__ void st_dev(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_dev(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
+// takes a ticket on its (unit, head group) counter (block_ticket_last); the
+// block that takes the last ticket merges all partials by log-sum-exp and
+// resets the counter, so the workspace is zero again when the launch ends.
 // Partial store: a device-scope write-through store when the launch merges in-kernel,
 // a plain store when the combine kernel (a later launch) reads it.
 __device__ __forceinline__ void st_part(const AttnArgs& a, float* p, float v) {
   if (a.fused) st_dev(p, v); else *p = v;
 }
 
-__device__ __forceinline__ bool attn_split_done(int* ctr, int splits) {
-  __shared__ int s_last;
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);     // this thread's partial stores have completed
-  __syncthreads();
-  if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == splits - 1;
-  __syncthreads();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  return s_last != 0;
-}
+__device__ __forceinline__ bool attn_split_done(int* ctr, int splits) { return block_ticket_last(ctr, splits); }
 
 // Merge the splits of heads [h0, h0 + nh) of one unit into out / lse (natural-log
 // lse) and reset the unit's ticket counter.  `lds` holds >= 2 * splits * nh + nh
@@ -168,7 +142,7 @@ __device__ void attn_merge_splits(const AttnArgs& a, int unit, int h0, int nh, i
       if (idx < total) a.out[(row0 + hl[u]) * Dv + (idx - hl[u] * Dv)] = O[u] * inv[hl[u]];
     }
   }
-  if (threadIdx.x == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) ticket_reset(ctr);
 }
 
 // Final output of a unit handled by one block (splits == 1): out = O / L, lse = M + log L.

@@ -150,7 +150,22 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(
 }
 
 // ------------------------------------------------------------------ top-k pages
-// One block per unit: page scores (staged in LDS when they fit) -> ascending view.
+// One block per unit: page scores -> ascending view.  Up to BLOCK * E pages
+// the scores stay in registers (block_topk_reg); longer caches use the LDS /
+// global-memory variant.
+template <int BLOCK, int E>
+__global__ __launch_bounds__(BLOCK) void quest_topk_reg_kernel(
+    const float* __restrict__ score, const int32_t* __restrict__ seq_len, int32_t* __restrict__ view_idx,
+    int32_t* __restrict__ view_len, int Hkv, int P, int n_cap_pages, int cap, int top_pages) {
+  __shared__ TopkRegShared sh;
+  const int unit = blockIdx.x, b = unit / Hkv;
+  const int n = min((min(seq_len[b], cap) + P - 1) / P, n_cap_pages);
+  const float* su = score + size_t(unit) * n_cap_pages;
+  const int kk = block_topk_reg<BLOCK, E>([&](int i) { return su[i]; }, n, top_pages,
+                                          view_idx + size_t(unit) * top_pages, sh);
+  if (threadIdx.x == 0) view_len[unit] = kk;
+}
+
 template <int BLOCK>
 __global__ __launch_bounds__(BLOCK) void quest_topk_block_kernel(
     const float* __restrict__ score, const int32_t* __restrict__ seq_len, int32_t* __restrict__ view_idx,
@@ -194,14 +209,16 @@ se_status launch_quest(const se_cache& c, const void* q, const void* kmin, const
   const int ncp = ceil_div(c.capacity, page_size);
   float* score = page_score ? page_score : (float*)ws;
   bool done = false;
+#define SE_MF(DD, HH) launch_score_mfma<DD, HH>(c, q, kmin, kmax, seq_len, score, page_size, ncp, s)
   if (c.dtype == SE_BF16) {
     done = true;
-    if (c.d_k == 128 && G <= 16) launch_score_mfma<128, 1>(c, q, kmin, kmax, seq_len, score, page_size, ncp, s);
-    else if (c.d_k == 128 && G <= 32) launch_score_mfma<128, 2>(c, q, kmin, kmax, seq_len, score, page_size, ncp, s);
-    else if (c.d_k == 64 && G <= 16) launch_score_mfma<64, 1>(c, q, kmin, kmax, seq_len, score, page_size, ncp, s);
-    else if (c.d_k == 576 && G <= 32) launch_score_mfma<576, 2>(c, q, kmin, kmax, seq_len, score, page_size, ncp, s);
+    if (c.d_k == 128 && G <= 16) SE_MF(128, 1);
+    else if (c.d_k == 128 && G <= 32) SE_MF(128, 2);
+    else if (c.d_k == 64 && G <= 16) SE_MF(64, 1);
+    else if (c.d_k == 576 && G <= 32) SE_MF(576, 2);
     else done = false;
   }
+#undef SE_MF
   if (!done) {
     const int ppb = 256 / G;
     dim3 grid(ceil_div(ncp, ppb), units);
@@ -217,8 +234,13 @@ se_status launch_quest(const se_cache& c, const void* q, const void* kmin, const
                          page_size, ncp);
   }
   if (hipGetLastError() != hipSuccess) return SE_ERR_HIP;
-  hipLaunchKernelGGL(quest_topk_block_kernel<256>, dim3(units), dim3(256), 0, s, score, seq_len, view_idx,
-                     view_len, c.n_kv_heads, page_size, ncp, c.capacity, top_pages);
+#define SE_TOPK(KERN, NT) hipLaunchKernelGGL(KERN, dim3(units), dim3(NT), 0, s, score, seq_len, view_idx, view_len, \
+                                          c.n_kv_heads, page_size, ncp, c.capacity, top_pages)
+  if (ncp <= 512 * 4) SE_TOPK((quest_topk_reg_kernel<512, 4>), 512);
+  else if (ncp <= 512 * 8) SE_TOPK((quest_topk_reg_kernel<512, 8>), 512);
+  else if (ncp <= 512 * 16) SE_TOPK((quest_topk_reg_kernel<512, 16>), 512);
+  else SE_TOPK(quest_topk_block_kernel<256>, 256);
+#undef SE_TOPK
   return launch_status();
 }
 

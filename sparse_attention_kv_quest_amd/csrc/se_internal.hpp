@@ -38,6 +38,31 @@ __device__ __forceinline__ uint64_t key_desc_score_asc_index(float s, uint32_t i
 }
 
 // ------------------------------------------------------------------ wave / block helpers
+// Wave-wide scans and reductions on DPP lane moves (no LDS round trips): a
+// Hillis-Steele scan inside each 16-lane row (row_shr 1, 2, 4, 8), then the
+// last lane of row 0 / 1 is broadcast into rows 1, 3 (row_bcast:15) and of
+// row 1 into rows 2, 3 (row_bcast:31).  A lane whose DPP source does not exist
+// keeps `identity`.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v, uint32_t identity, Op op) {
+  const int id = int(identity);
+  v = op(v, uint32_t(__builtin_amdgcn_update_dpp(id, int(v), 0x111, 0xf, 0xf, false)));   // row_shr:1
+  v = op(v, uint32_t(__builtin_amdgcn_update_dpp(id, int(v), 0x112, 0xf, 0xf, false)));   // row_shr:2
+  v = op(v, uint32_t(__builtin_amdgcn_update_dpp(id, int(v), 0x114, 0xf, 0xf, false)));   // row_shr:4
+  v = op(v, uint32_t(__builtin_amdgcn_update_dpp(id, int(v), 0x118, 0xf, 0xf, false)));   // row_shr:8
+  v = op(v, uint32_t(__builtin_amdgcn_update_dpp(id, int(v), 0x142, 0xa, 0xf, false)));   // row_bcast:15
+  v = op(v, uint32_t(__builtin_amdgcn_update_dpp(id, int(v), 0x143, 0xc, 0xf, false)));   // row_bcast:31
+  return v;
+}
+// Value of the last lane (the wave-wide reduction) as a wave-uniform value.
+__device__ __forceinline__ uint32_t wave_last(uint32_t v) { return uint32_t(__builtin_amdgcn_readlane(int(v), 63)); }
+
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+  return wave_last(wave_incl_scan_dpp(v, 0u, [](uint32_t a, uint32_t b) { return a | b; }));
+}
+__device__ __forceinline__ uint32_t wave_and(uint32_t v) {
+  return wave_last(wave_incl_scan_dpp(v, ~0u, [](uint32_t a, uint32_t b) { return a & b; }));
+}
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
   return v;
@@ -47,17 +72,11 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 __device__ __forceinline__ int wave_sum_i(int v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
-  return v;
+  return int(wave_last(wave_incl_scan_dpp(uint32_t(v), 0u, [](uint32_t a, uint32_t b) { return a + b; })));
 }
-// Inclusive prefix sum across the wave.
+// Inclusive prefix sum across the wave (every lane of the wave active).
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & (WAVE - 1);
-  for (int o = 1; o < WAVE; o <<= 1) {
-    int t = __shfl_up(v, o, WAVE);
-    if (lane >= o) v += t;
-  }
-  return v;
+  return int(wave_incl_scan_dpp(uint32_t(v), 0u, [](uint32_t a, uint32_t b) { return a + b; }));
 }
 
 // Exclusive prefix sum over the block; `tmp` is >= BLOCK/64 ints of LDS.  Also returns the total.
@@ -76,6 +95,40 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
   __syncthreads();
   *total = tot;
   return base + inc - v;
+}
+
+// ------------------------------------------------------------------ cross-block completion
+// A launch whose blocks each finish a share of some unit's work lets the block
+// that finishes last complete it (a top-k over all page scores, a merge of
+// split partials) inside the same launch.  The blocks of one unit run on
+// different XCDs, whose L2 caches are not coherent with each other, and a
+// device-scope fence would write back or invalidate a whole L2, stalling every
+// block streaming through that XCD.  So the shared data is written and read
+// only with relaxed device-scope atomic accesses (sc1 stores that write
+// through to the coherence point, sc1 loads that read from it); a block waits
+// for its stores to complete before it takes its ticket, and the last block
+// issues its loads only after its ticket shows every share done.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Takes this block's ticket on `ctr`; true in the block that takes ticket nblocks - 1.
+__device__ __forceinline__ bool block_ticket_last(int* ctr, int nblocks) {
+  __shared__ int s_last;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);     // this thread's stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nblocks - 1;
+  __syncthreads();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  return s_last != 0;
+}
+// The last block returns the counter to zero for the next launch.
+__device__ __forceinline__ void ticket_reset(int* ctr) {
+  __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------ block top-k
@@ -189,6 +242,139 @@ __device__ int block_topk_ascending(ScoreFn score, int n, int k, int32_t* out, T
   return kk;
 }
 
+
+// Register-resident variant for n <= BLOCK * E.  Wave w owns candidates
+// [64 E w, 64 E (w + 1)); its lane l holds 64 E w + 64 j + l for j < E, so
+// every load is coalesced.  Keys are 32-bit ordered scores; slots past n hold
+// key 0, which is below every real key (ordered_bits of a non-NaN float is
+// never 0), so they never enter the kept set and need no masks.  Radix select
+// on the score bits: the bits every candidate shares are skipped, then 8-bit
+// digits are counted in one LDS histogram per wave (zeroed by that wave), and
+// wave 0 alone scans the digit counts (DPP) and posts the crossing digit, so a
+// digit pass costs two block barriers.  The search stops when one digit bucket
+// holds exactly the keys still to choose, or when all 32 bits are resolved.
+// The kept set is every key above the resolved prefix plus the first `r` keys
+// of the prefix's bucket in index order (the lower-index tie rule); per-wave
+// counts give each wave its output offset and ballot prefix counts place each
+// kept candidate, so the view comes out in ascending index order.
+struct TopkRegShared {
+  uint32_t hist[16][256];     // one histogram per wave (BLOCK <= 1024)
+  uint32_t red_or[16], red_and[16];
+  int cnt_a[16], cnt_b[16];
+  int digit, rem, cnt;
+};
+
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
+}
+
+template <int BLOCK, int E, class LoadFn>
+__device__ int block_topk_reg(LoadFn load, int n, int k, int32_t* out, TopkRegShared& sh) {
+  static_assert(BLOCK >= 64 && BLOCK <= 1024 && BLOCK % WAVE == 0, "block size");
+  constexpr int NW = BLOCK / WAVE;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+  const int kk = k < n ? k : n;
+  const int base = w * WAVE * E + lane;
+  uint32_t key[E];
+#pragma unroll
+  for (int j = 0; j < E; ++j) key[j] = (base + j * WAVE < n) ? ordered_bits(load(base + j * WAVE)) : 0u;
+  uint32_t mask = 0u, prefix = 0u;   // resolved top bits and their value
+  int r = kk;                        // keys still to take from the bucket (key & mask) == prefix
+  if (kk > 0 && kk < n) {
+    uint32_t kor = 0u, kand = ~0u;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      kor |= key[j];
+      kand &= key[j] | (key[j] == 0u ? ~0u : 0u);   // padding does not clear common bits
+    }
+    kor = wave_or(kor);
+    kand = wave_and(kand);
+    if (lane == 0) { sh.red_or[w] = kor; sh.red_and[w] = kand; }
+    __syncthreads();
+    kor = 0u; kand = ~0u;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) { kor |= sh.red_or[i]; kand &= sh.red_and[i]; }
+    const uint32_t diff = kor ^ kand;
+    if (diff == 0u) {
+      mask = ~0u;          // every key equal: the first kk by index
+      prefix = kand;
+    } else {
+      const int top = 31 - __clz(diff);
+      mask = top == 31 ? 0u : (~0u << (top + 1));
+      prefix = kand & mask;
+      uint32_t* hist = sh.hist[w];
+      for (int hb = top; hb >= 0; hb -= 8) {
+        const int shift = hb >= 7 ? hb - 7 : 0;
+        const uint32_t dmask = (1u << (hb - shift + 1)) - 1u;
+        reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);   // in LDS order before the atomics
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+          if ((key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
+        __syncthreads();
+        if (w == 0) {
+          // lane l owns digits 255 - 4l .. 252 - 4l (descending); an inclusive scan over
+          // lanes counts the keys whose digit is >= the lane's lowest
+          int c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+#pragma unroll
+          for (int i = 0; i < NW; ++i) {
+            const uint4 h4 = reinterpret_cast<const uint4*>(sh.hist[i])[63 - lane];
+            c0 += int(h4.w); c1 += int(h4.z); c2 += int(h4.y); c3 += int(h4.x);
+          }
+          const int own = c0 + c1 + c2 + c3;
+          const int incl = wave_incl_scan(own);
+          int above = incl - own;
+          if (above < r && r <= incl) {
+            const int cs[4] = {c0, c1, c2, c3};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              if (above + cs[j] >= r) {
+                sh.digit = 255 - 4 * lane - j;
+                sh.rem = r - above;
+                sh.cnt = cs[j];
+                break;
+              }
+              above += cs[j];
+            }
+          }
+        }
+        __syncthreads();
+        const int fd = sh.digit, frem = sh.rem, fcnt = sh.cnt;
+        prefix |= uint32_t(fd) << shift;
+        mask |= dmask << shift;
+        r = frem;
+        if (fcnt == frem) break;   // the whole bucket is kept
+      }
+    }
+  }
+  // compaction in index order: above = (key & mask) > prefix, bucket = (key & mask) == prefix (real keys only)
+  int na = 0, nb = 0;
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const uint32_t km = key[j] & mask;
+    na += km > prefix;
+    nb += km == prefix && key[j] != 0u;
+  }
+  na = wave_sum_i(na);
+  nb = wave_sum_i(nb);
+  if (lane == 0) { sh.cnt_a[w] = na; sh.cnt_b[w] = nb; }
+  __syncthreads();
+  int ca = 0, cb = 0;
+  for (int i = 0; i < w; ++i) { ca += sh.cnt_a[i]; cb += sh.cnt_b[i]; }
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const uint32_t km = key[j] & mask;
+    const bool is_a = km > prefix;
+    const bool is_b = km == prefix && key[j] != 0u;
+    const uint64_t ma = __ballot(is_a), mb = __ballot(is_b);
+    const int pa = ca + lanes_below(ma), pb = cb + lanes_below(mb);
+    if (is_a) out[pa + min(pb, r)] = base + j * WAVE;
+    else if (is_b && pb < r) out[pa + pb] = base + j * WAVE;
+    ca += __popcll(ma);
+    cb += __popcll(mb);
+  }
+  for (int i = kk + tid; i < k; i += BLOCK) out[i] = -1;
+  return kk;
+}
 
 // ------------------------------------------------------------------ launch helpers
 inline se_status launch_status() {
