@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(AttnArgs a) {
   }
   if (!a.fused) return;
   int* ctr = a.counters + unit * ATTN_MAX_HG;
-  if (attn_split_done(ctr, a.splits)) attn_merge_splits<256>(a, unit, 0, G, ctr, smem);
+  if (attn_split_done(ctr, a.splits)) attn_merge_splits<256>(a, unit, 0, G, ctr);
 }
 
 // One block per (head of the group, unit): merge the split partials by log-sum-exp
@@ -202,8 +202,7 @@ se_status launch_attn_vector(const AttnArgs& a, hipStream_t s) {
   const int units = a.B * a.Hkv;
   const size_t lds_main = (size_t(a.G) * a.Dk + VT * a.Dk + (a.latent ? 0 : VT * a.Dv) + a.G * VT + 3 * a.G) *
                              sizeof(float) + VT * sizeof(int);
-  const size_t lds_merge = (size_t(2) * a.splits * a.G + a.G) * sizeof(float);   // reuses the same LDS afterwards
-  const size_t lds = std::max(lds_main, lds_merge);
+  const size_t lds = lds_main;
   if (lds > 160 * 1024) return SE_ERR_UNSUPPORTED;
   const int R = (a.G * a.Dv + 255) / 256;
   dim3 grid(a.splits, units);

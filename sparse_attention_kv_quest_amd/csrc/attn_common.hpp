@@ -74,73 +74,57 @@ __device__ __forceinline__ void st_part(const AttnArgs& a, float* p, float v) {
 __device__ __forceinline__ bool attn_split_done(int* ctr, int splits) { return block_ticket_last(ctr, splits); }
 
 // Merge the splits of heads [h0, h0 + nh) of one unit into out / lse (natural-log
-// lse) and reset the unit's ticket counter.  `lds` holds >= 2 * splits * nh + nh
-// floats.  The per-split weights exp(m_s - M) are formed once per (split, head);
-// the output pass then issues its independent loads back to back.
+// lse) and reset the unit's ticket counter.  A thread owns four consecutive
+// output columns of one head; for a batch of up to SU splits it issues every
+// load (max, sum and four partial outputs per split) before using any, and
+// folds the batch into a running (max, sum, output) by log-sum-exp, so a
+// merge of up to SU splits costs one round trip.
 template <int NT>
-__device__ void attn_merge_splits(const AttnArgs& a, int unit, int h0, int nh, int* ctr, float* lds) {
-  const int S = a.splits, G = a.G, Dv = a.Dv;
+__device__ void attn_merge_splits(const AttnArgs& a, int unit, int h0, int nh, int* ctr) {
+  constexpr int SU = 8;
+  const int S = a.splits, G = a.G, Dv = a.Dv;   // Dv is a multiple of 4
   const int b = unit / a.Hkv, kvh = unit % a.Hkv;
   const float* pml = a.part_ml + size_t(unit) * S * G * 2;
   const float* po = a.part_o + size_t(unit) * S * G * Dv;
-  float* wm = lds;              // [S][nh] running max, then weight
-  float* wl = lds + S * nh;     // [S][nh] running sum
-  float* inv = wl + S * nh;     // [nh] 1 / L
-  for (int i = threadIdx.x; i < S * nh; i += NT) {
-    const int s = i / nh, hl = i - s * nh;
-    const float m = ld_dev(pml + (s * G + h0 + hl) * 2);
-    const float l = ld_dev(pml + (s * G + h0 + hl) * 2 + 1);
-    wm[i] = m;
-    wl[i] = l;
-  }
-  __syncthreads();
   const size_t row0 = size_t(b) * a.Hq + size_t(kvh) * G + h0;
-  for (int hl = threadIdx.x; hl < nh; hl += NT) {
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, wm[s * nh + hl]);
-    float L = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float m = wm[s * nh + hl];
-      const float f = (m != -INFINITY) ? exp2f((m - M) * LOG2E) : 0.f;
-      wm[s * nh + hl] = f;
-      L += f * wl[s * nh + hl];
-    }
-    inv[hl] = L > 0.f ? 1.f / L : 0.f;
-    if (a.lse != nullptr) a.lse[row0 + hl] = L > 0.f ? M + logf(L) : -INFINITY;
-  }
-  __syncthreads();
-  // outputs in groups of OU per thread, splits in batches of SU: all OU x SU loads of a
-  // batch are issued before the first is used (a split past S repeats split S - 1 with weight 0)
-  constexpr int SU = 8, OU = 4;
-  const int total = nh * Dv;
-  for (int base = threadIdx.x; base < total; base += NT * OU) {
-    int hl[OU];
-    const float* src[OU];
-#pragma unroll
-    for (int u = 0; u < OU; ++u) {
-      const int idx = min(base + u * NT, total - 1);
-      hl[u] = idx / Dv;
-      src[u] = po + size_t(h0 + hl[u]) * Dv + (idx - hl[u] * Dv);
-    }
-    float O[OU];
-#pragma unroll
-    for (int u = 0; u < OU; ++u) O[u] = 0.f;
+  for (int e = threadIdx.x * 4; e < nh * Dv; e += NT * 4) {
+    const int hl = e / Dv, d0 = e - hl * Dv, h = h0 + hl;
+    float M = -INFINITY, L = 0.f, O[4] = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < S; s0 += SU) {
-      float x[SU][OU];
+      float mb[SU], lb[SU], ob[SU][4];
 #pragma unroll
-      for (int j = 0; j < SU; ++j)
+      for (int j = 0; j < SU; ++j) {
+        const int s = min(s0 + j, S - 1);
+        mb[j] = ld_dev(pml + (s * G + h) * 2);
+        lb[j] = ld_dev(pml + (s * G + h) * 2 + 1);
 #pragma unroll
-        for (int u = 0; u < OU; ++u) x[j][u] = ld_dev(src[u] + size_t(min(s0 + j, S - 1)) * G * Dv);
+        for (int u = 0; u < 4; ++u) ob[j][u] = ld_dev(po + (size_t(s) * G + h) * Dv + d0 + u);
+      }
+      float Mb = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < SU; ++j)
+      for (int j = 0; j < SU; ++j) {
+        if (s0 + j >= S) mb[j] = -INFINITY;   // a repeated split, not counted
+        Mb = fmaxf(Mb, mb[j]);
+      }
+      const float Mn = fmaxf(M, Mb);
+      if (Mn == -INFINITY) continue;
+      const float alpha = M == -INFINITY ? 0.f : exp2f((M - Mn) * LOG2E);
+      L *= alpha;
 #pragma unroll
-        for (int u = 0; u < OU; ++u) O[u] += (s0 + j < S ? wm[(s0 + j) * nh + hl[u]] : 0.f) * x[j][u];
+      for (int u = 0; u < 4; ++u) O[u] *= alpha;
+#pragma unroll
+      for (int j = 0; j < SU; ++j) {
+        const float f = mb[j] == -INFINITY ? 0.f : exp2f((mb[j] - Mn) * LOG2E);
+        L += f * lb[j];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) O[u] += f * ob[j][u];
+      }
+      M = Mn;
     }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
-    for (int u = 0; u < OU; ++u) {
-      const int idx = base + u * NT;
-      if (idx < total) a.out[(row0 + hl[u]) * Dv + (idx - hl[u] * Dv)] = O[u] * inv[hl[u]];
-    }
+    for (int u = 0; u < 4; ++u) a.out[(row0 + hl) * Dv + d0 + u] = O[u] * inv;
+    if (d0 == 0 && a.lse != nullptr) a.lse[row0 + hl] = L > 0.f ? M + logf(L) : -INFINITY;
   }
   if (threadIdx.x == 0) ticket_reset(ctr);
 }

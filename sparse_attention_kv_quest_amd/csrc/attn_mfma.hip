@@ -210,10 +210,7 @@ void attn_mfma_kernel(AttnArgs a) {
   constexpr int NDB = D / 16;
   constexpr int NKS = D / 32;
   static_assert(D == 64 || D == 128, "head width");
-  // V tiles; afterwards the wave merge and the split merge reuse the same LDS
-  constexpr int MERGE_U16 = (2 * (2 * ATTN_MAX_SPLITS * 16 + 16) + MF_WAVES - 1) / MF_WAVES;
-  constexpr int VT_U16 = D * PITCH > MERGE_U16 ? D * PITCH : MERGE_U16;
-  __shared__ __align__(16) uint16_t vt_lds[MF_WAVES][VT_U16];
+  __shared__ __align__(16) uint16_t vt_lds[MF_WAVES][D * PITCH];   // V tiles, then the wave merge
   __shared__ float red_m[MF_WAVES][16], red_l[MF_WAVES][16];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -361,8 +358,7 @@ void attn_mfma_kernel(AttnArgs a) {
   }
   if (a.fused) {
     int* ctr = a.counters + unit * ATTN_MAX_HG;
-    static_assert(2 * ATTN_MAX_SPLITS * 16 + 16 <= int(sizeof(vt_lds) / sizeof(float)), "merge scratch");
-    if (attn_split_done(ctr, a.splits)) attn_merge_splits<256>(a, unit, 0, G, ctr, red_o);
+    if (attn_split_done(ctr, a.splits)) attn_merge_splits<256>(a, unit, 0, G, ctr);
   }
 }
 

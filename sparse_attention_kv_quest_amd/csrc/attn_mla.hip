@@ -345,11 +345,7 @@ __global__ __launch_bounds__(ML_THREADS) void attn_mla_kernel(AttnArgs a) {
   }
   if (a.fused) {
     int* ctr = a.counters + unit * ATTN_MAX_HG + hg;
-    static_assert(2 * ATTN_MAX_SPLITS * 32 + 32 <= ML_LDS_BYTES / 4, "merge scratch");
-    if (attn_split_done(ctr, a.splits)) {
-      __syncthreads();   // every wave has stored its slice of the output transpose
-      attn_merge_splits<ML_THREADS>(a, unit, h0, min(32, G - h0), ctr, reinterpret_cast<float*>(lds));
-    }
+    if (attn_split_done(ctr, a.splits)) attn_merge_splits<ML_THREADS>(a, unit, h0, min(32, G - h0), ctr);
   }
 }
 
