@@ -161,7 +161,8 @@ se_status se_sparse_decode_attn(const se_cache* c, const void* q, const void* k,
  *   vote[j] (j < L - window) = sum over the group's heads and the window rows
  *   of the causal softmax weight the row gives key j (each row's softmax runs
  *   over keys 0 .. its own position); pooled = max-pool(vote, pool_kernel,
- *   stride 1, out-of-range ignored); kept = the budget - window best pooled
+ *   stride 1, out-of-range ignored; pool_kernel odd, 1..129); kept = the
+ *   budget - window best pooled
  *   positions (ties to the lower position) plus the window, ascending; with
  *   budget >= prompt_len every position is kept.
  *   kept_pos int32 [B][Hkv][budget] (-1 past min(budget, L)); k_out / v_out

@@ -172,7 +172,7 @@ se_status se_snapkv_score_compact(const se_cache* c, const void* q_obs, const vo
     return SE_ERR_SHAPE;
   if (prompt_len <= 0 || prompt_len > c->capacity) return SE_ERR_SHAPE;
   if (window < 1 || window >= prompt_len) return SE_ERR_BUDGET;
-  if (pool_kernel < 1 || pool_kernel % 2 == 0) return SE_ERR_BUDGET;
+  if (pool_kernel < 1 || pool_kernel % 2 == 0 || pool_kernel > 129) return SE_ERR_BUDGET;
   if (budget < window) return SE_ERR_BUDGET;
   if (out->capacity < std::min(budget, prompt_len)) return SE_ERR_BUDGET;
   if (!(scale > 0.f) || !(scale < 1e30f)) return SE_ERR_SHAPE;

@@ -21,12 +21,14 @@ namespace se {
 constexpr float SK_LOG2E = 1.4426950408889634f;
 constexpr int SK_CHUNK = 1024;        // keys per block in the MFMA passes
 constexpr float SK_MARGIN = 8.f;      // lazy running-max margin (log2 units)
-constexpr int SK_TOPK_BLOCK = 1024;
+
+struct SelState { uint32_t prefix, mask; int r, done; };   // per-unit radix-select state
 
 struct SnapArgs {
   const void* q; const void* k; const void* v;
   void* k_out; void* v_out;
   int32_t* kept; float* votes; float* pooled; float* part; float* lse2; int32_t* out_len;
+  uint32_t* sel_hist; SelState* sel_state; int32_t* sel_counts;   // multi-block select
   int B, Hq, Hkv, G, D, cap, out_cap, L, W, R, pool, budget, nchunks, dtype;
   float sc2;   // scale * log2(e)
 };
@@ -146,19 +148,48 @@ __global__ __launch_bounds__(256) void snap_mfma_kernel(SnapArgs a) {
   }
 }
 
-// One thread per (unit, row): merge the chunk partials into the row's log2-sum-exp2.
-__global__ void snap_lse_merge_kernel(SnapArgs a) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= a.B * a.Hkv * a.R) return;
-  const int unit = idx / a.R, row = idx % a.R;
-  float M = -INFINITY;
-  for (int c = 0; c < a.nchunks; ++c) M = fmaxf(M, a.part[((size_t(unit) * a.nchunks + c) * a.R + row) * 2]);
-  float S = 0.f;
-  for (int c = 0; c < a.nchunks; ++c) {
-    const float* p = a.part + ((size_t(unit) * a.nchunks + c) * a.R + row) * 2;
-    if (p[0] != -INFINITY) S += p[1] * exp2f(p[0] - M);
+// Eight threads per (unit, row): each folds every eighth chunk partial into a
+// running (max, sum) with all of its loads in flight together, then the eight
+// combine by lane exchange into the row's log2-sum-exp2.
+constexpr int SK_MERGE_LANES = 8;
+__global__ __launch_bounds__(256) void snap_lse_merge_kernel(SnapArgs a) {
+  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  const int idx = gid / SK_MERGE_LANES, part = gid % SK_MERGE_LANES;
+  const bool live = idx < a.B * a.Hkv * a.R;   // whole groups of eight share this (lanes stay active)
+  const int unit = live ? idx / a.R : 0, row = live ? idx % a.R : 0;
+  float M = -INFINITY, S = 0.f;
+  if (live) {
+    constexpr int BATCH = 8;
+    for (int c0 = part; c0 < a.nchunks; c0 += SK_MERGE_LANES * BATCH) {
+      float mb[BATCH], lb[BATCH];
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) {
+        const int c = min(c0 + j * SK_MERGE_LANES, a.nchunks - 1);
+        const float* p = a.part + ((size_t(unit) * a.nchunks + c) * a.R + row) * 2;
+        mb[j] = c0 + j * SK_MERGE_LANES < a.nchunks ? p[0] : -INFINITY;
+        lb[j] = p[1];
+      }
+      float Mb = M;
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) Mb = fmaxf(Mb, mb[j]);
+      if (Mb == -INFINITY) continue;
+      S = (M == -INFINITY) ? 0.f : S * exp2f(M - Mb);
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j)
+        if (mb[j] != -INFINITY) S += lb[j] * exp2f(mb[j] - Mb);
+      M = Mb;
+    }
   }
-  a.lse2[idx] = M + log2f(S);
+#pragma unroll
+  for (int o = 1; o < SK_MERGE_LANES; o <<= 1) {
+    const float Mo = __shfl_xor(M, o, 64), So = __shfl_xor(S, o, 64);
+    const float Mn = fmaxf(M, Mo);
+    if (Mn != -INFINITY) {
+      S = (M == -INFINITY ? 0.f : S * exp2f(M - Mn)) + (Mo == -INFINITY ? 0.f : So * exp2f(Mo - Mn));
+      M = Mn;
+    }
+  }
+  if (live && part == 0) a.lse2[idx] = M + log2f(S);
 }
 
 // ------------------------------------------------------------------ vector passes (any dtype)
@@ -216,29 +247,212 @@ __global__ __launch_bounds__(256) void snap_vec_vote_kernel(SnapArgs a) {
 }
 
 // ------------------------------------------------------------------ pool, select, gather
-__global__ void snap_pool_kernel(SnapArgs a) {
-  const int unit = blockIdx.y, n = a.L - a.W;
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= n) return;
-  const int r = a.pool / 2;
+// grid (tiles of SK_POOL_T votes, units): the tile and its halo are staged in LDS.
+constexpr int SK_POOL_T = 1024, SK_POOL_MAXR = 64;   // pool widths up to 129 (checked by the API)
+__global__ __launch_bounds__(256) void snap_pool_kernel(SnapArgs a) {
+  __shared__ float v_s[SK_POOL_T + 2 * SK_POOL_MAXR];
+  const int unit = blockIdx.y, n = a.L - a.W, r = a.pool / 2;
   const float* v = a.votes + size_t(unit) * n;
-  float mx = -INFINITY;
-  for (int d = max(0, j - r); d <= min(n - 1, j + r); ++d) mx = fmaxf(mx, v[d]);
-  a.pooled[size_t(unit) * n + j] = mx;
+  const int t0 = blockIdx.x * SK_POOL_T;
+  for (int i = threadIdx.x; i < SK_POOL_T + 2 * r; i += 256) {
+    const int j = t0 - r + i;
+    v_s[i] = (j >= 0 && j < n) ? v[j] : -INFINITY;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < SK_POOL_T; i += 256) {
+    const int j = t0 + i;
+    if (j >= n) break;
+    float mx = -INFINITY;
+    for (int d = 0; d <= 2 * r; ++d) mx = fmaxf(mx, v_s[i + d]);
+    a.pooled[size_t(unit) * n + j] = mx;
+  }
 }
 
-__global__ __launch_bounds__(SK_TOPK_BLOCK) void snap_select_kernel(SnapArgs a) {
-  __shared__ TopkShared sh;
+// ------------------------------------------------------------------ multi-block select
+// The kept history positions are the k = budget - W largest pooled votes (ties
+// to the lower position), in ascending order.  With n = L - W in the hundred
+// thousands per unit, the selection is spread over SK_SEL_CH-element slices
+// of every unit: three radix passes on the 32-bit ordered vote keys (digits of
+// 11, 11 and 10 bits) each count digits in a per-block LDS histogram that is
+// added into a per-unit global histogram, and a per-unit block finds the digit
+// holding the k-th key (it also zeroes the global histogram again).  The kept
+// set is every key above the resolved prefix plus the first r keys of its
+// bucket in index order; a count pass and a write pass place them.
+constexpr int SK_SEL_BLOCK = 256, SK_SEL_PER = 16, SK_SEL_CH = SK_SEL_BLOCK * SK_SEL_PER;
+constexpr int SK_SEL_BINS = 2048;
+
+__device__ __forceinline__ int sel_shift(int pass) { return pass == 0 ? 21 : pass == 1 ? 10 : 0; }
+__device__ __forceinline__ uint32_t sel_dmask(int pass) { return pass == 2 ? 0x3ffu : 0x7ffu; }
+
+// grid (slices, units)
+__global__ __launch_bounds__(SK_SEL_BLOCK) void snap_sel_hist_kernel(SnapArgs a, int pass) {
+  __shared__ uint32_t h[SK_SEL_BINS];
+  const int unit = blockIdx.y, n = a.L - a.W;
+  uint32_t prefix = 0u, mask = 0u;
+  if (pass > 0) {
+    const SelState st = a.sel_state[unit];
+    if (st.done) return;
+    prefix = st.prefix;
+    mask = st.mask;
+  }
+  for (int i = threadIdx.x; i < SK_SEL_BINS; i += SK_SEL_BLOCK) h[i] = 0u;
+  __syncthreads();
+  const float* pv = a.pooled + size_t(unit) * n;
+  const int shift = sel_shift(pass);
+  const uint32_t dm = sel_dmask(pass);
+  const int i0 = blockIdx.x * SK_SEL_CH;
+#pragma unroll 4
+  for (int j = 0; j < SK_SEL_PER; ++j) {
+    const int i = i0 + j * SK_SEL_BLOCK + threadIdx.x;
+    if (i < n) {
+      const uint32_t key = ordered_bits(pv[i]);
+      if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & dm], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t* gh = a.sel_hist + size_t(unit) * SK_SEL_BINS;
+  for (int i = threadIdx.x; i < SK_SEL_BINS; i += SK_SEL_BLOCK)
+    if (h[i] != 0u) atomicAdd(&gh[i], h[i]);
+}
+
+// grid (units): finds the digit holding the r-th largest remaining key; zeroes the histogram.
+__global__ __launch_bounds__(SK_SEL_BLOCK) void snap_sel_find_kernel(SnapArgs a, int pass, int kk) {
+  __shared__ int scan_tmp[SK_SEL_BLOCK / WAVE];
+  __shared__ int res[3];
   const int unit = blockIdx.x, n = a.L - a.W;
-  const float* pooled = a.pooled + size_t(unit) * n;
+  SelState st;
+  if (pass == 0) {
+    st.prefix = 0u; st.mask = 0u; st.r = kk;
+    st.done = (kk <= 0 || kk >= n) ? 1 : 0;
+  } else {
+    st = a.sel_state[unit];
+  }
+  uint32_t* gh = a.sel_hist + size_t(unit) * SK_SEL_BINS;
+  // thread t owns digits 2047 - 8t .. 2040 - 8t (descending)
+  constexpr int PER = SK_SEL_BINS / SK_SEL_BLOCK;
+  int c[PER];
+  int own = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int d = SK_SEL_BINS - 1 - PER * threadIdx.x - j;
+    c[j] = int(gh[d]);
+    gh[d] = 0u;
+    own += c[j];
+  }
+  if (st.done) {
+    if (pass == 0 && threadIdx.x == 0) a.sel_state[unit] = st;
+    return;
+  }
+  int total;
+  const int incl = block_excl_scan<SK_SEL_BLOCK>(own, scan_tmp, &total) + own;
+  int above = incl - own;
+  if (above < st.r && st.r <= incl) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (above + c[j] >= st.r) {
+        res[0] = SK_SEL_BINS - 1 - PER * threadIdx.x - j;
+        res[1] = st.r - above;
+        res[2] = c[j];
+        break;
+      }
+      above += c[j];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int shift = sel_shift(pass);
+    st.prefix |= uint32_t(res[0]) << shift;
+    st.mask |= sel_dmask(pass) << shift;
+    st.r = res[1];
+    st.done = (res[2] == res[1] || pass == 2) ? 1 : 0;
+    a.sel_state[unit] = st;
+  }
+}
+
+__device__ __forceinline__ void sel_classify(uint32_t key, const SelState& st, bool& above, bool& bucket) {
+  const uint32_t km = key & st.mask;
+  above = km > st.prefix;
+  bucket = km == st.prefix;
+}
+
+// grid (slices, units): per-slice counts of keys above the prefix and in its bucket;
+// slice 0 also writes the window entries, the -1 padding and out_len.
+__global__ __launch_bounds__(SK_SEL_BLOCK) void snap_sel_count_kernel(SnapArgs a, int kk) {
+  __shared__ int red[2][SK_SEL_BLOCK / WAVE];
+  const int unit = blockIdx.y, n = a.L - a.W;
+  const SelState st = a.sel_state[unit];
+  const float* pv = a.pooled + size_t(unit) * n;
+  const int i0 = blockIdx.x * SK_SEL_CH;
+  int na = 0, nb = 0;
+  for (int j = 0; j < SK_SEL_PER; ++j) {
+    const int i = i0 + j * SK_SEL_BLOCK + threadIdx.x;
+    if (i < n) {
+      bool ab, bu;
+      sel_classify(ordered_bits(pv[i]), st, ab, bu);
+      na += ab;
+      nb += bu;
+    }
+  }
+  na = wave_sum_i(na);
+  nb = wave_sum_i(nb);
+  const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
+  if (lane == 0) { red[0][w] = na; red[1][w] = nb; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int ta = 0, tb = 0;
+    for (int i = 0; i < SK_SEL_BLOCK / WAVE; ++i) { ta += red[0][i]; tb += red[1][i]; }
+    a.sel_counts[(size_t(unit) * gridDim.x + blockIdx.x) * 2] = ta;
+    a.sel_counts[(size_t(unit) * gridDim.x + blockIdx.x) * 2 + 1] = tb;
+  }
+  if (blockIdx.x == 0) {
+    int32_t* kept = a.kept + size_t(unit) * a.budget;
+    for (int i = threadIdx.x; i < a.W; i += SK_SEL_BLOCK) kept[kk + i] = n + i;
+    for (int i = kk + a.W + threadIdx.x; i < a.budget; i += SK_SEL_BLOCK) kept[i] = -1;
+    if (threadIdx.x == 0 && unit % a.Hkv == 0 && a.out_len != nullptr) a.out_len[unit / a.Hkv] = kk + a.W;
+  }
+}
+
+// grid (slices, units): writes the kept positions of the slice in ascending order.
+// Thread t handles the contiguous elements [i0 + 16 t, i0 + 16 t + 16).
+__global__ __launch_bounds__(SK_SEL_BLOCK) void snap_sel_write_kernel(SnapArgs a) {
+  __shared__ int scan_tmp[SK_SEL_BLOCK / WAVE];
+  const int unit = blockIdx.y, n = a.L - a.W;
+  const SelState st = a.sel_state[unit];
+  int ca = 0, cb = 0;
+  const int32_t* cnt = a.sel_counts + size_t(unit) * gridDim.x * 2;
+  for (int s = 0; s < int(blockIdx.x); ++s) { ca += cnt[2 * s]; cb += cnt[2 * s + 1]; }
+  const float* pv = a.pooled + size_t(unit) * n;
+  const int lo = blockIdx.x * SK_SEL_CH + threadIdx.x * SK_SEL_PER;
+  uint32_t key[SK_SEL_PER];
+  int na = 0, nb = 0;
+#pragma unroll
+  for (int j = 0; j < SK_SEL_PER; ++j) {
+    key[j] = lo + j < n ? ordered_bits(pv[lo + j]) : 0u;
+    bool ab, bu;
+    sel_classify(key[j], st, ab, bu);
+    const bool ok = lo + j < n;
+    na += ok && ab;
+    nb += ok && bu;
+  }
+  int total;
+  const int packed = block_excl_scan<SK_SEL_BLOCK>((na << 16) | nb, scan_tmp, &total);
+  ca += packed >> 16;
+  cb += packed & 0xffff;
   int32_t* kept = a.kept + size_t(unit) * a.budget;
-  const int k = a.budget - a.W;
-  const int kk = block_topk_ascending<SK_TOPK_BLOCK>([&](int i) { return pooled[i]; }, n, k, kept, sh);
-  __syncthreads();   // the top-k pads kept[kk .. k) with -1 before the window is written there
-  // the window follows the chosen history positions; everything past them is -1
-  for (int i = threadIdx.x; i < a.W; i += SK_TOPK_BLOCK) kept[kk + i] = n + i;
-  for (int i = kk + a.W + threadIdx.x; i < a.budget; i += SK_TOPK_BLOCK) kept[i] = -1;
-  if (threadIdx.x == 0 && unit % a.Hkv == 0 && a.out_len != nullptr) a.out_len[unit / a.Hkv] = kk + a.W;
+#pragma unroll
+  for (int j = 0; j < SK_SEL_PER; ++j) {
+    if (lo + j < n) {
+      bool ab, bu;
+      sel_classify(key[j], st, ab, bu);
+      if (ab) {
+        kept[ca + min(cb, st.r)] = lo + j;
+        ++ca;
+      } else if (bu) {
+        if (cb < st.r) kept[ca + cb] = lo + j;
+        ++cb;
+      }
+    }
+  }
 }
 
 // grid (row groups, units): copies kept rows of K and V (16-byte words).
@@ -266,11 +480,18 @@ static bool snap_mfma_ok(const se_cache& c, int W) {
 }
 
 static int snap_chunks(int L) { return ceil_div(L, SK_CHUNK); }
+static int sel_slices(int n) { return std::max(1, ceil_div(n, SK_SEL_CH)); }
+
+// Workspace: the select's digit histograms first (zero between calls), then its
+// state and slice counts, then the score partials, row lse, pooled and votes.
+static size_t sel_bytes(size_t units, int n) {
+  return units * (SK_SEL_BINS * sizeof(uint32_t) + sizeof(SelState) + size_t(sel_slices(n)) * 2 * sizeof(int32_t));
+}
 
 size_t snapkv_ws_bytes(const se_cache& c, int prompt_len, int window) {
   const size_t units = size_t(c.batch) * c.n_kv_heads, R = size_t(c.n_q_heads / c.n_kv_heads) * window;
   const size_t n = size_t(prompt_len - window);
-  return units * (size_t(snap_chunks(prompt_len)) * R * 2 + R + 2 * n) * sizeof(float);
+  return sel_bytes(units, int(n)) + units * (size_t(snap_chunks(prompt_len)) * R * 2 + R + 2 * n) * sizeof(float);
 }
 
 se_status launch_snapkv(const se_cache& c, const void* q_obs, const void* k, const void* v, int prompt_len,
@@ -284,7 +505,10 @@ se_status launch_snapkv(const se_cache& c, const void* q_obs, const void* k, con
   a.pool = pool_kernel; a.budget = budget; a.nchunks = snap_chunks(prompt_len); a.dtype = c.dtype;
   a.sc2 = scale * SK_LOG2E;
   const size_t units = size_t(a.B) * a.Hkv, n = size_t(prompt_len - window);
-  float* wsf = (float*)ws;
+  a.sel_hist = (uint32_t*)ws;
+  a.sel_state = (SelState*)(a.sel_hist + units * SK_SEL_BINS);
+  a.sel_counts = (int32_t*)(a.sel_state + units);
+  float* wsf = (float*)((char*)ws + sel_bytes(units, int(n)));
   a.part = wsf;
   a.lse2 = a.part + units * a.nchunks * a.R * 2;
   a.pooled = a.lse2 + units * a.R;
@@ -298,7 +522,7 @@ se_status launch_snapkv(const se_cache& c, const void* q_obs, const void* k, con
 #define SK_LAUNCH(DD, NN)                                                                          \
   do {                                                                                             \
     hipLaunchKernelGGL((snap_mfma_kernel<DD, NN, false>), ga, dim3(256), 0, s, a);                 \
-    hipLaunchKernelGGL(snap_lse_merge_kernel, dim3(ceil_div(int(units) * a.R, 256)), dim3(256), 0, s, a); \
+    hipLaunchKernelGGL(snap_lse_merge_kernel, dim3(ceil_div(int(units) * a.R * SK_MERGE_LANES, 256)), dim3(256), 0, s, a); \
     hipLaunchKernelGGL((snap_mfma_kernel<DD, NN, true>), gb, dim3(256), 0, s, a);                  \
   } while (0)
     if (c.d_k == 128) {
@@ -321,8 +545,15 @@ se_status launch_snapkv(const se_cache& c, const void* q_obs, const void* k, con
     }
   }
   if (hipGetLastError() != hipSuccess) return SE_ERR_HIP;
-  hipLaunchKernelGGL(snap_pool_kernel, vgrid, dim3(256), 0, s, a);
-  hipLaunchKernelGGL(snap_select_kernel, dim3(int(units)), dim3(SK_TOPK_BLOCK), 0, s, a);
+  hipLaunchKernelGGL(snap_pool_kernel, dim3(ceil_div(int(n), SK_POOL_T), int(units)), dim3(256), 0, s, a);
+  const int kk = std::min(budget - window, int(n));
+  const dim3 sgrid(sel_slices(int(n)), int(units));
+  for (int pass = 0; pass < 3; ++pass) {
+    hipLaunchKernelGGL(snap_sel_hist_kernel, sgrid, dim3(SK_SEL_BLOCK), 0, s, a, pass);
+    hipLaunchKernelGGL(snap_sel_find_kernel, dim3(int(units)), dim3(SK_SEL_BLOCK), 0, s, a, pass, kk);
+  }
+  hipLaunchKernelGGL(snap_sel_count_kernel, sgrid, dim3(SK_SEL_BLOCK), 0, s, a, kk);
+  hipLaunchKernelGGL(snap_sel_write_kernel, sgrid, dim3(SK_SEL_BLOCK), 0, s, a);
   const int esz = c.dtype == SE_F32 ? 4 : 2;
   const int row_words = c.d_k * esz / 16;
   const int rows_per_block = 256 / row_words;
