@@ -206,8 +206,9 @@ se_status se_h2o_accumulate_evict(const se_cache* c, const float* logits, const 
  *   j < seq_len[b] (logits / lse from a full-view se_sparse_decode_attn);
  *   view_idx int32 [B][Hkv][top_k]: the top_k best slots (ties to the lower
  *   slot), ascending, -1 padded; view_len int32 [B][Hkv] = min(top_k, seq_len[b]);
- *   scores: NULL or float [B][Hkv][logit_cap].
- *   ws: se_workspace_bytes(SE_OP_OMNIKV, c, logit_cap, top_k) bytes. */
+ *   scores: NULL or float [B][Hkv][logit_cap] (entries past seq_len[b] not written).
+ *   ws: se_workspace_bytes(SE_OP_OMNIKV, c, logit_cap, top_k) bytes (unused,
+ *   may be NULL, when scores is given: the scores are staged there). */
 se_status se_omnikv_topk(const se_cache* c, const float* logits, const float* lse, int32_t logit_cap,
                          const int32_t* seq_len, int32_t top_k, int32_t* view_idx,
                          int32_t* view_len, float* scores, void* ws, size_t ws_bytes,

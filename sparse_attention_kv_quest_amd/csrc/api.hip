@@ -10,6 +10,11 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Launch failures are read back with hipGetLastError after the launches; an
+// error left by an earlier, unrelated HIP call is cleared first so that it is
+// not reported as this call's.
+void clear_stale_error() { (void)hipGetLastError(); }
+
 bool trace_on() {
   static int on = -1;
   if (on < 0) {
@@ -76,6 +81,7 @@ se_status se_workspace_init(void* ws, size_t bytes, hipStream_t stream) {
   if (bytes == 0) return SE_OK;
   if (!ws) return SE_ERR_NULL;
   if (!aligned16(ws)) return SE_ERR_ALIGN;
+  clear_stale_error();
   return launch_zero_fill(ws, bytes, stream);
 }
 
@@ -88,6 +94,7 @@ se_status se_kv_append(const se_cache* c, void* k, void* v, const void* k_new, c
     return SE_ERR_ALIGN;
   SE_TRACE_CALL("kv_append B=%d Hkv=%d d_k=%d cap=%d slot=%p", c->batch, c->n_kv_heads, c->d_k, c->capacity,
                 (const void*)slot);
+  clear_stale_error();
   return launch_kv_append(*c, k, v, k_new, v_new, slot, seq_len, stream);
 }
 
@@ -101,6 +108,7 @@ se_status se_page_meta_update(const se_cache* c, const void* k, void* kmin, void
   if (page_size <= 0 || page_size > c->capacity || first_page < -1) return SE_ERR_SHAPE;
   SE_TRACE_CALL("page_meta B=%d Hkv=%d d_k=%d P=%d first=%d", c->batch, c->n_kv_heads, c->d_k, page_size,
                 first_page);
+  clear_stale_error();
   return launch_page_meta(*c, k, kmin, kmax, seq_len, page_size, first_page, stream);
 }
 
@@ -120,6 +128,7 @@ se_status se_quest_select(const se_cache* c, const void* q, const void* kmin, co
   }
   SE_TRACE_CALL("quest_select B=%d Hq=%d Hkv=%d d_k=%d P=%d k=%d", c->batch, c->n_q_heads, c->n_kv_heads,
                 c->d_k, page_size, top_pages);
+  clear_stale_error();
   return launch_quest(*c, q, kmin, kmax, seq_len, page_size, top_pages, view_idx, view_len, page_score, ws,
                       stream);
 }
@@ -148,6 +157,7 @@ se_status se_sparse_decode_attn(const se_cache* c, const void* q, const void* k,
   SE_TRACE_CALL("sparse_decode_attn B=%d Hq=%d Hkv=%d d_k=%d d_v=%d view=%s cap=%d g=%d splits=%d logits=%d",
                 c->batch, c->n_q_heads, c->n_kv_heads, c->d_k, c->d_v, view_idx ? "idx" : "identity",
                 view_cap, granularity, num_splits, logits ? logit_cap : 0);
+  clear_stale_error();
   return launch_attn(*c, q, k, v, seq_len, view_idx, view_len, view_cap, granularity, scale, out, lse, logits,
                      logit_cap, num_splits, ws, stream);
 }
@@ -180,6 +190,7 @@ se_status se_snapkv_score_compact(const se_cache* c, const void* q_obs, const vo
   if (!ws || ws_bytes < need) return SE_ERR_WORKSPACE;
   SE_TRACE_CALL("snapkv_score_compact B=%d Hq=%d Hkv=%d L=%d W=%d pool=%d budget=%d", c->batch, c->n_q_heads,
                 c->n_kv_heads, prompt_len, window, pool_kernel, budget);
+  clear_stale_error();
   return launch_snapkv(*c, q_obs, k, v, prompt_len, window, pool_kernel, budget, scale, *out, k_out, v_out,
                        kept_pos, votes, out_seq_len, ws, stream);
 }
@@ -197,6 +208,7 @@ se_status se_h2o_accumulate_evict(const se_cache* c, const float* logits, const 
   if (cur_pos < 0) return SE_ERR_SHAPE;
   SE_TRACE_CALL("h2o_accumulate_evict B=%d Hq=%d Hkv=%d cap=%d pos=%d heavy=%d recent=%d", c->batch,
                 c->n_q_heads, c->n_kv_heads, c->capacity, cur_pos, heavy_budget, recent_window);
+  clear_stale_error();
   return launch_h2o(*c, logits, lse, logit_cap, seq_len, slot_pos, acc, cur_pos, heavy_budget, recent_window,
                     evict_slot, stream);
 }
@@ -210,10 +222,11 @@ se_status se_omnikv_topk(const se_cache* c, const float* logits, const float* ls
   if (!logits || !lse || !seq_len || !view_idx || !view_len) return SE_ERR_NULL;
   if (logit_cap <= 0) return SE_ERR_SHAPE;
   if (top_k < 1 || top_k > logit_cap) return SE_ERR_BUDGET;
-  const size_t need = omnikv_ws_bytes(*c, logit_cap, top_k);
+  const size_t need = scores ? 0 : omnikv_ws_bytes(*c, logit_cap, top_k);
   if (need > 0 && (!ws || ws_bytes < need)) return SE_ERR_WORKSPACE;
   SE_TRACE_CALL("omnikv_topk B=%d Hq=%d Hkv=%d cap=%d k=%d", c->batch, c->n_q_heads, c->n_kv_heads, logit_cap,
                 top_k);
+  clear_stale_error();
   return launch_omnikv(*c, logits, lse, logit_cap, seq_len, top_k, view_idx, view_len, scores, ws, stream);
 }
 

@@ -367,11 +367,13 @@ bool attn_mfma_supported(const AttnArgs& a) {
          (a.view_idx == nullptr || a.gshift >= 0) && a.cap <= (1 << 30) / a.Dk;
 }
 
-// One block per CU when the units alone do not fill the chip.
+// Long views: two blocks per CU (512 blocks) as long as every split keeps at
+// least 1024 slots; otherwise one block per CU (256 blocks) with at least four
+// tiles per block.
 int attn_mfma_auto_splits(int units, int slots) {
-  const int target_blocks = 256;
-  int s = (target_blocks + units - 1) / units;
-  s = std::max(1, std::min(s, (slots + 4 * MF_TS - 1) / (4 * MF_TS)));
+  int s = (512 + units - 1) / units;
+  s = std::max(1, std::min(s, slots / 1024));
+  if (units * s < 256) s = std::max(1, std::min((256 + units - 1) / units, (slots + 4 * MF_TS - 1) / (4 * MF_TS)));
   return std::min(s, 256);
 }
 
