@@ -54,6 +54,16 @@ __device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v, uint32_t iden
   v = op(v, uint32_t(__builtin_amdgcn_update_dpp(id, int(v), 0x143, 0xc, 0xf, false)));   // row_bcast:31
   return v;
 }
+// Inclusive scan inside each 16-lane row only (lane 15 of a row ends with the row's total).
+template <class Op>
+__device__ __forceinline__ uint32_t row_incl_scan_dpp(uint32_t v, uint32_t identity, Op op) {
+  const int id = int(identity);
+  v = op(v, uint32_t(__builtin_amdgcn_update_dpp(id, int(v), 0x111, 0xf, 0xf, false)));   // row_shr:1
+  v = op(v, uint32_t(__builtin_amdgcn_update_dpp(id, int(v), 0x112, 0xf, 0xf, false)));   // row_shr:2
+  v = op(v, uint32_t(__builtin_amdgcn_update_dpp(id, int(v), 0x114, 0xf, 0xf, false)));   // row_shr:4
+  v = op(v, uint32_t(__builtin_amdgcn_update_dpp(id, int(v), 0x118, 0xf, 0xf, false)));   // row_shr:8
+  return v;
+}
 // Value of the last lane (the wave-wide reduction) as a wave-uniform value.
 __device__ __forceinline__ uint32_t wave_last(uint32_t v) { return uint32_t(__builtin_amdgcn_readlane(int(v), 63)); }
 
