@@ -2,8 +2,9 @@
 
 Headline: the Quest path on the 32K workload (16 x 32q/4kv x d128, pages of 16,
 top-128 pages).  A step is one decode token for every batch row through one
-layer: append the new K/V row, rebuild the last page's min/max, score and
-select pages, and run split-K decode attention over the selected pages.  Steps
+layer: append the new K/V row and rebuild the last page's min/max (one
+launch), score and select pages, and run split-K decode attention over the
+selected pages.  Steps
 rotate over --layers distinct layer caches so that each step's working set has
 left the 256 MB Infinity Cache before it is read again.  Inputs are resident in
 HBM before timing starts; steps are replayed from HIP graphs.
@@ -189,8 +190,7 @@ def run_quest(se, torch, args):
     torch.cuda.synchronize()
 
     def step(L):
-        se.se_kv_append(c, L.k, L.v, kn, vn, None, L.seq)
-        se.se_page_meta_update(c, L.k, L.kmin, L.kmax, L.seq, P, -1)
+        se.se_kv_append_meta(c, L.k, L.v, kn, vn, None, L.seq, L.kmin, L.kmax, P)
         se.se_quest_select(c, q, L.kmin, L.kmax, L.seq, P, k, L.view, L.vlen, None, ws_q)
         se.se_sparse_decode_attn(c, q, L.k, L.v, L.seq, L.view, L.vlen, k, P, cfg.softmax_scale, L.out, lse,
                                  num_splits=args.splits, ws=ws_a)
@@ -473,8 +473,7 @@ def run_mla(se, torch, args):
     ws_a = se.workspace(se.SE_OP_ATTN, c, k * P, 0)
 
     def step(Ly):
-        se.se_kv_append(c, Ly["c"], None, kn, None, None, Ly["seq"])
-        se.se_page_meta_update(c, Ly["c"], Ly["kmin"], Ly["kmax"], Ly["seq"], P, -1)
+        se.se_kv_append_meta(c, Ly["c"], None, kn, None, None, Ly["seq"], Ly["kmin"], Ly["kmax"], P)
         se.se_quest_select(c, q, Ly["kmin"], Ly["kmax"], Ly["seq"], P, k, Ly["view"], Ly["vlen"], None, ws_q)
         se.se_sparse_decode_attn(c, q, Ly["c"], None, Ly["seq"], Ly["view"], Ly["vlen"], k, P, cfg.softmax_scale,
                                  Ly["out"], lse, ws=ws_a)

@@ -113,6 +113,16 @@ se_status se_page_meta_update(const se_cache* c, const void* k, void* kmin, void
                               const int32_t* seq_len, int32_t page_size, int32_t first_page,
                               hipStream_t stream);
 
+/* Append and summary-index update in one launch (the decode-step hook of a
+ * Quest cache): writes k_new / v_new exactly as se_kv_append, then rebuilds
+ * kmin / kmax of the page holding each written slot over the slots below the
+ * new seq_len[b], then updates seq_len.  With slot == NULL this equals
+ * se_kv_append followed by se_page_meta_update(first_page = -1).  Arguments
+ * as for those two calls. */
+se_status se_kv_append_meta(const se_cache* c, void* k, void* v, const void* k_new, const void* v_new,
+                            const int32_t* slot, int32_t* seq_len, void* kmin, void* kmax, int32_t page_size,
+                            hipStream_t stream);
+
 /* Quest page selection.  tokendh.com explainer, section "历史太长,会撑爆什么"
  * (Quest picks pages dynamically from the query) and Netics blog
  * "SparseEngine 统一接入十五种稀疏注意力", section "SparseEngine 围绕 KV cache

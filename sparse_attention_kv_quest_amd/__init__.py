@@ -20,7 +20,7 @@ SE_OP_QUEST, SE_OP_ATTN, SE_OP_SNAPKV, SE_OP_OMNIKV = 1, 2, 3, 4
 STATUS = {0: "SE_OK", -1: "SE_ERR_NULL", -2: "SE_ERR_SHAPE", -3: "SE_ERR_DTYPE", -4: "SE_ERR_ALIGN",
           -5: "SE_ERR_BUDGET", -6: "SE_ERR_WORKSPACE", -7: "SE_ERR_UNSUPPORTED", -8: "SE_ERR_HIP"}
 
-EXPORTS = ("se_kv_append", "se_page_meta_update", "se_quest_select", "se_sparse_decode_attn",
+EXPORTS = ("se_kv_append", "se_kv_append_meta", "se_page_meta_update", "se_quest_select", "se_sparse_decode_attn",
            "se_snapkv_score_compact", "se_h2o_accumulate_evict", "se_omnikv_topk",
            "se_workspace_bytes", "se_workspace_init", "se_status_string", "se_abi_version")
 
@@ -43,6 +43,7 @@ _C = ctypes.POINTER(se_cache)
 _SIGS = {
     "se_kv_append": [_C, _P, _P, _P, _P, _P, _P, _P],
     "se_page_meta_update": [_C, _P, _P, _P, _P, _I32, _I32, _P],
+    "se_kv_append_meta": [_C, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P],
     "se_quest_select": [_C, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _SZ, _P],
     "se_sparse_decode_attn": [_C, _P, _P, _P, _P, _P, _P, _I32, _I32, _F32, _P, _P, _P, _I32, _I32, _P, _SZ, _P],
     "se_snapkv_score_compact": [_C, _P, _P, _P, _I32, _I32, _I32, _I32, _F32, _C, _P, _P, _P, _P, _P, _P, _SZ,
@@ -139,6 +140,12 @@ def se_workspace_init(ws, nbytes=None, stream=None):
 def se_kv_append(c, k, v, k_new, v_new, slot, seq_len, stream=None):
     _check("se_kv_append", load().se_kv_append(ctypes.byref(c), _ptr(k), _ptr(v), _ptr(k_new), _ptr(v_new),
                                                _ptr(slot), _ptr(seq_len), _stream(stream)))
+
+
+def se_kv_append_meta(c, k, v, k_new, v_new, slot, seq_len, kmin, kmax, page_size, stream=None):
+    _check("se_kv_append_meta", load().se_kv_append_meta(
+        ctypes.byref(c), _ptr(k), _ptr(v), _ptr(k_new), _ptr(v_new), _ptr(slot), _ptr(seq_len), _ptr(kmin),
+        _ptr(kmax), page_size, _stream(stream)))
 
 
 def se_page_meta_update(c, k, kmin, kmax, seq_len, page_size, first_page=-1, stream=None):

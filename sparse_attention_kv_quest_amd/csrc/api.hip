@@ -98,6 +98,22 @@ se_status se_kv_append(const se_cache* c, void* k, void* v, const void* k_new, c
   return launch_kv_append(*c, k, v, k_new, v_new, slot, seq_len, stream);
 }
 
+se_status se_kv_append_meta(const se_cache* c, void* k, void* v, const void* k_new, const void* v_new,
+                            const int32_t* slot, int32_t* seq_len, void* kmin, void* kmax, int32_t page_size,
+                            hipStream_t stream) {
+  se_status st = check_cache(c);
+  if (st != SE_OK) return st;
+  if (!k || !k_new || !seq_len || !kmin || !kmax || (!c->latent && (!v || !v_new))) return SE_ERR_NULL;
+  if (!aligned16(k) || !aligned16(k_new) || !aligned16(kmin) || !aligned16(kmax) ||
+      (!c->latent && (!aligned16(v) || !aligned16(v_new))))
+    return SE_ERR_ALIGN;
+  if (page_size <= 0 || page_size > c->capacity) return SE_ERR_SHAPE;
+  SE_TRACE_CALL("kv_append_meta B=%d Hkv=%d d_k=%d cap=%d P=%d slot=%p", c->batch, c->n_kv_heads, c->d_k,
+                c->capacity, page_size, (const void*)slot);
+  clear_stale_error();
+  return launch_kv_append_meta(*c, k, v, k_new, v_new, slot, seq_len, kmin, kmax, page_size, stream);
+}
+
 se_status se_page_meta_update(const se_cache* c, const void* k, void* kmin, void* kmax,
                               const int32_t* seq_len, int32_t page_size, int32_t first_page,
                               hipStream_t stream) {

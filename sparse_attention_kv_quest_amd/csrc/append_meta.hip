@@ -107,6 +107,87 @@ __global__ __launch_bounds__(256) void page_meta_kernel(
   }
 }
 
+// ------------------------------------------------------------------ append + metadata in one launch
+// One block per batch row: writes the new row of every KV head (as
+// kv_append_kernel), then rebuilds the min / max of the page holding each
+// written slot over the slots below the new length, then bumps seq_len.  Works
+// on 32-bit words: a bf16 word holds two dimensions, min / max taken on each.
+template <bool BF16>
+__global__ __launch_bounds__(256) void kv_append_meta_kernel(
+    uint32_t* __restrict__ k, uint32_t* __restrict__ v, const uint32_t* __restrict__ k_new,
+    const uint32_t* __restrict__ v_new, const int32_t* __restrict__ slot, int32_t* __restrict__ seq_len,
+    uint32_t* __restrict__ kmin, uint32_t* __restrict__ kmax, int Hkv, int cap, int kwords, int vwords, int P) {
+  const int b = blockIdx.x;
+  const int len = seq_len[b];
+  const bool bump = slot == nullptr || slot[b * Hkv] < 0;
+  const int new_len = (bump && len < cap) ? len + 1 : len;
+  const int n_cap_pages = (cap + P - 1) / P;
+  auto slot_of = [&](int h) { return (slot != nullptr && slot[b * Hkv + h] >= 0) ? slot[b * Hkv + h] : len; };
+  for (int i = threadIdx.x; i < Hkv * kwords; i += blockDim.x) {
+    const int h = i / kwords, wd = i - h * kwords, pos = slot_of(h);
+    if (pos < 0 || pos >= cap) continue;
+    const size_t unit = size_t(b) * Hkv + h;
+    k[(unit * cap + pos) * kwords + wd] = k_new[unit * kwords + wd];
+  }
+  if (v != nullptr)
+    for (int i = threadIdx.x; i < Hkv * vwords; i += blockDim.x) {
+      const int h = i / vwords, wd = i - h * vwords, pos = slot_of(h);
+      if (pos < 0 || pos >= cap) continue;
+      const size_t unit = size_t(b) * Hkv + h;
+      v[(unit * cap + pos) * vwords + wd] = v_new[unit * vwords + wd];
+    }
+  __syncthreads();   // the block's row writes are visible to its page reads
+  for (int i = threadIdx.x; i < Hkv * kwords; i += blockDim.x) {
+    const int h = i / kwords, wd = i - h * kwords, pos = slot_of(h);
+    if (pos < 0 || pos >= cap) continue;
+    const int page = pos / P, t0 = page * P, t1 = min(new_len, t0 + P);
+    if (t0 >= t1) continue;
+    const size_t unit = size_t(b) * Hkv + h;
+    const uint32_t* col = k + unit * cap * kwords + wd;
+    float mn0 = INFINITY, mx0 = -INFINITY, mn1 = INFINITY, mx1 = -INFINITY;
+#pragma unroll 4
+    for (int t = t0; t < t1; ++t) {
+      const uint32_t x = col[size_t(t) * kwords];
+      if (BF16) {
+        const float lo = bf16_lo(x), hi = bf16_hi(x);
+        mn0 = fminf(mn0, lo); mx0 = fmaxf(mx0, lo);
+        mn1 = fminf(mn1, hi); mx1 = fmaxf(mx1, hi);
+      } else {
+        const float f = __uint_as_float(x);
+        mn0 = fminf(mn0, f); mx0 = fmaxf(mx0, f);
+      }
+    }
+    const size_t o = (unit * n_cap_pages + page) * kwords + wd;
+    if (BF16) {   // exact: every value is a stored bf16
+      kmin[o] = (__float_as_uint(mn0) >> 16) | (__float_as_uint(mn1) & 0xffff0000u);
+      kmax[o] = (__float_as_uint(mx0) >> 16) | (__float_as_uint(mx1) & 0xffff0000u);
+    } else {
+      kmin[o] = __float_as_uint(mn0);
+      kmax[o] = __float_as_uint(mx0);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && new_len != len) seq_len[b] = new_len;
+}
+
+se_status launch_kv_append_meta(const se_cache& c, void* k, void* v, const void* k_new, const void* v_new,
+                                const int32_t* slot, int32_t* seq_len, void* kmin, void* kmax, int page_size,
+                                hipStream_t s) {
+  const int esz = c.dtype == SE_F32 ? 4 : 2;
+  const int kwords = c.d_k * esz / 4, vwords = c.d_v * esz / 4;
+  void* vv = c.latent ? nullptr : v;
+  const void* vn = c.latent ? nullptr : v_new;
+  if (c.dtype == SE_F32)
+    hipLaunchKernelGGL(kv_append_meta_kernel<false>, dim3(c.batch), dim3(256), 0, s, (uint32_t*)k, (uint32_t*)vv,
+                       (const uint32_t*)k_new, (const uint32_t*)vn, slot, seq_len, (uint32_t*)kmin,
+                       (uint32_t*)kmax, c.n_kv_heads, c.capacity, kwords, vwords, page_size);
+  else
+    hipLaunchKernelGGL(kv_append_meta_kernel<true>, dim3(c.batch), dim3(256), 0, s, (uint32_t*)k, (uint32_t*)vv,
+                       (const uint32_t*)k_new, (const uint32_t*)vn, slot, seq_len, (uint32_t*)kmin,
+                       (uint32_t*)kmax, c.n_kv_heads, c.capacity, kwords, vwords, page_size);
+  return launch_status();
+}
+
 se_status launch_page_meta(const se_cache& c, const void* k, void* kmin, void* kmax,
                            const int32_t* seq_len, int page_size, int first_page, hipStream_t s) {
   const int units = c.batch * c.n_kv_heads;

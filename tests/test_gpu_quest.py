@@ -144,3 +144,86 @@ def test_quest_32k_decode(se):
     view = host(st.view)
     assert np.all(np.diff(view, axis=-1) > 0)
     print(f"planted-page recall (diagnostic only): {np.mean(recall):.3f}")
+
+
+APPEND_CFGS = {
+    "bf16_d128_g8": get_config(0, dtype="bf16", batch=3, n_q_heads=16, n_kv_heads=2, d_k=128, d_v=128),
+    "f32_d64": get_config(0, batch=2, n_q_heads=4, n_kv_heads=2),
+    "mla_576": get_config(4, batch=2, context=200, page_size=64),
+}
+
+
+@pytest.mark.parametrize("name", list(APPEND_CFGS))
+def test_append_meta_matches_separate_calls(se, name):
+    """se_kv_append_meta = se_kv_append + se_page_meta_update(first_page=-1), bit for bit:
+    rows, every valid page's min / max and seq_len, across page boundaries and a full cache."""
+    cfg = APPEND_CFGS[name]
+    banner(f"append+meta {name}")
+    dt = tdtype(cfg)
+    B, H, D, Dv, P = cfg.batch, cfg.n_kv_heads, cfg.d_k, cfg.d_v, cfg.page_size
+    cap = 4 * P + 3
+    lens0 = [P - 1, 2 * P, cap - 2][:B] if B == 3 else [P - 1, cap - 2]
+    c = se.cache(B, cfg.n_q_heads, H, D, Dv, cap, cfg.dtype, cfg.latent)
+    K, V = gen.cache_kv(cfg, 5, cap, length=cap)
+    ncp = (cap + P - 1) // P
+    st = {}
+    for tag in ("fused", "separate"):
+        k = dev(K, dt)
+        v = None if cfg.latent else dev(V, dt)
+        kmin = torch.zeros((B, H, ncp, D), dtype=dt, device="cuda")
+        kmax = torch.zeros_like(kmin)
+        seq = torch.tensor(lens0, dtype=torch.int32, device="cuda")
+        se.se_page_meta_update(c, k, kmin, kmax, seq, P, 0)
+        st[tag] = (k, v, kmin, kmax, seq)
+    for step in range(5):          # crosses a page boundary and runs into the full cache
+        kn, vn = gen.decode_kv_new(cfg, 5, step)
+        knd = dev(kn, dt)
+        vnd = None if cfg.latent else dev(vn, dt)
+        k, v, kmin, kmax, seq = st["fused"]
+        se.se_kv_append_meta(c, k, v, knd, vnd, None, seq, kmin, kmax, P)
+        k, v, kmin, kmax, seq = st["separate"]
+        se.se_kv_append(c, k, v, knd, vnd, None, seq)
+        se.se_page_meta_update(c, k, kmin, kmax, seq, P, -1)
+        torch.cuda.synchronize()
+        a, b = st["fused"], st["separate"]
+        np.testing.assert_array_equal(host(a[4]), host(b[4]))
+        np.testing.assert_array_equal(host(a[0]), host(b[0]))
+        if not cfg.latent:
+            np.testing.assert_array_equal(host(a[1]), host(b[1]))
+        lens = host(a[4])
+        for bb in range(B):
+            npv = (int(lens[bb]) + P - 1) // P
+            np.testing.assert_array_equal(host(a[2])[bb, :, :npv], host(b[2])[bb, :, :npv])
+            np.testing.assert_array_equal(host(a[3])[bb, :, :npv], host(b[3])[bb, :, :npv])
+    assert list(host(st["fused"][4])) == [min(l + 5, cap) for l in lens0]
+
+
+def test_append_meta_into_freed_slot(se):
+    """With a slot per unit (a slot freed by eviction), the page holding that slot is
+    rebuilt over the valid slots and seq_len is unchanged."""
+    cfg = APPEND_CFGS["bf16_d128_g8"]
+    banner("append+meta into a slot")
+    B, H, D, P = cfg.batch, cfg.n_kv_heads, cfg.d_k, cfg.page_size
+    cap = 5 * P
+    c = se.cache(B, cfg.n_q_heads, H, D, D, cap, "bf16")
+    K, V = gen.cache_kv(cfg, 6, cap, length=cap)
+    ncp = cap // P
+    k, v = dev(K, torch.bfloat16), dev(V, torch.bfloat16)
+    kmin = torch.zeros((B, H, ncp, D), dtype=torch.bfloat16, device="cuda")
+    kmax = torch.zeros_like(kmin)
+    seq = torch.full((B,), cap, dtype=torch.int32, device="cuda")
+    se.se_page_meta_update(c, k, kmin, kmax, seq, P, 0)
+    slots = np.array([[3, 40], [17, 79], [0, 64]], np.int32)
+    kn, vn = gen.decode_kv_new(cfg, 6, 0)
+    se.se_kv_append_meta(c, k, v, dev(kn, torch.bfloat16), dev(vn, torch.bfloat16), dev(slots, torch.int32), seq,
+                         kmin, kmax, P)
+    torch.cuda.synchronize()
+    assert np.all(host(seq) == cap)
+    Kx = K.copy()
+    for bb in range(B):
+        for h in range(H):
+            Kx[bb, h, slots[bb, h]] = kn[bb, h]
+    np.testing.assert_array_equal(host(k), Kx)
+    mn, mx = oquest.page_meta(Kx, [cap] * B, P)
+    np.testing.assert_array_equal(host(kmin), mn)
+    np.testing.assert_array_equal(host(kmax), mx)
