@@ -195,11 +195,12 @@ template <int D, int HB>
 static void launch_score_mfma(const se_cache& c, const void* q, const void* kmin, const void* kmax,
                               const int32_t* seq_len, float* score, int P, int ncp, hipStream_t s) {
   const int units = c.batch * c.n_kv_heads, G = c.n_q_heads / c.n_kv_heads;
-  constexpr int BPW = D >= 512 ? 1 : 2;
-  dim3 grid(ceil_div(ncp, 64 * BPW), units);
-  hipLaunchKernelGGL((quest_score_mfma_kernel<D, HB, BPW>), grid, dim3(256), 0, s, (const uint16_t*)q,
-                     (const uint16_t*)kmin, (const uint16_t*)kmax, seq_len, score, c.n_kv_heads, G, P, ncp,
-                     c.capacity);
+  // one group of 16 pages per wave: many small blocks keep the most metadata loads in flight
+#define SE_SCORE(BB) hipLaunchKernelGGL((quest_score_mfma_kernel<D, HB, BB>), dim3(ceil_div(ncp, 64 * (BB)), units),  \
+                                        dim3(256), 0, s, (const uint16_t*)q, (const uint16_t*)kmin,                 \
+                                        (const uint16_t*)kmax, seq_len, score, c.n_kv_heads, G, P, ncp, c.capacity)
+  SE_SCORE(1);
+#undef SE_SCORE
 }
 
 se_status launch_quest(const se_cache& c, const void* q, const void* kmin, const void* kmax,
