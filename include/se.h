@@ -155,6 +155,7 @@ se_status se_quest_select(const se_cache* c, const void* q, const void* kmin, co
  *   num_splits: 0 chooses the split-K factor; otherwise the number of chunks
  *   (1..256) each unit's view is cut into (results agree to rounding for any
  *   value).
+ *   q, k, v and out must be 16-byte aligned (SE_ERR_ALIGN otherwise).
  *   ws: se_workspace_bytes(SE_OP_ATTN, c, view_cap * g, num_splits) bytes. */
 se_status se_sparse_decode_attn(const se_cache* c, const void* q, const void* k, const void* v,
                                 const int32_t* seq_len, const int32_t* view_idx,

@@ -158,7 +158,7 @@ se_status se_sparse_decode_attn(const se_cache* c, const void* q, const void* k,
   se_status st = check_cache(c);
   if (st != SE_OK) return st;
   if (!q || !k || !seq_len || !out || (!c->latent && !v)) return SE_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k) || (!c->latent && !aligned16(v))) return SE_ERR_ALIGN;
+  if (!aligned16(q) || !aligned16(k) || (!c->latent && !aligned16(v)) || !aligned16(out)) return SE_ERR_ALIGN;
   if (view_idx) {
     if (!view_len) return SE_ERR_NULL;
     if (view_cap <= 0 || granularity <= 0) return SE_ERR_SHAPE;

@@ -76,13 +76,12 @@ __device__ __forceinline__ bool attn_split_done(int* ctr, int splits) { return b
 // Merge the splits of heads [h0, h0 + nh) of one unit into out / lse (natural-log
 // lse) and reset the unit's ticket counter.  A thread owns four consecutive
 // output columns of one head; for a batch of up to SU splits it issues every
-// load (max, sum and four partial outputs per split) before using any, and
-// folds the batch into a running (max, sum, output) by log-sum-exp, so a
-// merge of up to SU splits costs one round trip.
-template <int NT>
-__device__ void attn_merge_splits(const AttnArgs& a, int unit, int h0, int nh, int* ctr) {
-  constexpr int SU = 8;
-  const int S = a.splits, G = a.G, Dv = a.Dv;   // Dv is a multiple of 4
+// load (max and sum as one 8-byte access, the four partial outputs as two)
+// before using any, and folds the batch into a running (max, sum, output) by
+// log-sum-exp, so a merge of up to SU splits costs one round trip.
+template <int NT, int SU>
+__device__ void attn_merge_splits_su(const AttnArgs& a, int unit, int h0, int nh, int* ctr) {
+  const int S = a.splits, G = a.G, Dv = a.Dv;   // Dv is a multiple of 8
   const int b = unit / a.Hkv, kvh = unit % a.Hkv;
   const float* pml = a.part_ml + size_t(unit) * S * G * 2;
   const float* po = a.part_o + size_t(unit) * S * G * Dv;
@@ -91,20 +90,20 @@ __device__ void attn_merge_splits(const AttnArgs& a, int unit, int h0, int nh, i
     const int hl = e / Dv, d0 = e - hl * Dv, h = h0 + hl;
     float M = -INFINITY, L = 0.f, O[4] = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < S; s0 += SU) {
-      float mb[SU], lb[SU], ob[SU][4];
+      float2 mlb[SU], ob0[SU], ob1[SU];
 #pragma unroll
       for (int j = 0; j < SU; ++j) {
         const int s = min(s0 + j, S - 1);
-        mb[j] = ld_dev(pml + (s * G + h) * 2);
-        lb[j] = ld_dev(pml + (s * G + h) * 2 + 1);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) ob[j][u] = ld_dev(po + (size_t(s) * G + h) * Dv + d0 + u);
+        mlb[j] = ld_dev2(pml + (s * G + h) * 2);
+        const float* op = po + (size_t(s) * G + h) * Dv + d0;
+        ob0[j] = ld_dev2(op);
+        ob1[j] = ld_dev2(op + 2);
       }
       float Mb = -INFINITY;
 #pragma unroll
       for (int j = 0; j < SU; ++j) {
-        if (s0 + j >= S) mb[j] = -INFINITY;   // a repeated split, not counted
-        Mb = fmaxf(Mb, mb[j]);
+        if (s0 + j >= S) mlb[j].x = -INFINITY;   // a repeated split, not counted
+        Mb = fmaxf(Mb, mlb[j].x);
       }
       const float Mn = fmaxf(M, Mb);
       if (Mn == -INFINITY) continue;
@@ -114,19 +113,26 @@ __device__ void attn_merge_splits(const AttnArgs& a, int unit, int h0, int nh, i
       for (int u = 0; u < 4; ++u) O[u] *= alpha;
 #pragma unroll
       for (int j = 0; j < SU; ++j) {
-        const float f = mb[j] == -INFINITY ? 0.f : exp2f((mb[j] - Mn) * LOG2E);
-        L += f * lb[j];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) O[u] += f * ob[j][u];
+        const float f = mlb[j].x == -INFINITY ? 0.f : exp2f((mlb[j].x - Mn) * LOG2E);
+        L += f * mlb[j].y;
+        O[0] += f * ob0[j].x;
+        O[1] += f * ob0[j].y;
+        O[2] += f * ob1[j].x;
+        O[3] += f * ob1[j].y;
       }
       M = Mn;
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) a.out[(row0 + hl) * Dv + d0 + u] = O[u] * inv;
+    *reinterpret_cast<float4*>(a.out + (row0 + hl) * Dv + d0) = make_float4(O[0] * inv, O[1] * inv, O[2] * inv, O[3] * inv);
     if (d0 == 0 && a.lse != nullptr) a.lse[row0 + hl] = L > 0.f ? M + logf(L) : -INFINITY;
   }
   if (threadIdx.x == 0) ticket_reset(ctr);
+}
+
+template <int NT>
+__device__ void attn_merge_splits(const AttnArgs& a, int unit, int h0, int nh, int* ctr) {
+  if (a.splits <= 4) attn_merge_splits_su<NT, 4>(a, unit, h0, nh, ctr);
+  else attn_merge_splits_su<NT, 8>(a, unit, h0, nh, ctr);
 }
 
 // Final output of a unit handled by one block (splits == 1): out = O / L, lse = M + log L.

@@ -271,69 +271,91 @@ void attn_mfma_kernel(AttnArgs a) {
                       ? a.logits + (size_t(b) * a.Hq + size_t(kvh) * G + c16) * a.logit_cap
                       : nullptr;
 
-  // This wave's tiles are w, w + 4, ...  The prefetch of the next tile is issued
-  // unconditionally (a tile past the chunk has no tokens and reads row 0), so the
-  // loop body is straight-line code and the compiler keeps exact wait counts:
-  // computing tile i waits only for tile i's loads, not for tile i + 1's.
+  // This wave's tiles are w, w + 4, ...  The steady-state loop runs only while
+  // every tile it prefetches exists: its loads are unconditional and an
+  // iteration ends with the same tiles in flight as it began, so the compiler's
+  // wait counts stay exact (computing a tile waits only for that tile's loads).
+  // The last two to four tiles are drained without further prefetch, so no wave
+  // ends waiting on a load it will not use.
   const int ntiles = (s1 - s0 + MF_TS - 1) / MF_TS;
   const int nmine = w < ntiles ? (ntiles - w + MF_WAVES - 1) / MF_WAVES : 0;
   constexpr int STEP = MF_WAVES * MF_TS;   // slots between this wave's consecutive tiles
+  const int first = s0 + w * MF_TS;
   if (OCC == 1) {
     MfTile<D> T0, T1, T2;                  // two tiles in flight while a third is computed
-    if (nmine > 0) {
-      const int first = s0 + w * MF_TS;
+    if (nmine == 1) {
+      mf_load<D, VC>(x, first, lane, T0);
+      mf_compute<D>(a, x, first, lane, qv, sc2, lg_row, vt, T0, st);
+    } else if (nmine > 1) {
       mf_load<D, VC>(x, first, lane, T0);
       mf_load<D, VC>(x, first + STEP, lane, T1);
-      for (int i = 0; i < nmine; i += 3) {
+      int i = 0;
+      for (; i + 4 < nmine; i += 3) {      // T0 = tile i, T1 = tile i + 1 in flight
         const int b0 = first + i * STEP;
         mf_load<D, VC>(x, b0 + 2 * STEP, lane, T2);
         mf_compute<D>(a, x, b0, lane, qv, sc2, lg_row, vt, T0, st);
-        if (i + 1 >= nmine) break;
         mf_load<D, VC>(x, b0 + 3 * STEP, lane, T0);
         mf_compute<D>(a, x, b0 + STEP, lane, qv, sc2, lg_row, vt, T1, st);
-        if (i + 2 >= nmine) break;
         mf_load<D, VC>(x, b0 + 4 * STEP, lane, T1);
         mf_compute<D>(a, x, b0 + 2 * STEP, lane, qv, sc2, lg_row, vt, T2, st);
       }
+      const int r = nmine - i;             // 2, 3 or 4 tiles left
+      const int b0 = first + i * STEP;
+      if (r >= 3) mf_load<D, VC>(x, b0 + 2 * STEP, lane, T2);
+      mf_compute<D>(a, x, b0, lane, qv, sc2, lg_row, vt, T0, st);
+      if (r == 4) mf_load<D, VC>(x, b0 + 3 * STEP, lane, T0);
+      mf_compute<D>(a, x, b0 + STEP, lane, qv, sc2, lg_row, vt, T1, st);
+      if (r >= 3) mf_compute<D>(a, x, b0 + 2 * STEP, lane, qv, sc2, lg_row, vt, T2, st);
+      if (r == 4) mf_compute<D>(a, x, b0 + 3 * STEP, lane, qv, sc2, lg_row, vt, T0, st);
     }
   } else {
     MfTile<D> T0, T1;                      // one tile in flight while the other is computed
     if (nmine > 0) {
-      const int first = s0 + w * MF_TS;
       mf_load<D, VC>(x, first, lane, T0);
-      for (int i = 0; i < nmine; i += 2) {
+      int i = 0;
+      for (; i + 2 < nmine; i += 2) {      // T0 = tile i in flight
         const int b0 = first + i * STEP;
         mf_load<D, VC>(x, b0 + STEP, lane, T1);
         mf_compute<D>(a, x, b0, lane, qv, sc2, lg_row, vt, T0, st);
-        if (i + 1 >= nmine) break;
         mf_load<D, VC>(x, b0 + 2 * STEP, lane, T0);
         mf_compute<D>(a, x, b0 + STEP, lane, qv, sc2, lg_row, vt, T1, st);
+      }
+      const int b0 = first + i * STEP;     // one or two tiles left
+      if (i + 1 < nmine) {
+        mf_load<D, VC>(x, b0 + STEP, lane, T1);
+        mf_compute<D>(a, x, b0, lane, qv, sc2, lg_row, vt, T0, st);
+        mf_compute<D>(a, x, b0 + STEP, lane, qv, sc2, lg_row, vt, T1, st);
+      } else {
+        mf_compute<D>(a, x, b0, lane, qv, sc2, lg_row, vt, T0, st);
       }
     }
   }
 
-  // ---- merge the four waves of the block
+  // ---- merge the waves of the block: per head, the waves' (max, sum) and
+  // outputs [wave][head][dim] (row pitch D + 4) go through LDS; a thread then
+  // owns four consecutive dims of one head.
   float lsum = st.lsum;
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
+  constexpr int OP = D + 4;
   __syncthreads();
-  float* red_o = reinterpret_cast<float*>(&vt_lds[0][0]);   // [MF_WAVES][D][16] fp32 (fits in the V tiles)
-  static_assert(MF_WAVES * D * 16 * sizeof(float) <= sizeof(vt_lds), "reduction buffer");
+  float* red_o = reinterpret_cast<float*>(&vt_lds[0][0]);
+  static_assert(MF_WAVES * 16 * OP * sizeof(float) <= sizeof(vt_lds), "reduction buffer");
   if (g == 0) { red_m[w][c16] = st.m2; red_l[w][c16] = lsum; }
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red_o[(w * D + 16 * db + 4 * g + i) * 16 + c16] = st.o[db][i];
+    *reinterpret_cast<f32x4*>(red_o + (w * 16 + c16) * OP + 16 * db + 4 * g) = st.o[db];
   __syncthreads();
   float* pml = a.part_ml + (size_t(unit) * a.splits + split) * G * 2;
   float* po = a.part_o + (size_t(unit) * a.splits + split) * G * D;
   const bool single = a.splits == 1;
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int h = idx / D, d = idx % D;
+  for (int idx = threadIdx.x * 4; idx < G * D; idx += 256 * 4) {
+    const int h = idx / D, d0 = idx % D;
     float M = red_m[0][h];
 #pragma unroll
     for (int ww = 1; ww < MF_WAVES; ++ww) M = fmaxf(M, red_m[ww][h]);
-    float L = 0.f, O = 0.f;
+    float L = 0.f;
+    f32x4 O = {0.f, 0.f, 0.f, 0.f};
     if (M != -INFINITY) {
 #pragma unroll
       for (int ww = 0; ww < MF_WAVES; ++ww) {
@@ -341,19 +363,24 @@ void attn_mfma_kernel(AttnArgs a) {
         if (mw != -INFINITY) {
           const float f = exp2f(mw - M);
           L += f * red_l[ww][h];
-          O += f * red_o[(ww * D + d) * 16 + h];
+          O += f * *reinterpret_cast<const f32x4*>(red_o + (ww * 16 + h) * OP + d0);
         }
       }
     }
     const float Mn = M == -INFINITY ? -INFINITY : M * 0.6931471805599453f;   // log2 -> natural units
     if (single) {
-      attn_write_final(a, size_t(b) * a.Hq + size_t(kvh) * G + h, d, Mn, L, O);
+      const size_t row = size_t(b) * a.Hq + size_t(kvh) * G + h;
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      *reinterpret_cast<f32x4*>(a.out + row * D + d0) = O * inv;
+      if (d0 == 0 && a.lse != nullptr) a.lse[row] = L > 0.f ? Mn + logf(L) : -INFINITY;
+    } else if (a.fused) {
+      st_dev2(po + h * D + d0, O[0], O[1]);
+      st_dev2(po + h * D + d0 + 2, O[2], O[3]);
+      if (d0 == 0) st_dev2(pml + 2 * h, Mn, L);
     } else {
-      st_part(a, po + h * D + d, O);
-      if (d == 0) {
-        st_part(a, pml + 2 * h, Mn);
-        st_part(a, pml + 2 * h + 1, L);
-      }
+      *reinterpret_cast<float2*>(po + h * D + d0) = make_float2(O[0], O[1]);
+      *reinterpret_cast<float2*>(po + h * D + d0 + 2) = make_float2(O[2], O[3]);
+      if (d0 == 0) *reinterpret_cast<float2*>(pml + 2 * h) = make_float2(Mn, L);
     }
   }
   if (a.fused) {

@@ -124,6 +124,15 @@ __device__ __forceinline__ void st_dev(float* p, float v) {
 __device__ __forceinline__ float ld_dev(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Two consecutive floats at an 8-byte aligned address, as one access.
+__device__ __forceinline__ void st_dev2(float* p, float x, float y) {
+  const uint64_t v = (uint64_t(__float_as_uint(y)) << 32) | __float_as_uint(x);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 ld_dev2(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float(uint32_t(v)), __uint_as_float(uint32_t(v >> 32)));
+}
 // Takes this block's ticket on `ctr`; true in the block that takes ticket nblocks - 1.
 __device__ __forceinline__ bool block_ticket_last(int* ctr, int nblocks) {
   __shared__ int s_last;
