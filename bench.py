@@ -162,7 +162,8 @@ def run_quest(se, torch, args):
     cfg = get_config(1)
     B, H, Hq, D, P, k = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.d_k, cfg.page_size, cfg.top_pages
     nL = args.layers
-    steps_per_layer = -(-(args.warmup + args.steps) // nL) + args.attn_reps + 4
+    # appends per layer: warm-up and timed steps, the append-only stage timing, slack
+    steps_per_layer = -(-(args.warmup + args.steps) // nL) + 2 * args.attn_reps + 4
     cap = cfg.context + steps_per_layer
     c = se.cache(B, Hq, H, D, D, cap, "bf16")
     log(f"quest_32k: B={B} Hq={Hq} Hkv={H} D={D} ctx={cfg.context} P={P} top={k} cap={cap} layers={nL}")
@@ -209,6 +210,13 @@ def run_quest(se, torch, args):
     n_steps = reps * nL
     ms_step = t_step.ms_per_replay(reps) / nL
     us_attn = t_attn.ms_per_replay(args.attn_reps) * 1e3 / nL
+    # the step's stages, each replayed alone over the same layers
+    t_sel = Timer(torch, lambda: [se.se_quest_select(c, q, L.kmin, L.kmax, L.seq, P, k, L.view, L.vlen, None, ws_q)
+                                  for L in layers], use_graph)
+    us_sel = t_sel.ms_per_replay(args.attn_reps) * 1e3 / nL
+    t_app = Timer(torch, lambda: [se.se_kv_append_meta(c, L.k, L.v, kn, vn, None, L.seq, L.kmin, L.kmax, P)
+                                  for L in layers], use_graph)
+    us_app = t_app.ms_per_replay(args.attn_reps) * 1e3 / nL
 
     # algorithmic bytes of one attention call: K and V rows of the selected tokens,
     # plus q, the views and the fp32 outputs
@@ -227,6 +235,7 @@ def run_quest(se, torch, args):
     free(torch)
     return cfg, {
         "tokens_per_s": B / (ms_step * 1e-3), "ms_per_step": ms_step, "steps": n_steps,
+        "stages_us": {"append_meta": round(us_app, 3), "quest_select": round(us_sel, 3), "attention": round(us_attn, 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "attn_mfma_kernel (se_sparse_decode_attn: split-K, splits merged in-kernel)", "us_per_launch": round(us_attn, 3),
@@ -538,7 +547,8 @@ def main():
                             "page_size": cfg.page_size, "top_pages": cfg.top_pages, "layers_rotated": args.layers,
                             "graph": not args.no_graph, "attn_splits": args.splits}
         result["roofline"] = r["roofline"]
-        log(f"quest_32k: {r['ms_per_step'] * 1e3:.2f} us/step, attention {r['roofline']['us_per_launch']} us")
+        result["stages_us"] = r["stages_us"]
+        log(f"quest_32k: {r['ms_per_step'] * 1e3:.2f} us/step; stages alone (us): {r['stages_us']}")
     else:
         result["config"] = {"workload": "none (headline skipped)"}
     runners = {"snapkv_128k": run_snapkv, "h2o_16k": run_h2o, "omnikv_16k": run_omnikv, "mla_128k": run_mla}

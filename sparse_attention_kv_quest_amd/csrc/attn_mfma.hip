@@ -220,14 +220,37 @@ void attn_mfma_kernel(AttnArgs a) {
   const int G = a.G;
   // A page / token view is chunked by its capacity, so the block can fetch its view
   // entries right away; slots past the view's length are masked.  The identity view
-  // is chunked by seq_len.
-  const bool identity = a.view_idx == nullptr;
+  // is chunked by seq_len.  With the LDS view cache (VC, page / token views only)
+  // the entry loads depend on kernel arguments alone and are issued before the
+  // lengths are read, so the two fetches overlap.
+  const bool identity = !VC && a.view_idx == nullptr;
+  constexpr int VPT = MF_VCACHE / 256;   // cached view entries per thread
+  int ventry[VPT];
+  int e0 = 0, s0, s1;
+  if (VC) {
+    const int n_slots = a.view_cap * a.gran;
+    int chunk = (n_slots + a.splits - 1) / a.splits;
+    chunk = (chunk + MF_TS - 1) / MF_TS * MF_TS;
+    s0 = min(n_slots, split * chunk);
+    s1 = min(n_slots, s0 + chunk);
+    e0 = s0 >> a.gshift;
+    const int e1 = s1 > s0 ? ((s1 - 1) >> a.gshift) + 1 : e0;
+    const int32_t* vrow = a.view_idx + size_t(unit) * a.view_cap;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int e = e0 + threadIdx.x + 256 * j;
+      ventry[j] = e < e1 ? vrow[e] : -1;
+    }
+  }
   const int len = min(a.seq_len[b], a.cap);
-  const int n_slots = identity ? len : a.view_cap * a.gran;
+  if (!VC) {
+    const int n_slots = identity ? len : a.view_cap * a.gran;
+    int chunk = (n_slots + a.splits - 1) / a.splits;
+    chunk = (chunk + MF_TS - 1) / MF_TS * MF_TS;
+    s0 = min(n_slots, split * chunk);
+    s1 = min(n_slots, s0 + chunk);
+  }
   const int s_valid = identity ? len : min(a.view_len[unit], a.view_cap) * a.gran;
-  int chunk = (n_slots + a.splits - 1) / a.splits;
-  chunk = (chunk + MF_TS - 1) / MF_TS * MF_TS;
-  const int s0 = min(n_slots, split * chunk), s1 = min(n_slots, s0 + chunk);
 
   MfCtx x;
   x.ku = (const uint16_t*)a.k + size_t(unit) * a.cap * D;
@@ -236,17 +259,8 @@ void attn_mfma_kernel(AttnArgs a) {
   x.s1 = min(s1, s_valid);
   x.gshift = a.gshift;
   x.identity = identity;
-  x.e0 = 0;
-  x.vglob = nullptr;
-  if (!x.identity) {
-    const int32_t* vrow = a.view_idx + size_t(unit) * a.view_cap;
-    x.vglob = vrow;
-    if (VC) {
-      const int e0 = s0 >> a.gshift, e1 = s1 > s0 ? ((s1 - 1) >> a.gshift) + 1 : e0;
-      for (int e = e0 + threadIdx.x; e < e1; e += 256) mf_vcache[e - e0] = vrow[e];
-      x.e0 = e0;
-    }
-  }
+  x.e0 = e0;
+  x.vglob = identity ? nullptr : a.view_idx + size_t(unit) * a.view_cap;
 
   // Q as the B operand: lane holds head c16, dims 32c + 8g .. 32c + 8g + 7 of k-step c
   u32x4 qv[NKS];
@@ -257,6 +271,11 @@ void attn_mfma_kernel(AttnArgs a) {
   } else {
 #pragma unroll
     for (int c = 0; c < NKS; ++c) qv[c] = u32x4{0, 0, 0, 0};
+  }
+  if (VC) {
+#pragma unroll
+    for (int j = 0; j < VPT; ++j)
+      if (threadIdx.x + 256 * j < MF_VCACHE) mf_vcache[threadIdx.x + 256 * j] = ventry[j];
   }
   __syncthreads();   // view cache ready
 
