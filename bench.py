@@ -2,12 +2,12 @@
 
 Headline: the Quest path on the 32K workload (16 x 32q/4kv x d128, pages of 16,
 top-128 pages).  A step is one decode token for every batch row through one
-layer: append the new K/V row and rebuild the last page's min/max (one
-launch), score and select pages, and run split-K decode attention over the
-selected pages.  Steps
-rotate over --layers distinct layer caches so that each step's working set has
-left the 256 MB Infinity Cache before it is read again.  Inputs are resident in
-HBM before timing starts; steps are replayed from HIP graphs.
+layer: one launch appends the new K/V row, rebuilds the last page's min/max,
+scores every page and selects the top pages (se_quest_append_select), then
+split-K decode attention runs over the selected pages.  Steps rotate over
+--layers distinct layer caches so that each step's working set has left the
+256 MB Infinity Cache before it is read again.  Inputs are resident in HBM
+before timing starts; steps are replayed from HIP graphs.
 
 The other workloads are timed the same way and reported under "workloads":
   snapkv_128k  prefill-end SnapKV eviction of a 131072-token prompt to 8192
@@ -162,7 +162,7 @@ def run_quest(se, torch, args):
     cfg = get_config(1)
     B, H, Hq, D, P, k = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.d_k, cfg.page_size, cfg.top_pages
     nL = args.layers
-    # appends per layer: warm-up and timed steps, the append-only stage timing, slack
+    # appends per layer: warm-up and timed steps, the append + select stage timing, slack
     steps_per_layer = -(-(args.warmup + args.steps) // nL) + 2 * args.attn_reps + 4
     cap = cfg.context + steps_per_layer
     c = se.cache(B, Hq, H, D, D, cap, "bf16")
@@ -178,7 +178,7 @@ def run_quest(se, torch, args):
     vn = torch.from_numpy(vn).to("cuda", torch.bfloat16)
     layers = [QuestLayer(se, cfg, c, K0, V0, 977 * i, torch) for i in range(nL)]
     del K0, V0
-    ws_q = se.workspace(se.SE_OP_QUEST, c, P, k)
+    ws_q = se.workspace(se.SE_OP_QUEST_APPEND, c, P, 0)
     ws_a = se.workspace(se.SE_OP_ATTN, c, k * P, args.splits)
     lse = torch.empty((B, Hq), device="cuda")
     torch.cuda.synchronize()
@@ -190,9 +190,11 @@ def run_quest(se, torch, args):
     del calib, calib_copy
     torch.cuda.synchronize()
 
+    def append_select(L):
+        se.se_quest_append_select(c, q, L.k, L.v, kn, vn, L.seq, L.kmin, L.kmax, P, k, L.view, L.vlen, None, ws_q)
+
     def step(L):
-        se.se_kv_append_meta(c, L.k, L.v, kn, vn, None, L.seq, L.kmin, L.kmax, P)
-        se.se_quest_select(c, q, L.kmin, L.kmax, L.seq, P, k, L.view, L.vlen, None, ws_q)
+        append_select(L)
         se.se_sparse_decode_attn(c, q, L.k, L.v, L.seq, L.view, L.vlen, k, P, cfg.softmax_scale, L.out, lse,
                                  num_splits=args.splits, ws=ws_a)
 
@@ -210,13 +212,9 @@ def run_quest(se, torch, args):
     n_steps = reps * nL
     ms_step = t_step.ms_per_replay(reps) / nL
     us_attn = t_attn.ms_per_replay(args.attn_reps) * 1e3 / nL
-    # the step's stages, each replayed alone over the same layers
-    t_sel = Timer(torch, lambda: [se.se_quest_select(c, q, L.kmin, L.kmax, L.seq, P, k, L.view, L.vlen, None, ws_q)
-                                  for L in layers], use_graph)
+    # the step's first stage replayed alone over the same layers (it appends a row per replay)
+    t_sel = Timer(torch, lambda: [append_select(L) for L in layers], use_graph)
     us_sel = t_sel.ms_per_replay(args.attn_reps) * 1e3 / nL
-    t_app = Timer(torch, lambda: [se.se_kv_append_meta(c, L.k, L.v, kn, vn, None, L.seq, L.kmin, L.kmax, P)
-                                  for L in layers], use_graph)
-    us_app = t_app.ms_per_replay(args.attn_reps) * 1e3 / nL
 
     # algorithmic bytes of one attention call: K and V rows of the selected tokens,
     # plus q, the views and the fp32 outputs
@@ -235,7 +233,7 @@ def run_quest(se, torch, args):
     free(torch)
     return cfg, {
         "tokens_per_s": B / (ms_step * 1e-3), "ms_per_step": ms_step, "steps": n_steps,
-        "stages_us": {"append_meta": round(us_app, 3), "quest_select": round(us_sel, 3), "attention": round(us_attn, 3)},
+        "stages_us": {"append_select": round(us_sel, 3), "attention": round(us_attn, 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "attn_mfma_kernel (se_sparse_decode_attn: split-K, splits merged in-kernel)", "us_per_launch": round(us_attn, 3),

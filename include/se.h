@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define SE_ABI_VERSION 2
+#define SE_ABI_VERSION 3
 
 typedef enum {
   SE_OK = 0,
@@ -88,7 +88,8 @@ typedef enum {
   SE_OP_QUEST = 1,      /* a0 = page_size, a1 = top_pages */
   SE_OP_ATTN = 2,       /* a0 = view_cap * granularity (slots per unit), a1 = num_splits (0 = auto) */
   SE_OP_SNAPKV = 3,     /* a0 = prompt_len, a1 = window */
-  SE_OP_OMNIKV = 4      /* a0 = logit_cap, a1 = top_k */
+  SE_OP_OMNIKV = 4,     /* a0 = logit_cap, a1 = top_k */
+  SE_OP_QUEST_APPEND = 5  /* a0 = page_size (a1 unused) */
 } se_op;
 
 /* Append one decode token's K/V row to every unit (helper of the hooks: the
@@ -140,6 +141,26 @@ se_status se_quest_select(const se_cache* c, const void* q, const void* kmin, co
                           const int32_t* seq_len, int32_t page_size, int32_t top_pages,
                           int32_t* view_idx, int32_t* view_len, float* page_score,
                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* One Quest decode step's cache update and page selection in one launch where
+ * the shape allows (bf16, d_k 64 / 128 with G <= 16 or 32, latent 576 with
+ * G <= 32, at most 8192 pages): the same results as
+ *   se_kv_append_meta(c, k, v, k_new, v_new, NULL, seq_len, kmin, kmax, page_size)
+ * followed by
+ *   se_quest_select(c, q, kmin, kmax, seq_len, page_size, top_pages, view_idx,
+ *                   view_len, page_score, ...)
+ * (bit-identical K / V rows, metadata, seq_len, views and scores) as long as
+ * kmin / kmax hold the min / max of each page's valid rows, as every call of
+ * this library leaves them (the appended page's values are updated with the new
+ * row rather than rebuilt from the cache); other shapes run those two calls'
+ * kernels.  Arguments as for those calls.
+ * ws: se_workspace_bytes(SE_OP_QUEST_APPEND, c, page_size, 0) bytes, 16-byte
+ * aligned, zero-filled once before first use (se_workspace_init); the call
+ * leaves its counters at zero. */
+se_status se_quest_append_select(const se_cache* c, const void* q, void* k, void* v, const void* k_new,
+                                 const void* v_new, int32_t* seq_len, void* kmin, void* kmax, int32_t page_size,
+                                 int32_t top_pages, int32_t* view_idx, int32_t* view_len, float* page_score,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Split-K flash decode over an AttentionView (tokendh.com explainer, section
  * "把边界划在'生命周期'上"; ai-feeds digest, section 方法 / 关键模块).

@@ -16,11 +16,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libse.so")
 
 SE_F32, SE_BF16 = 0, 1
-SE_OP_QUEST, SE_OP_ATTN, SE_OP_SNAPKV, SE_OP_OMNIKV = 1, 2, 3, 4
+SE_OP_QUEST, SE_OP_ATTN, SE_OP_SNAPKV, SE_OP_OMNIKV, SE_OP_QUEST_APPEND = 1, 2, 3, 4, 5
 STATUS = {0: "SE_OK", -1: "SE_ERR_NULL", -2: "SE_ERR_SHAPE", -3: "SE_ERR_DTYPE", -4: "SE_ERR_ALIGN",
           -5: "SE_ERR_BUDGET", -6: "SE_ERR_WORKSPACE", -7: "SE_ERR_UNSUPPORTED", -8: "SE_ERR_HIP"}
 
-EXPORTS = ("se_kv_append", "se_kv_append_meta", "se_page_meta_update", "se_quest_select", "se_sparse_decode_attn",
+EXPORTS = ("se_kv_append", "se_kv_append_meta", "se_page_meta_update", "se_quest_select", "se_quest_append_select",
+           "se_sparse_decode_attn",
            "se_snapkv_score_compact", "se_h2o_accumulate_evict", "se_omnikv_topk",
            "se_workspace_bytes", "se_workspace_init", "se_status_string", "se_abi_version")
 
@@ -45,6 +46,7 @@ _SIGS = {
     "se_page_meta_update": [_C, _P, _P, _P, _P, _I32, _I32, _P],
     "se_kv_append_meta": [_C, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P],
     "se_quest_select": [_C, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _SZ, _P],
+    "se_quest_append_select": [_C, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _SZ, _P],
     "se_sparse_decode_attn": [_C, _P, _P, _P, _P, _P, _P, _I32, _I32, _F32, _P, _P, _P, _I32, _I32, _P, _SZ, _P],
     "se_snapkv_score_compact": [_C, _P, _P, _P, _I32, _I32, _I32, _I32, _F32, _C, _P, _P, _P, _P, _P, _P, _SZ,
                                 _P],
@@ -158,6 +160,14 @@ def se_quest_select(c, q, kmin, kmax, seq_len, page_size, top_pages, view_idx, v
     _check("se_quest_select", load().se_quest_select(
         ctypes.byref(c), _ptr(q), _ptr(kmin), _ptr(kmax), _ptr(seq_len), page_size, top_pages, _ptr(view_idx),
         _ptr(view_len), _ptr(page_score), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def se_quest_append_select(c, q, k, v, k_new, v_new, seq_len, kmin, kmax, page_size, top_pages, view_idx, view_len,
+                           page_score=None, ws=None, stream=None):
+    _check("se_quest_append_select", load().se_quest_append_select(
+        ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(k_new), _ptr(v_new), _ptr(seq_len), _ptr(kmin), _ptr(kmax),
+        page_size, top_pages, _ptr(view_idx), _ptr(view_len), _ptr(page_score), _ptr(ws), _nbytes(ws),
+        _stream(stream)))
 
 
 def se_sparse_decode_attn(c, q, k, v, seq_len, view_idx, view_len, view_cap, granularity, scale, out, lse=None,

@@ -72,6 +72,7 @@ size_t se_workspace_bytes(int32_t op, const se_cache* c, int32_t a0, int32_t a1)
     case SE_OP_ATTN: return attn_ws_bytes(*c, a0 > 0 ? a0 : c->capacity, a1);
     case SE_OP_SNAPKV: return (a0 > a1 && a1 > 0) ? snapkv_ws_bytes(*c, a0, a1) : 0;
     case SE_OP_OMNIKV: return a0 > 0 ? omnikv_ws_bytes(*c, a0, a1) : 0;
+    case SE_OP_QUEST_APPEND: return a0 > 0 ? quest_append_ws_bytes(*c, a0) : 0;
     default: return 0;
   }
 }
@@ -147,6 +148,28 @@ se_status se_quest_select(const se_cache* c, const void* q, const void* kmin, co
   clear_stale_error();
   return launch_quest(*c, q, kmin, kmax, seq_len, page_size, top_pages, view_idx, view_len, page_score, ws,
                       stream);
+}
+
+se_status se_quest_append_select(const se_cache* c, const void* q, void* k, void* v, const void* k_new,
+                                 const void* v_new, int32_t* seq_len, void* kmin, void* kmax, int32_t page_size,
+                                 int32_t top_pages, int32_t* view_idx, int32_t* view_len, float* page_score,
+                                 void* ws, size_t ws_bytes, hipStream_t stream) {
+  se_status st = check_cache(c);
+  if (st != SE_OK) return st;
+  if (!q || !k || !k_new || !seq_len || !kmin || !kmax || !view_idx || !view_len || !ws ||
+      (!c->latent && (!v || !v_new)))
+    return SE_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(k_new) || !aligned16(kmin) || !aligned16(kmax) || !aligned16(ws) ||
+      (!c->latent && (!aligned16(v) || !aligned16(v_new))))
+    return SE_ERR_ALIGN;
+  if (page_size <= 0 || page_size > c->capacity) return SE_ERR_SHAPE;
+  if (top_pages < 1) return SE_ERR_BUDGET;
+  if (ws_bytes < quest_append_ws_bytes(*c, page_size)) return SE_ERR_WORKSPACE;
+  SE_TRACE_CALL("quest_append_select B=%d Hq=%d Hkv=%d d_k=%d P=%d k=%d", c->batch, c->n_q_heads, c->n_kv_heads,
+                c->d_k, page_size, top_pages);
+  clear_stale_error();
+  return launch_quest_append(*c, q, k, v, k_new, v_new, seq_len, kmin, kmax, page_size, top_pages, view_idx,
+                             view_len, page_score, ws, stream);
 }
 
 se_status se_sparse_decode_attn(const se_cache* c, const void* q, const void* k, const void* v,

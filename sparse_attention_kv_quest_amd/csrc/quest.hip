@@ -63,41 +63,96 @@ __global__ __launch_bounds__(256) void quest_score_vector_kernel(
 }
 
 // ------------------------------------------------------------------ MFMA scoring (bf16)
-// grid: (page groups, units); 4 waves, each scoring BPW blocks of 16 pages.  Every
-// metadata load of a wave is issued up front, before q is staged in LDS.
-// A operand of k-step s: lane (g, c) reads dims 32s + 8g .. 32s + 8g + 7 of page c.s max (then min) row;
+// grid: (page groups, units); 4 waves, each scoring one block of 16 pages, with
+// every metadata load issued before q is staged in LDS.
+// A operand of k-step s: lane (g, c) reads dims 32s + 8g .. 32s + 8g + 7 of page c's max (then min) row;
 // B operand: q+ (then q-) of head c (+16 per head block), the same dims, staged in
 // LDS in lane order.  Result lane (g, c): pages 4g..4g+3, head c.
-template <int D, int HB, int BPW>
+//
+// APP (the fused decode call): before scoring, the new token's K / V rows are
+// written at slot seq_len[b] and the new row is folded into the min / max of the
+// page receiving it (kmin / kmax hold each page's in-order min / max, as every
+// call here leaves them, so this equals the separate call's rebuild bit for
+// bit).  Pages are counted with the new length; seq_len itself is left for the
+// top-k launch to update, after every block of the batch row has read it.
+struct QuestAppendArgs {
+  uint16_t* k; uint16_t* v;                      // cache rows [units][cap][D]; v null for a latent cache
+  const uint16_t* k_new; const uint16_t* v_new;  // [units][D]
+  uint16_t* kmin_w; uint16_t* kmax_w;            // the metadata, written for the appended page
+};
+
+__device__ __forceinline__ uint32_t bf16x2_fmin(uint32_t acc, uint32_t x, bool mx) {
+  const float lo = mx ? fmaxf(bf16_lo(acc), bf16_lo(x)) : fminf(bf16_lo(acc), bf16_lo(x));
+  const float hi = mx ? fmaxf(bf16_hi(acc), bf16_hi(x)) : fminf(bf16_hi(acc), bf16_hi(x));
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+
+template <int D, int HB, bool APP>
 __global__ __launch_bounds__(256) void quest_score_mfma_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kmin, const uint16_t* __restrict__ kmax,
-    const int32_t* __restrict__ seq_len, float* __restrict__ score, int Hkv, int G, int P, int ncp, int cap) {
+    const uint16_t* __restrict__ q, const uint16_t* kmin, const uint16_t* kmax,
+    const int32_t* seq_len, float* score, int Hkv, int G, int P, int ncp, int cap, QuestAppendArgs ap) {
   constexpr int NKS = D / 32;
   __shared__ u32x4 qb[2 * NKS][HB][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
   const int unit = blockIdx.y, b = unit / Hkv, kvh = unit % Hkv;
-  const int npages = min((min(seq_len[b], cap) + P - 1) / P, ncp);
-  // issue the metadata loads of every block first: they do not depend on q
-  u32x4 amx[BPW][NKS], amn[BPW][NKS];
-#pragma unroll
-  for (int i = 0; i < BPW; ++i) {
-    // unconditional loads (pages past the last valid one read page 0; their scores are
-    // masked below) keep the wait counters exact
-    const int pg = ((blockIdx.x * 4 + w) * BPW + i) * 16 + c16;
+  const int len = min(seq_len[b], cap);
+  const bool app = APP && len < cap;                 // room for the new token
+  const int new_len = app ? len + 1 : len;
+  const int npages = min((new_len + P - 1) / P, ncp);
+  // unconditional loads (pages past the last valid one read page 0; their scores are
+  // masked below) keep the wait counters exact
+  u32x4 amx[NKS], amn[NKS];
+  const int pg = (blockIdx.x * 4 + w) * 16 + c16;
+  {
     const bool ok = pg < npages;
     const uint16_t* mxp = kmax + (size_t(unit) * ncp + (ok ? pg : 0)) * D + 8 * g;
     const uint16_t* mnp = kmin + (size_t(unit) * ncp + (ok ? pg : 0)) * D + 8 * g;
 #pragma unroll
     for (int c = 0; c < NKS; ++c) {
-      amx[i][c] = ld16(mxp + 32 * c);
-      amn[i][c] = ld16(mnp + 32 * c);
+      amx[c] = ld16(mxp + 32 * c);
+      amn[c] = ld16(mnp + 32 * c);
+    }
+  }
+  if (APP && app) {
+    const int plast = len / P;
+    const size_t urow = size_t(unit) * cap;
+    if (blockIdx.x == plast / 64) {   // this block writes the new K / V rows
+      for (int i = threadIdx.x; i < 2 * (D / 8); i += 256) {
+        const bool isv = i >= D / 8;
+        const int o = 8 * (isv ? i - D / 8 : i);
+        if (!isv) *reinterpret_cast<u32x4*>(ap.k + (urow + len) * D + o) = ld16(ap.k_new + size_t(unit) * D + o);
+        else if (ap.v != nullptr)
+          *reinterpret_cast<u32x4*>(ap.v + (urow + len) * D + o) = ld16(ap.v_new + size_t(unit) * D + o);
+      }
+    }
+    if (pg == plast) {
+      // this lane's dims of the appended page's min / max: the page's stored values
+      // with the new row folded in (the last step of the in-order rebuild the
+      // separate call runs, so bit-identical), or the new row alone on a fresh page
+      const bool fresh = len % P == 0;
+      const uint16_t* kn = ap.k_new + size_t(unit) * D + 8 * g;
+      const size_t mo = (size_t(unit) * ncp + plast) * D + 8 * g;
+#pragma unroll
+      for (int c = 0; c < NKS; ++c) {
+        const u32x4 x = ld16(kn + 32 * c);
+        u32x4 mn, mx;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          mn[j] = bf16x2_fmin(fresh ? 0x7f807f80u : amn[c][j], x[j], false);   // +inf pair on a fresh page
+          mx[j] = bf16x2_fmin(fresh ? 0xff80ff80u : amx[c][j], x[j], true);    // -inf pair
+        }
+        *reinterpret_cast<u32x4*>(ap.kmin_w + mo + 32 * c) = mn;
+        *reinterpret_cast<u32x4*>(ap.kmax_w + mo + 32 * c) = mx;
+        amn[c] = mn;
+        amx[c] = mx;
+      }
     }
   }
   const uint16_t* qg = q + (size_t(b) * Hkv * G + size_t(kvh) * G) * D;
   for (int idx = threadIdx.x; idx < 2 * NKS * HB * 64; idx += 256) {
-    const int ln = idx & 63, hb = (idx >> 6) % HB, s = idx / (64 * HB);
-    const bool neg = s >= NKS;
-    const int c = neg ? s - NKS : s;
+    const int ln = idx & 63, hb = (idx >> 6) % HB, sx = idx / (64 * HB);
+    const bool neg = sx >= NKS;
+    const int c = neg ? sx - NKS : sx;
     const int head = 16 * hb + (ln & 15), gg = ln >> 4;
     u32x4 x = {0, 0, 0, 0};
     if (head < G) {
@@ -109,13 +164,11 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(
         x[j] &= neg ? sgn : ~sgn;
       }
     }
-    qb[s][hb][ln] = x;
+    qb[sx][hb][ln] = x;
   }
   __syncthreads();
-#pragma unroll
-  for (int i = 0; i < BPW; ++i) {
-    const int p0 = ((blockIdx.x * 4 + w) * BPW + i) * 16;
-    if (p0 >= ncp) break;
+  const int p0 = (blockIdx.x * 4 + w) * 16;
+  if (p0 < ncp) {
     float best[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     if (p0 < npages) {
       f32x4 acc[HB];
@@ -124,11 +177,11 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(
 #pragma unroll
       for (int c = 0; c < NKS; ++c)
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma_bf16_16x16x32(amx[i][c], qb[c][hb][lane], acc[hb]);
+        for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma_bf16_16x16x32(amx[c], qb[c][hb][lane], acc[hb]);
 #pragma unroll
       for (int c = 0; c < NKS; ++c)
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma_bf16_16x16x32(amn[i][c], qb[NKS + c][hb][lane], acc[hb]);
+        for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma_bf16_16x16x32(amn[c], qb[NKS + c][hb][lane], acc[hb]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float v = -INFINITY;
@@ -153,17 +206,28 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(
 // One block per unit: page scores -> ascending view.  Up to BLOCK * E pages
 // the scores stay in registers (block_topk_reg); longer caches use the LDS /
 // global-memory variant.
-template <int BLOCK, int E>
+// APP (the fused decode call): pages are counted with the length after the
+// append, and the last block of a batch row (ticket on counters[b]) stores that
+// length once every block of the row has read the old one.
+template <int BLOCK, int E, bool APP = false>
 __global__ __launch_bounds__(BLOCK) void quest_topk_reg_kernel(
-    const float* __restrict__ score, const int32_t* __restrict__ seq_len, int32_t* __restrict__ view_idx,
-    int32_t* __restrict__ view_len, int Hkv, int P, int n_cap_pages, int cap, int top_pages) {
+    const float* __restrict__ score, int32_t* seq_len, int32_t* __restrict__ view_idx,
+    int32_t* __restrict__ view_len, int Hkv, int P, int n_cap_pages, int cap, int top_pages, int* counters) {
   __shared__ TopkRegShared sh;
   const int unit = blockIdx.x, b = unit / Hkv;
-  const int n = min((min(seq_len[b], cap) + P - 1) / P, n_cap_pages);
+  const int len = min(seq_len[b], cap);
+  const int new_len = (APP && len < cap) ? len + 1 : len;
+  const int n = min((new_len + P - 1) / P, n_cap_pages);
   const float* su = score + size_t(unit) * n_cap_pages;
   const int kk = block_topk_reg<BLOCK, E>([&](int i) { return su[i]; }, n, top_pages,
                                           view_idx + size_t(unit) * top_pages, sh);
   if (threadIdx.x == 0) view_len[unit] = kk;
+  if constexpr (APP) {
+    if (block_ticket_last(counters + b, Hkv) && threadIdx.x == 0) {
+      if (new_len != len) seq_len[b] = new_len;
+      ticket_reset(counters + b);
+    }
+  }
 }
 
 template <int BLOCK>
@@ -196,12 +260,13 @@ static void launch_score_mfma(const se_cache& c, const void* q, const void* kmin
                               const int32_t* seq_len, float* score, int P, int ncp, hipStream_t s) {
   const int units = c.batch * c.n_kv_heads, G = c.n_q_heads / c.n_kv_heads;
   // one group of 16 pages per wave: many small blocks keep the most metadata loads in flight
-#define SE_SCORE(BB) hipLaunchKernelGGL((quest_score_mfma_kernel<D, HB, BB>), dim3(ceil_div(ncp, 64 * (BB)), units),  \
-                                        dim3(256), 0, s, (const uint16_t*)q, (const uint16_t*)kmin,                 \
-                                        (const uint16_t*)kmax, seq_len, score, c.n_kv_heads, G, P, ncp, c.capacity)
-  SE_SCORE(1);
-#undef SE_SCORE
+  hipLaunchKernelGGL((quest_score_mfma_kernel<D, HB, false>), dim3(ceil_div(ncp, 64), units), dim3(256), 0, s,
+                     (const uint16_t*)q, (const uint16_t*)kmin, (const uint16_t*)kmax, seq_len, score, c.n_kv_heads,
+                     G, P, ncp, c.capacity, QuestAppendArgs{});
 }
+
+// Largest page count of the fused call's register top-k (512 threads x 16 keys).
+constexpr int QUEST_FUSED_MAX_PAGES = 512 * 16;
 
 se_status launch_quest(const se_cache& c, const void* q, const void* kmin, const void* kmax,
                        const int32_t* seq_len, int page_size, int top_pages, int32_t* view_idx,
@@ -235,13 +300,63 @@ se_status launch_quest(const se_cache& c, const void* q, const void* kmin, const
                          page_size, ncp);
   }
   if (hipGetLastError() != hipSuccess) return SE_ERR_HIP;
-#define SE_TOPK(KERN, NT) hipLaunchKernelGGL(KERN, dim3(units), dim3(NT), 0, s, score, seq_len, view_idx, view_len, \
-                                          c.n_kv_heads, page_size, ncp, c.capacity, top_pages)
+#define SE_TOPK(KERN, NT) hipLaunchKernelGGL(KERN, dim3(units), dim3(NT), 0, s, score, (int32_t*)seq_len, view_idx, \
+                                          view_len, c.n_kv_heads, page_size, ncp, c.capacity, top_pages, nullptr)
   if (ncp <= 512 * 4) SE_TOPK((quest_topk_reg_kernel<512, 4>), 512);
   else if (ncp <= 512 * 8) SE_TOPK((quest_topk_reg_kernel<512, 8>), 512);
   else if (ncp <= 512 * 16) SE_TOPK((quest_topk_reg_kernel<512, 16>), 512);
-  else SE_TOPK(quest_topk_block_kernel<256>, 256);
+  else hipLaunchKernelGGL(quest_topk_block_kernel<256>, dim3(units), dim3(256), 0, s, score, seq_len, view_idx,
+                          view_len, c.n_kv_heads, page_size, ncp, c.capacity, top_pages);
 #undef SE_TOPK
+  return launch_status();
+}
+
+size_t quest_append_ws_bytes(const se_cache& c, int page_size) {
+  const size_t ctr = size_t(c.batch) * sizeof(int);
+  return (ctr + 255) / 256 * 256 + quest_ws_bytes(c, page_size, 0);
+}
+
+// Two launches: append + page scores, then top-k + the new seq_len.
+se_status launch_quest_append(const se_cache& c, const void* q, void* k, void* v, const void* k_new,
+                              const void* v_new, int32_t* seq_len, void* kmin, void* kmax, int page_size,
+                              int top_pages, int32_t* view_idx, int32_t* view_len, float* page_score, void* ws,
+                              hipStream_t s) {
+  const int units = c.batch * c.n_kv_heads, G = c.n_q_heads / c.n_kv_heads;
+  const int ncp = ceil_div(c.capacity, page_size);
+  const size_t ctr_bytes = (size_t(c.batch) * sizeof(int) + 255) / 256 * 256;
+  float* score = page_score ? page_score : (float*)((char*)ws + ctr_bytes);
+  int* counters = (int*)ws;
+  QuestAppendArgs ap{};
+  ap.k = (uint16_t*)k; ap.v = c.latent ? nullptr : (uint16_t*)v;
+  ap.k_new = (const uint16_t*)k_new; ap.v_new = c.latent ? nullptr : (const uint16_t*)v_new;
+  ap.kmin_w = (uint16_t*)kmin; ap.kmax_w = (uint16_t*)kmax;
+  bool fused = c.dtype == SE_BF16 && ncp <= QUEST_FUSED_MAX_PAGES;
+  if (fused) {
+    const dim3 grid(ceil_div(ncp, 64), units);
+#define SE_AP(DD, HH) hipLaunchKernelGGL((quest_score_mfma_kernel<DD, HH, true>), grid, dim3(256), 0, s,           \
+                                         (const uint16_t*)q, (const uint16_t*)kmin, (const uint16_t*)kmax, seq_len, \
+                                         score, c.n_kv_heads, G, page_size, ncp, c.capacity, ap)
+    if (c.d_k == 128 && G <= 16) SE_AP(128, 1);
+    else if (c.d_k == 128 && G <= 32) SE_AP(128, 2);
+    else if (c.d_k == 64 && G <= 16) SE_AP(64, 1);
+    else if (c.d_k == 576 && G <= 32) SE_AP(576, 2);
+    else fused = false;
+#undef SE_AP
+  }
+  if (!fused) {   // other shapes: the separate append and selection launches (same results)
+    se_status st = launch_kv_append_meta(c, k, v, k_new, v_new, nullptr, seq_len, kmin, kmax, page_size, s);
+    if (st != SE_OK) return st;
+    return launch_quest(c, q, kmin, kmax, seq_len, page_size, top_pages, view_idx, view_len, page_score,
+                        (char*)ws + ctr_bytes, s);
+  }
+  if (hipGetLastError() != hipSuccess) return SE_ERR_HIP;
+#define SE_TK(EE) hipLaunchKernelGGL((quest_topk_reg_kernel<512, EE, true>), dim3(units), dim3(512), 0, s, score, \
+                                     seq_len, view_idx, view_len, c.n_kv_heads, page_size, ncp, c.capacity,      \
+                                     top_pages, counters)
+  if (ncp <= 512 * 4) SE_TK(4);
+  else if (ncp <= 512 * 8) SE_TK(8);
+  else SE_TK(16);
+#undef SE_TK
   return launch_status();
 }
 

@@ -411,6 +411,11 @@ se_status launch_kv_append_meta(const se_cache& c, void* k, void* v, const void*
                                 const int32_t* slot, int32_t* seq_len, void* kmin, void* kmax, int page_size,
                                 hipStream_t s);
 size_t quest_ws_bytes(const se_cache& c, int page_size, int top_pages);
+size_t quest_append_ws_bytes(const se_cache& c, int page_size);
+se_status launch_quest_append(const se_cache& c, const void* q, void* k, void* v, const void* k_new,
+                              const void* v_new, int32_t* seq_len, void* kmin, void* kmax, int page_size,
+                              int top_pages, int32_t* view_idx, int32_t* view_len, float* page_score, void* ws,
+                              hipStream_t s);
 se_status launch_quest(const se_cache& c, const void* q, const void* kmin, const void* kmax,
                        const int32_t* seq_len, int page_size, int top_pages, int32_t* view_idx,
                        int32_t* view_len, float* page_score, void* ws, hipStream_t s);

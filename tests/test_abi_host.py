@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert se.se_abi_version() == 2
+    assert se.se_abi_version() == 3
     assert se.se_status_string(0) == "ok"
     assert se.se_status_string(-6) == "workspace too small"
     assert se.se_status_string(123) == "unknown status"
@@ -42,6 +42,8 @@ def test_version_and_strings(lib):
 def test_workspace_sizes(lib):
     c = se.cache(16, 32, 4, 128, 128, 32832, "bf16")
     assert se.se_workspace_bytes(se.SE_OP_QUEST, c, 16, 128) == 16 * 4 * 2052 * 4
+    # fused append + select: 16 batch-row tickets (rounded up to 256 bytes), then the scores
+    assert se.se_workspace_bytes(se.SE_OP_QUEST_APPEND, c, 16, 0) == 256 + 16 * 4 * 2052 * 4
     n = se.se_workspace_bytes(se.SE_OP_ATTN, c, 2048, 8)
     counters = 512          # 64 units x 2 head groups x int32, rounded up to 256 bytes
     assert n == counters + 16 * 4 * 8 * 8 * (128 + 2) * 4
@@ -92,6 +94,14 @@ def test_other_entry_points_reject_bad_arguments(lib):
     assert lib.se_page_meta_update(cr, FAKE, FAKE, FAKE, FAKE, 16, -2, None) == -2
     assert lib.se_quest_select(cr, FAKE, FAKE, FAKE, FAKE, 16, 0, FAKE, FAKE, None, FAKE, 1 << 20, None) == -5
     assert lib.se_quest_select(cr, FAKE, FAKE, FAKE, FAKE, 16, 8, FAKE, FAKE, None, FAKE, 4, None) == -6
+    qa = lambda k_new=FAKE, P=16, top=8, ws=FAKE, ws_bytes=1 << 20: lib.se_quest_append_select(
+        cr, FAKE, FAKE, FAKE, k_new, FAKE, FAKE, FAKE, FAKE, P, top, FAKE, FAKE, None, ws, ws_bytes, None)
+    assert qa(k_new=None) == -1
+    assert qa(k_new=MIS) == -4
+    assert qa(P=0) == -2
+    assert qa(top=0) == -5
+    assert qa(ws=None) == -1                   # the fused call always needs its ticket counters
+    assert qa(ws_bytes=64) == -6
     oc = se.cache(2, 8, 2, 128, 128, 64, "bf16")
     ocr = ctypes.byref(oc)
     snap = lambda L, W, pool, budget, out=ocr: lib.se_snapkv_score_compact(
