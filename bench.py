@@ -18,7 +18,8 @@ The other workloads are timed the same way and reported under "workloads":
   omnikv_16k   48-layer OmniKV sweeps (dense layers 0-1, filter layers 2/8/16
                with top-2048 selection, 43 layers over the reused views);
   mla_128k     MLA latent Quest steps at 131072 tokens (576-wide latent rows,
-               pages of 64, top-64 pages, 32 heads).
+               pages of 64, top-64 pages, 32 heads): se_quest_append_select,
+               then the latent attention on MFMA.
 
 Prints one JSON line: tokens/s per layer-step of the headline, achieved HBM
 GB/s of its attention call against the 8 TB/s peak, per-workload figures, and
@@ -476,12 +477,12 @@ def run_mla(se, torch, args):
     q = dev_grid(torch, (B, Hq, D), 3900, torch.bfloat16)
     kn = dev_grid(torch, (B, 1, D), 3901, torch.bfloat16)
     lse = torch.empty((B, Hq), device="cuda")
-    ws_q = se.workspace(se.SE_OP_QUEST, c, P, k)
+    ws_q = se.workspace(se.SE_OP_QUEST_APPEND, c, P, 0)
     ws_a = se.workspace(se.SE_OP_ATTN, c, k * P, 0)
 
     def step(Ly):
-        se.se_kv_append_meta(c, Ly["c"], None, kn, None, None, Ly["seq"], Ly["kmin"], Ly["kmax"], P)
-        se.se_quest_select(c, q, Ly["kmin"], Ly["kmax"], Ly["seq"], P, k, Ly["view"], Ly["vlen"], None, ws_q)
+        se.se_quest_append_select(c, q, Ly["c"], None, kn, None, Ly["seq"], Ly["kmin"], Ly["kmax"], P, k, Ly["view"],
+                                  Ly["vlen"], None, ws_q)
         se.se_sparse_decode_attn(c, q, Ly["c"], None, Ly["seq"], Ly["view"], Ly["vlen"], k, P, cfg.softmax_scale,
                                  Ly["out"], lse, ws=ws_a)
 
