@@ -17,6 +17,9 @@ The other workloads are timed the same way and reported under "workloads":
                logits, accumulate + evict) over 1024 heavy + 256 recent slots;
   omnikv_16k   48-layer OmniKV sweeps (dense layers 0-1, filter layers 2/8/16
                with top-2048 selection, 43 layers over the reused views);
+  streaming_32k StreamingLLM decode steps on the Quest 32K shape: append, the
+               sink + recent token view (4 + 2044 positions, the same 2048-token
+               budget as the Quest view), attention over it;
   mla_128k     MLA latent Quest steps at 131072 tokens (576-wide latent rows,
                pages of 64, top-64 pages, 32 heads): se_quest_append_select,
                then the latent attention on MFMA.
@@ -42,7 +45,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-ALL_WORKLOADS = ("quest_32k", "snapkv_128k", "h2o_16k", "omnikv_16k", "mla_128k")
+ALL_WORKLOADS = ("quest_32k", "snapkv_128k", "h2o_16k", "omnikv_16k", "mla_128k", "streaming_32k")
 
 
 def parse():
@@ -514,6 +517,59 @@ def run_mla(se, torch, args):
             "attn_TFLOPs": round(tfl, 1), "attn_frac_of_mfma_peak": round(tfl / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
+# ---------------------------------------------------------------- StreamingLLM 32K
+
+def run_streaming(se, torch, args):
+    from workloads import get_config
+
+    cfg = get_config(1)
+    B, H, Hq, D = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.d_k
+    sink, recent = 4, cfg.top_pages * cfg.page_size - 4
+    nL = args.layers
+    steps = max(nL, args.steps // nL * nL)
+    cap = cfg.context + steps // nL + args.attn_reps + 8
+    log(f"streaming_32k: B={B} Hq={Hq} Hkv={H} D={D} ctx={cfg.context} sink={sink} recent={recent} layers={nL}")
+    c = se.cache(B, Hq, H, D, D, cap, "bf16")
+    vc = sink + recent
+    lay = []
+    for i in range(nL):
+        lay.append(dict(k=dev_grid(torch, (B, H, cap, D), 4000 + 2 * i, torch.bfloat16),
+                        v=dev_grid(torch, (B, H, cap, D), 4001 + 2 * i, torch.bfloat16),
+                        seq=torch.full((B,), cfg.context, dtype=torch.int32, device="cuda"),
+                        view=torch.empty((B, H, vc), dtype=torch.int32, device="cuda"),
+                        vlen=torch.empty((B, H), dtype=torch.int32, device="cuda"),
+                        out=torch.empty((B, Hq, D), device="cuda")))
+    q = dev_grid(torch, (B, Hq, D), 4100, torch.bfloat16)
+    kn = dev_grid(torch, (B, H, D), 4101, torch.bfloat16)
+    vn = dev_grid(torch, (B, H, D), 4102, torch.bfloat16)
+    lse = torch.empty((B, Hq), device="cuda")
+    ws_a = se.workspace(se.SE_OP_ATTN, c, vc, 0)
+
+    def attn(Ly):
+        se.se_sparse_decode_attn(c, q, Ly["k"], Ly["v"], Ly["seq"], Ly["view"], Ly["vlen"], vc, 1, cfg.softmax_scale,
+                                 Ly["out"], lse, ws=ws_a)
+
+    def step(Ly):
+        se.se_kv_append(c, Ly["k"], Ly["v"], kn, vn, None, Ly["seq"])
+        se.se_streaming_view(c, Ly["seq"], sink, recent, Ly["view"], Ly["vlen"])
+        attn(Ly)
+
+    for Ly in lay:
+        step(Ly)
+    t_s = Timer(torch, lambda: [step(Ly) for Ly in lay], not args.no_graph)
+    t_a = Timer(torch, lambda: [attn(Ly) for Ly in lay], not args.no_graph)
+    ms_step = t_s.ms_per_replay(steps // nL) / nL
+    us_attn = t_a.ms_per_replay(args.attn_reps) * 1e3 / nL
+    toks = int(lay[0]["vlen"].sum().item())
+    attn_bytes = toks * D * 2 * 2 + B * Hq * D * 2 + B * H * vc * 4 + B * Hq * (D + 1) * 4
+    gbps = attn_bytes / (us_attn * 1e-6) / 1e9
+    del lay, t_s, t_a
+    free(torch)
+    return {"workload": "streaming_32k", "batch": B, "context": cfg.context, "sink": sink, "recent": recent,
+            "tokens_per_s": round(B / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 5), "steps": steps,
+            "attn_us": round(us_attn, 3), "attn_GBps": round(gbps, 1), "attn_frac_of_hbm_peak": round(gbps / HBM_PEAK_GBS, 4)}
+
+
 # ---------------------------------------------------------------- main
 
 def main():
@@ -550,7 +606,8 @@ def main():
         log(f"quest_32k: {r['ms_per_step'] * 1e3:.2f} us/step; stages alone (us): {r['stages_us']}")
     else:
         result["config"] = {"workload": "none (headline skipped)"}
-    runners = {"snapkv_128k": run_snapkv, "h2o_16k": run_h2o, "omnikv_16k": run_omnikv, "mla_128k": run_mla}
+    runners = {"snapkv_128k": run_snapkv, "h2o_16k": run_h2o, "omnikv_16k": run_omnikv, "mla_128k": run_mla,
+               "streaming_32k": run_streaming}
     for w in wanted:
         if w in runners:
             extra[w] = runners[w](se, torch, args)

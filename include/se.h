@@ -162,6 +162,27 @@ se_status se_quest_append_select(const se_cache* c, const void* q, void* k, void
                                  int32_t top_pages, int32_t* view_idx, int32_t* view_len, float* page_score,
                                  void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* StreamingLLM view (Netics blog "SparseEngine 统一接入十五种稀疏注意力", section
+ * "哪些情况下加速幅度会缩小": named there beside PyramidKV and SnapKV).  Unit
+ * (b, h) attends over the first `sink` and the last `recent` positions below
+ * seq_len[b]: view_idx [B][Hkv][view_cap] int32 gets those positions in
+ * ascending order (-1 after them), view_len [B][Hkv] their count
+ * min(seq_len, sink + recent).  Hand it to se_sparse_decode_attn with
+ * granularity 1.  sink, recent >= 0, sink + recent >= 1 and
+ * view_cap >= sink + recent, else SE_ERR_BUDGET. */
+se_status se_streaming_view(const se_cache* c, const int32_t* seq_len, int32_t sink, int32_t recent,
+                            int32_t* view_idx, int32_t* view_len, int32_t view_cap, hipStream_t stream);
+
+/* PyramidKV layer budgets (same page and section; host computation, no GPU
+ * work).  budgets: HOST int32 [n_layers]; layer l (0 = first) gets
+ * min + (max - min) (n - 1 - l) / (n - 1) tokens with max = 2 avg - min, in
+ * whole tokens summing to exactly n_layers * avg_budget: every layer takes the
+ * floor, then the remaining tokens go one each to the layers with the largest
+ * fractional parts (the lower layer first on ties).  Each layer then selects as
+ * SnapKV does: se_snapkv_score_compact with its budget.  n_layers >= 1 (else
+ * SE_ERR_SHAPE), 0 <= min_budget <= avg_budget (else SE_ERR_BUDGET). */
+se_status se_pyramid_budgets(int32_t n_layers, int32_t avg_budget, int32_t min_budget, int32_t* budgets);
+
 /* Split-K flash decode over an AttentionView (tokendh.com explainer, section
  * "把边界划在'生命周期'上"; ai-feeds digest, section 方法 / 关键模块).
  *   view_idx: NULL = every slot below seq_len[b]; else int32 [B][Hkv][view_cap],

@@ -31,10 +31,13 @@ from .attention import view_tokens, decode_attention, unit_attention  # noqa: F4
 from .snapkv import snapkv_votes, snapkv_pool, snapkv_keep, snapkv_compact  # noqa: F401
 from .h2o import h2o_accumulate_evict, h2o_step  # noqa: F401
 from .omnikv import omnikv_scores, omnikv_select, omnikv_layer_views  # noqa: F401
+from .variants import streaming_kept, streaming_view, pyramid_budgets  # noqa: F401
 
 UNPINNED = (
     "Group aggregation of the Quest bound (max over the group's heads), "
     "whether the SnapKV window counts in its budget, the SnapKV softmax denominator, "
     "H2O's step order and candidate set, and OmniKV's per-KV-head selection are readings "
-    "of pages that state each method in one sentence; nothing on the pages confirms them."
+    "of pages that state each method in one sentence; nothing on the pages confirms them.  "
+    "StreamingLLM (first and last positions) and PyramidKV (arithmetic per-layer budgets "
+    "around SnapKV) are only named on the pages; their forms here are readings too."
 )

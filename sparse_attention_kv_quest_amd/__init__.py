@@ -21,7 +21,7 @@ STATUS = {0: "SE_OK", -1: "SE_ERR_NULL", -2: "SE_ERR_SHAPE", -3: "SE_ERR_DTYPE",
           -5: "SE_ERR_BUDGET", -6: "SE_ERR_WORKSPACE", -7: "SE_ERR_UNSUPPORTED", -8: "SE_ERR_HIP"}
 
 EXPORTS = ("se_kv_append", "se_kv_append_meta", "se_page_meta_update", "se_quest_select", "se_quest_append_select",
-           "se_sparse_decode_attn",
+           "se_sparse_decode_attn", "se_streaming_view", "se_pyramid_budgets",
            "se_snapkv_score_compact", "se_h2o_accumulate_evict", "se_omnikv_topk",
            "se_workspace_bytes", "se_workspace_init", "se_status_string", "se_abi_version")
 
@@ -48,6 +48,8 @@ _SIGS = {
     "se_quest_select": [_C, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _SZ, _P],
     "se_quest_append_select": [_C, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _SZ, _P],
     "se_sparse_decode_attn": [_C, _P, _P, _P, _P, _P, _P, _I32, _I32, _F32, _P, _P, _P, _I32, _I32, _P, _SZ, _P],
+    "se_streaming_view": [_C, _P, _I32, _I32, _P, _P, _I32, _P],
+    "se_pyramid_budgets": [_I32, _I32, _I32, _P],
     "se_snapkv_score_compact": [_C, _P, _P, _P, _I32, _I32, _I32, _I32, _F32, _C, _P, _P, _P, _P, _P, _P, _SZ,
                                 _P],
     "se_h2o_accumulate_evict": [_C, _P, _P, _I32, _P, _P, _P, _I32, _I32, _I32, _P, _P],
@@ -168,6 +170,18 @@ def se_quest_append_select(c, q, k, v, k_new, v_new, seq_len, kmin, kmax, page_s
         ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(k_new), _ptr(v_new), _ptr(seq_len), _ptr(kmin), _ptr(kmax),
         page_size, top_pages, _ptr(view_idx), _ptr(view_len), _ptr(page_score), _ptr(ws), _nbytes(ws),
         _stream(stream)))
+
+
+def se_streaming_view(c, seq_len, sink, recent, view_idx, view_len, stream=None):
+    _check("se_streaming_view", load().se_streaming_view(ctypes.byref(c), _ptr(seq_len), sink, recent, _ptr(view_idx),
+                                                         _ptr(view_len), view_idx.shape[-1], _stream(stream)))
+
+
+def se_pyramid_budgets(n_layers, avg_budget, min_budget):
+    """Per-layer budgets (list of ints, layer 0 first); host computation."""
+    out = (ctypes.c_int32 * max(1, n_layers))()
+    _check("se_pyramid_budgets", load().se_pyramid_budgets(n_layers, avg_budget, min_budget, out))
+    return list(out)[:n_layers]
 
 
 def se_sparse_decode_attn(c, q, k, v, seq_len, view_idx, view_len, view_cap, granularity, scale, out, lse=None,

@@ -172,6 +172,27 @@ se_status se_quest_append_select(const se_cache* c, const void* q, void* k, void
                              view_len, page_score, ws, stream);
 }
 
+se_status se_streaming_view(const se_cache* c, const int32_t* seq_len, int32_t sink, int32_t recent,
+                            int32_t* view_idx, int32_t* view_len, int32_t view_cap, hipStream_t stream) {
+  se_status st = check_cache(c);
+  if (st != SE_OK) return st;
+  if (!seq_len || !view_idx || !view_len) return SE_ERR_NULL;
+  if (sink < 0 || recent < 0 || int64_t(sink) + recent < 1 || view_cap < int64_t(sink) + recent)
+    return SE_ERR_BUDGET;
+  SE_TRACE_CALL("streaming_view B=%d Hkv=%d sink=%d recent=%d cap=%d", c->batch, c->n_kv_heads, sink, recent,
+                view_cap);
+  clear_stale_error();
+  return launch_streaming_view(*c, seq_len, sink, recent, view_idx, view_len, view_cap, stream);
+}
+
+se_status se_pyramid_budgets(int32_t n_layers, int32_t avg_budget, int32_t min_budget, int32_t* budgets) {
+  if (!budgets) return SE_ERR_NULL;
+  if (n_layers < 1) return SE_ERR_SHAPE;
+  if (min_budget < 0 || min_budget > avg_budget) return SE_ERR_BUDGET;
+  pyramid_budgets(n_layers, avg_budget, min_budget, budgets);
+  return SE_OK;
+}
+
 se_status se_sparse_decode_attn(const se_cache* c, const void* q, const void* k, const void* v,
                                 const int32_t* seq_len, const int32_t* view_idx,
                                 const int32_t* view_len, int32_t view_cap, int32_t granularity,

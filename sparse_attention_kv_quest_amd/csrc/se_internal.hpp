@@ -412,6 +412,9 @@ se_status launch_kv_append_meta(const se_cache& c, void* k, void* v, const void*
                                 hipStream_t s);
 size_t quest_ws_bytes(const se_cache& c, int page_size, int top_pages);
 size_t quest_append_ws_bytes(const se_cache& c, int page_size);
+se_status launch_streaming_view(const se_cache& c, const int32_t* seq_len, int sink, int recent,
+                                int32_t* view_idx, int32_t* view_len, int view_cap, hipStream_t s);
+void pyramid_budgets(int n, int avg, int bmin, int32_t* out);
 se_status launch_quest_append(const se_cache& c, const void* q, void* k, void* v, const void* k_new,
                               const void* v_new, int32_t* seq_len, void* kmin, void* kmax, int page_size,
                               int top_pages, int32_t* view_idx, int32_t* view_len, float* page_score, void* ws,
