@@ -32,6 +32,7 @@ from .snapkv import snapkv_votes, snapkv_pool, snapkv_keep, snapkv_compact  # no
 from .h2o import h2o_accumulate_evict, h2o_step  # noqa: F401
 from .omnikv import omnikv_scores, omnikv_select, omnikv_layer_views  # noqa: F401
 from .variants import streaming_kept, streaming_view, pyramid_budgets  # noqa: F401
+from .fp8 import e4m3_decode, e4m3_encode, quantize_rows, dequantize_rows  # noqa: F401
 
 UNPINNED = (
     "Group aggregation of the Quest bound (max over the group's heads), "
