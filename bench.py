@@ -20,6 +20,9 @@ The other workloads are timed the same way and reported under "workloads":
   streaming_32k StreamingLLM decode steps on the Quest 32K shape: append, the
                sink + recent token view (4 + 2044 positions, the same 2048-token
                budget as the Quest view), attention over it;
+  quest_32k_fp8 the Quest 32K step over FP8 KV rows (E4M3 codes, one power-of-two
+               scale per row): FP8 append + last-page metadata, page scores and
+               top-k, attention over the stored values;
   mla_128k     MLA latent Quest steps at 131072 tokens (576-wide latent rows,
                pages of 64, top-64 pages, 32 heads): se_quest_append_select,
                then the latent attention on MFMA.
@@ -45,7 +48,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-ALL_WORKLOADS = ("quest_32k", "snapkv_128k", "h2o_16k", "omnikv_16k", "mla_128k", "streaming_32k")
+ALL_WORKLOADS = ("quest_32k", "snapkv_128k", "h2o_16k", "omnikv_16k", "mla_128k", "streaming_32k", "quest_32k_fp8")
 
 
 def parse():
@@ -570,6 +573,74 @@ def run_streaming(se, torch, args):
             "attn_us": round(us_attn, 3), "attn_GBps": round(gbps, 1), "attn_frac_of_hbm_peak": round(gbps / HBM_PEAK_GBS, 4)}
 
 
+# ---------------------------------------------------------------- Quest 32K over FP8 rows
+
+def run_quest_fp8(se, torch, args):
+    from workloads import get_config
+
+    cfg = get_config(1)
+    B, H, Hq, D, P, k = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.d_k, cfg.page_size, cfg.top_pages
+    nL = args.layers
+    steps = max(nL, args.steps // nL * nL)
+    cap = cfg.context + steps // nL + args.attn_reps + 8
+    log(f"quest_32k_fp8: B={B} Hq={Hq} Hkv={H} D={D} ctx={cfg.context} P={P} top={k} layers={nL}")
+    c = se.cache(B, Hq, H, D, D, cap, "bf16")
+    ncp = (cap + P - 1) // P
+    lay = []
+    for i in range(nL):
+        Ly = dict(kq=torch.empty((B, H, cap, D), dtype=torch.uint8, device="cuda"),
+                  ks=torch.empty((B, H, cap), dtype=torch.uint8, device="cuda"),
+                  seq=torch.full((B,), cfg.context, dtype=torch.int32, device="cuda"),
+                  kmin=torch.empty((B, H, ncp, D), dtype=torch.bfloat16, device="cuda"),
+                  view=torch.empty((B, H, k), dtype=torch.int32, device="cuda"),
+                  vlen=torch.empty((B, H), dtype=torch.int32, device="cuda"),
+                  out=torch.empty((B, Hq, D), device="cuda"))
+        Ly["vq"], Ly["vs"], Ly["kmax"] = torch.empty_like(Ly["kq"]), torch.empty_like(Ly["ks"]), torch.empty_like(Ly["kmin"])
+        kb = dev_grid(torch, (B, H, cap, D), 5000 + 2 * i, torch.bfloat16)
+        vb = dev_grid(torch, (B, H, cap, D), 5001 + 2 * i, torch.bfloat16)
+        se.se_kv_quantize_fp8(c, kb, vb, Ly["seq"], Ly["kq"], Ly["vq"], Ly["ks"], Ly["vs"], Ly["kmin"], Ly["kmax"], P)
+        del kb, vb
+        lay.append(Ly)
+    free(torch)
+    q = dev_grid(torch, (B, Hq, D), 5100, torch.bfloat16)
+    kn = dev_grid(torch, (B, H, D), 5101, torch.bfloat16)
+    vn = dev_grid(torch, (B, H, D), 5102, torch.bfloat16)
+    lse = torch.empty((B, Hq), device="cuda")
+    ws_q = se.workspace(se.SE_OP_QUEST, c, P, k)
+    ws_a = se.workspace(se.SE_OP_ATTN, c, k * P, 0)
+
+    def attn(Ly):
+        se.se_sparse_decode_attn_fp8(c, q, Ly["kq"], Ly["vq"], Ly["ks"], Ly["vs"], Ly["seq"], Ly["view"], Ly["vlen"], k,
+                                     P, cfg.softmax_scale, Ly["out"], lse, ws=ws_a)
+
+    def step(Ly):
+        se.se_kv_append_fp8(c, Ly["kq"], Ly["vq"], Ly["ks"], Ly["vs"], kn, vn, Ly["seq"], Ly["kmin"], Ly["kmax"], P)
+        se.se_quest_select(c, q, Ly["kmin"], Ly["kmax"], Ly["seq"], P, k, Ly["view"], Ly["vlen"], None, ws_q)
+        attn(Ly)
+
+    for Ly in lay:
+        step(Ly)
+    t_s = Timer(torch, lambda: [step(Ly) for Ly in lay], not args.no_graph)
+    t_a = Timer(torch, lambda: [attn(Ly) for Ly in lay], not args.no_graph)
+    ms_step = t_s.ms_per_replay(steps // nL) / nL
+    us_attn = t_a.ms_per_replay(args.attn_reps) * 1e3 / nL
+    seq_h, vlen_h, view_h = lay[0]["seq"].cpu().numpy(), lay[0]["vlen"].cpu().numpy(), lay[0]["view"].cpu().numpy()
+    toks = 0
+    for b in range(B):
+        for h in range(H):
+            pages = view_h[b, h, :vlen_h[b, h]]
+            toks += int(np.minimum(P, np.maximum(0, seq_h[b] - pages * P)).sum())
+    # codes and scale bytes of the selected K and V rows, q, views, outputs
+    attn_bytes = toks * (D + 1) * 2 + B * Hq * D * 2 + B * H * k * 4 + B * Hq * (D + 1) * 4
+    gbps = attn_bytes / (us_attn * 1e-6) / 1e9
+    del lay, t_s, t_a
+    free(torch)
+    return {"workload": "quest_32k_fp8", "batch": B, "context": cfg.context, "page_size": P, "top_pages": k,
+            "kv_format": "E4M3 + one E8M0 scale per row",
+            "tokens_per_s": round(B / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 5), "steps": steps,
+            "attn_us": round(us_attn, 3), "attn_GBps": round(gbps, 1), "attn_frac_of_hbm_peak": round(gbps / HBM_PEAK_GBS, 4)}
+
+
 # ---------------------------------------------------------------- main
 
 def main():
@@ -607,7 +678,7 @@ def main():
     else:
         result["config"] = {"workload": "none (headline skipped)"}
     runners = {"snapkv_128k": run_snapkv, "h2o_16k": run_h2o, "omnikv_16k": run_omnikv, "mla_128k": run_mla,
-               "streaming_32k": run_streaming}
+               "streaming_32k": run_streaming, "quest_32k_fp8": run_quest_fp8}
     for w in wanted:
         if w in runners:
             extra[w] = runners[w](se, torch, args)

@@ -162,6 +162,45 @@ se_status se_quest_append_select(const se_cache* c, const void* q, void* k, void
                                  int32_t top_pages, int32_t* view_idx, int32_t* view_len, float* page_score,
                                  void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* FP8 KV rows (tokendh.com explainer, section "历史太长,会撑爆什么": KV
+ * quantization keeps the history at lower precision with what is needed to
+ * restore it).  Format: a stored row (one token of one KV head) is d_k OCP E4M3
+ * codes (uint8 [B][Hkv][capacity][d_k]) and one scale byte s = e + 127 (E8M0,
+ * uint8 [B][Hkv][capacity]); its values are code * 2^e, e being the smallest
+ * exponent >= -126 with max |x| * 2^-e <= 448 over the row (0 for a zero row),
+ * every code the nearest E4M3 value of x * 2^-e, ties to the even code.  Stored
+ * values are exact in bf16: kmin / kmax (bf16) hold the min / max of the
+ * stored K values and feed se_quest_select unchanged.  FP8 calls take a bf16
+ * cache descriptor (q, metadata, source rows) without latent, d_k 64 or 128:
+ * SE_ERR_DTYPE / SE_ERR_UNSUPPORTED otherwise.
+ *
+ * se_kv_quantize_fp8: rows [0, seq_len[b]) of bf16 K / V -> codes and scale
+ * bytes; kmin / kmax (both NULL or both set) are rebuilt for every page below
+ * seq_len from the stored values (page_size used only then). */
+se_status se_kv_quantize_fp8(const se_cache* c, const void* k, const void* v, const int32_t* seq_len, void* k_q,
+                             void* v_q, uint8_t* k_scale, uint8_t* v_scale, void* kmin, void* kmax, int32_t page_size,
+                             hipStream_t stream);
+
+/* Quantizes the new rows k_new / v_new (bf16 [B][Hkv][d_k]) into slot
+ * seq_len[b] (nothing when seq_len[b] == capacity), updates kmin / kmax of the
+ * page receiving it with the new stored K values (both NULL or both set; they
+ * must hold that page's min / max, as every call here leaves them) and bumps
+ * seq_len. */
+se_status se_kv_append_fp8(const se_cache* c, void* k_q, void* v_q, uint8_t* k_scale, uint8_t* v_scale,
+                           const void* k_new, const void* v_new, int32_t* seq_len, void* kmin, void* kmax,
+                           int32_t page_size, hipStream_t stream);
+
+/* se_sparse_decode_attn over FP8 rows: the same view, outputs, splits and
+ * workspace (se_workspace_bytes(SE_OP_ATTN, ...)), attention over the stored
+ * values; the operands are converted to bf16 in registers (exact) with the
+ * row scale folded in.  G <= 16 (SE_ERR_UNSUPPORTED otherwise). */
+se_status se_sparse_decode_attn_fp8(const se_cache* c, const void* q, const void* k_q, const void* v_q,
+                                    const uint8_t* k_scale, const uint8_t* v_scale, const int32_t* seq_len,
+                                    const int32_t* view_idx, const int32_t* view_len, int32_t view_cap,
+                                    int32_t granularity, float scale, float* out, float* lse, float* logits,
+                                    int32_t logit_cap, int32_t num_splits, void* ws, size_t ws_bytes,
+                                    hipStream_t stream);
+
 /* StreamingLLM view (Netics blog "SparseEngine 统一接入十五种稀疏注意力", section
  * "哪些情况下加速幅度会缩小": named there beside PyramidKV and SnapKV).  Unit
  * (b, h) attends over the first `sink` and the last `recent` positions below

@@ -11,8 +11,9 @@ the plainest one that keeps attention exact over what is stored:
     mantissa is NaN; largest finite magnitude 448; subnormals m * 2^-9);
   * one scale per stored row (one token of one KV head): a power of two 2^e,
     kept as the biased byte e + 127 (the E8M0 scale encoding of the OCP
-    microscaling formats), with e the smallest exponent for which every
-    |x| * 2^-e of the row is at most 448 (e = 0 for an all-zero row);
+    microscaling formats), with e the smallest exponent >= -126 for which
+    every |x| * 2^-e of the row is at most 448 (e = 0 for an all-zero row; the
+    bound keeps every scale a normal float32);
   * a code is x * 2^-e rounded to the nearest E4M3 value, ties to the even
     code; the stored value is code * 2^e, exact in bf16 and fp32;
   * attention, page metadata and selection read the stored values (the
@@ -70,16 +71,16 @@ def e4m3_encode_array(y):
 
 
 def row_exponent(amax):
-    """Smallest e with amax * 2^-e <= 448 (0 when amax is 0)."""
+    """Smallest e >= -126 with amax * 2^-e <= 448 (0 when amax is 0)."""
     amax = float(amax)
     if amax == 0.0:
         return 0
     e = int(np.floor(np.log2(amax))) - 9
     while amax * 2.0 ** -e > E4M3_MAX:
         e += 1
-    while amax * 2.0 ** -(e - 1) <= E4M3_MAX:
+    while e > -126 and amax * 2.0 ** -(e - 1) <= E4M3_MAX:
         e -= 1
-    return e
+    return max(e, -126)
 
 
 def quantize_rows(X):

@@ -22,6 +22,7 @@ STATUS = {0: "SE_OK", -1: "SE_ERR_NULL", -2: "SE_ERR_SHAPE", -3: "SE_ERR_DTYPE",
 
 EXPORTS = ("se_kv_append", "se_kv_append_meta", "se_page_meta_update", "se_quest_select", "se_quest_append_select",
            "se_sparse_decode_attn", "se_streaming_view", "se_pyramid_budgets",
+           "se_kv_quantize_fp8", "se_kv_append_fp8", "se_sparse_decode_attn_fp8",
            "se_snapkv_score_compact", "se_h2o_accumulate_evict", "se_omnikv_topk",
            "se_workspace_bytes", "se_workspace_init", "se_status_string", "se_abi_version")
 
@@ -49,6 +50,10 @@ _SIGS = {
     "se_quest_append_select": [_C, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _SZ, _P],
     "se_sparse_decode_attn": [_C, _P, _P, _P, _P, _P, _P, _I32, _I32, _F32, _P, _P, _P, _I32, _I32, _P, _SZ, _P],
     "se_streaming_view": [_C, _P, _I32, _I32, _P, _P, _I32, _P],
+    "se_kv_quantize_fp8": [_C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P],
+    "se_kv_append_fp8": [_C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P],
+    "se_sparse_decode_attn_fp8": [_C, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _F32, _P, _P, _P, _I32, _I32, _P, _SZ,
+                                  _P],
     "se_pyramid_budgets": [_I32, _I32, _I32, _P],
     "se_snapkv_score_compact": [_C, _P, _P, _P, _I32, _I32, _I32, _I32, _F32, _C, _P, _P, _P, _P, _P, _P, _SZ,
                                 _P],
@@ -170,6 +175,28 @@ def se_quest_append_select(c, q, k, v, k_new, v_new, seq_len, kmin, kmax, page_s
         ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(k_new), _ptr(v_new), _ptr(seq_len), _ptr(kmin), _ptr(kmax),
         page_size, top_pages, _ptr(view_idx), _ptr(view_len), _ptr(page_score), _ptr(ws), _nbytes(ws),
         _stream(stream)))
+
+
+def se_kv_quantize_fp8(c, k, v, seq_len, k_q, v_q, k_scale, v_scale, kmin=None, kmax=None, page_size=0,
+                       stream=None):
+    _check("se_kv_quantize_fp8", load().se_kv_quantize_fp8(
+        ctypes.byref(c), _ptr(k), _ptr(v), _ptr(seq_len), _ptr(k_q), _ptr(v_q), _ptr(k_scale), _ptr(v_scale),
+        _ptr(kmin), _ptr(kmax), page_size, _stream(stream)))
+
+
+def se_kv_append_fp8(c, k_q, v_q, k_scale, v_scale, k_new, v_new, seq_len, kmin=None, kmax=None, page_size=1,
+                     stream=None):
+    _check("se_kv_append_fp8", load().se_kv_append_fp8(
+        ctypes.byref(c), _ptr(k_q), _ptr(v_q), _ptr(k_scale), _ptr(v_scale), _ptr(k_new), _ptr(v_new), _ptr(seq_len),
+        _ptr(kmin), _ptr(kmax), page_size, _stream(stream)))
+
+
+def se_sparse_decode_attn_fp8(c, q, k_q, v_q, k_scale, v_scale, seq_len, view_idx, view_len, view_cap, granularity,
+                              scale, out, lse=None, logits=None, logit_cap=0, num_splits=0, ws=None, stream=None):
+    _check("se_sparse_decode_attn_fp8", load().se_sparse_decode_attn_fp8(
+        ctypes.byref(c), _ptr(q), _ptr(k_q), _ptr(v_q), _ptr(k_scale), _ptr(v_scale), _ptr(seq_len), _ptr(view_idx),
+        _ptr(view_len), view_cap, granularity, scale, _ptr(out), _ptr(lse), _ptr(logits), logit_cap, num_splits,
+        _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def se_streaming_view(c, seq_len, sink, recent, view_idx, view_len, stream=None):

@@ -44,6 +44,33 @@ se_status check_cache(const se_cache* c) {
   return SE_OK;
 }
 
+// Shared validation and launch of the attention calls (cache already checked);
+// k_scale / v_scale non-null for FP8 rows.
+se_status attn_impl(const se_cache* c, const void* q, const void* k, const void* v, const int32_t* seq_len,
+                    const int32_t* view_idx, const int32_t* view_len, int32_t view_cap, int32_t granularity,
+                    float scale, float* out, float* lse, float* logits, int32_t logit_cap, int32_t num_splits,
+                    void* ws, size_t ws_bytes, hipStream_t stream, const uint8_t* k_scale, const uint8_t* v_scale) {
+  if (!q || !k || !seq_len || !out || (!c->latent && !v)) return SE_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || (!c->latent && !aligned16(v)) || !aligned16(out)) return SE_ERR_ALIGN;
+  if (view_idx) {
+    if (!view_len) return SE_ERR_NULL;
+    if (view_cap <= 0 || granularity <= 0) return SE_ERR_SHAPE;
+    if (int64_t(view_cap) * granularity > (int64_t(1) << 30)) return SE_ERR_SHAPE;
+  }
+  if (logits && logit_cap <= 0) return SE_ERR_SHAPE;
+  if (num_splits < 0 || num_splits > 256) return SE_ERR_SHAPE;
+  if (!(scale > 0.f) || !(scale < 1e30f)) return SE_ERR_SHAPE;
+  const int slots = view_idx ? view_cap * granularity : c->capacity;
+  const size_t need = attn_ws_bytes(*c, slots, num_splits);
+  if (!ws || ws_bytes < need) return SE_ERR_WORKSPACE;
+  SE_TRACE_CALL("sparse_decode_attn%s B=%d Hq=%d Hkv=%d d_k=%d d_v=%d view=%s cap=%d g=%d splits=%d logits=%d",
+                k_scale ? "_fp8" : "", c->batch, c->n_q_heads, c->n_kv_heads, c->d_k, c->d_v, view_idx ? "idx" : "identity",
+                view_cap, granularity, num_splits, logits ? logit_cap : 0);
+  clear_stale_error();
+  return launch_attn(*c, q, k, v, seq_len, view_idx, view_len, view_cap, granularity, scale, out, lse, logits,
+                     logit_cap, num_splits, ws, stream, k_scale, v_scale);
+}
+
 }  // namespace
 
 extern "C" {
@@ -172,6 +199,60 @@ se_status se_quest_append_select(const se_cache* c, const void* q, void* k, void
                              view_len, page_score, ws, stream);
 }
 
+// FP8 caches: bf16 q / metadata / source rows, GQA with d_k 64 or 128.
+se_status check_fp8_cache(const se_cache* c) {
+  se_status st = check_cache(c);
+  if (st != SE_OK) return st;
+  if (c->dtype != SE_BF16) return SE_ERR_DTYPE;
+  if (c->latent || (c->d_k != 64 && c->d_k != 128)) return SE_ERR_UNSUPPORTED;
+  return SE_OK;
+}
+
+se_status se_kv_quantize_fp8(const se_cache* c, const void* k, const void* v, const int32_t* seq_len, void* k_q,
+                             void* v_q, uint8_t* k_scale, uint8_t* v_scale, void* kmin, void* kmax, int32_t page_size,
+                             hipStream_t stream) {
+  se_status st = check_fp8_cache(c);
+  if (st != SE_OK) return st;
+  if (!k || !v || !seq_len || !k_q || !v_q || !k_scale || !v_scale || (!kmin != !kmax)) return SE_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_q) || !aligned16(v_q) ||
+      (kmin && (!aligned16(kmin) || !aligned16(kmax))))
+    return SE_ERR_ALIGN;
+  if (kmin && (page_size <= 0 || page_size > c->capacity)) return SE_ERR_SHAPE;
+  SE_TRACE_CALL("kv_quantize_fp8 B=%d Hkv=%d d_k=%d cap=%d", c->batch, c->n_kv_heads, c->d_k, c->capacity);
+  clear_stale_error();
+  return launch_fp8_quantize(*c, k, v, seq_len, k_q, v_q, k_scale, v_scale, kmin, kmax, page_size, stream);
+}
+
+se_status se_kv_append_fp8(const se_cache* c, void* k_q, void* v_q, uint8_t* k_scale, uint8_t* v_scale,
+                           const void* k_new, const void* v_new, int32_t* seq_len, void* kmin, void* kmax,
+                           int32_t page_size, hipStream_t stream) {
+  se_status st = check_fp8_cache(c);
+  if (st != SE_OK) return st;
+  if (!k_q || !v_q || !k_scale || !v_scale || !k_new || !v_new || !seq_len || (!kmin != !kmax)) return SE_ERR_NULL;
+  if (!aligned16(k_q) || !aligned16(v_q) || !aligned16(k_new) || !aligned16(v_new) ||
+      (kmin && (!aligned16(kmin) || !aligned16(kmax))))
+    return SE_ERR_ALIGN;
+  if (page_size <= 0 || page_size > c->capacity) return SE_ERR_SHAPE;
+  SE_TRACE_CALL("kv_append_fp8 B=%d Hkv=%d d_k=%d cap=%d P=%d", c->batch, c->n_kv_heads, c->d_k, c->capacity,
+                page_size);
+  clear_stale_error();
+  return launch_fp8_append(*c, k_q, v_q, k_scale, v_scale, k_new, v_new, seq_len, kmin, kmax, page_size, stream);
+}
+
+se_status se_sparse_decode_attn_fp8(const se_cache* c, const void* q, const void* k_q, const void* v_q,
+                                    const uint8_t* k_scale, const uint8_t* v_scale, const int32_t* seq_len,
+                                    const int32_t* view_idx, const int32_t* view_len, int32_t view_cap,
+                                    int32_t granularity, float scale, float* out, float* lse, float* logits,
+                                    int32_t logit_cap, int32_t num_splits, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+  se_status st = check_fp8_cache(c);
+  if (st != SE_OK) return st;
+  if (c->n_q_heads / c->n_kv_heads > 16) return SE_ERR_UNSUPPORTED;
+  if (!k_scale || !v_scale || !v_q) return SE_ERR_NULL;
+  return attn_impl(c, q, k_q, v_q, seq_len, view_idx, view_len, view_cap, granularity, scale, out, lse, logits,
+                   logit_cap, num_splits, ws, ws_bytes, stream, k_scale, v_scale);
+}
+
 se_status se_streaming_view(const se_cache* c, const int32_t* seq_len, int32_t sink, int32_t recent,
                             int32_t* view_idx, int32_t* view_len, int32_t view_cap, hipStream_t stream) {
   se_status st = check_cache(c);
@@ -201,25 +282,8 @@ se_status se_sparse_decode_attn(const se_cache* c, const void* q, const void* k,
                                 void* ws, size_t ws_bytes, hipStream_t stream) {
   se_status st = check_cache(c);
   if (st != SE_OK) return st;
-  if (!q || !k || !seq_len || !out || (!c->latent && !v)) return SE_ERR_NULL;
-  if (!aligned16(q) || !aligned16(k) || (!c->latent && !aligned16(v)) || !aligned16(out)) return SE_ERR_ALIGN;
-  if (view_idx) {
-    if (!view_len) return SE_ERR_NULL;
-    if (view_cap <= 0 || granularity <= 0) return SE_ERR_SHAPE;
-    if (int64_t(view_cap) * granularity > (int64_t(1) << 30)) return SE_ERR_SHAPE;
-  }
-  if (logits && logit_cap <= 0) return SE_ERR_SHAPE;
-  if (num_splits < 0 || num_splits > 256) return SE_ERR_SHAPE;
-  if (!(scale > 0.f) || !(scale < 1e30f)) return SE_ERR_SHAPE;
-  const int slots = view_idx ? view_cap * granularity : c->capacity;
-  const size_t need = attn_ws_bytes(*c, slots, num_splits);
-  if (!ws || ws_bytes < need) return SE_ERR_WORKSPACE;
-  SE_TRACE_CALL("sparse_decode_attn B=%d Hq=%d Hkv=%d d_k=%d d_v=%d view=%s cap=%d g=%d splits=%d logits=%d",
-                c->batch, c->n_q_heads, c->n_kv_heads, c->d_k, c->d_v, view_idx ? "idx" : "identity",
-                view_cap, granularity, num_splits, logits ? logit_cap : 0);
-  clear_stale_error();
-  return launch_attn(*c, q, k, v, seq_len, view_idx, view_len, view_cap, granularity, scale, out, lse, logits,
-                     logit_cap, num_splits, ws, stream);
+  return attn_impl(c, q, k, v, seq_len, view_idx, view_len, view_cap, granularity, scale, out, lse, logits, logit_cap,
+                   num_splits, ws, ws_bytes, stream, nullptr, nullptr);
 }
 
 se_status se_snapkv_score_compact(const se_cache* c, const void* q_obs, const void* k, const void* v,

@@ -231,9 +231,13 @@ se_status launch_attn_vector(const AttnArgs& a, hipStream_t s) {
 se_status launch_attn(const se_cache& c, const void* q, const void* k, const void* v,
                       const int32_t* seq_len, const int32_t* view_idx, const int32_t* view_len,
                       int view_cap, int granularity, float scale, float* out, float* lse,
-                      float* logits, int logit_cap, int num_splits, void* ws, hipStream_t s) {
+                      float* logits, int logit_cap, int num_splits, void* ws, hipStream_t s,
+                      const uint8_t* k_scale, const uint8_t* v_scale) {
   AttnArgs a = make_attn_args(c, q, k, v, seq_len, view_idx, view_len, view_cap, granularity, scale, out,
                               lse, logits, logit_cap);
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.fp8 = k_scale != nullptr;
   const int slots = view_idx ? view_cap * granularity : c.capacity;
   a.splits = num_splits > 0 ? num_splits : attn_auto_splits(c, slots);
   a.counters = (int*)ws;
@@ -243,7 +247,10 @@ se_status launch_attn(const se_cache& c, const void* q, const void* k, const voi
   // (MLA: 32 heads x 512 columns per split) go to the combine kernel
   a.fused = a.splits > 1 && size_t(a.splits) * std::min(a.G, 32) * a.Dv * sizeof(float) <= ATTN_FUSED_MERGE_BYTES;
   se_status st = SE_ERR_UNSUPPORTED;
-  if (attn_mfma_supported(a)) st = launch_attn_mfma(a, s);
+  if (a.fp8) {   // FP8 rows: the MFMA kernel only
+    if (!attn_mfma_supported(a)) return SE_ERR_UNSUPPORTED;
+    st = launch_attn_mfma(a, s);
+  } else if (attn_mfma_supported(a)) st = launch_attn_mfma(a, s);
   else if (attn_mla_supported(a)) st = launch_attn_mla(a, s);
   if (st == SE_ERR_UNSUPPORTED) st = launch_attn_vector(a, s);
   if (st != SE_OK || a.splits == 1 || a.fused) return st;

@@ -17,6 +17,9 @@ struct AttnArgs {
   float* part_o;    // [units][splits][G][Dv]: unnormalised output
   int* counters;    // [units][ATTN_MAX_HG] split completion tickets, zero between calls
   int fused;        // splits > 1 and the last block of a unit merges them (else the combine kernel)
+  const uint8_t* k_scale;   // FP8 rows (fp8 != 0): one E8M0 scale byte per K / V row, [units][cap]
+  const uint8_t* v_scale;
+  int fp8;
   float scale;
   int B, Hq, Hkv, G, Dk, Dv, cap, latent, dtype;
   int k_stride, v_stride;  // elements per K / V row

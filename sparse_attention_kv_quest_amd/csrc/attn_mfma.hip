@@ -23,6 +23,8 @@
 // shift cancels in the final normalisation.  The four waves merge their
 // (max, sum, output) in LDS and the block writes one partial; the block that
 // finishes a unit's last split merges the splits, so a call is one launch.
+#include <type_traits>
+
 #include "attn_common.hpp"
 #include "mfma_util.hpp"
 
@@ -40,9 +42,26 @@ struct MfTile {
   int tk0, tk1;
 };
 
+// FP8 rows as loaded: the lane's d/4 contiguous K bytes of rows tk0 / tk1 (its k
+// columns are g d/4 .. g d/4 + d/4 - 1, k-step c taking the 8 from 8c on; q is
+// staged in the same order), 8 V bytes per row and pass (the bf16 layout's
+// dims), and every row's scale byte.
+template <int D>
+struct MfTileF8 {
+  u32x4 k0[D / 64], k1[D / 64];
+  uint2 v[D / 64][4];
+  uint32_t ks0, ks1, vs[4];
+  int tk0, tk1;
+};
+
+template <int D, bool F8>
+using MfRaw = std::conditional_t<F8, MfTileF8<D>, MfTile<D>>;
+
 struct MfCtx {
   const uint16_t* ku;
   const uint16_t* vu;
+  const uint8_t* ksc;    // FP8: scale bytes of the unit's rows
+  const uint8_t* vsc;
   const int32_t* vglob;  // view entries in global memory (used when they do not fit the LDS cache)
   int e0, len, s1, gshift;
   bool identity;
@@ -97,6 +116,77 @@ __device__ __forceinline__ void mf_load(const MfCtx& x, int base, int lane, MfTi
 #pragma unroll
     for (int p = 0; p < VPASS; ++p) T.v[p][r] = ld16(x.vu + rv + 64 * p);
   }
+}
+
+// Scale 2^(s - 127) of a scale byte, clamped to the normal float range.
+__device__ __forceinline__ float mf_scale(uint32_t sb) { return __uint_as_float(min(max(sb, 1u), 254u) << 23); }
+
+// Four bf16 pairs (8 values) of the 8 FP8 codes in w0, w1, each times `sc` (exact).
+__device__ __forceinline__ u32x4 mf_cvt8(uint32_t w0, uint32_t w1, float sc) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  const bf2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, false);
+  const bf2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, sc, true);
+  const bf2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, false);
+  const bf2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, sc, true);
+  return u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, c),
+               __builtin_bit_cast(uint32_t, d)};
+}
+
+template <int D, bool VC>
+__device__ __forceinline__ void mf_load_f8(const MfCtx& x, int base, int lane, MfTileF8<D>& T) {
+  constexpr int VPASS = D / 64;
+  const int g = lane >> 4, c16 = lane & 15, qa = lane & 7;
+  T.tk0 = mf_token<VC>(x, base + c16);
+  T.tk1 = mf_token<VC>(x, base + 16 + c16);
+  int vtok[4];
+  const int sq = base + 4 * qa;
+  if (x.identity || x.gshift >= 2) {
+    const int t0 = mf_token<VC>(x, sq);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vtok[r] = (t0 >= 0 && sq + r < x.s1 && t0 + r < x.len) ? t0 + r : -1;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vtok[r] = mf_token<VC>(x, sq + r);
+  }
+  // unconditional loads, as in the bf16 tile (slots without a token read row 0)
+  const uint8_t* ku = reinterpret_cast<const uint8_t*>(x.ku);
+  const uint8_t* vu = reinterpret_cast<const uint8_t*>(x.vu);
+  const uint32_t t0 = uint32_t(max(T.tk0, 0)), t1 = uint32_t(max(T.tk1, 0));
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) {
+    T.k0[j] = ld16(ku + t0 * D + g * (D / 4) + 16 * j);
+    T.k1[j] = ld16(ku + t1 * D + g * (D / 4) + 16 * j);
+  }
+  T.ks0 = x.ksc[t0];
+  T.ks1 = x.ksc[t1];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t tv = uint32_t(max(vtok[r], 0));
+#pragma unroll
+    for (int p = 0; p < VPASS; ++p) T.v[p][r] = *reinterpret_cast<const uint2*>(vu + tv * D + 8 * (lane >> 3) + 64 * p);
+    T.vs[r] = x.vsc[tv];
+  }
+}
+
+// FP8 tile -> the bf16 operands of the MFMA tile (stored values, exact).
+template <int D>
+__device__ __forceinline__ void mf_convert(const MfTileF8<D>& T, MfTile<D>& B) {
+  constexpr int NKS = D / 32, VPASS = D / 64;
+  const float s0 = mf_scale(T.ks0), s1 = mf_scale(T.ks1);
+#pragma unroll
+  for (int c = 0; c < NKS; ++c) {   // k-step c: bytes 8c .. 8c + 7 of the lane's span
+    const int j = c / 2, w = 2 * (c % 2);
+    B.k0[c] = mf_cvt8(T.k0[j][w], T.k0[j][w + 1], s0);
+    B.k1[c] = mf_cvt8(T.k1[j][w], T.k1[j][w + 1], s1);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float sv = mf_scale(T.vs[r]);
+#pragma unroll
+    for (int p = 0; p < VPASS; ++p) B.v[p][r] = mf_cvt8(T.v[p][r].x, T.v[p][r].y, sv);
+  }
+  B.tk0 = T.tk0;
+  B.tk1 = T.tk1;
 }
 
 template <int D>
@@ -203,7 +293,26 @@ __device__ __forceinline__ void mf_compute(const AttnArgs& a, const MfCtx& x, in
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D, bool VC, int OCC>
+template <int D, bool VC, bool F8>
+__device__ __forceinline__ void mf_fetch(const MfCtx& x, int base, int lane, MfRaw<D, F8>& T) {
+  if constexpr (F8) mf_load_f8<D, VC>(x, base, lane, T);
+  else mf_load<D, VC>(x, base, lane, T);
+}
+
+template <int D, bool F8>
+__device__ __forceinline__ void mf_step(const AttnArgs& a, const MfCtx& x, int base, int lane, const u32x4* qv,
+                                        float sc2, float* lg_row, uint16_t* vt, const MfRaw<D, F8>& T,
+                                        MfState<D>& st) {
+  if constexpr (F8) {
+    MfTile<D> B;
+    mf_convert<D>(T, B);
+    mf_compute<D>(a, x, base, lane, qv, sc2, lg_row, vt, B, st);
+  } else {
+    mf_compute<D>(a, x, base, lane, qv, sc2, lg_row, vt, T, st);
+  }
+}
+
+template <int D, bool VC, int OCC, bool F8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void attn_mfma_kernel(AttnArgs a) {
   constexpr int PITCH = MF_TS + 4;          // u16 per transposed V row (72 bytes)
@@ -253,8 +362,11 @@ void attn_mfma_kernel(AttnArgs a) {
   const int s_valid = identity ? len : min(a.view_len[unit], a.view_cap) * a.gran;
 
   MfCtx x;
-  x.ku = (const uint16_t*)a.k + size_t(unit) * a.cap * D;
-  x.vu = (const uint16_t*)a.v + size_t(unit) * a.cap * D;
+  const size_t ebytes = F8 ? 1 : 2;   // bytes per stored element
+  x.ku = reinterpret_cast<const uint16_t*>(static_cast<const char*>(a.k) + size_t(unit) * a.cap * D * ebytes);
+  x.vu = reinterpret_cast<const uint16_t*>(static_cast<const char*>(a.v) + size_t(unit) * a.cap * D * ebytes);
+  x.ksc = F8 ? a.k_scale + size_t(unit) * a.cap : nullptr;
+  x.vsc = F8 ? a.v_scale + size_t(unit) * a.cap : nullptr;
   x.len = len;
   x.s1 = min(s1, s_valid);
   x.gshift = a.gshift;
@@ -265,9 +377,9 @@ void attn_mfma_kernel(AttnArgs a) {
   // Q as the B operand: lane holds head c16, dims 32c + 8g .. 32c + 8g + 7 of k-step c
   u32x4 qv[NKS];
   if (c16 < G) {
-    const uint16_t* qp = (const uint16_t*)a.q + (size_t(b) * a.Hq + size_t(kvh) * G + c16) * D + 8 * g;
+    const uint16_t* qh = (const uint16_t*)a.q + (size_t(b) * a.Hq + size_t(kvh) * G + c16) * D;
 #pragma unroll
-    for (int c = 0; c < NKS; ++c) qv[c] = ld16(qp + 32 * c);
+    for (int c = 0; c < NKS; ++c) qv[c] = ld16(qh + (F8 ? g * (D / 4) + 8 * c : 8 * g + 32 * c));
   } else {
 #pragma unroll
     for (int c = 0; c < NKS; ++c) qv[c] = u32x4{0, 0, 0, 0};
@@ -301,51 +413,51 @@ void attn_mfma_kernel(AttnArgs a) {
   constexpr int STEP = MF_WAVES * MF_TS;   // slots between this wave's consecutive tiles
   const int first = s0 + w * MF_TS;
   if (OCC == 1) {
-    MfTile<D> T0, T1, T2;                  // two tiles in flight while a third is computed
+    MfRaw<D, F8> T0, T1, T2;               // two tiles in flight while a third is computed
     if (nmine == 1) {
-      mf_load<D, VC>(x, first, lane, T0);
-      mf_compute<D>(a, x, first, lane, qv, sc2, lg_row, vt, T0, st);
+      mf_fetch<D, VC, F8>(x, first, lane, T0);
+      mf_step<D, F8>(a, x, first, lane, qv, sc2, lg_row, vt, T0, st);
     } else if (nmine > 1) {
-      mf_load<D, VC>(x, first, lane, T0);
-      mf_load<D, VC>(x, first + STEP, lane, T1);
+      mf_fetch<D, VC, F8>(x, first, lane, T0);
+      mf_fetch<D, VC, F8>(x, first + STEP, lane, T1);
       int i = 0;
       for (; i + 4 < nmine; i += 3) {      // T0 = tile i, T1 = tile i + 1 in flight
         const int b0 = first + i * STEP;
-        mf_load<D, VC>(x, b0 + 2 * STEP, lane, T2);
-        mf_compute<D>(a, x, b0, lane, qv, sc2, lg_row, vt, T0, st);
-        mf_load<D, VC>(x, b0 + 3 * STEP, lane, T0);
-        mf_compute<D>(a, x, b0 + STEP, lane, qv, sc2, lg_row, vt, T1, st);
-        mf_load<D, VC>(x, b0 + 4 * STEP, lane, T1);
-        mf_compute<D>(a, x, b0 + 2 * STEP, lane, qv, sc2, lg_row, vt, T2, st);
+        mf_fetch<D, VC, F8>(x, b0 + 2 * STEP, lane, T2);
+        mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_row, vt, T0, st);
+        mf_fetch<D, VC, F8>(x, b0 + 3 * STEP, lane, T0);
+        mf_step<D, F8>(a, x, b0 + STEP, lane, qv, sc2, lg_row, vt, T1, st);
+        mf_fetch<D, VC, F8>(x, b0 + 4 * STEP, lane, T1);
+        mf_step<D, F8>(a, x, b0 + 2 * STEP, lane, qv, sc2, lg_row, vt, T2, st);
       }
       const int r = nmine - i;             // 2, 3 or 4 tiles left
       const int b0 = first + i * STEP;
-      if (r >= 3) mf_load<D, VC>(x, b0 + 2 * STEP, lane, T2);
-      mf_compute<D>(a, x, b0, lane, qv, sc2, lg_row, vt, T0, st);
-      if (r == 4) mf_load<D, VC>(x, b0 + 3 * STEP, lane, T0);
-      mf_compute<D>(a, x, b0 + STEP, lane, qv, sc2, lg_row, vt, T1, st);
-      if (r >= 3) mf_compute<D>(a, x, b0 + 2 * STEP, lane, qv, sc2, lg_row, vt, T2, st);
-      if (r == 4) mf_compute<D>(a, x, b0 + 3 * STEP, lane, qv, sc2, lg_row, vt, T0, st);
+      if (r >= 3) mf_fetch<D, VC, F8>(x, b0 + 2 * STEP, lane, T2);
+      mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_row, vt, T0, st);
+      if (r == 4) mf_fetch<D, VC, F8>(x, b0 + 3 * STEP, lane, T0);
+      mf_step<D, F8>(a, x, b0 + STEP, lane, qv, sc2, lg_row, vt, T1, st);
+      if (r >= 3) mf_step<D, F8>(a, x, b0 + 2 * STEP, lane, qv, sc2, lg_row, vt, T2, st);
+      if (r == 4) mf_step<D, F8>(a, x, b0 + 3 * STEP, lane, qv, sc2, lg_row, vt, T0, st);
     }
   } else {
-    MfTile<D> T0, T1;                      // one tile in flight while the other is computed
+    MfRaw<D, F8> T0, T1;                   // one tile in flight while the other is computed
     if (nmine > 0) {
-      mf_load<D, VC>(x, first, lane, T0);
+      mf_fetch<D, VC, F8>(x, first, lane, T0);
       int i = 0;
       for (; i + 2 < nmine; i += 2) {      // T0 = tile i in flight
         const int b0 = first + i * STEP;
-        mf_load<D, VC>(x, b0 + STEP, lane, T1);
-        mf_compute<D>(a, x, b0, lane, qv, sc2, lg_row, vt, T0, st);
-        mf_load<D, VC>(x, b0 + 2 * STEP, lane, T0);
-        mf_compute<D>(a, x, b0 + STEP, lane, qv, sc2, lg_row, vt, T1, st);
+        mf_fetch<D, VC, F8>(x, b0 + STEP, lane, T1);
+        mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_row, vt, T0, st);
+        mf_fetch<D, VC, F8>(x, b0 + 2 * STEP, lane, T0);
+        mf_step<D, F8>(a, x, b0 + STEP, lane, qv, sc2, lg_row, vt, T1, st);
       }
       const int b0 = first + i * STEP;     // one or two tiles left
       if (i + 1 < nmine) {
-        mf_load<D, VC>(x, b0 + STEP, lane, T1);
-        mf_compute<D>(a, x, b0, lane, qv, sc2, lg_row, vt, T0, st);
-        mf_compute<D>(a, x, b0 + STEP, lane, qv, sc2, lg_row, vt, T1, st);
+        mf_fetch<D, VC, F8>(x, b0 + STEP, lane, T1);
+        mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_row, vt, T0, st);
+        mf_step<D, F8>(a, x, b0 + STEP, lane, qv, sc2, lg_row, vt, T1, st);
       } else {
-        mf_compute<D>(a, x, b0, lane, qv, sc2, lg_row, vt, T0, st);
+        mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_row, vt, T0, st);
       }
     }
   }
@@ -430,12 +542,15 @@ se_status launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
   int chunk = (slots + a.splits - 1) / a.splits;
   chunk = (chunk + MF_TS - 1) / MF_TS * MF_TS;
   const bool vc = a.view_idx != nullptr && chunk / a.gran + 2 <= MF_VCACHE;
-#define SE_MF_LAUNCH(DD, VV, OO) hipLaunchKernelGGL((attn_mfma_kernel<DD, VV, OO>), grid, dim3(256), 0, s, a)
-  if (a.Dk == 128) {
-    if (vc) SE_MF_LAUNCH(128, true, 2); else SE_MF_LAUNCH(128, false, 2);
-  } else {
-    if (vc) SE_MF_LAUNCH(64, true, 1); else SE_MF_LAUNCH(64, false, 1);
+#define SE_MF_LAUNCH(DD, VV, OO, FF) hipLaunchKernelGGL((attn_mfma_kernel<DD, VV, OO, FF>), grid, dim3(256), 0, s, a)
+#define SE_MF_D(FF)                                                                  \
+  if (a.Dk == 128) {                                                                 \
+    if (vc) SE_MF_LAUNCH(128, true, 2, FF); else SE_MF_LAUNCH(128, false, 2, FF);    \
+  } else {                                                                           \
+    if (vc) SE_MF_LAUNCH(64, true, 1, FF); else SE_MF_LAUNCH(64, false, 1, FF);      \
   }
+  if (a.fp8) { SE_MF_D(true) } else { SE_MF_D(false) }
+#undef SE_MF_D
 #undef SE_MF_LAUNCH
   return launch_status();
 }

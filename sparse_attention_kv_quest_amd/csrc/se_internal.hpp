@@ -424,10 +424,16 @@ se_status launch_quest(const se_cache& c, const void* q, const void* kmin, const
                        int32_t* view_len, float* page_score, void* ws, hipStream_t s);
 int attn_auto_splits(const se_cache& c, int slots);
 size_t attn_ws_bytes(const se_cache& c, int slots, int num_splits);
+// k_scale / v_scale non-null: K / V hold FP8 rows with one scale byte per row.
 se_status launch_attn(const se_cache& c, const void* q, const void* k, const void* v,
                       const int32_t* seq_len, const int32_t* view_idx, const int32_t* view_len,
                       int view_cap, int granularity, float scale, float* out, float* lse,
-                      float* logits, int logit_cap, int num_splits, void* ws, hipStream_t s);
+                      float* logits, int logit_cap, int num_splits, void* ws, hipStream_t s,
+                      const uint8_t* k_scale = nullptr, const uint8_t* v_scale = nullptr);
+se_status launch_fp8_quantize(const se_cache& c, const void* k, const void* v, const int32_t* seq_len, void* kq,
+                              void* vq, void* ks, void* vs, void* kmin, void* kmax, int page_size, hipStream_t s);
+se_status launch_fp8_append(const se_cache& c, void* kq, void* vq, void* ks, void* vs, const void* k_new,
+                            const void* v_new, int32_t* seq_len, void* kmin, void* kmax, int page_size, hipStream_t s);
 size_t snapkv_ws_bytes(const se_cache& c, int prompt_len, int window);
 se_status launch_snapkv(const se_cache& c, const void* q_obs, const void* k, const void* v,
                         int prompt_len, int window, int pool_kernel, int budget, float scale,

@@ -47,11 +47,18 @@ def test_encode_round_trip_and_ties_to_even():
     assert fp8.e4m3_encode(-(2.0 ** -6 + 2.0 ** -10)) == 0x88
 
 
-@pytest.mark.parametrize("amax", [1e-30, 2.0 ** -20, 0.3, 1.0, 3.5, 448.0, 449.0, 896.0, 1e6, 7.9e-3])
+@pytest.mark.parametrize("amax", [1e-30, 2.0 ** -20, 0.3, 1.0, 3.5, 448.0, 449.0, 896.0, 1e6, 7.9e-3, 3.3e38])
 def test_row_exponent_is_the_smallest_that_fits(amax):
     e = fp8.row_exponent(amax)
     assert amax * 2.0 ** -e <= 448.0 < amax * 2.0 ** -(e - 1)
     assert fp8.row_exponent(0.0) == 0
+
+
+def test_row_exponent_lower_bound():
+    # rows far below the E4M3 range keep the smallest normal float32 scale
+    assert fp8.row_exponent(1e-40) == -126 and fp8.row_exponent(2.0 ** -140) == -126
+    assert fp8.row_exponent(448.0 * 2.0 ** -126) == -126
+    assert fp8.row_exponent(449.0 * 2.0 ** -126) == -125
 
 
 def test_quantized_rows_error_bound_and_bf16_exactness():
