@@ -222,6 +222,37 @@ se_status se_streaming_view(const se_cache* c, const int32_t* seq_len, int32_t s
  * SE_ERR_SHAPE), 0 <= min_budget <= avg_budget (else SE_ERR_BUDGET). */
 se_status se_pyramid_budgets(int32_t n_layers, int32_t avg_budget, int32_t min_budget, int32_t* budgets);
 
+/* Chain Cache (tokendh.com explainer, section "聊天记录也能'续命':Chain Cache";
+ * Netics blog, section "SparseEngine 围绕 KV cache 构建了什么": the
+ * ChainCacheIndex ties a session to its retained per-layer KV, method metadata
+ * and logical token prefix).  The logical prefix (tokens said) is kept apart
+ * from the physical rows still stored; a new turn that continues a stored
+ * prefix reuses that session's rows and only its new tokens are processed.
+ *
+ * se_chain_match (host computation, no GPU work): tokens / prefixes are HOST
+ * int32 arrays; prefixes[s] (prefix_lens[s] tokens) is session s's logical
+ * prefix.  *session = the session whose prefix `tokens` continues (the prefix
+ * is a prefix of tokens), the longest one, the lower index on equal lengths;
+ * -1 (and *matched_len 0) when none does. */
+se_status se_chain_match(const int32_t* tokens, int32_t n_tokens, const int32_t* const* prefixes,
+                         const int32_t* prefix_lens, int32_t n_prefixes, int32_t* session, int32_t* matched_len);
+
+/* Position map after a compaction.  map_out int32 [B][Hkv][c_out->capacity]:
+ * map_out[u][i] = map_in[u][kept[u][i]] for i < kept_len[b] (map_in NULL: the
+ * identity, i.e. kept[u][i] itself), -1 for the remaining entries and for kept
+ * entries outside [0, cap_in).  map_in int32 [B][Hkv][cap_in] or NULL; kept
+ * int32 [B][Hkv][kept_stride] physical rows, ascending (e.g. SnapKV's kept
+ * positions); kept_len int32 [B] (e.g. SnapKV's out_seq_len). */
+se_status se_chain_remap(const se_cache* c_out, const int32_t* map_in, int32_t cap_in, const int32_t* kept,
+                         int32_t kept_stride, const int32_t* kept_len, int32_t* map_out, hipStream_t stream);
+
+/* Positions of n_new rows about to be appended after the seq_len[b] retained
+ * rows: pos_map[u][seq_len[b] + j] = logical_len[b] + j (entries past the
+ * capacity skipped).  Call before the rows are appended.  pos_map int32
+ * [B][Hkv][capacity]; seq_len, logical_len int32 [B]. */
+se_status se_chain_append_positions(const se_cache* c, int32_t* pos_map, const int32_t* seq_len,
+                                    const int32_t* logical_len, int32_t n_new, hipStream_t stream);
+
 /* Split-K flash decode over an AttentionView (tokendh.com explainer, section
  * "把边界划在'生命周期'上"; ai-feeds digest, section 方法 / 关键模块).
  *   view_idx: NULL = every slot below seq_len[b]; else int32 [B][Hkv][view_cap],

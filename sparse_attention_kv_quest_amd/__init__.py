@@ -23,6 +23,7 @@ STATUS = {0: "SE_OK", -1: "SE_ERR_NULL", -2: "SE_ERR_SHAPE", -3: "SE_ERR_DTYPE",
 EXPORTS = ("se_kv_append", "se_kv_append_meta", "se_page_meta_update", "se_quest_select", "se_quest_append_select",
            "se_sparse_decode_attn", "se_streaming_view", "se_pyramid_budgets",
            "se_kv_quantize_fp8", "se_kv_append_fp8", "se_sparse_decode_attn_fp8",
+           "se_chain_match", "se_chain_remap", "se_chain_append_positions",
            "se_snapkv_score_compact", "se_h2o_accumulate_evict", "se_omnikv_topk",
            "se_workspace_bytes", "se_workspace_init", "se_status_string", "se_abi_version")
 
@@ -55,6 +56,9 @@ _SIGS = {
     "se_sparse_decode_attn_fp8": [_C, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _F32, _P, _P, _P, _I32, _I32, _P, _SZ,
                                   _P],
     "se_pyramid_budgets": [_I32, _I32, _I32, _P],
+    "se_chain_match": [_P, _I32, _P, _P, _I32, _P, _P],
+    "se_chain_remap": [_C, _P, _I32, _P, _I32, _P, _P, _P],
+    "se_chain_append_positions": [_C, _P, _P, _P, _I32, _P],
     "se_snapkv_score_compact": [_C, _P, _P, _P, _I32, _I32, _I32, _I32, _F32, _C, _P, _P, _P, _P, _P, _P, _SZ,
                                 _P],
     "se_h2o_accumulate_evict": [_C, _P, _P, _I32, _P, _P, _P, _I32, _I32, _I32, _P, _P],
@@ -202,6 +206,29 @@ def se_sparse_decode_attn_fp8(c, q, k_q, v_q, k_scale, v_scale, seq_len, view_id
 def se_streaming_view(c, seq_len, sink, recent, view_idx, view_len, stream=None):
     _check("se_streaming_view", load().se_streaming_view(ctypes.byref(c), _ptr(seq_len), sink, recent, _ptr(view_idx),
                                                          _ptr(view_len), view_idx.shape[-1], _stream(stream)))
+
+
+def se_chain_match(tokens, prefixes):
+    """(session index or -1, matched length) for host token lists; host computation."""
+    arrs = [(ctypes.c_int32 * max(1, len(p)))(*p) for p in prefixes]
+    ptrs = (ctypes.c_void_p * max(1, len(arrs)))(*[ctypes.cast(a, ctypes.c_void_p) for a in arrs])
+    lens = (ctypes.c_int32 * max(1, len(prefixes)))(*[len(p) for p in prefixes])
+    toks = (ctypes.c_int32 * max(1, len(tokens)))(*tokens)
+    sess, n = ctypes.c_int32(), ctypes.c_int32()
+    _check("se_chain_match", load().se_chain_match(toks, len(tokens), ptrs, lens, len(prefixes), ctypes.byref(sess),
+                                                   ctypes.byref(n)))
+    return sess.value, n.value
+
+
+def se_chain_remap(c_out, map_in, kept, kept_len, map_out, stream=None):
+    _check("se_chain_remap", load().se_chain_remap(
+        ctypes.byref(c_out), _ptr(map_in), 0 if map_in is None else map_in.shape[-1], _ptr(kept), kept.shape[-1],
+        _ptr(kept_len), _ptr(map_out), _stream(stream)))
+
+
+def se_chain_append_positions(c, pos_map, seq_len, logical_len, n_new, stream=None):
+    _check("se_chain_append_positions", load().se_chain_append_positions(
+        ctypes.byref(c), _ptr(pos_map), _ptr(seq_len), _ptr(logical_len), n_new, _stream(stream)))
 
 
 def se_pyramid_budgets(n_layers, avg_budget, min_budget):

@@ -266,6 +266,43 @@ se_status se_streaming_view(const se_cache* c, const int32_t* seq_len, int32_t s
   return launch_streaming_view(*c, seq_len, sink, recent, view_idx, view_len, view_cap, stream);
 }
 
+se_status se_chain_match(const int32_t* tokens, int32_t n_tokens, const int32_t* const* prefixes,
+                         const int32_t* prefix_lens, int32_t n_prefixes, int32_t* session, int32_t* matched_len) {
+  if (!session || !matched_len) return SE_ERR_NULL;
+  if (n_tokens < 0 || n_prefixes < 0) return SE_ERR_SHAPE;
+  if ((n_tokens > 0 && !tokens) || (n_prefixes > 0 && (!prefixes || !prefix_lens))) return SE_ERR_NULL;
+  for (int s = 0; s < n_prefixes; ++s) {
+    if (prefix_lens[s] < 0) return SE_ERR_SHAPE;
+    if (prefix_lens[s] > 0 && !prefixes[s]) return SE_ERR_NULL;
+  }
+  chain_match(tokens, n_tokens, prefixes, prefix_lens, n_prefixes, session, matched_len);
+  return SE_OK;
+}
+
+se_status se_chain_remap(const se_cache* c_out, const int32_t* map_in, int32_t cap_in, const int32_t* kept,
+                         int32_t kept_stride, const int32_t* kept_len, int32_t* map_out, hipStream_t stream) {
+  se_status st = check_cache(c_out);
+  if (st != SE_OK) return st;
+  if (!kept || !kept_len || !map_out) return SE_ERR_NULL;
+  if (kept_stride < 1 || (map_in && cap_in < 1)) return SE_ERR_SHAPE;
+  SE_TRACE_CALL("chain_remap B=%d Hkv=%d cap_out=%d stride=%d", c_out->batch, c_out->n_kv_heads, c_out->capacity,
+                kept_stride);
+  clear_stale_error();
+  return launch_chain_remap(*c_out, map_in, map_in ? cap_in : 0x7fffffff, kept, kept_stride, kept_len, map_out,
+                            stream);
+}
+
+se_status se_chain_append_positions(const se_cache* c, int32_t* pos_map, const int32_t* seq_len,
+                                    const int32_t* logical_len, int32_t n_new, hipStream_t stream) {
+  se_status st = check_cache(c);
+  if (st != SE_OK) return st;
+  if (!pos_map || !seq_len || !logical_len) return SE_ERR_NULL;
+  if (n_new < 0) return SE_ERR_SHAPE;
+  if (n_new == 0) return SE_OK;
+  clear_stale_error();
+  return launch_chain_append(*c, pos_map, seq_len, logical_len, n_new, stream);
+}
+
 se_status se_pyramid_budgets(int32_t n_layers, int32_t avg_budget, int32_t min_budget, int32_t* budgets) {
   if (!budgets) return SE_ERR_NULL;
   if (n_layers < 1) return SE_ERR_SHAPE;

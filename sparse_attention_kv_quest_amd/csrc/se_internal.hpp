@@ -415,6 +415,12 @@ size_t quest_append_ws_bytes(const se_cache& c, int page_size);
 se_status launch_streaming_view(const se_cache& c, const int32_t* seq_len, int sink, int recent,
                                 int32_t* view_idx, int32_t* view_len, int view_cap, hipStream_t s);
 void pyramid_budgets(int n, int avg, int bmin, int32_t* out);
+void chain_match(const int32_t* tokens, int n_tokens, const int32_t* const* prefixes, const int32_t* lens,
+                 int n_prefixes, int32_t* session, int32_t* matched);
+se_status launch_chain_remap(const se_cache& c, const int32_t* map_in, int cap_in, const int32_t* kept,
+                             int kept_stride, const int32_t* kept_len, int32_t* map_out, hipStream_t s);
+se_status launch_chain_append(const se_cache& c, int32_t* pos_map, const int32_t* seq_len, const int32_t* logical_len,
+                              int n_new, hipStream_t s);
 se_status launch_quest_append(const se_cache& c, const void* q, void* k, void* v, const void* k_new,
                               const void* v_new, int32_t* seq_len, void* kmin, void* kmax, int page_size,
                               int top_pages, int32_t* view_idx, int32_t* view_len, float* page_score, void* ws,
