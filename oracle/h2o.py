@@ -63,3 +63,40 @@ def h2o_step(Kslots, Vslots, slot_pos, acc, n_slots, free_slot, qg, k_new, v_new
     slot_pos, acc, ev = h2o_accumulate_evict(logits, lse, slot_pos, acc, n_slots, cur_pos, slot, heavy, recent,
                                              gap_out)
     return out, lse, slot_pos, acc, n_slots, ev
+
+
+def prefill_scores(qg, Kt, L, scale):
+    """H2O scores after a prefill of L tokens, one unit: qg [G][L][D] (every prompt
+    query of the group's heads), Kt [>=L][D].  acc0[j] = sum over heads and over the
+    queries i >= j of the causal softmax weight of key j (float64, [L]).
+
+    [tokendh] sections "历史太长,会撑爆什么" / "把边界划在'生命周期'上": H2O's table
+    accumulates the attention every token receives; at the end of the prefill that
+    is the attention of every prompt query (reading: causal, summed over the
+    group's heads, all prompt queries included)."""
+    qg = np.asarray(qg, np.float64)
+    Kt = np.asarray(Kt, np.float64)[:L]
+    acc = np.zeros(L)
+    for h in range(qg.shape[0]):
+        S = scale * (qg[h, :L] @ Kt.T)                     # [L queries][L keys]
+        S[np.triu_indices(L, 1)] = -np.inf                 # causal: key <= query
+        m = S.max(axis=1, keepdims=True)
+        P = np.exp(S - m)
+        P /= P.sum(axis=1, keepdims=True)
+        acc += P.sum(axis=0)
+    return acc
+
+
+def prefill_state(acc0, L, heavy, recent, cap):
+    """Slot state after the prefill (reading: the SnapKV-style keep rule on the scores,
+    no pooling): the `heavy` best positions below L - recent (ties to the lower
+    position) and the recent window, ascending, in slots 0..; slot_pos -1 and score 0
+    for the remaining slots.  Returns (kept positions, slot_pos [cap], acc [cap])."""
+    from .snapkv import snapkv_keep
+    kept = snapkv_keep(np.asarray(acc0[:L - recent], np.float64), L, recent, heavy + recent)
+    slot_pos = np.full(cap, -1, np.int64)
+    acc = np.zeros(cap)
+    slot_pos[:len(kept)] = kept
+    acc[:len(kept)] = np.asarray(acc0, np.float64)[kept]
+    return kept, slot_pos, acc
+
