@@ -89,7 +89,8 @@ typedef enum {
   SE_OP_ATTN = 2,       /* a0 = view_cap * granularity (slots per unit), a1 = num_splits (0 = auto) */
   SE_OP_SNAPKV = 3,     /* a0 = prompt_len, a1 = window */
   SE_OP_OMNIKV = 4,     /* a0 = logit_cap, a1 = top_k */
-  SE_OP_QUEST_APPEND = 5  /* a0 = page_size (a1 unused) */
+  SE_OP_QUEST_APPEND = 5, /* a0 = page_size (a1 unused) */
+  SE_OP_H2O_PREFILL = 6   /* a0 = prompt_len, a1 = recent_window */
 } se_op;
 
 /* Append one decode token's K/V row to every unit (helper of the hooks: the
@@ -321,6 +322,26 @@ se_status se_h2o_accumulate_evict(const se_cache* c, const float* logits, const 
                                   int32_t logit_cap, const int32_t* seq_len, int32_t* slot_pos,
                                   float* acc, int32_t cur_pos, int32_t heavy_budget,
                                   int32_t recent_window, int32_t* evict_slot, hipStream_t stream);
+
+/* H2O state at the end of a prefill (tokendh.com explainer, sections
+ * "历史太长,会撑爆什么" and "把边界划在'生命周期'上": H2O's table accumulates the
+ * attention every token receives).  scores[u][j] = sum over the group's heads
+ * and the prompt queries i >= j of softmax_i(scale q_i . k)[j] (causal), from
+ * q_prompt bf16 [B][Hq][prompt_len][d_k] and the prompt's rows k / v (cache c,
+ * rows below prompt_len).  The kept slots are the heavy_budget best scores
+ * below prompt_len - recent_window (ties to the lower position) and the recent
+ * window, ascending (all positions when they fit): their rows are copied to
+ * k_slots / v_slots (cache `slots`, capacity >= heavy + recent + 1), slot_pos
+ * int32 [B][Hkv][slots.capacity] gets their positions (-1 after them) and acc
+ * float [B][Hkv][slots.capacity] their scores (0 after them) — the state
+ * se_h2o_accumulate_evict continues from.  scores: NULL or float
+ * [B][Hkv][prompt_len].  bf16, d_k 64 / 128, G <= 16.
+ * ws: se_workspace_bytes(SE_OP_H2O_PREFILL, c, prompt_len, recent_window) bytes,
+ * zero-filled once before first use (its selection counters return to zero). */
+se_status se_h2o_prefill_init(const se_cache* c, const void* q_prompt, const void* k, const void* v,
+                              int32_t prompt_len, int32_t heavy_budget, int32_t recent_window, float scale,
+                              const se_cache* slots, void* k_slots, void* v_slots, int32_t* slot_pos, float* acc,
+                              float* scores, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* OmniKV filter-layer top-k.  tokendh.com explainer, section
  * "把边界划在'生命周期'上": some layers judge which history matters and later

@@ -16,14 +16,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libse.so")
 
 SE_F32, SE_BF16 = 0, 1
-SE_OP_QUEST, SE_OP_ATTN, SE_OP_SNAPKV, SE_OP_OMNIKV, SE_OP_QUEST_APPEND = 1, 2, 3, 4, 5
+SE_OP_QUEST, SE_OP_ATTN, SE_OP_SNAPKV, SE_OP_OMNIKV, SE_OP_QUEST_APPEND, SE_OP_H2O_PREFILL = 1, 2, 3, 4, 5, 6
 STATUS = {0: "SE_OK", -1: "SE_ERR_NULL", -2: "SE_ERR_SHAPE", -3: "SE_ERR_DTYPE", -4: "SE_ERR_ALIGN",
           -5: "SE_ERR_BUDGET", -6: "SE_ERR_WORKSPACE", -7: "SE_ERR_UNSUPPORTED", -8: "SE_ERR_HIP"}
 
 EXPORTS = ("se_kv_append", "se_kv_append_meta", "se_page_meta_update", "se_quest_select", "se_quest_append_select",
            "se_sparse_decode_attn", "se_streaming_view", "se_pyramid_budgets",
            "se_kv_quantize_fp8", "se_kv_append_fp8", "se_sparse_decode_attn_fp8",
-           "se_chain_match", "se_chain_remap", "se_chain_append_positions",
+           "se_chain_match", "se_chain_remap", "se_chain_append_positions", "se_h2o_prefill_init",
            "se_snapkv_score_compact", "se_h2o_accumulate_evict", "se_omnikv_topk",
            "se_workspace_bytes", "se_workspace_init", "se_status_string", "se_abi_version")
 
@@ -59,6 +59,7 @@ _SIGS = {
     "se_chain_match": [_P, _I32, _P, _P, _I32, _P, _P],
     "se_chain_remap": [_C, _P, _I32, _P, _I32, _P, _P, _P],
     "se_chain_append_positions": [_C, _P, _P, _P, _I32, _P],
+    "se_h2o_prefill_init": [_C, _P, _P, _P, _I32, _I32, _I32, _F32, _C, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "se_snapkv_score_compact": [_C, _P, _P, _P, _I32, _I32, _I32, _I32, _F32, _C, _P, _P, _P, _P, _P, _P, _SZ,
                                 _P],
     "se_h2o_accumulate_evict": [_C, _P, _P, _I32, _P, _P, _P, _I32, _I32, _I32, _P, _P],
@@ -206,6 +207,13 @@ def se_sparse_decode_attn_fp8(c, q, k_q, v_q, k_scale, v_scale, seq_len, view_id
 def se_streaming_view(c, seq_len, sink, recent, view_idx, view_len, stream=None):
     _check("se_streaming_view", load().se_streaming_view(ctypes.byref(c), _ptr(seq_len), sink, recent, _ptr(view_idx),
                                                          _ptr(view_len), view_idx.shape[-1], _stream(stream)))
+
+
+def se_h2o_prefill_init(c, q_prompt, k, v, prompt_len, heavy, recent, scale, slots, k_slots, v_slots, slot_pos, acc,
+                        scores=None, ws=None, stream=None):
+    _check("se_h2o_prefill_init", load().se_h2o_prefill_init(
+        ctypes.byref(c), _ptr(q_prompt), _ptr(k), _ptr(v), prompt_len, heavy, recent, scale, ctypes.byref(slots),
+        _ptr(k_slots), _ptr(v_slots), _ptr(slot_pos), _ptr(acc), _ptr(scores), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def se_chain_match(tokens, prefixes):

@@ -100,6 +100,7 @@ size_t se_workspace_bytes(int32_t op, const se_cache* c, int32_t a0, int32_t a1)
     case SE_OP_SNAPKV: return (a0 > a1 && a1 > 0) ? snapkv_ws_bytes(*c, a0, a1) : 0;
     case SE_OP_OMNIKV: return a0 > 0 ? omnikv_ws_bytes(*c, a0, a1) : 0;
     case SE_OP_QUEST_APPEND: return a0 > 0 ? quest_append_ws_bytes(*c, a0) : 0;
+    case SE_OP_H2O_PREFILL: return (a0 > a1 && a1 > 0) ? h2o_prefill_ws_bytes(*c, a0, a1) : 0;
     default: return 0;
   }
 }
@@ -372,6 +373,36 @@ se_status se_h2o_accumulate_evict(const se_cache* c, const float* logits, const 
   clear_stale_error();
   return launch_h2o(*c, logits, lse, logit_cap, seq_len, slot_pos, acc, cur_pos, heavy_budget, recent_window,
                     evict_slot, stream);
+}
+
+se_status se_h2o_prefill_init(const se_cache* c, const void* q_prompt, const void* k, const void* v,
+                              int32_t prompt_len, int32_t heavy_budget, int32_t recent_window, float scale,
+                              const se_cache* slots, void* k_slots, void* v_slots, int32_t* slot_pos, float* acc,
+                              float* scores, void* ws, size_t ws_bytes, hipStream_t stream) {
+  se_status st = check_cache(c);
+  if (st != SE_OK) return st;
+  st = check_cache(slots);
+  if (st != SE_OK) return st;
+  if (!q_prompt || !k || !v || !k_slots || !v_slots || !slot_pos || !acc || !ws) return SE_ERR_NULL;
+  if (!aligned16(q_prompt) || !aligned16(k) || !aligned16(v) || !aligned16(k_slots) || !aligned16(v_slots) ||
+      !aligned16(ws))
+    return SE_ERR_ALIGN;
+  if (c->dtype != SE_BF16) return SE_ERR_DTYPE;
+  if (c->latent || (c->d_k != 64 && c->d_k != 128) || c->n_q_heads / c->n_kv_heads > 16) return SE_ERR_UNSUPPORTED;
+  if (slots->batch != c->batch || slots->n_q_heads != c->n_q_heads || slots->n_kv_heads != c->n_kv_heads ||
+      slots->d_k != c->d_k || slots->d_v != c->d_v || slots->dtype != c->dtype || slots->latent != c->latent)
+    return SE_ERR_SHAPE;
+  if (prompt_len < 2 || prompt_len > c->capacity) return SE_ERR_SHAPE;
+  if (recent_window < 1 || recent_window >= prompt_len || heavy_budget < 1 ||
+      int64_t(heavy_budget) + recent_window + 1 > slots->capacity)
+    return SE_ERR_BUDGET;
+  if (!(scale > 0.f) || !(scale < 1e30f)) return SE_ERR_SHAPE;
+  if (ws_bytes < h2o_prefill_ws_bytes(*c, prompt_len, recent_window)) return SE_ERR_WORKSPACE;
+  SE_TRACE_CALL("h2o_prefill_init B=%d Hq=%d Hkv=%d d_k=%d L=%d heavy=%d recent=%d", c->batch, c->n_q_heads,
+                c->n_kv_heads, c->d_k, prompt_len, heavy_budget, recent_window);
+  clear_stale_error();
+  return launch_h2o_prefill(*c, q_prompt, k, v, prompt_len, heavy_budget, recent_window, scale, *slots, k_slots,
+                            v_slots, slot_pos, acc, scores, ws, stream);
 }
 
 se_status se_omnikv_topk(const se_cache* c, const float* logits, const float* lse, int32_t logit_cap,

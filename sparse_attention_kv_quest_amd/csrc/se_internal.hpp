@@ -415,6 +415,14 @@ size_t quest_append_ws_bytes(const se_cache& c, int page_size);
 se_status launch_streaming_view(const se_cache& c, const int32_t* seq_len, int sink, int recent,
                                 int32_t* view_idx, int32_t* view_len, int view_cap, hipStream_t s);
 void pyramid_budgets(int n, int avg, int bmin, int32_t* out);
+se_status launch_h2o_prefill_scores(const se_cache& c, const void* q, const void* k, int L, int n_cand, float scale,
+                                    float* lse2, float* acc0, float* votes, hipStream_t s);
+se_status launch_h2o_state(const se_cache& c_slots, const int32_t* kept, int kept_stride, const int32_t* kept_len,
+                           const float* acc0, int L, int32_t* slot_pos, float* acc, hipStream_t s);
+size_t h2o_prefill_ws_bytes(const se_cache& c, int L, int recent);
+se_status launch_h2o_prefill(const se_cache& c, const void* q, const void* k, const void* v, int L, int heavy,
+                             int recent, float scale, const se_cache& slots, void* k_slots, void* v_slots,
+                             int32_t* slot_pos, float* acc, float* scores_out, void* ws, hipStream_t s);
 void chain_match(const int32_t* tokens, int n_tokens, const int32_t* const* prefixes, const int32_t* lens,
                  int n_prefixes, int32_t* session, int32_t* matched);
 se_status launch_chain_remap(const se_cache& c, const int32_t* map_in, int cap_in, const int32_t* kept,

@@ -494,6 +494,28 @@ size_t snapkv_ws_bytes(const se_cache& c, int prompt_len, int window) {
   return sel_bytes(units, int(n)) + units * (size_t(snap_chunks(prompt_len)) * R * 2 + R + 2 * n) * sizeof(float);
 }
 
+// The keep rule and the compaction, from the scores in a.votes: max-pool, top
+// (budget - W) of the L - W candidates plus the window, ascending, then the kept
+// rows gathered into k_out / v_out.
+static se_status snap_keep_compact(const SnapArgs& a, const se_cache& c, hipStream_t s) {
+  const size_t units = size_t(a.B) * a.Hkv, n = size_t(a.L - a.W);
+  hipLaunchKernelGGL(snap_pool_kernel, dim3(ceil_div(int(n), SK_POOL_T), int(units)), dim3(256), 0, s, a);
+  const int kk = std::min(a.budget - a.W, int(n));
+  const dim3 sgrid(sel_slices(int(n)), int(units));
+  for (int pass = 0; pass < 3; ++pass) {
+    hipLaunchKernelGGL(snap_sel_hist_kernel, sgrid, dim3(SK_SEL_BLOCK), 0, s, a, pass);
+    hipLaunchKernelGGL(snap_sel_find_kernel, dim3(int(units)), dim3(SK_SEL_BLOCK), 0, s, a, pass, kk);
+  }
+  hipLaunchKernelGGL(snap_sel_count_kernel, sgrid, dim3(SK_SEL_BLOCK), 0, s, a, kk);
+  hipLaunchKernelGGL(snap_sel_write_kernel, sgrid, dim3(SK_SEL_BLOCK), 0, s, a);
+  const int esz = c.dtype == SE_F32 ? 4 : 2;
+  const int row_words = c.d_k * esz / 16;
+  const int rows_per_block = 256 / row_words;
+  hipLaunchKernelGGL(snap_gather_kernel, dim3(ceil_div(std::min(a.budget, a.L), rows_per_block), int(units)),
+                     dim3(256), 0, s, a, row_words);
+  return launch_status();
+}
+
 se_status launch_snapkv(const se_cache& c, const void* q_obs, const void* k, const void* v, int prompt_len,
                         int window, int pool_kernel, int budget, float scale, const se_cache& out, void* k_out,
                         void* v_out, int32_t* kept_pos, float* votes, int32_t* out_seq_len, void* ws,
@@ -545,21 +567,56 @@ se_status launch_snapkv(const se_cache& c, const void* q_obs, const void* k, con
     }
   }
   if (hipGetLastError() != hipSuccess) return SE_ERR_HIP;
-  hipLaunchKernelGGL(snap_pool_kernel, dim3(ceil_div(int(n), SK_POOL_T), int(units)), dim3(256), 0, s, a);
-  const int kk = std::min(budget - window, int(n));
-  const dim3 sgrid(sel_slices(int(n)), int(units));
-  for (int pass = 0; pass < 3; ++pass) {
-    hipLaunchKernelGGL(snap_sel_hist_kernel, sgrid, dim3(SK_SEL_BLOCK), 0, s, a, pass);
-    hipLaunchKernelGGL(snap_sel_find_kernel, dim3(int(units)), dim3(SK_SEL_BLOCK), 0, s, a, pass, kk);
-  }
-  hipLaunchKernelGGL(snap_sel_count_kernel, sgrid, dim3(SK_SEL_BLOCK), 0, s, a, kk);
-  hipLaunchKernelGGL(snap_sel_write_kernel, sgrid, dim3(SK_SEL_BLOCK), 0, s, a);
-  const int esz = c.dtype == SE_F32 ? 4 : 2;
-  const int row_words = c.d_k * esz / 16;
-  const int rows_per_block = 256 / row_words;
-  hipLaunchKernelGGL(snap_gather_kernel, dim3(ceil_div(std::min(budget, prompt_len), rows_per_block), int(units)),
-                     dim3(256), 0, s, a, row_words);
-  return launch_status();
+  return snap_keep_compact(a, c, s);
+}
+
+// H2O state at the end of a prefill: scores (two MFMA passes), the keep rule on
+// them with no pooling (the heavy best below L - recent, plus the recent window),
+// the kept rows gathered into the slot cache, and the slots' positions / scores.
+static size_t h2o_prefill_layout(const se_cache& c, int L, int recent, size_t* off) {
+  const size_t units = size_t(c.batch) * c.n_kv_heads, G = c.n_q_heads / c.n_kv_heads;
+  const size_t n = size_t(L - recent), budget = size_t(L);   // kept rows per unit: at most L
+  size_t o = sel_bytes(units, int(n));
+  off[0] = o; o += units * n * sizeof(float);                 // pooled
+  off[1] = o; o += units * n * sizeof(float);                 // candidate scores (votes)
+  off[2] = o; o += (units * budget * sizeof(int32_t) + 15) / 16 * 16;   // kept positions
+  off[3] = o; o += (size_t(c.batch) * sizeof(int32_t) + 15) / 16 * 16;  // kept counts
+  off[4] = o; o += units * G * size_t(L) * sizeof(float);     // row log2-sum-exp2
+  off[5] = o; o += units * size_t(L) * sizeof(float);         // scores of every key
+  return o;
+}
+
+size_t h2o_prefill_ws_bytes(const se_cache& c, int L, int recent) {
+  size_t off[6];
+  return h2o_prefill_layout(c, L, recent, off);
+}
+
+se_status launch_h2o_prefill(const se_cache& c, const void* q, const void* k, const void* v, int L, int heavy,
+                             int recent, float scale, const se_cache& slots, void* k_slots, void* v_slots,
+                             int32_t* slot_pos, float* acc, float* scores_out, void* ws, hipStream_t s) {
+  size_t off[6];
+  h2o_prefill_layout(c, L, recent, off);
+  char* w = (char*)ws;
+  float* acc0 = scores_out ? scores_out : (float*)(w + off[5]);
+  se_status st = launch_h2o_prefill_scores(c, q, k, L, L - recent, scale, (float*)(w + off[4]), acc0,
+                                           (float*)(w + off[1]), s);
+  if (st != SE_OK) return st;
+  SnapArgs a{};
+  a.k = k; a.v = v; a.k_out = k_slots; a.v_out = v_slots;
+  a.B = c.batch; a.Hq = c.n_q_heads; a.Hkv = c.n_kv_heads; a.G = c.n_q_heads / c.n_kv_heads; a.D = c.d_k;
+  a.cap = c.capacity; a.out_cap = slots.capacity; a.L = L; a.W = recent; a.R = 0; a.pool = 1;
+  a.budget = std::min(heavy + recent, L); a.nchunks = 0; a.dtype = c.dtype; a.sc2 = 0.f;
+  a.sel_hist = (uint32_t*)ws;
+  const size_t units = size_t(a.B) * a.Hkv;
+  a.sel_state = (SelState*)(a.sel_hist + units * SK_SEL_BINS);
+  a.sel_counts = (int32_t*)(a.sel_state + units);
+  a.pooled = (float*)(w + off[0]);
+  a.votes = (float*)(w + off[1]);
+  a.kept = (int32_t*)(w + off[2]);
+  a.out_len = (int32_t*)(w + off[3]);
+  st = snap_keep_compact(a, c, s);
+  if (st != SE_OK) return st;
+  return launch_h2o_state(slots, a.kept, a.budget, a.out_len, acc0, L, slot_pos, acc, s);
 }
 
 }  // namespace se
