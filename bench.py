@@ -14,7 +14,9 @@ The other workloads are timed the same way and reported under "workloads":
                tokens (timed per call), then decode steps over the compacted
                cache (append + attention);
   h2o_16k      H2O decode steps (append into the freed slot, attention with
-               logits, accumulate + evict) over 1024 heavy + 256 recent slots;
+               logits, accumulate + evict) over 1024 heavy + 256 recent slots,
+               and the prefill-end initialisation (scores of every prompt key
+               over the full causal prefill, heavy + recent kept slots);
   omnikv_16k   48-layer OmniKV sweeps (dense layers 0-1, filter layers 2/8/16
                with top-2048 selection, 43 layers over the reused views);
   streaming_32k StreamingLLM decode steps on the Quest 32K shape: append, the
@@ -377,9 +379,41 @@ def run_h2o(se, torch, args):
     step_bytes = B * H * cap * (2 * D * 2 + 2 * G * 4 + 4 * 3) + B * Hq * D * (2 + 4)
     del lay, t_s
     free(torch)
+    pre = h2o_prefill_timing(se, torch, cfg, c)
     return {"workload": "h2o_16k", "batch": B, "heavy": heavy, "recent": recent,
             "tokens_per_s": round(B / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 5), "steps": steps,
-            "step_algorithmic_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1)}
+            "step_algorithmic_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1), "prefill_init": pre}
+
+
+def h2o_prefill_timing(se, torch, cfg, slots):
+    """se_h2o_prefill_init on the full prompt (every prompt query of every head): its
+    time, prompt tokens/s and the MFMA rate of its two causal passes."""
+    B, H, Hq, D, L = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.d_k, cfg.context
+    heavy, recent = cfg.h2o_heavy, cfg.h2o_recent
+    c = se.cache(B, Hq, H, D, D, L, "bf16")
+    qp = dev_grid(torch, (B, Hq, L, D), 33, torch.bfloat16)
+    kp = dev_grid(torch, (B, H, L, D), 34, torch.bfloat16)
+    vp = dev_grid(torch, (B, H, L, D), 35, torch.bfloat16)
+    cap = slots.capacity
+    k_s = torch.empty((B, H, cap, D), dtype=torch.bfloat16, device="cuda")
+    v_s = torch.empty_like(k_s)
+    pos = torch.empty((B, H, cap), dtype=torch.int32, device="cuda")
+    acc = torch.empty((B, H, cap), device="cuda")
+    ws = se.workspace(se.SE_OP_H2O_PREFILL, c, L, recent)
+
+    def call():
+        se.se_h2o_prefill_init(c, qp, kp, vp, L, heavy, recent, cfg.softmax_scale, slots, k_s, v_s, pos, acc, None, ws)
+
+    call()
+    torch.cuda.synchronize()
+    t = Timer(torch, call, False)
+    ms = t.ms_per_replay(2)
+    flops = 2 * 2 * B * Hq * (L * (L + 1) / 2) * D        # q.k over the causal half, in each of the two passes
+    del qp, kp, vp, k_s, v_s, ws, t
+    free(torch)
+    return {"ms_per_call": round(ms, 3), "prompt_tokens_per_s": round(B * L / (ms * 1e-3), 1),
+            "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
+            "frac_of_mfma_peak": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
 # ---------------------------------------------------------------- OmniKV 16K, 48 layers

@@ -335,7 +335,8 @@ se_status se_h2o_accumulate_evict(const se_cache* c, const float* logits, const 
  * int32 [B][Hkv][slots.capacity] gets their positions (-1 after them) and acc
  * float [B][Hkv][slots.capacity] their scores (0 after them) — the state
  * se_h2o_accumulate_evict continues from.  scores: NULL or float
- * [B][Hkv][prompt_len].  bf16, d_k 64 / 128, G <= 16.
+ * [B][Hkv][prompt_len].  bf16, d_k 64 / 128, G <= 16, prompt_len * G <= 2^30
+ * (SE_ERR_SHAPE beyond).
  * ws: se_workspace_bytes(SE_OP_H2O_PREFILL, c, prompt_len, recent_window) bytes,
  * zero-filled once before first use (its selection counters return to zero). */
 se_status se_h2o_prefill_init(const se_cache* c, const void* q_prompt, const void* k, const void* v,

@@ -393,6 +393,7 @@ se_status se_h2o_prefill_init(const se_cache* c, const void* q_prompt, const voi
       slots->d_k != c->d_k || slots->d_v != c->d_v || slots->dtype != c->dtype || slots->latent != c->latent)
     return SE_ERR_SHAPE;
   if (prompt_len < 2 || prompt_len > c->capacity) return SE_ERR_SHAPE;
+  if (int64_t(prompt_len) * (c->n_q_heads / c->n_kv_heads) > (int64_t(1) << 30)) return SE_ERR_SHAPE;   // query rows index in int
   if (recent_window < 1 || recent_window >= prompt_len || heavy_budget < 1 ||
       int64_t(heavy_budget) + recent_window + 1 > slots->capacity)
     return SE_ERR_BUDGET;

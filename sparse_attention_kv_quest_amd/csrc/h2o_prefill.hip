@@ -8,10 +8,10 @@
 // the causal half of the (query, key) square:
 //   A: per (head, query) row, the log2-sum-exp2 of sc2 * q . k over keys <= i;
 //   B: per key, the sum of exp2(sc2 * q . k - lse2) over the later queries.
-// Both use S^T[key][head] = K . Q^T with the group's heads (G <= 16) in the MFMA
-// N dimension: A = 16 key rows (lane: key c16, dims 32c + 8g ..), B = one
-// position's queries (lane: head c16, the same dims).  K tiles (pass A) and Q
-// tiles (pass B) go through double-buffered LDS shared by the block's 8 waves.
+// Both compute S^T[key][row] = K . Q^T on 16x16x32 MFMA: A = 16 keys (lane: key
+// c16, dims 32c + 8g ..), B = 16 consecutive (position, head) query rows (lane:
+// row c16, the same dims).  K tiles (pass A) and Q tiles (pass B) go through
+// double-buffered LDS shared by the block's 8 waves.
 // The kept set then follows the SnapKV keep rule on acc0 (no pooling).
 #include "se_internal.hpp"
 #include "mfma_util.hpp"
@@ -19,115 +19,153 @@
 namespace se {
 
 constexpr int HP_WAVES = 8;
-constexpr int HP_PPW = 8;                       // pass A: query positions per wave
-constexpr int HP_POS = HP_WAVES * HP_PPW;       // pass A: 64 positions per block
-constexpr int HP_KT = 32;                       // pass A: keys per K tile
+constexpr int HP_NG = 8;                        // pass A: 16-row groups per wave
+constexpr int HP_RPW = HP_NG * 16;              // pass A: (position, head) rows per wave
+constexpr int HP_ROWS = HP_WAVES * HP_RPW;      // pass A: 1024 rows per block
+constexpr int HP_KT = 64;                       // pass A: keys per K tile
 constexpr int HP_KB = 4;                        // pass B: 16-key blocks per wave
 constexpr int HP_KEYS = HP_WAVES * HP_KB * 16;  // pass B: 512 keys per block
-constexpr int HP_QT = 8;                        // pass B: positions per Q tile
+constexpr int HP_QR = 128;                      // pass B: (position, head) rows per Q tile
+constexpr float HP_MARGIN = 8.f;                // pass A: log2 headroom before the running max moves
 
 struct HpArgs {
   const uint16_t* q;    // [B][Hq][L][D] every prompt query
   const uint16_t* k;    // [B][Hkv][cap][D]
-  float* lse2;          // [units][G][L]
+  float* lse2;          // [units][L * G], row r = position r / G, head r % G
   float* acc0;          // [units][L]
   float* votes;         // [units][L - recent]: acc0 of the candidates of the keep rule
   int Hq, Hkv, G, cap, L, n_cand;
   float sc2;            // scale * log2(e)
 };
 
+// v_exp_f32 as it stands: results below 2^-126 come out as zero.  Every sum here
+// holds a term >= 1 (pass A) or is a probability sum compared at 1e-6 absolute,
+// so terms that small do not change a result.
+__device__ __forceinline__ float hp_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// The group's queries are taken as L * G rows (position-major, head-minor) and go
+// sixteen at a time into the MFMA N dimension, so no column is spent on padding
+// whatever G is.
+
 template <int D>
 __global__ __launch_bounds__(512) void hp_rowlse_kernel(HpArgs a) {
   constexpr int NKS = D / 32, PITCH = D + 8, CH = D / 8;   // CH 16-byte chunks per row
+  constexpr int TPT = HP_KT * CH / 512;                     // K tile chunks per thread
   __shared__ __align__(16) uint16_t kt[2][HP_KT][PITCH];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
+  const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int unit = blockIdx.y, b = unit / a.Hkv, kvh = unit % a.Hkv;
-  const int L = a.L, p_blk = blockIdx.x * HP_POS;
-  if (p_blk >= L) return;                              // uniform per block
-  const int p_w = p_blk + w * HP_PPW;
+  const int L = a.L, G = a.G, nrows = L * G;
+  const int r_blk = blockIdx.x * HP_ROWS;
+  if (r_blk >= nrows) return;                          // uniform per block
+  const int r_w = r_blk + w * HP_RPW;
   const uint16_t* ku = a.k + size_t(unit) * a.cap * D;
-  u32x4 qv[HP_PPW][NKS];
+  const uint16_t* qu = a.q + (size_t(b) * a.Hq + size_t(kvh) * G) * size_t(L) * D;
+  u32x4 qv[HP_NG][NKS];
+  int lpos[HP_NG], pmin[HP_NG], pmax[HP_NG];
 #pragma unroll
-  for (int pp = 0; pp < HP_PPW; ++pp) {
-    const bool ok = c16 < a.G && p_w + pp < L;
-    const uint16_t* qp = a.q + ((size_t(b) * a.Hq + size_t(kvh) * a.G + (ok ? c16 : 0)) * L + (ok ? p_w + pp : 0)) * D;
+  for (int j = 0; j < HP_NG; ++j) {
+    const int r = r_w + 16 * j + c16;
+    const bool ok = r < nrows;
+    lpos[j] = r / G;
+    pmin[j] = (r_w + 16 * j) / G;                      // wave-uniform bounds of the group's positions
+    pmax[j] = (r_w + 16 * j + 15) / G;
+    const uint16_t* qp = qu + (ok ? (size_t(r % G) * L + r / G) * D : 0);
 #pragma unroll
-    for (int c = 0; c < NKS; ++c) qv[pp][c] = ok ? ld16(qp + 8 * g + 32 * c) : u32x4{0, 0, 0, 0};
+    for (int c = 0; c < NKS; ++c) qv[j][c] = ok ? ld16(qp + 8 * g + 32 * c) : u32x4{0, 0, 0, 0};
   }
-  float m[HP_PPW], l[HP_PPW];
+  float m[HP_NG], l[HP_NG];
 #pragma unroll
-  for (int pp = 0; pp < HP_PPW; ++pp) { m[pp] = -INFINITY; l[pp] = 0.f; }
-  const int ntiles = (min(L, p_blk + HP_POS) - 1) / HP_KT + 1;   // keys up to the block's last position
-  // one 16-byte chunk of the tile per thread (threads past the tile idle)
-  const int lk = threadIdx.x / CH, lc = threadIdx.x % CH;
-  const bool loader = lk < HP_KT;
-  auto fetch = [&](int t) -> u32x4 {
-    const int key = min(t * HP_KT + lk, L - 1);
-    return ld16(ku + size_t(key) * D + 8 * lc);
+  for (int j = 0; j < HP_NG; ++j) { m[j] = -INFINITY; l[j] = 0.f; }
+  const int last_pos = (min(nrows, r_blk + HP_ROWS) - 1) / G;
+  const int ntiles = last_pos / HP_KT + 1;             // keys up to the block's last position
+  u32x4 stage[TPT];
+  auto fetch = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      const int e = threadIdx.x + 512 * i;
+      const int key = min(t * HP_KT + e / CH, L - 1);
+      stage[i] = ld16(ku + size_t(key) * D + 8 * (e % CH));
+    }
   };
-  if (loader) *reinterpret_cast<u32x4*>(&kt[0][lk][8 * lc]) = fetch(0);
+  auto put = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      const int e = threadIdx.x + 512 * i;
+      *reinterpret_cast<u32x4*>(&kt[buf][e / CH][8 * (e % CH)]) = stage[i];
+    }
+  };
+  fetch(0);
+  put(0);
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
-    u32x4 nxt = {0, 0, 0, 0};
-    if (loader && t + 1 < ntiles) nxt = fetch(t + 1);
+    if (t + 1 < ntiles) fetch(t + 1);
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
+    for (int sb = 0; sb < HP_KT / 16; ++sb) {
+      const int key0 = t * HP_KT + 16 * sb;
+      if (key0 > pmax[HP_NG - 1]) break;               // later than every position of the wave
       u32x4 ak[NKS];
 #pragma unroll
-      for (int c = 0; c < NKS; ++c) ak[c] = *reinterpret_cast<const u32x4*>(&kt[buf][hf * 16 + c16][8 * g + 32 * c]);
-      const int kbase = t * HP_KT + hf * 16 + 4 * g;
+      for (int c = 0; c < NKS; ++c) ak[c] = *reinterpret_cast<const u32x4*>(&kt[buf][16 * sb + c16][8 * g + 32 * c]);
+      const int kbase = key0 + 4 * g;
 #pragma unroll
-      for (int pp = 0; pp < HP_PPW; ++pp) {
-        const int pos = p_w + pp;
+      for (int j = 0; j < HP_NG; ++j) {
+        if (key0 > pmax[j]) continue;                  // every key of the block comes later
         f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NKS; ++c) s = mfma_bf16_16x16x32(ak[c], qv[pp][c], s);
-        float v[4], hm = -INFINITY;
+        for (int c = 0; c < NKS; ++c) s = mfma_bf16_16x16x32(ak[c], qv[j][c], s);
+        float v[4];
+        if (key0 + 15 <= pmin[j]) {                    // the whole block is causal for the group
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          v[ii] = kbase + ii <= pos ? s[ii] * a.sc2 : -INFINITY;   // causal (pos < L implies key < L)
-          hm = fmaxf(hm, v[ii]);
-        }
-        hm = fmaxf(hm, __shfl_xor(hm, 16, 64));
-        hm = fmaxf(hm, __shfl_xor(hm, 32, 64));
-        if (hm > m[pp]) {
-          l[pp] = m[pp] == -INFINITY ? 0.f : l[pp] * exp2f(m[pp] - hm);
-          m[pp] = hm;
-        }
-        if (m[pp] != -INFINITY) {
+          for (int ii = 0; ii < 4; ++ii) v[ii] = s[ii] * a.sc2;
+        } else {
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii) l[pp] += exp2f(v[ii] - m[pp]);
+          for (int ii = 0; ii < 4; ++ii) v[ii] = kbase + ii <= lpos[j] ? s[ii] * a.sc2 : -INFINITY;
         }
+        // this lane's own keys: running max moved only when exceeded by more than 2^8
+        const float hm = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+        if (hm > m[j] + HP_MARGIN) {
+          l[j] = m[j] == -INFINITY ? 0.f : l[j] * hp_exp2(m[j] - hm);
+          m[j] = hm;
+        }
+        const float mr = m[j] == -INFINITY ? 0.f : m[j];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) l[j] += hp_exp2(v[ii] - mr);
       }
     }
-    if (loader && t + 1 < ntiles) *reinterpret_cast<u32x4*>(&kt[buf ^ 1][lk][8 * lc]) = nxt;
+    if (t + 1 < ntiles) put(buf ^ 1);
     __syncthreads();
   }
+  // merge the four lanes of each row: they saw disjoint keys; lanes that saw none
+  // (m = -inf) add nothing, and key 0 makes the row's maximum finite
 #pragma unroll
-  for (int pp = 0; pp < HP_PPW; ++pp) {
-    float lt = l[pp];
+  for (int j = 0; j < HP_NG; ++j) {
+    float mt = fmaxf(m[j], __shfl_xor(m[j], 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    float lt = m[j] == -INFINITY ? 0.f : l[j] * hp_exp2(m[j] - mt);
     lt += __shfl_xor(lt, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
-    const int pos = p_w + pp;
-    if (g == 0 && c16 < a.G && pos < L) a.lse2[(size_t(unit) * a.G + c16) * L + pos] = m[pp] + log2f(lt);
+    const int r = r_w + 16 * j + c16;
+    if (g == 0 && r < nrows) a.lse2[size_t(unit) * nrows + r] = mt + log2f(lt);
   }
 }
 
 template <int D>
 __global__ __launch_bounds__(512) void hp_colsum_kernel(HpArgs a) {
   constexpr int NKS = D / 32, PITCH = D + 8, CH = D / 8;
-  constexpr int TCH = HP_QT * 16 * CH;                  // 16-byte chunks of one Q tile (16 head rows per position)
-  constexpr int TPT = (TCH + 511) / 512;                // chunks per thread
-  __shared__ __align__(16) uint16_t qt[2][HP_QT][16][PITCH];
-  __shared__ float lt[2][HP_QT][16];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
+  constexpr int TPT = HP_QR * CH / 512;                 // Q tile chunks per thread
+  constexpr int NQG = HP_QR / 16;                       // 16-row groups per Q tile
+  __shared__ __align__(16) uint16_t qt[2][HP_QR][PITCH];
+  __shared__ float lt[2][HP_QR];
+  const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int unit = blockIdx.y, b = unit / a.Hkv, kvh = unit % a.Hkv;
-  const int L = a.L, j_blk = blockIdx.x * HP_KEYS;
+  const int L = a.L, G = a.G, nrows = L * G, j_blk = blockIdx.x * HP_KEYS;
   if (j_blk >= L) return;                               // uniform per block
   const uint16_t* ku = a.k + size_t(unit) * a.cap * D;
-  const uint16_t* qu = a.q + (size_t(b) * a.Hq + size_t(kvh) * a.G) * size_t(L) * D;
-  const float* lu = a.lse2 + size_t(unit) * a.G * L;
+  const uint16_t* qu = a.q + (size_t(b) * a.Hq + size_t(kvh) * G) * size_t(L) * D;
+  const float* lu = a.lse2 + size_t(unit) * nrows;
   // this wave's keys: j_w + 16 kb + c16 as A rows
   const int j_w = j_blk + w * HP_KB * 16;
   u32x4 ak[HP_KB][NKS];
@@ -142,65 +180,86 @@ __global__ __launch_bounds__(512) void hp_colsum_kernel(HpArgs a) {
   for (int kb = 0; kb < HP_KB; ++kb)
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) col[kb][ii] = 0.f;
-  const int i_end = L, i_beg = j_blk;                   // queries before the block's first key give it nothing
-  const int ntiles = (i_end - i_beg + HP_QT - 1) / HP_QT;
-  // Q tile chunk e: position e / (16 CH), head (e / CH) % 16, chunk e % CH (zeros for heads >= G or past L)
+  const int r_beg = j_blk * G;                          // rows of earlier positions give the block nothing
+  const int r_full = (j_blk + HP_KEYS) * G;             // rows from here on come after every key of the block
+  const int ntiles = (nrows - r_beg + HP_QR - 1) / HP_QR;
+  // Q tile chunk e: row e / CH, chunk e % CH; rows past the end are zero with lse +inf (weight 0)
   u32x4 stage[TPT];
   float lstage = 0.f;
   auto fetch = [&](int t) {
+    const int r0 = r_beg + t * HP_QR;
 #pragma unroll
-    for (int j = 0; j < TPT; ++j) {
-      const int e = threadIdx.x + 512 * j;
-      const int pp = e / (16 * CH), h = (e / CH) % 16, ch = e % CH;
-      const int pos = i_beg + t * HP_QT + pp;
-      const bool ok = e < TCH && h < a.G && pos < L;
-      stage[j] = ok ? ld16(qu + (size_t(h) * L + pos) * D + 8 * ch) : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < TPT; ++i) {
+      const int e = threadIdx.x + 512 * i;
+      const int r = r0 + e / CH;
+      stage[i] = r < nrows ? ld16(qu + (size_t(r % G) * L + r / G) * D + 8 * (e % CH)) : u32x4{0, 0, 0, 0};
     }
-    if (threadIdx.x < HP_QT * 16) {
-      const int pp = threadIdx.x / 16, h = threadIdx.x % 16, pos = i_beg + t * HP_QT + pp;
-      lstage = (h < a.G && pos < L) ? lu[size_t(h) * L + pos] : 0.f;
-    }
+    if (threadIdx.x < HP_QR) lstage = r0 + int(threadIdx.x) < nrows ? lu[r0 + threadIdx.x] : INFINITY;
   };
   auto put = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < TPT; ++j) {
-      const int e = threadIdx.x + 512 * j;
-      if (e < TCH) *reinterpret_cast<u32x4*>(&qt[buf][e / (16 * CH)][(e / CH) % 16][8 * (e % CH)]) = stage[j];
+    for (int i = 0; i < TPT; ++i) {
+      const int e = threadIdx.x + 512 * i;
+      *reinterpret_cast<u32x4*>(&qt[buf][e / CH][8 * (e % CH)]) = stage[i];
     }
-    if (threadIdx.x < HP_QT * 16) lt[buf][threadIdx.x / 16][threadIdx.x % 16] = lstage;
+    if (threadIdx.x < HP_QR) lt[buf][threadIdx.x] = lstage;
   };
   fetch(0);
   put(0);
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+    const int buf = t & 1, r0 = r_beg + t * HP_QR;
     if (t + 1 < ntiles) fetch(t + 1);
+    if (r0 >= r_full) {                                 // no causal test anywhere in the tile
 #pragma unroll
-    for (int pp = 0; pp < HP_QT; ++pp) {
-      const int pos = i_beg + t * HP_QT + pp;
-      if (pos >= L) break;                              // uniform across the block
-      u32x4 bq[NKS];
+      for (int j = 0; j < NQG; ++j) {
+        if (r0 + 16 * j >= nrows) break;                // uniform across the block
+        u32x4 bq[NKS];
 #pragma unroll
-      for (int c = 0; c < NKS; ++c) bq[c] = *reinterpret_cast<const u32x4*>(&qt[buf][pp][c16][8 * g + 32 * c]);
-      const float lse = lt[buf][pp][c16];
-      const bool head_ok = c16 < a.G;
+        for (int c = 0; c < NKS; ++c) bq[c] = *reinterpret_cast<const u32x4*>(&qt[buf][16 * j + c16][8 * g + 32 * c]);
+        const float nlse = -lt[buf][16 * j + c16];
 #pragma unroll
-      for (int kb = 0; kb < HP_KB; ++kb) {
-        if (j_w + 16 * kb > pos) continue;              // every key of this block comes after the query
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb < HP_KB; ++kb) {
+          f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NKS; ++c) s = mfma_bf16_16x16x32(ak[kb][c], bq[c], s);
+          for (int c = 0; c < NKS; ++c) s = mfma_bf16_16x16x32(ak[kb][c], bq[c], s);
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int key = j_w + 16 * kb + 4 * g + ii;
-          if (head_ok && key <= pos) col[kb][ii] += exp2f(s[ii] * a.sc2 - lse);
+          for (int ii = 0; ii < 4; ++ii) col[kb][ii] += hp_exp2(fmaf(s[ii], a.sc2, nlse));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NQG; ++j) {
+        const int rg = r0 + 16 * j;
+        if (rg >= nrows) break;                         // uniform across the block
+        const int pmin = rg / G, pmax = (rg + 15) / G, lpos = (rg + c16) / G;
+        u32x4 bq[NKS];
+#pragma unroll
+        for (int c = 0; c < NKS; ++c) bq[c] = *reinterpret_cast<const u32x4*>(&qt[buf][16 * j + c16][8 * g + 32 * c]);
+        const float nlse = -lt[buf][16 * j + c16];
+#pragma unroll
+        for (int kb = 0; kb < HP_KB; ++kb) {
+          if (j_w + 16 * kb > pmax) continue;           // every key of this block comes after the group
+          f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < NKS; ++c) s = mfma_bf16_16x16x32(ak[kb][c], bq[c], s);
+          if (j_w + 16 * kb + 15 <= pmin) {
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) col[kb][ii] += hp_exp2(fmaf(s[ii], a.sc2, nlse));
+          } else {
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+              const int key = j_w + 16 * kb + 4 * g + ii;
+              if (key <= lpos) col[kb][ii] += hp_exp2(fmaf(s[ii], a.sc2, nlse));
+            }
+          }
         }
       }
     }
     if (t + 1 < ntiles) put(buf ^ 1);
     __syncthreads();
   }
-  // sum over the 16 head lanes of each key
+  // sum over the 16 row lanes of each key
 #pragma unroll
   for (int kb = 0; kb < HP_KB; ++kb)
 #pragma unroll
@@ -240,7 +299,7 @@ se_status launch_h2o_prefill_scores(const se_cache& c, const void* q, const void
   a.n_cand = n_cand;
   a.sc2 = scale * 1.4426950408889634f;
   const int units = c.batch * c.n_kv_heads;
-  const dim3 ga(ceil_div(L, HP_POS), units), gb(ceil_div(L, HP_KEYS), units);
+  const dim3 ga(ceil_div(L * a.G, HP_ROWS), units), gb(ceil_div(L, HP_KEYS), units);
   if (c.d_k == 128) {
     hipLaunchKernelGGL(hp_rowlse_kernel<128>, ga, dim3(512), 0, s, a);
     hipLaunchKernelGGL(hp_colsum_kernel<128>, gb, dim3(512), 0, s, a);
