@@ -81,9 +81,9 @@ __global__ __launch_bounds__(256) void attn_vector_kernel(AttnArgs a) {
       const float mo = ms[h], mn = fmaxf(mo, mt);
       float alpha = 1.f, sum = 0.f;
       if (mn != -INFINITY) {
-        alpha = exp2f((mo - mn) * LOG2E);
+        alpha = ex2((mo - mn) * LOG2E);
         for (int j = 0; j < VT; ++j) {
-          float p = exp2f((pt[h * VT + j] - mn) * LOG2E);
+          float p = ex2((pt[h * VT + j] - mn) * LOG2E);
           pt[h * VT + j] = p;
           sum += p;
         }
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   float lloc = 0.f;
   for (int s = threadIdx.x; s < S; s += 128) {
     const float ms = f_s[s];
-    const float f = (ms != -INFINITY) ? exp2f((ms - M) * LOG2E) : 0.f;
+    const float f = (ms != -INFINITY) ? ex2((ms - M) * LOG2E) : 0.f;
     f_s[s] = f;
     lloc += f * pml[(s * G + h) * 2 + 1];
   }

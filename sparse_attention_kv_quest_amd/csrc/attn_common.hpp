@@ -110,13 +110,13 @@ __device__ void attn_merge_splits_su(const AttnArgs& a, int unit, int h0, int nh
       }
       const float Mn = fmaxf(M, Mb);
       if (Mn == -INFINITY) continue;
-      const float alpha = M == -INFINITY ? 0.f : exp2f((M - Mn) * LOG2E);
+      const float alpha = M == -INFINITY ? 0.f : ex2((M - Mn) * LOG2E);
       L *= alpha;
 #pragma unroll
       for (int u = 0; u < 4; ++u) O[u] *= alpha;
 #pragma unroll
       for (int j = 0; j < SU; ++j) {
-        const float f = mlb[j].x == -INFINITY ? 0.f : exp2f((mlb[j].x - Mn) * LOG2E);
+        const float f = mlb[j].x == -INFINITY ? 0.f : ex2((mlb[j].x - Mn) * LOG2E);
         L += f * mlb[j].y;
         O[0] += f * ob0[j].x;
         O[1] += f * ob0[j].y;

@@ -235,7 +235,7 @@ __device__ __forceinline__ void mf_compute(const AttnArgs& a, const MfCtx& x, in
   const bool grow = tmax > st.m2 + MF_RESCALE_MARGIN;
   if (__ballot(grow) != 0) {
     const float mnew = grow ? tmax : st.m2;
-    const float alpha = (grow && st.m2 != -INFINITY) ? exp2f(st.m2 - mnew) : 1.f;
+    const float alpha = (grow && st.m2 != -INFINITY) ? ex2(st.m2 - mnew) : 1.f;
     st.lsum *= alpha;
 #pragma unroll
     for (int i = 0; i < NDB; ++i) st.o[i] *= alpha;
@@ -247,7 +247,7 @@ __device__ __forceinline__ void mf_compute(const AttnArgs& a, const MfCtx& x, in
   float psum = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    p[i] = exp2f(sv[i] - mref);   // 0 for masked slots; at most 2^8 otherwise
+    p[i] = ex2(sv[i] - mref);   // 0 for masked slots; at most 2^8 otherwise
     psum += p[i];
   }
   st.lsum += psum;
@@ -492,7 +492,7 @@ void attn_mfma_kernel(AttnArgs a) {
       for (int ww = 0; ww < MF_WAVES; ++ww) {
         const float mw = red_m[ww][h];
         if (mw != -INFINITY) {
-          const float f = exp2f(mw - M);
+          const float f = ex2(mw - M);
           L += f * red_l[ww][h];
           O += f * *reinterpret_cast<const f32x4*>(red_o + (ww * 16 + h) * OP + d0);
         }

@@ -207,7 +207,7 @@ __global__ __launch_bounds__(ML_THREADS) void attn_mla_kernel(AttnArgs a) {
       const bool grow = tmax > m2[hb] + ML_MARGIN;
       if (__ballot(grow) != 0) {
         const float mnew = grow ? tmax : m2[hb];
-        const float alpha = (grow && m2[hb] != -INFINITY) ? exp2f(m2[hb] - mnew) : 1.f;
+        const float alpha = (grow && m2[hb] != -INFINITY) ? ex2(m2[hb] - mnew) : 1.f;
         lsum[hb] *= alpha;
 #pragma unroll
         for (int db = 0; db < ML_DW / 16; ++db) o[db][hb] *= alpha;
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(ML_THREADS) void attn_mla_kernel(AttnArgs a) {
       float p[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[i] = exp2f(sv[hb][i] - mref);   // 0 for masked slots, at most 2^8 otherwise
+        p[i] = ex2(sv[hb][i] - mref);   // 0 for masked slots, at most 2^8 otherwise
         lsum[hb] += p[i];
       }
       uint2 hi, lo;

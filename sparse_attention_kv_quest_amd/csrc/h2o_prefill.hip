@@ -38,11 +38,6 @@ struct HpArgs {
   float sc2;            // scale * log2(e)
 };
 
-// v_exp_f32 as it stands: results below 2^-126 come out as zero.  Every sum here
-// holds a term >= 1 (pass A) or is a probability sum compared at 1e-6 absolute,
-// so terms that small do not change a result.
-__device__ __forceinline__ float hp_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
 // The group's queries are taken as L * G rows (position-major, head-minor) and go
 // sixteen at a time into the MFMA N dimension, so no column is spent on padding
 // whatever G is.
@@ -126,12 +121,12 @@ __global__ __launch_bounds__(512) void hp_rowlse_kernel(HpArgs a) {
         // this lane's own keys: running max moved only when exceeded by more than 2^8
         const float hm = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
         if (hm > m[j] + HP_MARGIN) {
-          l[j] = m[j] == -INFINITY ? 0.f : l[j] * hp_exp2(m[j] - hm);
+          l[j] = m[j] == -INFINITY ? 0.f : l[j] * ex2(m[j] - hm);
           m[j] = hm;
         }
         const float mr = m[j] == -INFINITY ? 0.f : m[j];
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) l[j] += hp_exp2(v[ii] - mr);
+        for (int ii = 0; ii < 4; ++ii) l[j] += ex2(v[ii] - mr);
       }
     }
     if (t + 1 < ntiles) put(buf ^ 1);
@@ -143,7 +138,7 @@ __global__ __launch_bounds__(512) void hp_rowlse_kernel(HpArgs a) {
   for (int j = 0; j < HP_NG; ++j) {
     float mt = fmaxf(m[j], __shfl_xor(m[j], 16, 64));
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    float lt = m[j] == -INFINITY ? 0.f : l[j] * hp_exp2(m[j] - mt);
+    float lt = m[j] == -INFINITY ? 0.f : l[j] * ex2(m[j] - mt);
     lt += __shfl_xor(lt, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
     const int r = r_w + 16 * j + c16;
@@ -224,7 +219,7 @@ __global__ __launch_bounds__(512) void hp_colsum_kernel(HpArgs a) {
 #pragma unroll
           for (int c = 0; c < NKS; ++c) s = mfma_bf16_16x16x32(ak[kb][c], bq[c], s);
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii) col[kb][ii] += hp_exp2(fmaf(s[ii], a.sc2, nlse));
+          for (int ii = 0; ii < 4; ++ii) col[kb][ii] += ex2(fmaf(s[ii], a.sc2, nlse));
         }
       }
     } else {
@@ -245,12 +240,12 @@ __global__ __launch_bounds__(512) void hp_colsum_kernel(HpArgs a) {
           for (int c = 0; c < NKS; ++c) s = mfma_bf16_16x16x32(ak[kb][c], bq[c], s);
           if (j_w + 16 * kb + 15 <= pmin) {
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) col[kb][ii] += hp_exp2(fmaf(s[ii], a.sc2, nlse));
+            for (int ii = 0; ii < 4; ++ii) col[kb][ii] += ex2(fmaf(s[ii], a.sc2, nlse));
           } else {
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
               const int key = j_w + 16 * kb + 4 * g + ii;
-              if (key <= lpos) col[kb][ii] += hp_exp2(fmaf(s[ii], a.sc2, nlse));
+              if (key <= lpos) col[kb][ii] += ex2(fmaf(s[ii], a.sc2, nlse));
             }
           }
         }

@@ -13,6 +13,12 @@ constexpr int WAVE = 64;
 // ------------------------------------------------------------------ element access
 struct bf16_t { uint16_t bits; };
 
+// 2^x from v_exp_f32 alone.  Results below 2^-126 come out as zero; exp2f adds
+// five VALU operations around the same instruction only to produce those
+// subnormal results.  A softmax denominator holds a term >= 2^0 (the running
+// maximum's own), so a dropped term is below its rounding; a sum of
+// probabilities loses at most 2^-126 per term.
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float(uint32_t(x.bits) << 16); }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -35,9 +35,11 @@ struct SnapArgs {
 
 // ------------------------------------------------------------------ MFMA passes (bf16)
 // grid (chunks, units); 4 waves, each owning NRB 16-row blocks of the R = 64 * NRB rows.
-// S^T[key][row] = K[key] . Q[row]: A = 16 key rows (lane: key c16, dims 32c + 8g..),
-// B = Q^T of one 16-row block (lane: row c16, same dims); lane (g, c16) then holds
-// keys 4g..4g+3 of row c16.
+// Pass A takes S^T[key][row] = K[key] . Q[row]: A = 16 key rows (lane: key c16,
+// dims 32c + 8g..), B = Q^T of one 16-row block (lane: row c16, same dims), so
+// lane (g, c16) holds keys 4g..4g+3 of row c16 and a row's statistics stay in
+// four lanes.  Pass B swaps the operands: lane (g, c16) holds rows 4g..4g+3 of
+// key c16, and a key's vote stays in four lanes.
 template <int D, int NRB, bool PASS_B>
 __global__ __launch_bounds__(256) void snap_mfma_kernel(SnapArgs a) {
   constexpr int NKS = D / 32;
@@ -53,20 +55,24 @@ __global__ __launch_bounds__(256) void snap_mfma_kernel(SnapArgs a) {
   // Q operand of this wave's row blocks
   u32x4 qv[NRB][NKS];
   int rowpos[NRB];
-  float lse2[NRB];
+  float nlse[NRB][4];   // pass B: -lse2 of rows 4g + i of each block (keys in the N dimension)
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     const int row = (w * NRB + rb) * 16 + c16;
     rowpos[rb] = a.L - a.W + row % a.W;
 #pragma unroll
     for (int c = 0; c < NKS; ++c) qv[rb][c] = ld16(qu + size_t(row) * D + 32 * c + 8 * g);
-    lse2[rb] = PASS_B ? a.lse2[size_t(unit) * a.R + row] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      nlse[rb][i] = PASS_B ? -a.lse2[size_t(unit) * a.R + (w * NRB + rb) * 16 + 4 * g + i] : 0.f;
   }
   float m[NRB], l[NRB];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) { m[rb] = -INFINITY; l[rb] = 0.f; }
 
   const int nblk = (k1 - k0 + 15) / 16;
+  // blocks below `plain` hold no key past k1 and no window key, so no row masks any of them
+  const int plain = (min(k1, n_hist) - k0) / 16;
   u32x4 kc[NKS], kn[NKS];
   auto load = [&](int blk, u32x4* dst) {
     const int key = k0 + blk * 16 + c16;
@@ -78,45 +84,49 @@ __global__ __launch_bounds__(256) void snap_mfma_kernel(SnapArgs a) {
   for (int blk = 0; blk < nblk; ++blk) {
     load(blk + 1 < nblk ? blk + 1 : blk, kn);
     const int kb = k0 + blk * 16;
-    float kvals[NRB][4];
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < NKS; ++c) s = mfma_bf16_16x16x32(kc[c], qv[rb][c], s);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kb + 4 * g + i;
-        const bool ok = key < k1 && key <= rowpos[rb];
-        kvals[rb][i] = ok ? s[i] * a.sc2 : -INFINITY;
-      }
-    }
     if (!PASS_B) {
+      // S^T[key][row]: lane (g, c16) holds keys kb + 4g + i of row c16
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
-        const float bm = fmaxf(fmaxf(kvals[rb][0], kvals[rb][1]), fmaxf(kvals[rb][2], kvals[rb][3]));
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NKS; ++c) s = mfma_bf16_16x16x32(kc[c], qv[rb][c], s);
+        float v[4];
+        if (blk < plain) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = s[i] * a.sc2;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kb + 4 * g + i;
+            v[i] = key < k1 && key <= rowpos[rb] ? s[i] * a.sc2 : -INFINITY;
+          }
+        }
+        const float bm = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
         if (bm > m[rb] + SK_MARGIN) {
-          l[rb] *= (m[rb] == -INFINITY) ? 0.f : exp2f(m[rb] - bm);
+          l[rb] *= (m[rb] == -INFINITY) ? 0.f : ex2(m[rb] - bm);
           m[rb] = bm;
         }
         const float mref = m[rb] == -INFINITY ? 0.f : m[rb];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) l[rb] += exp2f(kvals[rb][i] - mref);
+        for (int i = 0; i < 4; ++i) l[rb] += ex2(v[i] - mref);
       }
     } else {
-      float ks[4];
+      // S[row][key]: lane (g, c16) holds rows 4g + i of key kb + c16, so a key's sum
+      // over the wave's rows stays in its lane until two exchanges across g.
+      // History keys precede every window row: only keys past k1 are dropped.
+      float t = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float t = 0.f;
+      for (int rb = 0; rb < NRB; ++rb) {
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) t += exp2f(kvals[rb][i] - lse2[rb]);
-        for (int o = 1; o < 16; o <<= 1) t += __shfl_xor(t, o, 64);   // over the 16 rows of the lane group
-        ks[i] = t;
+        for (int c = 0; c < NKS; ++c) s = mfma_bf16_16x16x32(qv[rb][c], kc[c], s);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t += ex2(fmaf(s[i], a.sc2, nlse[rb][i]));
       }
-      if (c16 == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vsum[w][blk][4 * g + i] = ks[i];
-      }
+      t += __shfl_xor(t, 16, 64);
+      t += __shfl_xor(t, 32, 64);
+      if (g == 0) vsum[w][blk][c16] = kb + c16 < k1 ? t : 0.f;
     }
 #pragma unroll
     for (int c = 0; c < NKS; ++c) kc[c] = kn[c];
@@ -128,7 +138,7 @@ __global__ __launch_bounds__(256) void snap_mfma_kernel(SnapArgs a) {
       float mm = m[rb];
       mm = fmaxf(mm, __shfl_xor(mm, 16, 64));
       mm = fmaxf(mm, __shfl_xor(mm, 32, 64));
-      float ll = (m[rb] == -INFINITY) ? 0.f : l[rb] * exp2f(m[rb] - mm);
+      float ll = (m[rb] == -INFINITY) ? 0.f : l[rb] * ex2(m[rb] - mm);
       ll += __shfl_xor(ll, 16, 64);
       ll += __shfl_xor(ll, 32, 64);
       if (g == 0) {
@@ -173,10 +183,10 @@ __global__ __launch_bounds__(256) void snap_lse_merge_kernel(SnapArgs a) {
 #pragma unroll
       for (int j = 0; j < BATCH; ++j) Mb = fmaxf(Mb, mb[j]);
       if (Mb == -INFINITY) continue;
-      S = (M == -INFINITY) ? 0.f : S * exp2f(M - Mb);
+      S = (M == -INFINITY) ? 0.f : S * ex2(M - Mb);
 #pragma unroll
       for (int j = 0; j < BATCH; ++j)
-        if (mb[j] != -INFINITY) S += lb[j] * exp2f(mb[j] - Mb);
+        if (mb[j] != -INFINITY) S += lb[j] * ex2(mb[j] - Mb);
       M = Mb;
     }
   }
@@ -185,7 +195,7 @@ __global__ __launch_bounds__(256) void snap_lse_merge_kernel(SnapArgs a) {
     const float Mo = __shfl_xor(M, o, 64), So = __shfl_xor(S, o, 64);
     const float Mn = fmaxf(M, Mo);
     if (Mn != -INFINITY) {
-      S = (M == -INFINITY ? 0.f : S * exp2f(M - Mn)) + (Mo == -INFINITY ? 0.f : So * exp2f(Mo - Mn));
+      S = (M == -INFINITY ? 0.f : S * ex2(M - Mn)) + (Mo == -INFINITY ? 0.f : So * ex2(Mo - Mn));
       M = Mn;
     }
   }
@@ -209,11 +219,11 @@ __global__ __launch_bounds__(256) void snap_vec_lse_kernel(SnapArgs a) {
     float dot = 0.f;
     for (int d = 0; d < D; ++d) dot += qrow[d] * to_f32(ku[size_t(j) * D + d]);
     const float s = dot * a.sc2;
-    if (s > m) { l = l * exp2f(m - s); m = s; }
-    l += exp2f(s - m);
+    if (s > m) { l = l * ex2(m - s); m = s; }
+    l += ex2(s - m);
   }
   const float mw = wave_max(m);
-  l = (m == -INFINITY) ? 0.f : l * exp2f(m - mw);
+  l = (m == -INFINITY) ? 0.f : l * ex2(m - mw);
   l = wave_sum(l);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (lane == 0) { rm[w] = mw; rl[w] = l; }
@@ -221,7 +231,7 @@ __global__ __launch_bounds__(256) void snap_vec_lse_kernel(SnapArgs a) {
   if (threadIdx.x == 0) {
     float M = fmaxf(fmaxf(rm[0], rm[1]), fmaxf(rm[2], rm[3])), S = 0.f;
     for (int i = 0; i < 4; ++i)
-      if (rm[i] != -INFINITY) S += rl[i] * exp2f(rm[i] - M);
+      if (rm[i] != -INFINITY) S += rl[i] * ex2(rm[i] - M);
     a.lse2[size_t(unit) * a.R + row] = M + log2f(S);
   }
 }
@@ -241,7 +251,7 @@ __global__ __launch_bounds__(256) void snap_vec_vote_kernel(SnapArgs a) {
   for (int r = 0; r < a.R; ++r) {
     float dot = 0.f;
     for (int d = 0; d < D; ++d) dot += qs[r * D + d] * to_f32(ku[size_t(j) * D + d]);
-    vote += exp2f(dot * a.sc2 - a.lse2[size_t(unit) * a.R + r]);
+    vote += ex2(dot * a.sc2 - a.lse2[size_t(unit) * a.R + r]);
   }
   a.votes[size_t(unit) * n_hist + j] = vote;
 }
