@@ -21,6 +21,7 @@ namespace se {
 constexpr float SK_LOG2E = 1.4426950408889634f;
 constexpr int SK_CHUNK = 1024;        // keys per block in the MFMA passes
 constexpr float SK_MARGIN = 8.f;      // lazy running-max margin (log2 units)
+constexpr int SK_KT = 64;             // keys per LDS tile in the MFMA passes
 
 struct SelState { uint32_t prefix, mask; int r, done; };   // per-unit radix-select state
 
@@ -42,7 +43,8 @@ struct SnapArgs {
 // key c16, and a key's vote stays in four lanes.
 template <int D, int NRB, bool PASS_B>
 __global__ __launch_bounds__(256) void snap_mfma_kernel(SnapArgs a) {
-  constexpr int NKS = D / 32;
+  constexpr int NKS = D / 32, PITCH = D + 8, CH = D / 8, TPT = SK_KT * CH / 256;
+  __shared__ __align__(16) uint16_t kt[2][SK_KT][PITCH];
   __shared__ float vsum[4][SK_CHUNK / 16][16];   // pass B: per-wave key sums of each 16-key block
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
   const int unit = blockIdx.y, chunk = blockIdx.x;
@@ -73,63 +75,86 @@ __global__ __launch_bounds__(256) void snap_mfma_kernel(SnapArgs a) {
   const int nblk = (k1 - k0 + 15) / 16;
   // blocks below `plain` hold no key past k1 and no window key, so no row masks any of them
   const int plain = (min(k1, n_hist) - k0) / 16;
-  u32x4 kc[NKS], kn[NKS];
-  auto load = [&](int blk, u32x4* dst) {
-    const int key = k0 + blk * 16 + c16;
-    const uint32_t off = uint32_t(min(max(key, 0), a.cap - 1)) * D + 8 * g;   // clamped: masked below
+  // K tiles of SK_KT keys go through double-buffered LDS, loaded by the whole block
+  // one tile ahead (keys past k1 are clamped rows, masked below)
+  const int ntile = (k1 - k0 + SK_KT - 1) / SK_KT;   // >= 1: every chunk of the grid starts below k1
+  u32x4 stage[TPT];
+  auto fetch = [&](int t) {
 #pragma unroll
-    for (int c = 0; c < NKS; ++c) dst[c] = ld16(ku + off + 32 * c);
-  };
-  if (nblk > 0) load(0, kc);
-  for (int blk = 0; blk < nblk; ++blk) {
-    load(blk + 1 < nblk ? blk + 1 : blk, kn);
-    const int kb = k0 + blk * 16;
-    if (!PASS_B) {
-      // S^T[key][row]: lane (g, c16) holds keys kb + 4g + i of row c16
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < NKS; ++c) s = mfma_bf16_16x16x32(kc[c], qv[rb][c], s);
-        float v[4];
-        if (blk < plain) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = s[i] * a.sc2;
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = kb + 4 * g + i;
-            v[i] = key < k1 && key <= rowpos[rb] ? s[i] * a.sc2 : -INFINITY;
-          }
-        }
-        const float bm = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
-        if (bm > m[rb] + SK_MARGIN) {
-          l[rb] *= (m[rb] == -INFINITY) ? 0.f : ex2(m[rb] - bm);
-          m[rb] = bm;
-        }
-        const float mref = m[rb] == -INFINITY ? 0.f : m[rb];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) l[rb] += ex2(v[i] - mref);
-      }
-    } else {
-      // S[row][key]: lane (g, c16) holds rows 4g + i of key kb + c16, so a key's sum
-      // over the wave's rows stays in its lane until two exchanges across g.
-      // History keys precede every window row: only keys past k1 are dropped.
-      float t = 0.f;
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < NKS; ++c) s = mfma_bf16_16x16x32(qv[rb][c], kc[c], s);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) t += ex2(fmaf(s[i], a.sc2, nlse[rb][i]));
-      }
-      t += __shfl_xor(t, 16, 64);
-      t += __shfl_xor(t, 32, 64);
-      if (g == 0) vsum[w][blk][c16] = kb + c16 < k1 ? t : 0.f;
+    for (int i = 0; i < TPT; ++i) {
+      const int e = threadIdx.x + 256 * i;
+      const int key = min(k0 + t * SK_KT + e / CH, a.cap - 1);
+      stage[i] = ld16(ku + size_t(key) * D + 8 * (e % CH));
     }
+  };
+  auto put = [&](int buf) {
 #pragma unroll
-    for (int c = 0; c < NKS; ++c) kc[c] = kn[c];
+    for (int i = 0; i < TPT; ++i) {
+      const int e = threadIdx.x + 256 * i;
+      *reinterpret_cast<u32x4*>(&kt[buf][e / CH][8 * (e % CH)]) = stage[i];
+    }
+  };
+  fetch(0);
+  put(0);
+  __syncthreads();
+  for (int t = 0; t < ntile; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntile) fetch(t + 1);
+#pragma unroll
+    for (int sb = 0; sb < SK_KT / 16; ++sb) {
+      const int blk = t * (SK_KT / 16) + sb;
+      if (blk >= nblk) break;                          // uniform across the block
+      u32x4 kc[NKS];
+#pragma unroll
+      for (int c = 0; c < NKS; ++c) kc[c] = *reinterpret_cast<const u32x4*>(&kt[buf][16 * sb + c16][8 * g + 32 * c]);
+      const int kb = k0 + blk * 16;
+      if (!PASS_B) {
+        // S^T[key][row]: lane (g, c16) holds keys kb + 4g + i of row c16
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < NKS; ++c) s = mfma_bf16_16x16x32(kc[c], qv[rb][c], s);
+          float v[4];
+          if (blk < plain) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = s[i] * a.sc2;
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = kb + 4 * g + i;
+              v[i] = key < k1 && key <= rowpos[rb] ? s[i] * a.sc2 : -INFINITY;
+            }
+          }
+          const float bm = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+          if (bm > m[rb] + SK_MARGIN) {
+            l[rb] *= (m[rb] == -INFINITY) ? 0.f : ex2(m[rb] - bm);
+            m[rb] = bm;
+          }
+          const float mref = m[rb] == -INFINITY ? 0.f : m[rb];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) l[rb] += ex2(v[i] - mref);
+        }
+      } else {
+        // S[row][key]: lane (g, c16) holds rows 4g + i of key kb + c16, so a key's sum
+        // over the wave's rows stays in its lane until two exchanges across g.
+        // History keys precede every window row: only keys past k1 are dropped.
+        float vote = 0.f;
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < NKS; ++c) s = mfma_bf16_16x16x32(qv[rb][c], kc[c], s);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vote += ex2(fmaf(s[i], a.sc2, nlse[rb][i]));
+        }
+        vote += __shfl_xor(vote, 16, 64);
+        vote += __shfl_xor(vote, 32, 64);
+        if (g == 0) vsum[w][blk][c16] = kb + c16 < k1 ? vote : 0.f;
+      }
+    }
+    if (t + 1 < ntile) put(buf ^ 1);
+    __syncthreads();
   }
   if (!PASS_B) {
     // merge the 4 lanes of each row (g = 0..3), then write the chunk's partial
