@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb)
           if (16 * hb + c16 < G) v = fmaxf(v, acc[hb][r]);
-        for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+        v = row16_max(v);
         best[r] = (p0 + 4 * g + r < npages) ? v : -INFINITY;
       }
     }
@@ -207,8 +207,8 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(
 // the scores stay in registers (block_topk_reg); longer caches use the LDS /
 // global-memory variant.
 // APP (the fused decode call): pages are counted with the length after the
-// append, and the last block of a batch row (ticket on counters[b]) stores that
-// length once every block of the row has read the old one.
+// append, and the block holding the last ticket of its batch row (counters[b],
+// taken once the old length is read) stores the new length.
 template <int BLOCK, int E, bool APP = false>
 __global__ __launch_bounds__(BLOCK) void quest_topk_reg_kernel(
     const float* __restrict__ score, int32_t* seq_len, int32_t* __restrict__ view_idx,
@@ -218,15 +218,23 @@ __global__ __launch_bounds__(BLOCK) void quest_topk_reg_kernel(
   const int len = min(seq_len[b], cap);
   const int new_len = (APP && len < cap) ? len + 1 : len;
   const int n = min((new_len + P - 1) / P, n_cap_pages);
+  // APP: the row ticket is taken as soon as the old length has been read and its
+  // value is looked at only at the end, so the atomic's round trip overlaps the
+  // selection instead of following it
+  int ticket = 0;
+  if (APP && threadIdx.x == 0) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);   // the old length has been read
+    ticket = __hip_atomic_fetch_add(counters + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  }
   const float* su = score + size_t(unit) * n_cap_pages;
   const int kk = block_topk_reg<BLOCK, E>([&](int i) { return su[i]; }, n, top_pages,
                                           view_idx + size_t(unit) * top_pages, sh);
   if (threadIdx.x == 0) view_len[unit] = kk;
-  if constexpr (APP) {
-    if (block_ticket_last(counters + b, Hkv) && threadIdx.x == 0) {
-      if (new_len != len) seq_len[b] = new_len;
-      ticket_reset(counters + b);
-    }
+  if (APP && threadIdx.x == 0 && ticket == Hkv - 1) {   // every block of the row has read the old length
+    if (new_len != len) seq_len[b] = new_len;
+    ticket_reset(counters + b);
   }
 }
 

@@ -60,6 +60,17 @@ __device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v, uint32_t iden
   v = op(v, uint32_t(__builtin_amdgcn_update_dpp(id, int(v), 0x143, 0xc, 0xf, false)));   // row_bcast:31
   return v;
 }
+// Maximum over each 16-lane row, in every lane of the row, by DPP lane moves:
+// quad_perm [1,0,3,2] and [2,3,0,1] give each lane its quad's maximum,
+// row_half_mirror (lane i <- 7 - i) joins the two quads of each half row and
+// row_mirror (lane i <- 15 - i) the two halves.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4e, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false)));
+  return v;
+}
 // Inclusive scan inside each 16-lane row only (lane 15 of a row ends with the row's total).
 template <class Op>
 __device__ __forceinline__ uint32_t row_incl_scan_dpp(uint32_t v, uint32_t identity, Op op) {
