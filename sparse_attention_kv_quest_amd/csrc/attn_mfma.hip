@@ -229,8 +229,7 @@ __device__ __forceinline__ void mf_compute(const AttnArgs& a, const MfCtx& x, in
   float tmax = sv[0];
 #pragma unroll
   for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, sv[i]);
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+  tmax = rows4_max(tmax);
   // move the running max only when this tile exceeds it by more than the margin
   const bool grow = tmax > st.m2 + MF_RESCALE_MARGIN;
   if (__ballot(grow) != 0) {
@@ -466,8 +465,7 @@ void attn_mfma_kernel(AttnArgs a) {
   // outputs [wave][head][dim] (row pitch D + 4) go through LDS; a thread then
   // owns four consecutive dims of one head.
   float lsum = st.lsum;
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
+  lsum = rows4_sum(lsum);
   constexpr int OP = D + 4;
   __syncthreads();
   float* red_o = reinterpret_cast<float*>(&vt_lds[0][0]);

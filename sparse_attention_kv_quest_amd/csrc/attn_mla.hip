@@ -193,8 +193,7 @@ __global__ __launch_bounds__(ML_THREADS) void attn_mla_kernel(AttnArgs a) {
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
       float m = fmaxf(fmaxf(sv[hb][0], sv[hb][1]), fmaxf(sv[hb][2], sv[hb][3]));
-      m = fmaxf(m, __shfl_xor(m, 16, 64));
-      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      m = rows4_max(m);
       if (g == 0) wmax[w][16 * hb + c16] = m;
     }
     __syncthreads();
@@ -282,8 +281,7 @@ __global__ __launch_bounds__(ML_THREADS) void attn_mla_kernel(AttnArgs a) {
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
     float s = lsum[hb];
-    s += __shfl_xor(s, 16, 64);
-    s += __shfl_xor(s, 32, 64);
+    s = rows4_sum(s);
     if (g == 0) wsum[w][16 * hb + c16] = s;
   }
   __syncthreads();   // also: every wave is done with Q, P and its V tile

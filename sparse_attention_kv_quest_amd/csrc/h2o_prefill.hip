@@ -136,11 +136,9 @@ __global__ __launch_bounds__(512) void hp_rowlse_kernel(HpArgs a) {
   // (m = -inf) add nothing, and key 0 makes the row's maximum finite
 #pragma unroll
   for (int j = 0; j < HP_NG; ++j) {
-    float mt = fmaxf(m[j], __shfl_xor(m[j], 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float mt = rows4_max(m[j]);
     float lt = m[j] == -INFINITY ? 0.f : l[j] * ex2(m[j] - mt);
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
+    lt = rows4_sum(lt);
     const int r = r_w + 16 * j + c16;
     if (g == 0 && r < nrows) a.lse2[size_t(unit) * nrows + r] = mt + log2f(lt);
   }

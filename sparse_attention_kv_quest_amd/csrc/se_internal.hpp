@@ -71,6 +71,23 @@ __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false)));
   return v;
 }
+// Maximum / sum over the four 16-lane rows of a wave (lanes l, l ^ 16, l ^ 32,
+// l ^ 48), in every lane, by the row swaps of gfx950: v_permlane16_swap hands each
+// lane the pair {row 2i, row 2i + 1} of its column, v_permlane32_swap the pair of
+// half waves, always in that order, so every lane gets the same value (the same
+// one as exchanges across 16, then 32, since + and max are commutative).
+__device__ __forceinline__ float rows4_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float rows4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
 // Inclusive scan inside each 16-lane row only (lane 15 of a row ends with the row's total).
 template <class Op>
 __device__ __forceinline__ uint32_t row_incl_scan_dpp(uint32_t v, uint32_t identity, Op op) {

@@ -148,8 +148,7 @@ __global__ __launch_bounds__(256) void snap_mfma_kernel(SnapArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) vote += ex2(fmaf(s[i], a.sc2, nlse[rb][i]));
         }
-        vote += __shfl_xor(vote, 16, 64);
-        vote += __shfl_xor(vote, 32, 64);
+        vote = rows4_sum(vote);
         if (g == 0) vsum[w][blk][c16] = kb + c16 < k1 ? vote : 0.f;
       }
     }
@@ -161,11 +160,9 @@ __global__ __launch_bounds__(256) void snap_mfma_kernel(SnapArgs a) {
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       float mm = m[rb];
-      mm = fmaxf(mm, __shfl_xor(mm, 16, 64));
-      mm = fmaxf(mm, __shfl_xor(mm, 32, 64));
+      mm = rows4_max(mm);
       float ll = (m[rb] == -INFINITY) ? 0.f : l[rb] * ex2(m[rb] - mm);
-      ll += __shfl_xor(ll, 16, 64);
-      ll += __shfl_xor(ll, 32, 64);
+      ll = rows4_sum(ll);
       if (g == 0) {
         const int row = (w * NRB + rb) * 16 + c16;
         float* p = a.part + ((size_t(unit) * a.nchunks + chunk) * a.R + row) * 2;
