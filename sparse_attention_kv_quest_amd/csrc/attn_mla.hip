@@ -168,7 +168,6 @@ __global__ __launch_bounds__(ML_THREADS) void attn_mla_kernel(AttnArgs a) {
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb) sa[hb] = mfma_bf16_16x16x32(kr[c], qs[(c * 2 + hb) * 64 + lane], sa[hb]);
     const uint64_t valid = __ballot(tk >= 0);
-    tk = ml_load_k(x, vcache, tb + ML_TS, w, lane, kr);   // next tile's rows
 
     float sv[NHB][4];
 #pragma unroll
@@ -274,7 +273,11 @@ __global__ __launch_bounds__(ML_THREADS) void attn_mla_kernel(AttnArgs a) {
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
-    ml_load_v(x, vcache, tb + ML_TS, w, lane, vr);   // next tile's value columns
+    // next tile: its rows and this wave's value columns of them go out together, so
+    // the column reads (rows other waves fetch) meet those rows in flight or fresh in
+    // L2; fetched half a tile apart, a tile step's rows (~4.7 MB per XCD) evicted them
+    tk = ml_load_k(x, vcache, tb + ML_TS, w, lane, kr);
+    ml_load_v(x, vcache, tb + ML_TS, w, lane, vr);
   }
 
   // ---- sums over lanes and waves (every wave shares the same running max)
