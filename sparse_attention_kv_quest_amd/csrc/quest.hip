@@ -202,6 +202,187 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(
   }
 }
 
+// ------------------------------------------------------------------ wide-row scoring (latent 576)
+// A group of 16 latent pages is 2 x 18 u32x4 of metadata per lane: too many
+// registers to hold a second group as well, so blocks of one group per wave
+// need two rounds of the GPU, the second starting only as the first drains.
+// Here each wave scores NGW groups and streams them through one group's worth
+// of registers: chunk r (16 pages x 32 columns) of group i is consumed by its
+// MFMAs and its slot then reloads chunk r of group i + 1, so the wave keeps a
+// group's worth of loads in flight across group boundaries.  The grid is two
+// blocks per CU, each with an equal share of a unit's pages (groups dealt to
+// its waves in turn), so every CU streams the same bytes in one round.  APP: the block holding the appended page folds the
+// new row into that page's min / max while it stages q (the rebuild's last
+// step), and the wave holding the page scores it again from the folded row.
+template <int D, int HB, bool APP, int NGW>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void quest_score_ring_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* kmin, const uint16_t* kmax,
+    const int32_t* seq_len, float* score, int Hkv, int G, int P, int ncp, int cap, int ppb, QuestAppendArgs ap) {
+  constexpr int NKS = D / 32, NCH = 2 * NKS;   // chunks per group: max rows k-steps 0.., then min rows
+  __shared__ u32x4 qb[2 * NKS][HB][64];
+  __shared__ __align__(16) uint16_t frow[APP ? 2 * D : 8];   // the appended page's folded max, min rows
+  const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int unit = blockIdx.y, b = unit / Hkv, kvh = unit % Hkv;
+  const int len = min(seq_len[b], cap);
+  const bool app = APP && len < cap;                 // room for the new token
+  const int new_len = app ? len + 1 : len;
+  const int npages = min((new_len + P - 1) / P, ncp);
+  const int plast = len / P;
+  const bool fresh = len % P == 0;
+  // the block's pages p_blk .. p_end - 1 in groups of 16; this wave's groups are
+  // w, w + 4, ..  (its group gi starts at page p_blk + 16 (w + 4 gi))
+  const int p_blk = blockIdx.x * ppb, p_end = min(ncp, p_blk + ppb);
+  auto grp_page = [&](int gi) { return p_blk + 16 * (w + 4 * gi); };
+  // chunk r of group gi; pages past the valid ones (and groups past the block's)
+  // read page 0: unconditional loads keep the wait counts exact; their bounds are
+  // masked or not stored
+  auto chunk_ptr = [&](int gi, int r) -> const uint16_t* {
+    const int pg = grp_page(gi) + c16;
+    const size_t row = size_t(unit) * ncp + (pg < npages ? pg : 0);
+    return (r < NKS ? kmax : kmin) + row * D + 8 * g + 32 * (r % NKS);
+  };
+  u32x4 ring[NCH];
+#pragma unroll
+  for (int r = 0; r < NCH; ++r) ring[r] = ld16(chunk_ptr(0, r));
+  const bool owner = app && p_blk <= plast && plast < p_end;   // the block holding the appended page
+  if (APP && owner) {
+    // the new K / V rows, and the appended page's min / max with the new row
+    // folded in (the last step of the in-order rebuild), or the new row alone on
+    // a fresh page; the stream still reads the old values of that page, whose
+    // bound the wave holding it recomputes below
+    const size_t urow = size_t(unit) * cap, mo = (size_t(unit) * ncp + plast) * D;
+    for (int i = threadIdx.x; i < 2 * (D / 8); i += 256) {
+      const bool isv = i >= D / 8;
+      const int o = 8 * (isv ? i - D / 8 : i);
+      if (!isv) {
+        const u32x4 x = ld16(ap.k_new + size_t(unit) * D + o);
+        *reinterpret_cast<u32x4*>(ap.k + (urow + len) * D + o) = x;
+        const u32x4 omx = ld16(kmax + mo + o), omn = ld16(kmin + mo + o);
+        u32x4 mx, mn;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          mx[jj] = bf16x2_fmin(fresh ? 0xff80ff80u : omx[jj], x[jj], true);    // -inf pair on a fresh page
+          mn[jj] = bf16x2_fmin(fresh ? 0x7f807f80u : omn[jj], x[jj], false);   // +inf pair
+        }
+        *reinterpret_cast<u32x4*>(ap.kmax_w + mo + o) = mx;
+        *reinterpret_cast<u32x4*>(ap.kmin_w + mo + o) = mn;
+        *reinterpret_cast<u32x4*>(&frow[o]) = mx;
+        *reinterpret_cast<u32x4*>(&frow[D + o]) = mn;
+      } else if (ap.v != nullptr) {
+        *reinterpret_cast<u32x4*>(ap.v + (urow + len) * D + o) = ld16(ap.v_new + size_t(unit) * D + o);
+      }
+    }
+  }
+  const uint16_t* qg = q + (size_t(b) * Hkv * G + size_t(kvh) * G) * D;
+  for (int idx = threadIdx.x; idx < 2 * NKS * HB * 64; idx += 256) {
+    const int ln = idx & 63, hb = (idx >> 6) % HB, sx = idx / (64 * HB);
+    const bool neg = sx >= NKS;
+    const int c = neg ? sx - NKS : sx;
+    const int head = 16 * hb + (ln & 15), gg = ln >> 4;
+    u32x4 x = {0, 0, 0, 0};
+    if (head < G) {
+      x = ld16(qg + size_t(head) * D + 32 * c + 8 * gg);
+      // q- keeps the halves whose sign bit is set, q+ the others
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const uint32_t sgn = ((x[jj] >> 15) & 1u) * 0xffffu | ((x[jj] >> 31) & 1u) * 0xffff0000u;
+        x[jj] &= neg ? sgn : ~sgn;
+      }
+    }
+    qb[sx][hb][ln] = x;
+  }
+  __syncthreads();
+  // the group (-1: none) and lane row of this wave that hold the appended page
+  const int rel = plast - p_blk;   // block group rel / 16 = wave (rel / 16) % 4, its group (rel / 16) / 4
+  const int fold_gi = __builtin_amdgcn_readfirstlane((APP && owner && (rel >> 4) % 4 == w) ? (rel >> 4) / 4 : -1);
+  const int fold_lane = rel & 15;
+  f32x4 acc[HB];
+  auto consume = [&](int r) {
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma_bf16_16x16x32(ring[r], qb[r][hb][lane], acc[hb]);
+  };
+  auto finish = [&](int gi) {   // the group's bounds: maximum over the heads of each page
+    const int p0 = grp_page(gi);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float v = -INFINITY;
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb)
+        if (16 * hb + c16 < G) v = fmaxf(v, acc[hb][r]);
+      v = row16_max(v);
+      const int page = p0 + 4 * g + r;
+      const bool stale = APP && fold_gi == gi && page == plast;   // scored again below
+      if (c16 == 0 && page < p_end && !stale) score[size_t(unit) * ncp + page] = page < npages ? v : -INFINITY;
+    }
+  };
+#pragma unroll
+  for (int gi = 0; gi + 1 < NGW; ++gi) {   // the next group exists: its chunks load behind this one's
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < NCH; ++r) {
+      consume(r);
+      ring[r] = ld16(chunk_ptr(gi + 1, r));
+    }
+    finish(gi);
+  }
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int r = 0; r < NCH; ++r) consume(r);
+  finish(NGW - 1);
+  if (APP && fold_gi >= 0) {   // wave-uniform: the appended page's bound from its folded rows
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < NCH; ++r) {
+      const u32x4 x = c16 == fold_lane ? *reinterpret_cast<const u32x4*>(&frow[(r < NKS ? 0 : D) + 8 * g + 32 * (r % NKS)])
+                                       : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma_bf16_16x16x32(x, qb[r][hb][lane], acc[hb]);
+    }
+    // row fold_lane sits in lanes g = fold_lane / 4, element fold_lane % 4
+    float v = -INFINITY;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      const f32x4 a4 = acc[hb];
+      const float e = (fold_lane & 3) == 0 ? a4[0] : (fold_lane & 3) == 1 ? a4[1] : (fold_lane & 3) == 2 ? a4[2] : a4[3];
+      if (16 * hb + c16 < G) v = fmaxf(v, e);
+    }
+    v = row16_max(v);
+    if (g == (fold_lane >> 2) && c16 == 0) score[size_t(unit) * ncp + plast] = v;   // plast < npages
+  }
+}
+
+// Grid of the wide-row kernel: two 4-wave blocks per CU (the q staging's LDS
+// allows no more), split evenly over the units; at most 4 groups per wave.
+static void quest_ring_grid(int ncp, int units, int* nbpu, int* ppb, int* ngw) {
+  int n = std::max(1, std::min(512 / units, ceil_div(ncp, 16)));
+  int p = ceil_div(ceil_div(ncp, n), 16) * 16;
+  if (p > 4 * 4 * 16) p = 4 * 4 * 16;   // more blocks instead of more groups per wave
+  *ppb = p;
+  *nbpu = ceil_div(ncp, p);
+  *ngw = ceil_div(p, 4 * 16);
+}
+
+template <bool APP>
+static void launch_score_ring576(const se_cache& c, const void* q, const void* kmin, const void* kmax,
+                                 const int32_t* seq_len, float* score, int P, int ncp, QuestAppendArgs ap,
+                                 hipStream_t s) {
+  const int units = c.batch * c.n_kv_heads, G = c.n_q_heads / c.n_kv_heads;
+  int nbpu, ppb, ngw;
+  quest_ring_grid(ncp, units, &nbpu, &ppb, &ngw);
+#define SE_RG(NG) hipLaunchKernelGGL((quest_score_ring_kernel<576, 2, APP, NG>), dim3(nbpu, units), dim3(256), 0, s,   \
+                                     (const uint16_t*)q, (const uint16_t*)kmin, (const uint16_t*)kmax, seq_len, score, \
+                                     c.n_kv_heads, G, P, ncp, c.capacity, ppb, ap)
+  if (ngw == 1) SE_RG(1);
+  else if (ngw == 2) SE_RG(2);
+  else if (ngw == 3) SE_RG(3);
+  else SE_RG(4);
+#undef SE_RG
+}
+
 // ------------------------------------------------------------------ top-k pages
 // One block per unit: page scores -> ascending view.  Up to BLOCK * E pages
 // the scores stay in registers (block_topk_reg); longer caches use the LDS /
@@ -289,7 +470,7 @@ se_status launch_quest(const se_cache& c, const void* q, const void* kmin, const
     if (c.d_k == 128 && G <= 16) SE_MF(128, 1);
     else if (c.d_k == 128 && G <= 32) SE_MF(128, 2);
     else if (c.d_k == 64 && G <= 16) SE_MF(64, 1);
-    else if (c.d_k == 576 && G <= 32) SE_MF(576, 2);
+    else if (c.d_k == 576 && G <= 32) launch_score_ring576<false>(c, q, kmin, kmax, seq_len, score, page_size, ncp, QuestAppendArgs{}, s);
     else done = false;
   }
 #undef SE_MF
@@ -347,7 +528,7 @@ se_status launch_quest_append(const se_cache& c, const void* q, void* k, void* v
     if (c.d_k == 128 && G <= 16) SE_AP(128, 1);
     else if (c.d_k == 128 && G <= 32) SE_AP(128, 2);
     else if (c.d_k == 64 && G <= 16) SE_AP(64, 1);
-    else if (c.d_k == 576 && G <= 32) SE_AP(576, 2);
+    else if (c.d_k == 576 && G <= 32) launch_score_ring576<true>(c, q, kmin, kmax, seq_len, score, page_size, ncp, ap, s);
     else fused = false;
 #undef SE_AP
   }
