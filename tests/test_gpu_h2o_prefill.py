@@ -23,6 +23,9 @@ CASES = {
     "d128_g16_ragged": (get_config(0, dtype="bf16", batch=1, n_q_heads=32, n_kv_heads=2, d_k=128, d_v=128), 1033, 100,
                         50),
     "d64_g4": (get_config(0, dtype="bf16", batch=2, n_q_heads=8, n_kv_heads=2), 333, 40, 16),
+    # G = 6: the (position, head) query rows straddle the 16-row MFMA column blocks
+    "d128_g6_ragged": (get_config(0, dtype="bf16", batch=2, n_q_heads=12, n_kv_heads=2, d_k=128, d_v=128), 1111, 90,
+                       33),
     "keep_all": (get_config(0, dtype="bf16", batch=1, n_q_heads=8, n_kv_heads=2), 90, 64, 32),
 }
 
