@@ -117,20 +117,27 @@ __global__ __launch_bounds__(256) void h2o_reg_kernel(
     sc[j] = ok ? a[s] : 0.f;
     if (s == ns) { p[j] = cur_pos; sc[j] = 0.f; }
   }
-  // accumulate: every occupied slot adds the group's softmax weight on it
+  // accumulate: every occupied slot adds the group's softmax weight on it, heads in
+  // ascending order; the logit loads of HC heads go out together (one memory round
+  // trip per HC heads, not per head)
+  constexpr int HC = E <= 8 ? 8 : 4;
   int cnt = 0;
-  for (int h = 0; h < G; ++h) {
-    const float l = lse[row0 + h];
-    if (l == -INFINITY) continue;
-    float x[E];
+  for (int h0 = 0; h0 < G; h0 += HC) {
+    float l[HC], x[HC][E];
 #pragma unroll
-    for (int j = 0; j < E; ++j) {
-      const int s = min(j * 256 + int(threadIdx.x), logit_cap - 1);
-      x[j] = lg[size_t(h) * logit_cap + s];
+    for (int hh = 0; hh < HC; ++hh) {
+      const int h = min(h0 + hh, G - 1);
+      l[hh] = h0 + hh < G ? lse[row0 + h] : -INFINITY;
+#pragma unroll
+      for (int j = 0; j < E; ++j) x[hh][j] = lg[size_t(h) * logit_cap + min(j * 256 + int(threadIdx.x), logit_cap - 1)];
     }
 #pragma unroll
-    for (int j = 0; j < E; ++j)
-      if (p[j] >= 0) sc[j] += expf(x[j] - l);
+    for (int hh = 0; hh < HC; ++hh) {
+      if (l[hh] == -INFINITY) continue;
+#pragma unroll
+      for (int j = 0; j < E; ++j)
+        if (p[j] >= 0) sc[j] += expf(x[hh][j] - l[hh]);
+    }
   }
 #pragma unroll
   for (int j = 0; j < E; ++j) {
@@ -213,14 +220,23 @@ __global__ __launch_bounds__(256) void omnikv_score_kernel(const float* __restri
   const float* lg = logits + row0 * logit_cap;
   const int j0 = blockIdx.x * 256 * OMNI_SPT + threadIdx.x;
   float p[OMNI_SPT] = {};
-  for (int h = 0; h < G; ++h) {
-    const float l = lse[row0 + h];
-    if (l == -INFINITY) continue;
-    float x[OMNI_SPT];
+  // heads in ascending order; the logit loads of 8 heads go out together
+  constexpr int HC = 8;
+  for (int h0 = 0; h0 < G; h0 += HC) {
+    float l[HC], x[HC][OMNI_SPT];
 #pragma unroll
-    for (int u = 0; u < OMNI_SPT; ++u) x[u] = lg[size_t(h) * logit_cap + min(j0 + 256 * u, logit_cap - 1)];
+    for (int hh = 0; hh < HC; ++hh) {
+      const int h = min(h0 + hh, G - 1);
+      l[hh] = h0 + hh < G ? lse[row0 + h] : -INFINITY;
 #pragma unroll
-    for (int u = 0; u < OMNI_SPT; ++u) p[u] += expf(x[u] - l);
+      for (int u = 0; u < OMNI_SPT; ++u) x[hh][u] = lg[size_t(h) * logit_cap + min(j0 + 256 * u, logit_cap - 1)];
+    }
+#pragma unroll
+    for (int hh = 0; hh < HC; ++hh) {
+      if (l[hh] == -INFINITY) continue;
+#pragma unroll
+      for (int u = 0; u < OMNI_SPT; ++u) p[u] += expf(x[hh][u] - l[hh]);
+    }
   }
 #pragma unroll
   for (int u = 0; u < OMNI_SPT; ++u)
