@@ -298,11 +298,11 @@ def run_snapkv(se, torch, args):
     vn = dev_grid(torch, (B, H, D), 26, torch.bfloat16)
     lse = torch.empty((B, Hq), device="cuda")
     ws_a = se.workspace(se.SE_OP_ATTN, oc, cap_out, 0)
+    ws_aa = se.workspace(se.SE_OP_APPEND_ATTN, oc, cap_out, 0)
 
-    def step(Ly):
-        se.se_kv_append(oc, Ly["k"], Ly["v"], kn, vn, None, Ly["seq"])
-        se.se_sparse_decode_attn(oc, q, Ly["k"], Ly["v"], Ly["seq"], None, None, 0, 1, cfg.softmax_scale,
-                                 Ly["out"], lse, ws=ws_a)
+    def step(Ly):   # append + attention over the compacted cache, one launch
+        se.se_kv_append_decode_attn(oc, q, Ly["k"], Ly["v"], kn, vn, None, Ly["seq"], None, None, 0, 1,
+                                    cfg.softmax_scale, Ly["out"], lse, ws=ws_aa)
 
     def attn(Ly):
         se.se_sparse_decode_attn(oc, q, Ly["k"], Ly["v"], Ly["seq"], None, None, 0, 1, cfg.softmax_scale,
@@ -362,13 +362,12 @@ def run_h2o(se, torch, args):
     vn = dev_grid(torch, (B, H, D), 28, torch.bfloat16)
     lse = torch.empty((B, Hq), device="cuda")
     logits = torch.empty((B, Hq, cap), device="cuda")
-    ws_a = se.workspace(se.SE_OP_ATTN, c, cap, 0)
+    ws_aa = se.workspace(se.SE_OP_APPEND_ATTN, c, cap, 0)
 
     # each captured layer slot runs at its own position; replays repeat the same work
-    def step(Ly):
-        se.se_kv_append(c, Ly["k"], Ly["v"], kn, vn, Ly["evict"], Ly["seq"])
-        se.se_sparse_decode_attn(c, q, Ly["k"], Ly["v"], Ly["seq"], None, None, 0, 1, cfg.softmax_scale, Ly["out"],
-                                 lse, logits, cap, 0, ws_a)
+    def step(Ly):   # the new row into the freed slot + attention with logits in one launch, then H2O
+        se.se_kv_append_decode_attn(c, q, Ly["k"], Ly["v"], kn, vn, Ly["evict"], Ly["seq"], None, None, 0, 1,
+                                    cfg.softmax_scale, Ly["out"], lse, logits, cap, 0, ws_aa)
         se.se_h2o_accumulate_evict(c, logits, lse, cap, Ly["seq"], Ly["pos"], Ly["acc"], Ly["cur"], heavy, recent,
                                    Ly["evict"])
 
@@ -455,22 +454,21 @@ def run_omnikv(se, torch, args):
     out = torch.empty((B, Hq, D), device="cuda")
     lse = torch.empty((B, Hq), device="cuda")
     logits = torch.empty((B, Hq, cap), device="cuda")
-    ws_dense = se.workspace(se.SE_OP_ATTN, c, cap, 0)
-    ws_sparse = se.workspace(se.SE_OP_ATTN, c, top, 0)
+    ws_dense = se.workspace(se.SE_OP_APPEND_ATTN, c, cap, 0)
+    ws_sparse = se.workspace(se.SE_OP_APPEND_ATTN, c, top, 0)
     ws_topk = se.workspace(se.SE_OP_OMNIKV, c, cap, top)
 
-    def sweep():
+    def sweep():   # every layer: the append and its attention in one launch
         for layer, (mode, src) in enumerate(plan):
-            se.se_kv_append(c, ks[layer], vs[layer], kn, vn, None, seqs[layer])
             if mode == "sparse":
-                se.se_sparse_decode_attn(c, qs[layer], ks[layer], vs[layer], seqs[layer], views[src], vlens[src], top,
-                                         1, cfg.softmax_scale, out, lse, ws=ws_sparse)
+                se.se_kv_append_decode_attn(c, qs[layer], ks[layer], vs[layer], kn, vn, None, seqs[layer], views[src],
+                                            vlens[src], top, 1, cfg.softmax_scale, out, lse, ws=ws_sparse)
             elif mode == "dense":
-                se.se_sparse_decode_attn(c, qs[layer], ks[layer], vs[layer], seqs[layer], None, None, 0, 1,
-                                         cfg.softmax_scale, out, lse, ws=ws_dense)
+                se.se_kv_append_decode_attn(c, qs[layer], ks[layer], vs[layer], kn, vn, None, seqs[layer], None, None,
+                                            0, 1, cfg.softmax_scale, out, lse, ws=ws_dense)
             else:
-                se.se_sparse_decode_attn(c, qs[layer], ks[layer], vs[layer], seqs[layer], None, None, 0, 1,
-                                         cfg.softmax_scale, out, lse, logits, cap, 0, ws_dense)
+                se.se_kv_append_decode_attn(c, qs[layer], ks[layer], vs[layer], kn, vn, None, seqs[layer], None, None,
+                                            0, 1, cfg.softmax_scale, out, lse, logits, cap, 0, ws_dense)
                 se.se_omnikv_topk(c, logits, lse, cap, seqs[layer], top, views[layer], vlens[layer], None, ws_topk)
 
     sweep()

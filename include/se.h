@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define SE_ABI_VERSION 3
+#define SE_ABI_VERSION 4
 
 typedef enum {
   SE_OK = 0,
@@ -90,7 +90,8 @@ typedef enum {
   SE_OP_SNAPKV = 3,     /* a0 = prompt_len, a1 = window */
   SE_OP_OMNIKV = 4,     /* a0 = logit_cap, a1 = top_k */
   SE_OP_QUEST_APPEND = 5, /* a0 = page_size (a1 unused) */
-  SE_OP_H2O_PREFILL = 6   /* a0 = prompt_len, a1 = recent_window */
+  SE_OP_H2O_PREFILL = 6,  /* a0 = prompt_len, a1 = recent_window */
+  SE_OP_APPEND_ATTN = 7   /* a0 = view_cap * granularity (slots per unit), a1 = num_splits (0 = auto) */
 } se_op;
 
 /* Append one decode token's K/V row to every unit (helper of the hooks: the
@@ -276,6 +277,29 @@ se_status se_sparse_decode_attn(const se_cache* c, const void* q, const void* k,
                                 float scale, float* out, float* lse, float* logits,
                                 int32_t logit_cap, int32_t num_splits,
                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* A decode step's append and attention in one launch (the hooks' append-then-
+ * attend, as for a SnapKV-compacted or H2O cache): the same results, bit for
+ * bit, as
+ *   se_kv_append(c, k, v, k_new, v_new, slot, seq_len)
+ * followed by
+ *   se_sparse_decode_attn(c, q, k, v, seq_len, view_idx, view_len, view_cap,
+ *                         granularity, scale, out, lse, logits, logit_cap,
+ *                         num_splits, ...).
+ * The attention reads the new rows from k_new / v_new where the view meets the
+ * slot they go to, one block per unit writes them into k / v, and seq_len is
+ * updated once every block of its batch row has read the old value (bf16 GQA
+ * caches the MFMA attention serves; other shapes run the two calls' kernels).
+ * Arguments as for those calls; k_new / v_new must be 16-byte aligned.
+ * ws: se_workspace_bytes(SE_OP_APPEND_ATTN, c, view_cap * granularity,
+ * num_splits) bytes, zero-filled once before first use (se_workspace_init);
+ * the call leaves its counters at zero. */
+se_status se_kv_append_decode_attn(const se_cache* c, const void* q, void* k, void* v, const void* k_new,
+                                   const void* v_new, const int32_t* slot, int32_t* seq_len,
+                                   const int32_t* view_idx, const int32_t* view_len, int32_t view_cap,
+                                   int32_t granularity, float scale, float* out, float* lse, float* logits,
+                                   int32_t logit_cap, int32_t num_splits, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
 
 /* SnapKV prefill-end eviction.  tokendh.com explainer, section
  * "把边界划在'生命周期'上": the method looks at how the last few prompt tokens

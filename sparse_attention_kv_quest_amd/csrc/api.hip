@@ -101,6 +101,7 @@ size_t se_workspace_bytes(int32_t op, const se_cache* c, int32_t a0, int32_t a1)
     case SE_OP_OMNIKV: return a0 > 0 ? omnikv_ws_bytes(*c, a0, a1) : 0;
     case SE_OP_QUEST_APPEND: return a0 > 0 ? quest_append_ws_bytes(*c, a0) : 0;
     case SE_OP_H2O_PREFILL: return (a0 > a1 && a1 > 0) ? h2o_prefill_ws_bytes(*c, a0, a1) : 0;
+    case SE_OP_APPEND_ATTN: return attn_append_ws_bytes(*c, a0 > 0 ? a0 : c->capacity, a1);
     default: return 0;
   }
 }
@@ -322,6 +323,36 @@ se_status se_sparse_decode_attn(const se_cache* c, const void* q, const void* k,
   if (st != SE_OK) return st;
   return attn_impl(c, q, k, v, seq_len, view_idx, view_len, view_cap, granularity, scale, out, lse, logits, logit_cap,
                    num_splits, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+se_status se_kv_append_decode_attn(const se_cache* c, const void* q, void* k, void* v, const void* k_new,
+                                   const void* v_new, const int32_t* slot, int32_t* seq_len,
+                                   const int32_t* view_idx, const int32_t* view_len, int32_t view_cap,
+                                   int32_t granularity, float scale, float* out, float* lse, float* logits,
+                                   int32_t logit_cap, int32_t num_splits, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  se_status st = check_cache(c);
+  if (st != SE_OK) return st;
+  if (!q || !k || !k_new || !seq_len || !out || (!c->latent && (!v || !v_new))) return SE_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(k_new) || !aligned16(out) ||
+      (!c->latent && (!aligned16(v) || !aligned16(v_new))))
+    return SE_ERR_ALIGN;
+  if (view_idx) {
+    if (!view_len) return SE_ERR_NULL;
+    if (view_cap <= 0 || granularity <= 0) return SE_ERR_SHAPE;
+    if (int64_t(view_cap) * granularity > (int64_t(1) << 30)) return SE_ERR_SHAPE;
+  }
+  if (logits && logit_cap <= 0) return SE_ERR_SHAPE;
+  if (num_splits < 0 || num_splits > 256) return SE_ERR_SHAPE;
+  if (!(scale > 0.f) || !(scale < 1e30f)) return SE_ERR_SHAPE;
+  const int slots = view_idx ? view_cap * granularity : c->capacity;
+  if (!ws || ws_bytes < attn_append_ws_bytes(*c, slots, num_splits)) return SE_ERR_WORKSPACE;
+  SE_TRACE_CALL("kv_append_decode_attn B=%d Hq=%d Hkv=%d d_k=%d view=%s cap=%d g=%d splits=%d slot=%p logits=%d",
+                c->batch, c->n_q_heads, c->n_kv_heads, c->d_k, view_idx ? "idx" : "identity", view_cap, granularity,
+                num_splits, (const void*)slot, logits ? logit_cap : 0);
+  clear_stale_error();
+  return launch_append_attn(*c, q, k, v, k_new, v_new, slot, seq_len, view_idx, view_len, view_cap, granularity,
+                            scale, out, lse, logits, logit_cap, num_splits, ws, stream);
 }
 
 se_status se_snapkv_score_compact(const se_cache* c, const void* q_obs, const void* k, const void* v,

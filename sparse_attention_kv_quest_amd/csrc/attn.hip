@@ -228,6 +228,41 @@ se_status launch_attn_vector(const AttnArgs& a, hipStream_t s) {
   return launch_status();
 }
 
+// Fused append + attention: per batch row a ticket counter, then the attention workspace.
+static size_t attn_row_ctr_bytes(const se_cache& c) { return (size_t(c.batch) * sizeof(int) + 255) / 256 * 256; }
+
+size_t attn_append_ws_bytes(const se_cache& c, int slots, int num_splits) {
+  return attn_row_ctr_bytes(c) + attn_ws_bytes(c, slots, num_splits);
+}
+
+se_status launch_append_attn(const se_cache& c, const void* q, void* k, void* v, const void* k_new,
+                             const void* v_new, const int32_t* slot, int32_t* seq_len, const int32_t* view_idx,
+                             const int32_t* view_len, int view_cap, int granularity, float scale, float* out,
+                             float* lse, float* logits, int logit_cap, int num_splits, void* ws, hipStream_t s) {
+  void* aws = (char*)ws + attn_row_ctr_bytes(c);
+  AttnArgs a = make_attn_args(c, q, k, v, seq_len, view_idx, view_len, view_cap, granularity, scale, out,
+                              lse, logits, logit_cap);
+  const int slots = view_idx ? view_cap * granularity : c.capacity;
+  a.splits = num_splits > 0 ? num_splits : attn_auto_splits(c, slots);
+  if (!attn_mfma_supported(a)) {   // other shapes: the two calls' kernels (the same results)
+    se_status st = launch_kv_append(c, k, v, k_new, v_new, slot, seq_len, s);
+    if (st != SE_OK) return st;
+    return launch_attn(c, q, k, v, seq_len, view_idx, view_len, view_cap, granularity, scale, out, lse, logits,
+                       logit_cap, num_splits, aws, s);
+  }
+  a.counters = (int*)aws;
+  a.part_ml = (float*)((char*)aws + attn_counter_bytes(c));
+  a.part_o = a.part_ml + size_t(a.B) * a.Hkv * a.splits * a.G * 2;
+  a.fused = a.splits > 1 && size_t(a.splits) * std::min(a.G, 32) * a.Dv * sizeof(float) <= ATTN_FUSED_MERGE_BYTES;
+  a.app = 1;
+  a.k_new = k_new; a.v_new = v_new; a.k_w = k; a.v_w = v;
+  a.slot = slot; a.seq_len_w = seq_len; a.row_ctr = (int*)ws;
+  se_status st = launch_attn_mfma(a, s);
+  if (st != SE_OK || a.splits == 1 || a.fused) return st;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(a.G, a.B * a.Hkv), dim3(128), 0, s, a);
+  return launch_status();
+}
+
 se_status launch_attn(const se_cache& c, const void* q, const void* k, const void* v,
                       const int32_t* seq_len, const int32_t* view_idx, const int32_t* view_len,
                       int view_cap, int granularity, float scale, float* out, float* lse,

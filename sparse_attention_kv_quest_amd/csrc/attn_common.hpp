@@ -24,6 +24,15 @@ struct AttnArgs {
   int B, Hq, Hkv, G, Dk, Dv, cap, latent, dtype;
   int k_stride, v_stride;  // elements per K / V row
   int view_cap, gran, gshift, logit_cap, splits;   // gshift = log2(gran) or -1
+  // Fused append (app != 0): before attending, row (b, h) of k_new / v_new goes to
+  // the cache by se_kv_append's rule (slot[b][h] if slot is given and >= 0, else
+  // slot seq_len[b]; a slot at or past the capacity is dropped; seq_len[b] grows
+  // by one unless slot[b][0] >= 0).  The launch reads that row from k_new / v_new,
+  // one block per unit writes it into k_w / v_w, and the block holding the last
+  // ticket of the batch row (row_ctr[b], taken once the old length is read) stores
+  // the new length into seq_len_w.
+  const void* k_new; const void* v_new; void* k_w; void* v_w;
+  const int32_t* slot; int32_t* seq_len_w; int* row_ctr; int app;
 };
 
 // Number of view slots of a unit: view entries times granularity, or seq_len for the identity view.

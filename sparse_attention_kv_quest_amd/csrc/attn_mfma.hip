@@ -63,7 +63,10 @@ struct MfCtx {
   const uint8_t* ksc;    // FP8: scale bytes of the unit's rows
   const uint8_t* vsc;
   const int32_t* vglob;  // view entries in global memory (used when they do not fit the LDS cache)
+  const uint16_t* knew;  // fused append: the unit's new K / V rows, read in place of cache slot tgt
+  const uint16_t* vnew;
   int e0, len, s1, gshift;
+  int tgt;               // fused append: the slot receiving the new row (-2: none)
   bool identity;
 };
 
@@ -84,7 +87,7 @@ __device__ __forceinline__ int mf_token(const MfCtx& x, int s) {
   return (s < x.s1 && t >= 0 && t < x.len) ? t : -1;
 }
 
-template <int D, bool VC>
+template <int D, bool VC, bool APP = false>
 __device__ __forceinline__ void mf_load(const MfCtx& x, int base, int lane, MfTile<D>& T) {
   constexpr int NKS = D / 32, VPASS = D / 64;
   const int g = lane >> 4, c16 = lane & 15, qa = lane & 7;
@@ -105,16 +108,32 @@ __device__ __forceinline__ void mf_load(const MfCtx& x, int base, int lane, MfTi
   // the loads unconditional keeps the compiler's wait counters exact across the
   // prefetch.  Offsets stay 32-bit within the unit.
   const uint32_t r0 = uint32_t(max(T.tk0, 0)) * D + 8 * g, r1 = uint32_t(max(T.tk1, 0)) * D + 8 * g;
+  if constexpr (APP) {   // the slot receiving the new row reads it from k_new / v_new
+    const uint16_t* p0 = T.tk0 == x.tgt ? x.knew + 8 * g : x.ku + r0;
+    const uint16_t* p1 = T.tk1 == x.tgt ? x.knew + 8 * g : x.ku + r1;
 #pragma unroll
-  for (int c = 0; c < NKS; ++c) {
-    T.k0[c] = ld16(x.ku + r0 + 32 * c);
-    T.k1[c] = ld16(x.ku + r1 + 32 * c);
-  }
+    for (int c = 0; c < NKS; ++c) {
+      T.k0[c] = ld16(p0 + 32 * c);
+      T.k1[c] = ld16(p1 + 32 * c);
+    }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint32_t rv = uint32_t(max(vtok[r], 0)) * D + 8 * (lane >> 3);
+    for (int r = 0; r < 4; ++r) {
+      const uint16_t* pv = vtok[r] == x.tgt ? x.vnew + 8 * (lane >> 3) : x.vu + uint32_t(max(vtok[r], 0)) * D + 8 * (lane >> 3);
 #pragma unroll
-    for (int p = 0; p < VPASS; ++p) T.v[p][r] = ld16(x.vu + rv + 64 * p);
+      for (int p = 0; p < VPASS; ++p) T.v[p][r] = ld16(pv + 64 * p);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < NKS; ++c) {
+      T.k0[c] = ld16(x.ku + r0 + 32 * c);
+      T.k1[c] = ld16(x.ku + r1 + 32 * c);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t rv = uint32_t(max(vtok[r], 0)) * D + 8 * (lane >> 3);
+#pragma unroll
+      for (int p = 0; p < VPASS; ++p) T.v[p][r] = ld16(x.vu + rv + 64 * p);
+    }
   }
 }
 
@@ -292,10 +311,10 @@ __device__ __forceinline__ void mf_compute(const AttnArgs& a, const MfCtx& x, in
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int D, bool VC, bool F8>
+template <int D, bool VC, bool F8, bool APP>
 __device__ __forceinline__ void mf_fetch(const MfCtx& x, int base, int lane, MfRaw<D, F8>& T) {
   if constexpr (F8) mf_load_f8<D, VC>(x, base, lane, T);
-  else mf_load<D, VC>(x, base, lane, T);
+  else mf_load<D, VC, APP>(x, base, lane, T);
 }
 
 template <int D, bool F8>
@@ -311,9 +330,10 @@ __device__ __forceinline__ void mf_step(const AttnArgs& a, const MfCtx& x, int b
   }
 }
 
-template <int D, bool VC, int OCC, bool F8>
+template <int D, bool VC, int OCC, bool F8, bool APP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void attn_mfma_kernel(AttnArgs a) {
+  static_assert(!(APP && F8), "the fused append writes bf16 rows");
   constexpr int PITCH = MF_TS + 4;          // u16 per transposed V row (72 bytes)
   constexpr int NDB = D / 16;
   constexpr int NKS = D / 32;
@@ -350,7 +370,30 @@ void attn_mfma_kernel(AttnArgs a) {
       ventry[j] = e < e1 ? vrow[e] : -1;
     }
   }
-  const int len = min(a.seq_len[b], a.cap);
+  const int len0 = min(a.seq_len[b], a.cap);
+  int len = len0, tgt = -2, row_ticket = 0;
+  if constexpr (APP) {
+    // se_kv_append's rule, per unit; every block of the batch row takes a ticket
+    // once the old length is read, and the last one stores the new length
+    const bool bump = a.slot == nullptr || a.slot[size_t(b) * a.Hkv] < 0;
+    const int sl = a.slot != nullptr ? a.slot[unit] : -1;
+    const int pos = sl >= 0 ? sl : len0;
+    tgt = (pos >= 0 && pos < a.cap) ? pos : -2;
+    if (bump && len0 < a.cap) len = len0 + 1;
+    if (threadIdx.x == 0) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0);   // the old length has been read
+      row_ticket = __hip_atomic_fetch_add(a.row_ctr + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    }
+    if (split == 0 && tgt >= 0 && threadIdx.x < 2 * (D / 8)) {   // the cache row, for later steps
+      const bool isv = threadIdx.x >= D / 8;
+      const int o = 8 * (isv ? threadIdx.x - D / 8 : threadIdx.x);
+      const uint16_t* src = static_cast<const uint16_t*>(isv ? a.v_new : a.k_new) + size_t(unit) * D + o;
+      uint16_t* dst = static_cast<uint16_t*>(isv ? a.v_w : a.k_w) + (size_t(unit) * a.cap + tgt) * D + o;
+      *reinterpret_cast<u32x4*>(dst) = ld16(src);
+    }
+  }
   if (!VC) {
     const int n_slots = identity ? len : a.view_cap * a.gran;
     int chunk = (n_slots + a.splits - 1) / a.splits;
@@ -371,6 +414,9 @@ void attn_mfma_kernel(AttnArgs a) {
   x.gshift = a.gshift;
   x.identity = identity;
   x.e0 = e0;
+  x.tgt = tgt;
+  x.knew = APP ? static_cast<const uint16_t*>(a.k_new) + size_t(unit) * D : nullptr;
+  x.vnew = APP ? static_cast<const uint16_t*>(a.v_new) + size_t(unit) * D : nullptr;
   x.vglob = identity ? nullptr : a.view_idx + size_t(unit) * a.view_cap;
 
   // Q as the B operand: lane holds head c16, dims 32c + 8g .. 32c + 8g + 7 of k-step c
@@ -414,26 +460,26 @@ void attn_mfma_kernel(AttnArgs a) {
   if (OCC == 1) {
     MfRaw<D, F8> T0, T1, T2;               // two tiles in flight while a third is computed
     if (nmine == 1) {
-      mf_fetch<D, VC, F8>(x, first, lane, T0);
+      mf_fetch<D, VC, F8, APP>(x, first, lane, T0);
       mf_step<D, F8>(a, x, first, lane, qv, sc2, lg_row, vt, T0, st);
     } else if (nmine > 1) {
-      mf_fetch<D, VC, F8>(x, first, lane, T0);
-      mf_fetch<D, VC, F8>(x, first + STEP, lane, T1);
+      mf_fetch<D, VC, F8, APP>(x, first, lane, T0);
+      mf_fetch<D, VC, F8, APP>(x, first + STEP, lane, T1);
       int i = 0;
       for (; i + 4 < nmine; i += 3) {      // T0 = tile i, T1 = tile i + 1 in flight
         const int b0 = first + i * STEP;
-        mf_fetch<D, VC, F8>(x, b0 + 2 * STEP, lane, T2);
+        mf_fetch<D, VC, F8, APP>(x, b0 + 2 * STEP, lane, T2);
         mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_row, vt, T0, st);
-        mf_fetch<D, VC, F8>(x, b0 + 3 * STEP, lane, T0);
+        mf_fetch<D, VC, F8, APP>(x, b0 + 3 * STEP, lane, T0);
         mf_step<D, F8>(a, x, b0 + STEP, lane, qv, sc2, lg_row, vt, T1, st);
-        mf_fetch<D, VC, F8>(x, b0 + 4 * STEP, lane, T1);
+        mf_fetch<D, VC, F8, APP>(x, b0 + 4 * STEP, lane, T1);
         mf_step<D, F8>(a, x, b0 + 2 * STEP, lane, qv, sc2, lg_row, vt, T2, st);
       }
       const int r = nmine - i;             // 2, 3 or 4 tiles left
       const int b0 = first + i * STEP;
-      if (r >= 3) mf_fetch<D, VC, F8>(x, b0 + 2 * STEP, lane, T2);
+      if (r >= 3) mf_fetch<D, VC, F8, APP>(x, b0 + 2 * STEP, lane, T2);
       mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_row, vt, T0, st);
-      if (r == 4) mf_fetch<D, VC, F8>(x, b0 + 3 * STEP, lane, T0);
+      if (r == 4) mf_fetch<D, VC, F8, APP>(x, b0 + 3 * STEP, lane, T0);
       mf_step<D, F8>(a, x, b0 + STEP, lane, qv, sc2, lg_row, vt, T1, st);
       if (r >= 3) mf_step<D, F8>(a, x, b0 + 2 * STEP, lane, qv, sc2, lg_row, vt, T2, st);
       if (r == 4) mf_step<D, F8>(a, x, b0 + 3 * STEP, lane, qv, sc2, lg_row, vt, T0, st);
@@ -441,18 +487,18 @@ void attn_mfma_kernel(AttnArgs a) {
   } else {
     MfRaw<D, F8> T0, T1;                   // one tile in flight while the other is computed
     if (nmine > 0) {
-      mf_fetch<D, VC, F8>(x, first, lane, T0);
+      mf_fetch<D, VC, F8, APP>(x, first, lane, T0);
       int i = 0;
       for (; i + 2 < nmine; i += 2) {      // T0 = tile i in flight
         const int b0 = first + i * STEP;
-        mf_fetch<D, VC, F8>(x, b0 + STEP, lane, T1);
+        mf_fetch<D, VC, F8, APP>(x, b0 + STEP, lane, T1);
         mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_row, vt, T0, st);
-        mf_fetch<D, VC, F8>(x, b0 + 2 * STEP, lane, T0);
+        mf_fetch<D, VC, F8, APP>(x, b0 + 2 * STEP, lane, T0);
         mf_step<D, F8>(a, x, b0 + STEP, lane, qv, sc2, lg_row, vt, T1, st);
       }
       const int b0 = first + i * STEP;     // one or two tiles left
       if (i + 1 < nmine) {
-        mf_fetch<D, VC, F8>(x, b0 + STEP, lane, T1);
+        mf_fetch<D, VC, F8, APP>(x, b0 + STEP, lane, T1);
         mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_row, vt, T0, st);
         mf_step<D, F8>(a, x, b0 + STEP, lane, qv, sc2, lg_row, vt, T1, st);
       } else {
@@ -516,6 +562,10 @@ void attn_mfma_kernel(AttnArgs a) {
     int* ctr = a.counters + unit * ATTN_MAX_HG;
     if (attn_split_done(ctr, a.splits)) attn_merge_splits<256>(a, unit, 0, G, ctr);
   }
+  if (APP && threadIdx.x == 0 && row_ticket == a.Hkv * a.splits - 1) {   // every block of the row has read it
+    if (len != len0) a.seq_len_w[b] = len;
+    ticket_reset(a.row_ctr + b);
+  }
 }
 
 bool attn_mfma_supported(const AttnArgs& a) {
@@ -540,14 +590,21 @@ se_status launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
   int chunk = (slots + a.splits - 1) / a.splits;
   chunk = (chunk + MF_TS - 1) / MF_TS * MF_TS;
   const bool vc = a.view_idx != nullptr && chunk / a.gran + 2 <= MF_VCACHE;
-#define SE_MF_LAUNCH(DD, VV, OO, FF) hipLaunchKernelGGL((attn_mfma_kernel<DD, VV, OO, FF>), grid, dim3(256), 0, s, a)
-#define SE_MF_D(FF)                                                                  \
-  if (a.Dk == 128) {                                                                 \
-    if (vc) SE_MF_LAUNCH(128, true, 2, FF); else SE_MF_LAUNCH(128, false, 2, FF);    \
-  } else {                                                                           \
-    if (vc) SE_MF_LAUNCH(64, true, 1, FF); else SE_MF_LAUNCH(64, false, 1, FF);      \
+#define SE_MF_LAUNCH(DD, VV, OO, FF, AA) \
+  hipLaunchKernelGGL((attn_mfma_kernel<DD, VV, OO, FF, AA>), grid, dim3(256), 0, s, a)
+#define SE_MF_D(FF, AA)                                                                              \
+  if (a.Dk == 128) {                                                                                 \
+    if (vc) SE_MF_LAUNCH(128, true, 2, FF, AA); else SE_MF_LAUNCH(128, false, 2, FF, AA);            \
+  } else {                                                                                           \
+    if (vc) SE_MF_LAUNCH(64, true, 1, FF, AA); else SE_MF_LAUNCH(64, false, 1, FF, AA);              \
   }
-  if (a.fp8) { SE_MF_D(true) } else { SE_MF_D(false) }
+  if (a.app) {   // the fused append writes bf16 rows
+    SE_MF_D(false, true)
+  } else if (a.fp8) {
+    SE_MF_D(true, false)
+  } else {
+    SE_MF_D(false, false)
+  }
 #undef SE_MF_D
 #undef SE_MF_LAUNCH
   return launch_status();

@@ -473,6 +473,11 @@ se_status launch_quest(const se_cache& c, const void* q, const void* kmin, const
 int attn_auto_splits(const se_cache& c, int slots);
 size_t attn_ws_bytes(const se_cache& c, int slots, int num_splits);
 // k_scale / v_scale non-null: K / V hold FP8 rows with one scale byte per row.
+size_t attn_append_ws_bytes(const se_cache& c, int slots, int num_splits);
+se_status launch_append_attn(const se_cache& c, const void* q, void* k, void* v, const void* k_new,
+                             const void* v_new, const int32_t* slot, int32_t* seq_len, const int32_t* view_idx,
+                             const int32_t* view_len, int view_cap, int granularity, float scale, float* out,
+                             float* lse, float* logits, int logit_cap, int num_splits, void* ws, hipStream_t s);
 se_status launch_attn(const se_cache& c, const void* q, const void* k, const void* v,
                       const int32_t* seq_len, const int32_t* view_idx, const int32_t* view_len,
                       int view_cap, int granularity, float scale, float* out, float* lse,

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert se.se_abi_version() == 3
+    assert se.se_abi_version() == 4
     assert se.se_status_string(0) == "ok"
     assert se.se_status_string(-6) == "workspace too small"
     assert se.se_status_string(123) == "unknown status"
