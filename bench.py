@@ -584,10 +584,12 @@ def run_streaming(se, torch, args):
         se.se_sparse_decode_attn(c, q, Ly["k"], Ly["v"], Ly["seq"], Ly["view"], Ly["vlen"], vc, 1, cfg.softmax_scale,
                                  Ly["out"], lse, ws=ws_a)
 
-    def step(Ly):
-        se.se_kv_append(c, Ly["k"], Ly["v"], kn, vn, None, Ly["seq"])
-        se.se_streaming_view(c, Ly["seq"], sink, recent, Ly["view"], Ly["vlen"])
-        attn(Ly)
+    ws_aa = se.workspace(se.SE_OP_APPEND_ATTN, c, vc, 0)
+
+    def step(Ly):   # the view one append ahead, then the append and the attention in one launch
+        se.se_streaming_view(c, Ly["seq"], sink, recent, Ly["view"], Ly["vlen"], 1)
+        se.se_kv_append_decode_attn(c, q, Ly["k"], Ly["v"], kn, vn, None, Ly["seq"], Ly["view"], Ly["vlen"], vc, 1,
+                                    cfg.softmax_scale, Ly["out"], lse, ws=ws_aa)
 
     for Ly in lay:
         step(Ly)

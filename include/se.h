@@ -206,13 +206,17 @@ se_status se_sparse_decode_attn_fp8(const se_cache* c, const void* q, const void
 /* StreamingLLM view (Netics blog "SparseEngine 统一接入十五种稀疏注意力", section
  * "哪些情况下加速幅度会缩小": named there beside PyramidKV and SnapKV).  Unit
  * (b, h) attends over the first `sink` and the last `recent` positions below
- * seq_len[b]: view_idx [B][Hkv][view_cap] int32 gets those positions in
- * ascending order (-1 after them), view_len [B][Hkv] their count
- * min(seq_len, sink + recent).  Hand it to se_sparse_decode_attn with
+ * the length L = min(seq_len[b] + pending, capacity): view_idx
+ * [B][Hkv][view_cap] int32 gets those positions in ascending order (-1 after
+ * them), view_len [B][Hkv] their count min(L, sink + recent).  pending = 0
+ * gives the view of the cache as it is; pending = 1 the view it will have after
+ * the next append, for se_kv_append_decode_attn.  Hand it to the attention with
  * granularity 1.  sink, recent >= 0, sink + recent >= 1 and
- * view_cap >= sink + recent, else SE_ERR_BUDGET. */
+ * view_cap >= sink + recent, else SE_ERR_BUDGET; 0 <= pending <= capacity,
+ * else SE_ERR_SHAPE. */
 se_status se_streaming_view(const se_cache* c, const int32_t* seq_len, int32_t sink, int32_t recent,
-                            int32_t* view_idx, int32_t* view_len, int32_t view_cap, hipStream_t stream);
+                            int32_t* view_idx, int32_t* view_len, int32_t view_cap, int32_t pending,
+                            hipStream_t stream);
 
 /* PyramidKV layer budgets (same page and section; host computation, no GPU
  * work).  budgets: HOST int32 [n_layers]; layer l (0 = first) gets

@@ -53,7 +53,7 @@ _SIGS = {
     "se_sparse_decode_attn": [_C, _P, _P, _P, _P, _P, _P, _I32, _I32, _F32, _P, _P, _P, _I32, _I32, _P, _SZ, _P],
     "se_kv_append_decode_attn": [_C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _F32, _P, _P, _P, _I32, _I32, _P,
                                  _SZ, _P],
-    "se_streaming_view": [_C, _P, _I32, _I32, _P, _P, _I32, _P],
+    "se_streaming_view": [_C, _P, _I32, _I32, _P, _P, _I32, _I32, _P],
     "se_kv_quantize_fp8": [_C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P],
     "se_kv_append_fp8": [_C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P],
     "se_sparse_decode_attn_fp8": [_C, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _F32, _P, _P, _P, _I32, _I32, _P, _SZ,
@@ -207,9 +207,9 @@ def se_sparse_decode_attn_fp8(c, q, k_q, v_q, k_scale, v_scale, seq_len, view_id
         _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
-def se_streaming_view(c, seq_len, sink, recent, view_idx, view_len, stream=None):
+def se_streaming_view(c, seq_len, sink, recent, view_idx, view_len, pending=0, stream=None):
     _check("se_streaming_view", load().se_streaming_view(ctypes.byref(c), _ptr(seq_len), sink, recent, _ptr(view_idx),
-                                                         _ptr(view_len), view_idx.shape[-1], _stream(stream)))
+                                                         _ptr(view_len), view_idx.shape[-1], pending, _stream(stream)))
 
 
 def se_h2o_prefill_init(c, q_prompt, k, v, prompt_len, heavy, recent, scale, slots, k_slots, v_slots, slot_pos, acc,

@@ -256,16 +256,18 @@ se_status se_sparse_decode_attn_fp8(const se_cache* c, const void* q, const void
 }
 
 se_status se_streaming_view(const se_cache* c, const int32_t* seq_len, int32_t sink, int32_t recent,
-                            int32_t* view_idx, int32_t* view_len, int32_t view_cap, hipStream_t stream) {
+                            int32_t* view_idx, int32_t* view_len, int32_t view_cap, int32_t pending,
+                            hipStream_t stream) {
   se_status st = check_cache(c);
   if (st != SE_OK) return st;
   if (!seq_len || !view_idx || !view_len) return SE_ERR_NULL;
   if (sink < 0 || recent < 0 || int64_t(sink) + recent < 1 || view_cap < int64_t(sink) + recent)
     return SE_ERR_BUDGET;
+  if (pending < 0 || pending > c->capacity) return SE_ERR_SHAPE;
   SE_TRACE_CALL("streaming_view B=%d Hkv=%d sink=%d recent=%d cap=%d", c->batch, c->n_kv_heads, sink, recent,
                 view_cap);
   clear_stale_error();
-  return launch_streaming_view(*c, seq_len, sink, recent, view_idx, view_len, view_cap, stream);
+  return launch_streaming_view(*c, seq_len, sink, recent, view_idx, view_len, view_cap, pending, stream);
 }
 
 se_status se_chain_match(const int32_t* tokens, int32_t n_tokens, const int32_t* const* prefixes,

@@ -29,8 +29,8 @@ struct AttnArgs {
   // slot seq_len[b]; a slot at or past the capacity is dropped; seq_len[b] grows
   // by one unless slot[b][0] >= 0).  The launch reads that row from k_new / v_new,
   // one block per unit writes it into k_w / v_w, and the block holding the last
-  // ticket of the batch row (row_ctr[b], taken once the old length is read) stores
-  // the new length into seq_len_w.
+  // ticket of the batch row (row_ctr[b], taken after its tiles, long after it read
+  // the old length) stores the new length into seq_len_w.
   const void* k_new; const void* v_new; void* k_w; void* v_w;
   const int32_t* slot; int32_t* seq_len_w; int* row_ctr; int app;
 };

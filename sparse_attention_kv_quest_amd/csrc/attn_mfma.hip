@@ -372,26 +372,18 @@ void attn_mfma_kernel(AttnArgs a) {
   }
   const int len0 = min(a.seq_len[b], a.cap);
   int len = len0, tgt = -2, row_ticket = 0;
+  u32x4 app_row = {0, 0, 0, 0};   // this thread's 16 bytes of the new row, stored after the tiles
   if constexpr (APP) {
-    // se_kv_append's rule, per unit; every block of the batch row takes a ticket
-    // once the old length is read, and the last one stores the new length
+    // se_kv_append's rule, per unit
     const bool bump = a.slot == nullptr || a.slot[size_t(b) * a.Hkv] < 0;
     const int sl = a.slot != nullptr ? a.slot[unit] : -1;
     const int pos = sl >= 0 ? sl : len0;
     tgt = (pos >= 0 && pos < a.cap) ? pos : -2;
     if (bump && len0 < a.cap) len = len0 + 1;
-    if (threadIdx.x == 0) {
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      __builtin_amdgcn_s_waitcnt(0);   // the old length has been read
-      row_ticket = __hip_atomic_fetch_add(a.row_ctr + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    }
     if (split == 0 && tgt >= 0 && threadIdx.x < 2 * (D / 8)) {   // the cache row, for later steps
       const bool isv = threadIdx.x >= D / 8;
       const int o = 8 * (isv ? threadIdx.x - D / 8 : threadIdx.x);
-      const uint16_t* src = static_cast<const uint16_t*>(isv ? a.v_new : a.k_new) + size_t(unit) * D + o;
-      uint16_t* dst = static_cast<uint16_t*>(isv ? a.v_w : a.k_w) + (size_t(unit) * a.cap + tgt) * D + o;
-      *reinterpret_cast<u32x4*>(dst) = ld16(src);
+      app_row = ld16(static_cast<const uint16_t*>(isv ? a.v_new : a.k_new) + size_t(unit) * D + o);
     }
   }
   if (!VC) {
@@ -507,6 +499,18 @@ void attn_mfma_kernel(AttnArgs a) {
     }
   }
 
+  if (APP && threadIdx.x == 0) {
+    // every block of the batch row takes a ticket, long after it read the old length
+    // (issued here, not up front, so that no tile's loads wait for its return); the
+    // last one stores the new length at the end
+    row_ticket = __hip_atomic_fetch_add(a.row_ctr + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (APP && split == 0 && tgt >= 0 && threadIdx.x < 2 * (D / 8)) {   // its load went out before the tiles
+    const bool isv = threadIdx.x >= D / 8;
+    const int o = 8 * (isv ? threadIdx.x - D / 8 : threadIdx.x);
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(isv ? a.v_w : a.k_w) + (size_t(unit) * a.cap + tgt) * D + o) =
+        app_row;
+  }
   // ---- merge the waves of the block: per head, the waves' (max, sum) and
   // outputs [wave][head][dim] (row pitch D + 4) go through LDS; a thread then
   // owns four consecutive dims of one head.

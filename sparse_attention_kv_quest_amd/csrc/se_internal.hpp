@@ -447,7 +447,7 @@ se_status launch_kv_append_meta(const se_cache& c, void* k, void* v, const void*
 size_t quest_ws_bytes(const se_cache& c, int page_size, int top_pages);
 size_t quest_append_ws_bytes(const se_cache& c, int page_size);
 se_status launch_streaming_view(const se_cache& c, const int32_t* seq_len, int sink, int recent,
-                                int32_t* view_idx, int32_t* view_len, int view_cap, hipStream_t s);
+                                int32_t* view_idx, int32_t* view_len, int view_cap, int pending, hipStream_t s);
 void pyramid_budgets(int n, int avg, int bmin, int32_t* out);
 se_status launch_h2o_prefill_scores(const se_cache& c, const void* q, const void* k, int L, int n_cand, float scale,
                                     float* lse2, float* acc0, float* votes, hipStream_t s);

@@ -22,9 +22,9 @@ namespace se {
 __global__ __launch_bounds__(256) void streaming_view_kernel(const int32_t* __restrict__ seq_len,
                                                              int32_t* __restrict__ view_idx,
                                                              int32_t* __restrict__ view_len, int Hkv, int cap,
-                                                             int sink, int recent, int view_cap) {
+                                                             int sink, int recent, int view_cap, int pending) {
   const int unit = blockIdx.x, b = unit / Hkv;
-  const int len = min(max(seq_len[b], 0), cap);
+  const int len = int(min(int64_t(max(seq_len[b], 0)) + pending, int64_t(cap)));   // after `pending` appends
   const int n_head = min(sink, len);
   const int tail0 = max(n_head, len - recent);    // first recent position not already in the sink
   const int n = n_head + (len - tail0);
@@ -35,9 +35,9 @@ __global__ __launch_bounds__(256) void streaming_view_kernel(const int32_t* __re
 }
 
 se_status launch_streaming_view(const se_cache& c, const int32_t* seq_len, int sink, int recent,
-                                int32_t* view_idx, int32_t* view_len, int view_cap, hipStream_t s) {
+                                int32_t* view_idx, int32_t* view_len, int view_cap, int pending, hipStream_t s) {
   hipLaunchKernelGGL(streaming_view_kernel, dim3(c.batch * c.n_kv_heads), dim3(256), 0, s, seq_len, view_idx,
-                     view_len, c.n_kv_heads, c.capacity, sink, recent, view_cap);
+                     view_len, c.n_kv_heads, c.capacity, sink, recent, view_cap, pending);
   return launch_status();
 }
 

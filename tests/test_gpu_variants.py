@@ -37,6 +37,61 @@ def test_streaming_view_matches_oracle(se, sink, recent):
     np.testing.assert_array_equal(host(view), rv)
 
 
+@pytest.mark.parametrize("pending", [1, 3])
+def test_streaming_view_ahead_of_appends(se, pending):
+    """pending > 0: the view of the length seq_len + pending (capped at the capacity)."""
+    banner(f"streaming view pending={pending}")
+    B, H, cap, sink, recent = 5, 3, 3000, 4, 60
+    lens = [0, 1, sink + recent - 1, cap - 2, cap]
+    c = se.cache(B, 2 * H, H, 64, 64, cap, "bf16")
+    vc = sink + recent
+    view = torch.full((B, H, vc), 77, dtype=torch.int32, device="cuda")
+    vlen = torch.full((B, H), 77, dtype=torch.int32, device="cuda")
+    se.se_streaming_view(c, torch.tensor(lens, dtype=torch.int32, device="cuda"), sink, recent, view, vlen, pending)
+    torch.cuda.synchronize()
+    rv, rl = ov.streaming_view([min(x + pending, cap) for x in lens], H, sink, recent, vc)
+    np.testing.assert_array_equal(host(vlen), rl)
+    np.testing.assert_array_equal(host(view), rv)
+
+
+def test_streaming_step_with_fused_append(se):
+    """The view taken one append ahead, then se_kv_append_decode_attn, gives the same
+    caches, lengths and outputs (bit for bit) as append, view, attention."""
+    cfg = get_config(0, dtype="bf16", batch=2, n_q_heads=16, n_kv_heads=2, d_k=128, d_v=128, context=900)
+    banner("streaming step with the fused append")
+    B, H, Hq, D = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.d_k
+    cap, sink, recent = cfg.context + 8, 4, 200
+    vc = sink + recent
+    K, V = gen.cache_kv(cfg, 6, cap)
+    side = {}
+    for t in ("fused", "sep"):
+        side[t] = dict(k=dev(K, torch.bfloat16), v=dev(V, torch.bfloat16),
+                       seq=torch.tensor([cfg.context, 150], dtype=torch.int32, device="cuda"),
+                       view=torch.zeros((B, H, vc), dtype=torch.int32, device="cuda"),
+                       vlen=torch.zeros((B, H), dtype=torch.int32, device="cuda"),
+                       out=zeros((B, Hq, D)), lse=zeros((B, Hq)))
+    c = se.cache(B, Hq, H, D, D, cap, "bf16")
+    ws_f = se.workspace(se.SE_OP_APPEND_ATTN, c, vc, 0)
+    ws_s = se.workspace(se.SE_OP_ATTN, c, vc, 0)
+    for step in range(4):
+        q = dev(gen.decode_query(cfg, 6, step), torch.bfloat16)
+        kn, vn = gen.decode_kv_new(cfg, 6, step)
+        knd, vnd = dev(kn, torch.bfloat16), dev(vn, torch.bfloat16)
+        f, s_ = side["fused"], side["sep"]
+        se.se_streaming_view(c, f["seq"], sink, recent, f["view"], f["vlen"], 1)
+        se.se_kv_append_decode_attn(c, q, f["k"], f["v"], knd, vnd, None, f["seq"], f["view"], f["vlen"], vc, 1,
+                                    cfg.softmax_scale, f["out"], f["lse"], ws=ws_f)
+        se.se_kv_append(c, s_["k"], s_["v"], knd, vnd, None, s_["seq"])
+        se.se_streaming_view(c, s_["seq"], sink, recent, s_["view"], s_["vlen"])
+        se.se_sparse_decode_attn(c, q, s_["k"], s_["v"], s_["seq"], s_["view"], s_["vlen"], vc, 1, cfg.softmax_scale,
+                                 s_["out"], s_["lse"], ws=ws_s)
+        torch.cuda.synchronize()
+        for key in ("k", "v", "seq", "view", "vlen", "out", "lse"):
+            x, y = f[key], s_[key]
+            dt = torch.int16 if x.element_size() == 2 else torch.int32
+            assert torch.equal(x.view(dt), y.view(dt)), f"step {step}: {key} differ"
+
+
 ATTN_CFGS = {
     "bf16_d128_g8": (get_config(0, dtype="bf16", batch=2, n_q_heads=16, n_kv_heads=2, d_k=128, d_v=128,
                                 context=3000), 4, 700),
