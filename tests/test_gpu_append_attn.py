@@ -76,7 +76,7 @@ def run_case(se, cfg, cap, lens, steps, seed, view=None, gran=1, slots=None, spl
 
 
 @pytest.mark.parametrize("name", list(CFGS))
-@pytest.mark.parametrize("splits", [0, 1, 3])
+@pytest.mark.parametrize("splits", [0, 1, 3, 20])   # 20: partials merged by the combine kernel
 def test_identity_append_at_seq_len(se, name, splits):
     """Appends at seq_len: ragged lengths, one batch row reaching the capacity (its
     later appends are dropped), logits on."""
