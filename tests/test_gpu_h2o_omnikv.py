@@ -25,7 +25,9 @@ def attempts_of(name):
 
 # ------------------------------------------------------------------ H2O
 
-def run_h2o(se, cfg, units, attempts):
+def run_h2o(se, cfg, units, attempts, fused=False):
+    """fused: the step's append and attention through se_kv_append_decode_attn (the
+    bench's call) instead of se_kv_append then se_sparse_decode_attn."""
     B, H, Hq, D = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.d_k
     G = cfg.group
     cap = cfg.h2o_heavy + cfg.h2o_recent + 1
@@ -41,7 +43,7 @@ def run_h2o(se, cfg, units, attempts):
     seq = torch.full((B,), cap, dtype=torch.int32, device="cuda")
     evict = torch.full((B, H), cap - 1, dtype=torch.int32, device="cuda")
     out, lse, logits = zeros((B, Hq, D)), zeros((B, Hq)), zeros((B, Hq, cap))
-    ws = se.workspace(se.SE_OP_ATTN, c, cap, 0)
+    ws = se.workspace(se.SE_OP_APPEND_ATTN if fused else se.SE_OP_ATTN, c, cap, 0)
     # oracle state of the compared units
     ost = {u: dict(zip(("k", "v", "pos", "acc"), h2o_unit_start(cfg, u))) for u in units}
     for u in units:
@@ -49,9 +51,14 @@ def run_h2o(se, cfg, units, attempts):
         ost[u]["n"], ost[u]["free"] = cap, cap - 1
     for t in range(cfg.decode_steps):
         q, kn, vn = h2o_step_inputs(cfg, t, attempts)
-        se.se_kv_append(c, k, v, dev(kn, torch.bfloat16), dev(vn, torch.bfloat16), evict, seq)
-        se.se_sparse_decode_attn(c, dev(q, torch.bfloat16), k, v, seq, None, None, 0, 1, cfg.softmax_scale, out, lse,
-                                 logits, cap, 0, ws)
+        if fused:
+            se.se_kv_append_decode_attn(c, dev(q, torch.bfloat16), k, v, dev(kn, torch.bfloat16),
+                                        dev(vn, torch.bfloat16), evict, seq, None, None, 0, 1, cfg.softmax_scale, out,
+                                        lse, logits, cap, 0, ws)
+        else:
+            se.se_kv_append(c, k, v, dev(kn, torch.bfloat16), dev(vn, torch.bfloat16), evict, seq)
+            se.se_sparse_decode_attn(c, dev(q, torch.bfloat16), k, v, seq, None, None, 0, 1, cfg.softmax_scale, out,
+                                     lse, logits, cap, 0, ws)
         se.se_h2o_accumulate_evict(c, logits, lse, cap, seq, slot_pos, acc_d, cfg.context + t, cfg.h2o_heavy,
                                    cfg.h2o_recent, evict)
         torch.cuda.synchronize()
@@ -75,21 +82,23 @@ def run_h2o(se, cfg, units, attempts):
         assert set(range(last - cfg.h2o_recent + 1, last + 1)) <= set(p.tolist())
 
 
-def test_h2o_tiny_all_units_all_steps(se):
+@pytest.mark.parametrize("fused", [False, True])
+def test_h2o_tiny_all_units_all_steps(se, fused):
     cfg = h2o_config(False)
-    banner("h2o tiny")
-    run_h2o(se, cfg, range(cfg.units), {})
+    banner(f"h2o tiny fused={fused}")
+    run_h2o(se, cfg, range(cfg.units), {}, fused)
 
 
 def test_h2o_16k_sampled_units(se):
+    """The bench's step: the append into the freed slot and the attention in one launch."""
     cfg = h2o_config(True)
     banner("h2o 16K: 64 x 4 units, 128 steps")
-    run_h2o(se, cfg, H2O_UNITS, attempts_of("h2o_16k"))
+    run_h2o(se, cfg, H2O_UNITS, attempts_of("h2o_16k"), fused=True)
 
 
 # ------------------------------------------------------------------ OmniKV
 
-def run_omni(se, cfg, units, check_steps, attempts):
+def run_omni(se, cfg, units, check_steps, attempts, fused=False):
     B, H, Hq, D = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.d_k
     G = cfg.group
     n_steps = max(check_steps) + 1
@@ -107,8 +116,9 @@ def run_omni(se, cfg, units, check_steps, attempts):
     views = {f: torch.zeros((B, H, cfg.omni_top_k), dtype=torch.int32, device="cuda") for f in cfg.omni_filters}
     vlens = {f: torch.zeros((B, H), dtype=torch.int32, device="cuda") for f in cfg.omni_filters}
     out, lse, logits = zeros((B, Hq, D)), zeros((B, Hq)), zeros((B, Hq, cap))
-    ws_dense = se.workspace(se.SE_OP_ATTN, c, cap, 0)
-    ws_sparse = se.workspace(se.SE_OP_ATTN, c, cfg.omni_top_k, 0)
+    op = se.SE_OP_APPEND_ATTN if fused else se.SE_OP_ATTN
+    ws_dense = se.workspace(op, c, cap, 0)
+    ws_sparse = se.workspace(op, c, cfg.omni_top_k, 0)
     ws_topk = se.workspace(se.SE_OP_OMNIKV, c, cap, cfg.omni_top_k)
     for s in range(n_steps):
         outs, qs = {}, []
@@ -119,19 +129,22 @@ def run_omni(se, cfg, units, check_steps, attempts):
             for u in units:
                 hk, hv = host_units[layer][u]
                 hk[cfg.context + s], hv[cfg.context + s] = kn[u // H, u % H], vn[u // H, u % H]
-            se.se_kv_append(c, ks[layer], vs[layer], dev(kn, torch.bfloat16), dev(vn, torch.bfloat16), None,
-                            seqs[layer])
+            knd, vnd = dev(kn, torch.bfloat16), dev(vn, torch.bfloat16)
+            if not fused:
+                se.se_kv_append(c, ks[layer], vs[layer], knd, vnd, None, seqs[layer])
             qd = dev(q, torch.bfloat16)
-            if mode == "sparse":
-                se.se_sparse_decode_attn(c, qd, ks[layer], vs[layer], seqs[layer], views[src], vlens[src],
-                                         cfg.omni_top_k, 1, cfg.softmax_scale, out, lse, ws=ws_sparse)
+            lg = logits if mode == "filter" else None
+            vi, vl, vc = (views[src], vlens[src], cfg.omni_top_k) if mode == "sparse" else (None, None, 0)
+            wsx = ws_sparse if mode == "sparse" else ws_dense
+            if fused:
+                se.se_kv_append_decode_attn(c, qd, ks[layer], vs[layer], knd, vnd, None, seqs[layer], vi, vl, vc, 1,
+                                            cfg.softmax_scale, out, lse, lg, cap if lg is not None else 0, 0, wsx)
             else:
-                lg = logits if mode == "filter" else None
-                se.se_sparse_decode_attn(c, qd, ks[layer], vs[layer], seqs[layer], None, None, 0, 1,
-                                         cfg.softmax_scale, out, lse, lg, cap if lg is not None else 0, 0, ws_dense)
-                if mode == "filter":
-                    se.se_omnikv_topk(c, logits, lse, cap, seqs[layer], cfg.omni_top_k, views[layer], vlens[layer],
-                                      None, ws_topk)
+                se.se_sparse_decode_attn(c, qd, ks[layer], vs[layer], seqs[layer], vi, vl, vc, 1, cfg.softmax_scale,
+                                         out, lse, lg, cap if lg is not None else 0, 0, wsx)
+            if mode == "filter":
+                se.se_omnikv_topk(c, logits, lse, cap, seqs[layer], cfg.omni_top_k, views[layer], vlens[layer], None,
+                                  ws_topk)
             if s in check_steps:
                 outs[layer] = host(out)
         if s not in check_steps:
@@ -153,13 +166,15 @@ def run_omni(se, cfg, units, check_steps, attempts):
                                            atol=TOL["bf16"], err_msg=f"step {s} unit {u} layer {layer}")
 
 
-def test_omnikv_tiny_all_units(se):
+@pytest.mark.parametrize("fused", [False, True])
+def test_omnikv_tiny_all_units(se, fused):
     cfg = omni_config(False)
-    banner("omnikv tiny")
-    run_omni(se, cfg, range(cfg.units), range(cfg.extra["omni_steps"]), {})
+    banner(f"omnikv tiny fused={fused}")
+    run_omni(se, cfg, range(cfg.units), range(cfg.extra["omni_steps"]), {}, fused)
 
 
 def test_omnikv_16k_sampled_units(se):
+    """The bench's sweep: each layer's append and attention in one launch."""
     cfg = omni_config(True)
     banner("omnikv 16K: 64 x 4 units, 18 layers, filters 2/8/16, top-2048")
-    run_omni(se, cfg, OMNI_UNITS, OMNI_STEPS, attempts_of("omnikv_16k"))
+    run_omni(se, cfg, OMNI_UNITS, OMNI_STEPS, attempts_of("omnikv_16k"), fused=True)

@@ -13,7 +13,9 @@ from workloads import get_config
 pytestmark = pytest.mark.gpu
 
 
-def run_mla(se, cfg, units, steps=1):
+def run_mla(se, cfg, units, steps=1, fused=False):
+    """fused: append, metadata, scores and view through se_quest_append_select (the
+    bench's call) instead of se_kv_append, se_page_meta_update, se_quest_select."""
     B, Hq, D, Dv, P, k = cfg.batch, cfg.n_q_heads, cfg.d_k, cfg.d_v, cfg.page_size, cfg.top_pages
     cap = cfg.context + steps
     C, _ = gen.cache_kv(cfg, 0, cap)                       # [B][1][cap][576]
@@ -28,16 +30,21 @@ def run_mla(se, cfg, units, steps=1):
     score = torch.zeros((B, 1, ncp), device="cuda")
     out, lse = zeros((B, Hq, Dv)), zeros((B, Hq))
     ws_q = se.workspace(se.SE_OP_QUEST, c, P, k)
+    ws_qa = se.workspace(se.SE_OP_QUEST_APPEND, c, P, 0)
     ws_a = se.workspace(se.SE_OP_ATTN, c, k * P, 0)
     se.se_page_meta_update(c, cd, kmin, kmax, seq, P, 0)
     for s in range(steps):
         q = gen.decode_query(cfg, 0, s)                     # [B][32][576]
         kn, _ = gen.decode_kv_new(cfg, 0, s)
         C[:, :, cfg.context + s] = kn
-        se.se_kv_append(c, cd, None, dev(kn, torch.bfloat16), None, None, seq)
-        se.se_page_meta_update(c, cd, kmin, kmax, seq, P, -1)
         qd = dev(q, torch.bfloat16)
-        se.se_quest_select(c, qd, kmin, kmax, seq, P, k, view, vlen, score, ws_q)
+        if fused:
+            se.se_quest_append_select(c, qd, cd, None, dev(kn, torch.bfloat16), None, seq, kmin, kmax, P, k, view,
+                                      vlen, score, ws_qa)
+        else:
+            se.se_kv_append(c, cd, None, dev(kn, torch.bfloat16), None, None, seq)
+            se.se_page_meta_update(c, cd, kmin, kmax, seq, P, -1)
+            se.se_quest_select(c, qd, kmin, kmax, seq, P, k, view, vlen, score, ws_q)
         se.se_sparse_decode_attn(c, qd, cd, None, seq, view, vlen, k, P, cfg.softmax_scale, out, lse, ws=ws_a)
     torch.cuda.synchronize()
     L = cfg.context + steps
@@ -57,13 +64,15 @@ def run_mla(se, cfg, units, steps=1):
         np.testing.assert_allclose(g["lse"][b], rlse[0], rtol=0, atol=TOL["bf16"])
 
 
-def test_mla_small_all_units(se):
+@pytest.mark.parametrize("fused", [False, True])
+def test_mla_small_all_units(se, fused):
     cfg = get_config(4, batch=3, context=3000, top_pages=8)
-    banner("mla small")
-    run_mla(se, cfg, range(cfg.batch), steps=3)
+    banner(f"mla small fused={fused}")
+    run_mla(se, cfg, range(cfg.batch), steps=3, fused=fused)
 
 
 def test_mla_128k_sampled_units(se):
+    """The bench's calls: the fused append + selection, then the attention."""
     cfg = get_config(4)
     banner("mla 128K: 32 x 131072 latent rows, top-64 pages")
-    run_mla(se, cfg, (0, 19, 31))
+    run_mla(se, cfg, (0, 19, 31), fused=True)

@@ -33,20 +33,27 @@ class QuestState:
         self.out = zeros((B, Hq, cfg.d_v))
         self.lse = zeros((B, Hq))
         self.ws_q = se.workspace(se.SE_OP_QUEST, self.c, P, cfg.top_pages)
+        self.ws_qa = se.workspace(se.SE_OP_QUEST_APPEND, self.c, P, 0)
         self.ws_a = se.workspace(se.SE_OP_ATTN, self.c, cfg.top_pages * P, 0)
         se.se_page_meta_update(self.c, self.k, self.kmin, self.kmax, self.seq, P, 0)
 
-    def step(self, se, step, splits=0):
+    def step(self, se, step, splits=0, fused=False):
+        """fused: append, metadata, scores and view through se_quest_append_select (the
+        bench's call) instead of se_kv_append, se_page_meta_update, se_quest_select."""
         cfg, dt, P = self.cfg, tdtype(self.cfg), self.cfg.page_size
         q = gen.decode_query(cfg, 0, step)
         kn, vn = gen.decode_kv_new(cfg, 0, step)
         L = cfg.context + step
         self.K[:, :, L], self.V[:, :, L] = kn, vn
-        se.se_kv_append(self.c, self.k, self.v, dev(kn, dt), dev(vn, dt), None, self.seq)
-        se.se_page_meta_update(self.c, self.k, self.kmin, self.kmax, self.seq, P, -1)
         qd = dev(q, dt)
-        se.se_quest_select(self.c, qd, self.kmin, self.kmax, self.seq, P, cfg.top_pages, self.view, self.vlen,
-                           self.score, self.ws_q)
+        if fused:
+            se.se_quest_append_select(self.c, qd, self.k, self.v, dev(kn, dt), dev(vn, dt), self.seq, self.kmin,
+                                      self.kmax, P, cfg.top_pages, self.view, self.vlen, self.score, self.ws_qa)
+        else:
+            se.se_kv_append(self.c, self.k, self.v, dev(kn, dt), dev(vn, dt), None, self.seq)
+            se.se_page_meta_update(self.c, self.k, self.kmin, self.kmax, self.seq, P, -1)
+            se.se_quest_select(self.c, qd, self.kmin, self.kmax, self.seq, P, cfg.top_pages, self.view, self.vlen,
+                               self.score, self.ws_q)
         se.se_sparse_decode_attn(self.c, qd, self.k, self.v, self.seq, self.view, self.vlen, cfg.top_pages, P,
                                  cfg.softmax_scale, self.out, self.lse, num_splits=splits,
                                  ws=se.workspace(se.SE_OP_ATTN, self.c, cfg.top_pages * P, splits))
@@ -93,13 +100,14 @@ def test_tiny_f32_quest_decode_all_units_all_steps(se):
             check_unit(cfg, st, q, L, unit, got)
 
 
-def test_tiny_bf16_quest_decode_with_partial_pages(se):
+@pytest.mark.parametrize("fused", [False, True])
+def test_tiny_bf16_quest_decode_with_partial_pages(se, fused):
     cfg = get_config(0, dtype="bf16", batch=3, n_q_heads=8, n_kv_heads=2, d_k=128, d_v=128, context=300,
                       top_pages=5, decode_steps=20)
-    banner("tiny bf16 quest pipeline, ragged pages")
+    banner(f"tiny bf16 quest pipeline, ragged pages, fused={fused}")
     st = QuestState(se, cfg, cfg.context + cfg.decode_steps)
     for step in range(cfg.decode_steps):
-        q, L = st.step(se, step)
+        q, L = st.step(se, step, fused=fused)
         torch.cuda.synchronize()
         got = snapshot(st)
         for unit in range(cfg.units):
@@ -122,15 +130,16 @@ def test_quest_top_k_edges(se, k_pages):
 
 
 def test_quest_32k_decode(se):
-    """The 32K Quest workload at full size: every step runs on the GPU; all units are
-    compared at the first step, sampled units at later steps."""
+    """The 32K Quest workload at full size through the bench's calls (the fused append +
+    selection, then the attention): every step runs on the GPU; all units are compared
+    at the first step, sampled units at later steps."""
     cfg = get_config(1)
     banner("quest 32K: building caches")
     st = QuestState(se, cfg, cfg.context + cfg.decode_steps)
     sample_steps = {0: range(cfg.units), 31: (5, 42), cfg.decode_steps - 1: (0, 17, 63)}
     recall = []
     for step in range(cfg.decode_steps):
-        q, L = st.step(se, step)
+        q, L = st.step(se, step, fused=True)
         if step in sample_steps:
             torch.cuda.synchronize()
             banner(f"quest 32K: checking step {step}")

@@ -7,9 +7,10 @@ import numpy as np
 import pytest
 import torch
 
+from oracle import attention as oatt
 from oracle import boundary_gap
 from oracle import snapkv as osnap
-from tests.gpu_util import banner, dev, host
+from tests.gpu_util import TOL, banner, dev, host, zeros
 from tests.sampled_units import SNAP_UNITS
 from workloads import generator as gen
 from workloads import get_config
@@ -24,7 +25,9 @@ def attempts_of(name):
     return {tuple(int(x) for x in k.split(",")): v for k, v in ATTEMPTS.get(name, {}).items()}
 
 
-def run_snap(se, cfg, units, attempts, cap=None, budget=None, check_gap=True):
+def run_snap(se, cfg, units, attempts, cap=None, budget=None, check_gap=True, decode=False):
+    """decode: then one decode step over the compacted cache as the bench runs it (the
+    new row appended and attended in one launch), checked on the sampled units."""
     B, H, Hq, D = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.d_k
     L, W, pool = cfg.context, cfg.snap_window, cfg.snap_pool
     budget = cfg.snap_budget if budget is None else budget
@@ -47,6 +50,7 @@ def run_snap(se, cfg, units, attempts, cap=None, budget=None, check_gap=True):
     g_kept, g_votes, g_k, g_v = host(kept), host(votes), host(k_out), host(v_out)
     assert np.all(host(olen) == nkeep)
     G = cfg.group
+    kept_ref = {}
     for u in units:
         b, h = divmod(u, H)
         ref_votes = osnap.unit_votes(qo[b, h * G:(h + 1) * G], K[b, h], L, W, cfg.softmax_scale)
@@ -59,6 +63,28 @@ def run_snap(se, cfg, units, attempts, cap=None, budget=None, check_gap=True):
         assert np.all(g_kept[b, h, nkeep:] == -1)
         np.testing.assert_array_equal(g_k[b, h, :nkeep], K[b, h][ref_kept])
         np.testing.assert_array_equal(g_v[b, h, :nkeep], V[b, h][ref_kept])
+        if decode:
+            kept_ref[u] = ref_kept
+    if decode:
+        q = gen.decode_query(cfg, 0, 0)
+        kn, vn = gen.decode_kv_new(cfg, 0, 0)
+        out, lse = zeros((B, Hq, D)), zeros((B, Hq))
+        se.se_kv_append_decode_attn(oc, dev(q, dt), k_out, v_out, dev(kn, dt), dev(vn, dt), None, olen, None, None, 0,
+                                    1, cfg.softmax_scale, out, lse,
+                                    ws=se.workspace(se.SE_OP_APPEND_ATTN, oc, nkeep + 3, 0))
+        torch.cuda.synchronize()
+        assert np.all(host(olen) == nkeep + 1)
+        g_out, g_lse = host(out), host(lse)
+        kq = torch.from_numpy(np.asarray(kn, np.float32)).to(dt).float().numpy()   # rows as stored
+        vq = torch.from_numpy(np.asarray(vn, np.float32)).to(dt).float().numpy()
+        for u in units:
+            b, h = divmod(u, H)
+            Ku = np.concatenate([K[b, h][kept_ref[u]], kq[b, h][None]])[None, None]
+            Vu = np.concatenate([V[b, h][kept_ref[u]], vq[b, h][None]])[None, None]
+            ro, rl, _ = oatt.decode_attention(q[b:b + 1, h * G:(h + 1) * G], Ku, Vu, [nkeep + 1], cfg.softmax_scale)
+            tol = TOL[cfg.dtype]
+            np.testing.assert_allclose(g_out[b, h * G:(h + 1) * G], ro[0], atol=tol, rtol=0, err_msg=f"unit {u} out")
+            np.testing.assert_allclose(g_lse[b, h * G:(h + 1) * G], rl[0], atol=tol, rtol=0, err_msg=f"unit {u} lse")
     return g_kept
 
 
@@ -99,5 +125,5 @@ def test_snapkv_budget_covers_prompt_and_window_only(se):
 
 def test_snapkv_128k_sampled_units(se):
     cfg = get_config(2)
-    banner("snapkv 128K: 8 x 4 units, 131072 -> 8192")
-    run_snap(se, cfg, SNAP_UNITS, attempts_of("snapkv_128k"))
+    banner("snapkv 128K: 8 x 4 units, 131072 -> 8192, then a decode step")
+    run_snap(se, cfg, SNAP_UNITS, attempts_of("snapkv_128k"), decode=True)
