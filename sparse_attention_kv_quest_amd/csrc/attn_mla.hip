@@ -8,22 +8,29 @@
 //   S^T[token][head] = C[token][:] . Q[head][:]          (576-deep)
 //   O^T[dim][head]  += C[token][dim]^T . P^T[token][head] (dims 0..511)
 //
-// Block: 8 waves, one (unit, split, group of 32 heads); tiles of 128 view
-// slots.  Wave w scores slots 16w..16w+15 of a tile over all 576 columns (K
-// rows go from HBM straight into A-operand registers; Q is staged once in LDS
-// in B-operand order), and owns output dims 64w..64w+63 for all heads: it
-// loads those 64 columns of all 128 rows a second time in a four-token-per-
-// lane order (an L2 hit), which a v_perm transpose turns into V^T in a
-// wave-private LDS tile.  Softmax state is shared through LDS: the waves post
-// their per-head maxima, all of them take the same tile maximum and make the
-// same (lazy, 2^8-margin) rescaling decision, and each wave posts P of its own
-// slots as bf16 hi + lo pairs that every wave then reads as the B operand.
-// The next tile's K loads are issued as soon as the scores are formed and its
-// V loads as soon as the transposes are done, so a tile of rows is always in
-// flight.  Each split stores a partial (max, sum, output), which the combine
-// kernel merges (or, for small partials, the block finishing the last split).
+// Groups of up to 16 heads (attn_mla_kernel): 8 waves per (unit, split, head
+// group), tiles of 128 view slots.  Wave w scores slots 16w..16w+15 of a tile
+// over all 576 columns (K rows go from HBM straight into A-operand registers;
+// Q is staged once in LDS in B-operand order), and owns output dims
+// 64w..64w+63 for all heads: it loads those 64 columns of all 128 rows a second
+// time in a four-token-per-lane order (an L2 hit), which a v_perm transpose
+// turns into V^T in a wave-private LDS tile.  Softmax state is shared through
+// LDS: the waves post their per-head maxima, all of them take the same tile
+// maximum and make the same (lazy, 2^8-margin) rescaling decision, and each
+// wave posts P of its own slots as bf16 hi + lo pairs that every wave then reads
+// as the B operand.  The next tile's rows and value columns are issued together
+// at the end of a tile.
+//
+// Groups of 17..32 heads take attn_mla_pf_kernel below: 64-slot tiles, the next
+// tile's rows in flight in registers while the current one is used, and the
+// values read from LDS copies of the rows already loaded.
+//
+// Each split stores a partial (max, sum, output), which the combine kernel
+// merges (or, for small partials, the block finishing the last split).
 #include "attn_common.hpp"
 #include "mfma_util.hpp"
+
+#include <type_traits>
 
 namespace se {
 
@@ -350,6 +357,323 @@ __global__ __launch_bounds__(ML_THREADS) void attn_mla_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Groups of 17..32 heads: 64-slot tiles with the next tile's rows in flight.
+//
+// Wave w = 4 ch + sg loads the rows of slots 16 sg .. 16 sg + 15 of a tile,
+// columns 288 ch .. 288 ch + 287 (nine 32-column k-steps), into one of two
+// register buffers: while a tile is scored and multiplied, the next tile's rows
+// are already being fetched.  The two waves of a slot group each form partial
+// scores over their column half for all 32 heads and swap the head block the
+// other one owns through LDS, so wave (sg, ch) ends with the full scores of its
+// 16 slots for heads 16 ch .. 16 ch + 15 and makes their P.  The rows' first
+// 512 columns (the values) go from the same registers into a row-major LDS
+// tile, which the P.V product reads with the gfx950 transposing LDS read
+// (ds_read_b64_tr_b16): each row is fetched from HBM once and never re-read.
+// Wave w owns output dims 64 w .. 64 w + 63 for all heads.
+constexpr int MP_TS = 64;                                   // slots per tile
+constexpr int MP_KH = ML_NKS / 2;                           // k-steps per column half (9)
+constexpr int MP_VP = ML_DV + 16;                           // u16 per LDS value row (8-word bank skew)
+constexpr int MP_V_BYTES = MP_TS * MP_VP * 2;               // 67584
+constexpr int MP_P_BYTES = 2 * 2 * 2 * 2 * 64 * 8;          // 8192: [kstep][half][hb][hi/lo][lane] uint2
+constexpr int MP_X_BYTES = 4 * 2 * 64 * 16;                 // 8192: [sg][hb][lane] partial scores
+constexpr int MP_MAIN_BYTES = ML_Q_BYTES + MP_V_BYTES + MP_P_BYTES + MP_X_BYTES;
+constexpr int MP_LDS_BYTES = MP_MAIN_BYTES > ML_OB_BYTES ? MP_MAIN_BYTES : ML_OB_BYTES;
+
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 mp_bf16x4;
+
+// Transposing LDS read: within each 16-lane group, lane 4e + c supplies the address
+// of 4 consecutive u16 (row e of a 4 x 16 block, columns 4c .. 4c + 3) and lane i
+// receives column i of the block, rows 0..3.
+__device__ __forceinline__ uint2 mp_read_tr(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) mp_bf16x4* lds_p;
+  const mp_bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_p)(const __attribute__((address_space(3))) void*)p);
+  uint2 r;
+  __builtin_memcpy(&r, &v, 8);
+  return r;
+}
+
+// This wave's rows (slot 16 sg + (lane & 15)) and column half: lane holds columns
+// 288 ch + 32 c + 8 (lane >> 4) .. + 7 of k-step c.
+__device__ __forceinline__ int mp_load(const MlCtx& x, const int32_t* vcache, int tb, int sg, int ch, int lane,
+                                       u32x4 (&k)[MP_KH]) {
+  const int tk = ml_token(x, vcache, tb + 16 * sg + (lane & 15));
+  // unconditional loads keep the wait counts exact; a slot without a token reads row 0
+  const uint32_t r = uint32_t(max(tk, 0)) * ML_DK + 288 * ch + 8 * (lane >> 4);
+#pragma unroll
+  for (int c = 0; c < MP_KH; ++c) k[c] = ld16(x.cu + r + 32 * c);
+  return tk;
+}
+
+__global__ __launch_bounds__(ML_THREADS) void attn_mla_pf_kernel(AttnArgs a) {
+  __shared__ __align__(16) unsigned char lds[MP_LDS_BYTES];
+  __shared__ float wmax[4][32];
+  __shared__ float wsum[4][32];
+  __shared__ int32_t vcache[ML_VCACHE];
+  const u32x4* qs = reinterpret_cast<const u32x4*>(lds);                                  // [NKS][hb][lane]
+  uint16_t* vl = reinterpret_cast<uint16_t*>(lds + ML_Q_BYTES);                           // [slot][MP_VP]
+  uint2* ps = reinterpret_cast<uint2*>(lds + ML_Q_BYTES + MP_V_BYTES);                    // [j][half][hb][hl][lane]
+  f32x4* xs = reinterpret_cast<f32x4*>(lds + ML_Q_BYTES + MP_V_BYTES + MP_P_BYTES);      // [sg][hb][lane]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int sg = w & 3, ch = w >> 2;
+
+  const int unit = blockIdx.y, split = blockIdx.x, hg = blockIdx.z;
+  const int b = unit / a.Hkv, kvh = unit % a.Hkv;
+  const int G = a.G, h0 = 32 * hg;
+  const bool identity = a.view_idx == nullptr;
+  const int len = min(a.seq_len[b], a.cap);
+  const int n_slots = identity ? len : a.view_cap * a.gran;
+  const int s_valid = identity ? len : min(a.view_len[unit], a.view_cap) * a.gran;
+  int chunk = (n_slots + a.splits - 1) / a.splits;
+  chunk = (chunk + MP_TS - 1) / MP_TS * MP_TS;
+  const int s0 = min(n_slots, split * chunk), s1 = min(n_slots, s0 + chunk);
+  const int ntiles = (s1 - s0 + MP_TS - 1) / MP_TS;
+
+  MlCtx x;
+  x.cu = (const uint16_t*)a.k + size_t(unit) * a.cap * ML_DK;
+  x.len = len;
+  x.s1 = min(s1, s_valid);
+  x.gshift = a.gshift;
+  x.identity = identity;
+  x.e0 = 0;
+  // Q (in B-operand order: entry (c, hb, lane) = head h0 + 16 hb + (lane & 15), columns
+  // 32c + 8(lane >> 4) .. + 7) and the view entries of this split are fetched together
+  constexpr int QN = ML_NKS * 2 * 64, QR = (QN + ML_THREADS - 1) / ML_THREADS;
+  u32x4 qv[QR];
+#pragma unroll
+  for (int r = 0; r < QR; ++r) {
+    const int i = threadIdx.x + r * ML_THREADS;
+    const int l = i & 63, hb = (i >> 6) & 1, c = i >> 7;
+    const int h = h0 + 16 * hb + (l & 15);
+    // unconditional loads (clamped in range, zeroed after) keep the wait counts exact
+    const int hc = min(h, G - 1), cc = min(c, ML_NKS - 1);
+    qv[r] = ld16((const uint16_t*)a.q + (size_t(b) * a.Hq + size_t(kvh) * G + hc) * ML_DK + 32 * cc + 8 * (l >> 4));
+    if (!(i < QN && h < G)) qv[r] = u32x4{0u, 0u, 0u, 0u};
+  }
+  // at most ML_VCACHE - 1 entries (attn_mla_supported)
+  constexpr int VR = ML_VCACHE / ML_THREADS;
+  int32_t ve[VR];
+  int e0 = 0, e1 = 0;
+  if (!identity) {
+    const int32_t* vrow = a.view_idx + size_t(unit) * a.view_cap;
+    e0 = s0 >> a.gshift;
+    e1 = s1 > s0 ? ((s1 - 1) >> a.gshift) + 1 : e0;
+#pragma unroll
+    for (int r = 0; r < VR; ++r) {
+      const int e = e0 + threadIdx.x + r * ML_THREADS;
+      ve[r] = e < e1 ? vrow[e] : -1;
+    }
+    x.e0 = e0;
+  }
+#pragma unroll
+  for (int r = 0; r < QR; ++r) {
+    const int i = threadIdx.x + r * ML_THREADS;
+    if (i < QN) reinterpret_cast<u32x4*>(lds)[i] = qv[r];
+  }
+  if (!identity) {
+#pragma unroll
+    for (int r = 0; r < VR; ++r) {
+      const int e = e0 + threadIdx.x + r * ML_THREADS;
+      if (e < e1) vcache[e - e0] = ve[r];
+    }
+  }
+  __syncthreads();
+  u32x4 kb0[MP_KH], kb1[MP_KH];
+  // unconditional (slots past the split read row 0): the loop's wait counts stay exact
+  int tk0 = mp_load(x, vcache, s0, sg, ch, lane, kb0), tk1 = -1;
+
+  const float sc2 = a.scale * LOG2E;
+  f32x4 o[ML_DW / 16][2];
+#pragma unroll
+  for (int db = 0; db < ML_DW / 16; ++db) o[db][0] = o[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m2[2] = {-INFINITY, -INFINITY};
+  float lsum = 0.f;                  // head 16 ch + c16, this wave's slots
+  // transposing-read source row / column of this lane (see mp_read_tr)
+  const int tr_row = 4 * g + ((lane >> 2) & 3), tr_col = ML_DW * w + 4 * (lane & 3);
+
+  auto step = [&](u32x4 (&cur)[MP_KH], int& tkc, u32x4 (&nxt)[MP_KH], int& tkn, int it, auto pref) {
+    const int tb = s0 + it * MP_TS;
+    if constexpr (decltype(pref)::value) {
+      tkn = mp_load(x, vcache, tb + MP_TS, sg, ch, lane, nxt);
+    }
+    // ---- partial scores over this wave's column half, both head blocks
+    f32x4 sa0 = {0.f, 0.f, 0.f, 0.f}, sa1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < MP_KH; ++c) {
+      sa0 = mfma_bf16_16x16x32(cur[c], qs[((MP_KH * ch + c) * 2 + 0) * 64 + lane], sa0);
+      sa1 = mfma_bf16_16x16x32(cur[c], qs[((MP_KH * ch + c) * 2 + 1) * 64 + lane], sa1);
+    }
+    xs[(sg * 2 + (1 - ch)) * 64 + lane] = ch ? sa0 : sa1;   // the partner's head block
+    __syncthreads();
+    const f32x4 oth = xs[(sg * 2 + ch) * 64 + lane];
+    const f32x4 own = ch ? sa1 : sa0;
+    // value columns of these rows into the LDS tile (rope columns 512.. stay out)
+    uint16_t* vdst = vl + (16 * sg + c16) * MP_VP + 288 * ch + 8 * g;
+#pragma unroll
+    for (int c = 0; c < MP_KH; ++c)
+      if (ch == 0 || c < 7) *reinterpret_cast<u32x4*>(vdst + 32 * c) = cur[c];
+    const uint64_t valid = __ballot(tkc >= 0);
+    float sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = ((valid >> (4 * g + i)) & 1) ? (own[i] + oth[i]) * sc2 : -INFINITY;
+    if (a.logits != nullptr) {
+      const int h = h0 + 16 * ch + c16;
+      if (h < G) {
+        float* row = a.logits + (size_t(b) * a.Hq + size_t(kvh) * G + h) * a.logit_cap;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s = tb + 16 * sg + 4 * g + i;
+          if (s < x.s1 && s < a.logit_cap)
+            row[s] = ((valid >> (4 * g + i)) & 1) ? (own[i] + oth[i]) * a.scale : -INFINITY;
+        }
+      }
+    }
+    {
+      float m = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      m = rows4_max(m);
+      if (g == 0) wmax[sg][16 * ch + c16] = m;
+    }
+    __syncthreads();
+    // ---- tile maxima of both head blocks; every wave takes the same decisions
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const float tmax = fmaxf(fmaxf(wmax[0][16 * hb + c16], wmax[1][16 * hb + c16]),
+                               fmaxf(wmax[2][16 * hb + c16], wmax[3][16 * hb + c16]));
+      const bool grow = tmax > m2[hb] + ML_MARGIN;
+      if (__ballot(grow) != 0) {
+        const float mnew = grow ? tmax : m2[hb];
+        const float alpha = (grow && m2[hb] != -INFINITY) ? ex2(m2[hb] - mnew) : 1.f;
+        if (hb == ch) lsum *= alpha;
+#pragma unroll
+        for (int db = 0; db < ML_DW / 16; ++db) o[db][hb] *= alpha;
+        m2[hb] = mnew;
+      }
+    }
+    {
+      const float mo = ch ? m2[1] : m2[0];
+      const float mref = mo == -INFINITY ? 0.f : mo;
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = ex2(sv[i] - mref);   // 0 for masked slots, at most 2^8 otherwise
+        lsum += p[i];
+      }
+      uint2 hi, lo;
+      hi.x = pack_bf16(p[0], p[1]);
+      hi.y = pack_bf16(p[2], p[3]);
+      lo.x = pack_bf16(p[0] - bf16x2_lo_f32(hi.x), p[1] - bf16x2_hi_f32(hi.x));
+      lo.y = pack_bf16(p[2] - bf16x2_lo_f32(hi.y), p[3] - bf16x2_hi_f32(hi.y));
+      // slots 16 sg + 4g + i: k-step sg >> 1, half sg & 1
+      ps[((((sg >> 1) * 2 + (sg & 1)) * 2 + ch) * 2 + 0) * 64 + lane] = hi;
+      ps[((((sg >> 1) * 2 + (sg & 1)) * 2 + ch) * 2 + 1) * 64 + lane] = lo;
+    }
+    __syncthreads();
+    // ---- O^T += V^T P^T over the tile's two 32-slot k-steps.  Both operands take the
+    // k order (4a .. 4a + 3, 16 + 4a .. 16 + 4a + 3) for lane group a.
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      u32x4 ph[2], pl[2];
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const uint2 h0v = ps[(((j * 2 + 0) * 2 + hb) * 2 + 0) * 64 + lane];
+        const uint2 h1v = ps[(((j * 2 + 1) * 2 + hb) * 2 + 0) * 64 + lane];
+        const uint2 l0v = ps[(((j * 2 + 0) * 2 + hb) * 2 + 1) * 64 + lane];
+        const uint2 l1v = ps[(((j * 2 + 1) * 2 + hb) * 2 + 1) * 64 + lane];
+        ph[hb] = u32x4{h0v.x, h0v.y, h1v.x, h1v.y};
+        pl[hb] = u32x4{l0v.x, l0v.y, l1v.x, l1v.y};
+      }
+#pragma unroll
+      for (int db = 0; db < ML_DW / 16; ++db) {
+        const uint16_t* src = vl + (32 * j + tr_row) * MP_VP + tr_col + 16 * db;
+        const uint2 x0 = mp_read_tr(src), x1 = mp_read_tr(src + 16 * MP_VP);
+        const u32x4 av = {x0.x, x0.y, x1.x, x1.y};
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          o[db][hb] = mfma_bf16_16x16x32(av, ph[hb], o[db][hb]);
+          o[db][hb] = mfma_bf16_16x16x32(av, pl[hb], o[db][hb]);
+        }
+      }
+    }
+  };
+  using Pf = std::integral_constant<bool, true>;
+  using NoPf = std::integral_constant<bool, false>;
+  int it = 0;
+  for (; it + 2 < ntiles; it += 2) {
+    step(kb0, tk0, kb1, tk1, it, Pf{});
+    step(kb1, tk1, kb0, tk0, it + 1, Pf{});
+  }
+  if (ntiles - it == 2) {
+    step(kb0, tk0, kb1, tk1, it, Pf{});
+    step(kb1, tk1, kb0, tk0, it + 1, NoPf{});
+  } else if (ntiles - it == 1) {
+    step(kb0, tk0, kb1, tk1, it, NoPf{});
+  }
+
+  // ---- sums over lanes and slot groups (every wave shares the same running max)
+  {
+    const float s = rows4_sum(lsum);
+    if (g == 0) wsum[sg][16 * ch + c16] = s;
+  }
+  __syncthreads();   // also: every wave is done with Q, P and the value tile
+  float* ob = reinterpret_cast<float*>(lds) + w * 32 * ML_OB_PITCH;   // [head][dim] of this wave's 64 dims
+#pragma unroll
+  for (int db = 0; db < ML_DW / 16; ++db)
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ob[(16 * hb + c16) * ML_OB_PITCH + 16 * db + 4 * g + i] = o[db][hb][i];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float* pml = a.part_ml + (size_t(unit) * a.splits + split) * G * 2;
+  float* po = a.part_o + (size_t(unit) * a.splits + split) * G * ML_DV;
+  const bool single = a.splits == 1;
+  const size_t row0 = size_t(b) * a.Hq + size_t(kvh) * G;
+  // 32 heads x 64 dims of this wave: 16 float4 per head row, 512 float4 per wave
+  for (int idx = lane; idx < 32 * 16; idx += 64) {
+    const int hl = idx >> 4, d4 = idx & 15, h = h0 + hl;
+    if (h < G) {
+      const float* src = ob + hl * ML_OB_PITCH + 4 * d4;
+      float4 v = make_float4(src[0], src[1], src[2], src[3]);
+      if (single) {
+        const float L = (wsum[0][hl] + wsum[1][hl]) + (wsum[2][hl] + wsum[3][hl]);
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        v = make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
+        *reinterpret_cast<float4*>(a.out + (row0 + h) * ML_DV + ML_DW * w + 4 * d4) = v;
+      } else {
+        float* dst = po + size_t(h) * ML_DV + ML_DW * w + 4 * d4;
+        if (a.fused) {
+          st_dev(dst, v.x);
+          st_dev(dst + 1, v.y);
+          st_dev(dst + 2, v.z);
+          st_dev(dst + 3, v.w);
+        } else {
+          *reinterpret_cast<float4*>(dst) = v;
+        }
+      }
+    }
+  }
+  if (w == 0 && lane < 32) {
+    const int h = h0 + lane;
+    if (h < G) {
+      const float L = (wsum[0][lane] + wsum[1][lane]) + (wsum[2][lane] + wsum[3][lane]);
+      const float M = (lane >> 4) ? m2[1] : m2[0];
+      const float Mn = (M == -INFINITY) ? -INFINITY : M * 0.6931471805599453f;
+      if (single) {
+        if (a.lse != nullptr) a.lse[row0 + h] = L > 0.f ? Mn + logf(L) : -INFINITY;
+      } else {
+        st_part(a, pml + 2 * h, Mn);
+        st_part(a, pml + 2 * h + 1, L);
+      }
+    }
+  }
+  if (a.fused) {
+    int* ctr = a.counters + unit * ATTN_MAX_HG + hg;
+    if (attn_split_done(ctr, a.splits)) attn_merge_splits<ML_THREADS>(a, unit, h0, min(32, G - h0), ctr);
+  }
+}
+
 bool attn_mla_supported(const AttnArgs& a) {
   if (!(a.dtype == SE_BF16 && a.latent && a.Dk == ML_DK && a.Dv == ML_DV && a.G <= 64)) return false;
   if (a.cap > (1 << 30) / ML_DK) return false;
@@ -376,7 +700,7 @@ se_status launch_attn_mla(const AttnArgs& a, hipStream_t s) {
   if (a.G <= 16)
     hipLaunchKernelGGL((attn_mla_kernel<1>), grid, dim3(ML_THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL((attn_mla_kernel<2>), grid, dim3(ML_THREADS), 0, s, a);
+    hipLaunchKernelGGL(attn_mla_pf_kernel, grid, dim3(ML_THREADS), 0, s, a);
   return launch_status();
 }
 
