@@ -99,8 +99,22 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(
   const bool app = APP && len < cap;                 // room for the new token
   const int new_len = app ? len + 1 : len;
   const int npages = min((new_len + P - 1) / P, ncp);
-  // unconditional loads (pages past the last valid one read page 0; their scores are
-  // masked below) keep the wait counters exact
+  // q first (each 16-byte piece feeds both the q+ and the q- entry), then the
+  // page metadata: all in flight together, and q's wait leaves the metadata
+  // loads outstanding.  Unconditional loads (a clamped entry and head; pages past
+  // the last valid one read page 0, their scores masked below) keep the wait
+  // counters exact.
+  const uint16_t* qg = q + (size_t(b) * Hkv * G + size_t(kvh) * G) * D;
+  constexpr int QE = NKS * HB * 64, QR = (QE + 255) / 256;
+  u32x4 qv[QR];
+#pragma unroll
+  for (int t = 0; t < QR; ++t) {
+    const int idx = min(int(threadIdx.x) + 256 * t, QE - 1);
+    const int ln = idx & 63, hb = (idx >> 6) % HB, c = idx / (64 * HB);
+    const int head = 16 * hb + (ln & 15);
+    qv[t] = ld16(qg + size_t(min(head, G - 1)) * D + 32 * c + 8 * (ln >> 4));
+  }
+  __builtin_amdgcn_sched_barrier(0);   // q's loads stay ahead of the metadata's
   u32x4 amx[NKS], amn[NKS];
   const int pg = (blockIdx.x * 4 + w) * 16 + c16;
   {
@@ -132,9 +146,12 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(
       const bool fresh = len % P == 0;
       const uint16_t* kn = ap.k_new + size_t(unit) * D + 8 * g;
       const size_t mo = (size_t(unit) * ncp + plast) * D + 8 * g;
+      u32x4 xk[NKS];   // all of the new row's pieces in flight before the stores
+#pragma unroll
+      for (int c = 0; c < NKS; ++c) xk[c] = ld16(kn + 32 * c);
 #pragma unroll
       for (int c = 0; c < NKS; ++c) {
-        const u32x4 x = ld16(kn + 32 * c);
+        const u32x4 x = xk[c];
         u32x4 mn, mx;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -148,23 +165,24 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(
       }
     }
   }
-  const uint16_t* qg = q + (size_t(b) * Hkv * G + size_t(kvh) * G) * D;
-  for (int idx = threadIdx.x; idx < 2 * NKS * HB * 64; idx += 256) {
-    const int ln = idx & 63, hb = (idx >> 6) % HB, sx = idx / (64 * HB);
-    const bool neg = sx >= NKS;
-    const int c = neg ? sx - NKS : sx;
-    const int head = 16 * hb + (ln & 15), gg = ln >> 4;
-    u32x4 x = {0, 0, 0, 0};
-    if (head < G) {
-      x = ld16(qg + size_t(head) * D + 32 * c + 8 * gg);
-      // q- keeps the halves whose sign bit is set, q+ the others
+  // threads past the last entry store that entry again (the same values): no branch
+  // for the compiler to sink a load into
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t sgn = ((x[j] >> 15) & 1u) * 0xffffu | ((x[j] >> 31) & 1u) * 0xffff0000u;
-        x[j] &= neg ? sgn : ~sgn;
-      }
+  for (int t = 0; t < QR; ++t) {
+    const int idx = min(int(threadIdx.x) + 256 * t, QE - 1);
+    const int ln = idx & 63, hb = (idx >> 6) % HB, c = idx / (64 * HB);
+    const int head = 16 * hb + (ln & 15);
+    const u32x4 x = head < G ? qv[t] : u32x4{0, 0, 0, 0};
+    u32x4 xp, xn;
+    // q- keeps the halves whose sign bit is set, q+ the others
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t sgn = ((x[j] >> 15) & 1u) * 0xffffu | ((x[j] >> 31) & 1u) * 0xffff0000u;
+      xp[j] = x[j] & ~sgn;
+      xn[j] = x[j] & sgn;
     }
-    qb[sx][hb][ln] = x;
+    qb[c][hb][ln] = xp;
+    qb[NKS + c][hb][ln] = xn;
   }
   __syncthreads();
   const int p0 = (blockIdx.x * 4 + w) * 16;
@@ -242,9 +260,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const size_t row = size_t(unit) * ncp + (pg < npages ? pg : 0);
     return (r < NKS ? kmax : kmin) + row * D + 8 * g + 32 * (r % NKS);
   };
+  // q first (each 16-byte piece feeds both the q+ and the q- entry), then the
+  // first group's chunks: all in flight together, and q's wait leaves the ring's
+  // loads outstanding.  Unconditional loads (a clamped head, zeroed after) keep
+  // the wait counts exact.
+  const uint16_t* qg = q + (size_t(b) * Hkv * G + size_t(kvh) * G) * D;
+  constexpr int QE = NKS * HB * 64, QR = QE / 256;
+  static_assert(QE % 256 == 0, "q entries are dealt evenly to the block's threads");
+  u32x4 qv[QR];
+#pragma unroll
+  for (int t = 0; t < QR; ++t) {
+    const int idx = threadIdx.x + 256 * t;
+    const int ln = idx & 63, hb = (idx >> 6) % HB, c = idx / (64 * HB);
+    const int head = 16 * hb + (ln & 15);
+    qv[t] = ld16(qg + size_t(min(head, G - 1)) * D + 32 * c + 8 * (ln >> 4));
+  }
+  __builtin_amdgcn_sched_barrier(0);   // q's loads stay ahead of the ring's
   u32x4 ring[NCH];
 #pragma unroll
   for (int r = 0; r < NCH; ++r) ring[r] = ld16(chunk_ptr(0, r));
+#pragma unroll
+  for (int t = 0; t < QR; ++t) {
+    const int idx = threadIdx.x + 256 * t;
+    const int ln = idx & 63, hb = (idx >> 6) % HB, c = idx / (64 * HB);
+    const int head = 16 * hb + (ln & 15);
+    const u32x4 x = head < G ? qv[t] : u32x4{0, 0, 0, 0};
+    u32x4 xp, xn;
+    // q- keeps the halves whose sign bit is set, q+ the others
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const uint32_t sgn = ((x[jj] >> 15) & 1u) * 0xffffu | ((x[jj] >> 31) & 1u) * 0xffff0000u;
+      xp[jj] = x[jj] & ~sgn;
+      xn[jj] = x[jj] & sgn;
+    }
+    qb[c][hb][ln] = xp;
+    qb[NKS + c][hb][ln] = xn;
+  }
   const bool owner = app && p_blk <= plast && plast < p_end;   // the block holding the appended page
   if (APP && owner) {
     // the new K / V rows, and the appended page's min / max with the new row
@@ -273,24 +324,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         *reinterpret_cast<u32x4*>(ap.v + (urow + len) * D + o) = ld16(ap.v_new + size_t(unit) * D + o);
       }
     }
-  }
-  const uint16_t* qg = q + (size_t(b) * Hkv * G + size_t(kvh) * G) * D;
-  for (int idx = threadIdx.x; idx < 2 * NKS * HB * 64; idx += 256) {
-    const int ln = idx & 63, hb = (idx >> 6) % HB, sx = idx / (64 * HB);
-    const bool neg = sx >= NKS;
-    const int c = neg ? sx - NKS : sx;
-    const int head = 16 * hb + (ln & 15), gg = ln >> 4;
-    u32x4 x = {0, 0, 0, 0};
-    if (head < G) {
-      x = ld16(qg + size_t(head) * D + 32 * c + 8 * gg);
-      // q- keeps the halves whose sign bit is set, q+ the others
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const uint32_t sgn = ((x[jj] >> 15) & 1u) * 0xffffu | ((x[jj] >> 31) & 1u) * 0xffff0000u;
-        x[jj] &= neg ? sgn : ~sgn;
-      }
-    }
-    qb[sx][hb][ln] = x;
   }
   __syncthreads();
   // the group (-1: none) and lane row of this wave that hold the appended page
