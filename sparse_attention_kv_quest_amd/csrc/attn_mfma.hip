@@ -81,7 +81,13 @@ __device__ __forceinline__ int mf_token(const MfCtx& x, int s) {
     t = s;
   } else {
     const int e = s >> x.gshift;
-    const int page = (s < x.s1) ? (VC ? mf_vcache[e - x.e0] : x.vglob[e]) : -1;
+    int page;
+    if (VC) {   // read unconditionally (clamped index): no branch, no wait per lookup
+      const int pv = mf_vcache[min(max(e - x.e0, 0), MF_VCACHE - 1)];
+      page = s < x.s1 ? pv : -1;
+    } else {
+      page = s < x.s1 ? x.vglob[e] : -1;
+    }
     t = page < 0 ? -1 : (page << x.gshift) + (s & ((1 << x.gshift) - 1));
   }
   return (s < x.s1 && t >= 0 && t < x.len) ? t : -1;

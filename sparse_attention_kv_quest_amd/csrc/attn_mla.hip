@@ -63,7 +63,9 @@ __device__ __forceinline__ int ml_token(const MlCtx& x, const int32_t* vcache, i
   if (x.identity) {
     t = s;
   } else {
-    const int page = s < x.s1 ? vcache[(s >> x.gshift) - x.e0] : -1;
+    // read unconditionally (clamped index): no branch, no wait per lookup
+    const int pv = vcache[min(max((s >> x.gshift) - x.e0, 0), ML_VCACHE - 1)];
+    const int page = s < x.s1 ? pv : -1;
     t = page < 0 ? -1 : (page << x.gshift) + (s & ((1 << x.gshift) - 1));
   }
   return (s < x.s1 && t >= 0 && t < x.len) ? t : -1;
