@@ -269,7 +269,8 @@ se_status se_chain_append_positions(const se_cache* c, int32_t* pos_map, const i
  *   empty view); lse: NULL or float [B][Hq] natural-log sum of exp(scale q.k)
  *   (-inf for an empty view); logits: NULL or float [B][Hq][logit_cap], the
  *   scaled logit of view slot i (entry * g + offset) at index i, -inf where the
- *   slot holds no valid token (indices >= view_cap * g are not written).
+ *   slot holds no valid token (indices >= view_cap * g are not written);
+ *   (n_q_heads / n_kv_heads) * logit_cap must not exceed 2^31 - 1 (SE_ERR_SHAPE).
  *   num_splits: 0 chooses the split-K factor; otherwise the number of chunks
  *   (1..256) each unit's view is cut into (results agree to rounding for any
  *   value).

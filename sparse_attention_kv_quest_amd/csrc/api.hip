@@ -58,6 +58,8 @@ se_status attn_impl(const se_cache* c, const void* q, const void* k, const void*
     if (int64_t(view_cap) * granularity > (int64_t(1) << 30)) return SE_ERR_SHAPE;
   }
   if (logits && logit_cap <= 0) return SE_ERR_SHAPE;
+  // a group's logit rows are addressed with 32-bit offsets
+  if (logits && int64_t(c->n_q_heads / c->n_kv_heads) * logit_cap > INT32_MAX) return SE_ERR_SHAPE;
   if (num_splits < 0 || num_splits > 256) return SE_ERR_SHAPE;
   if (!(scale > 0.f) || !(scale < 1e30f)) return SE_ERR_SHAPE;
   const int slots = view_idx ? view_cap * granularity : c->capacity;
@@ -345,6 +347,8 @@ se_status se_kv_append_decode_attn(const se_cache* c, const void* q, void* k, vo
     if (int64_t(view_cap) * granularity > (int64_t(1) << 30)) return SE_ERR_SHAPE;
   }
   if (logits && logit_cap <= 0) return SE_ERR_SHAPE;
+  // a group's logit rows are addressed with 32-bit offsets
+  if (logits && int64_t(c->n_q_heads / c->n_kv_heads) * logit_cap > INT32_MAX) return SE_ERR_SHAPE;
   if (num_splits < 0 || num_splits > 256) return SE_ERR_SHAPE;
   if (!(scale > 0.f) || !(scale < 1e30f)) return SE_ERR_SHAPE;
   const int slots = view_idx ? view_cap * granularity : c->capacity;

@@ -222,7 +222,7 @@ struct MfState {
 
 template <int D>
 __device__ __forceinline__ void mf_compute(const AttnArgs& a, const MfCtx& x, int base, int lane, const u32x4* qv,
-                                           float sc2, float* lg_row, uint16_t* vt, const MfTile<D>& T,
+                                           float sc2, float* lg_base, uint16_t* vt, const MfTile<D>& T,
                                            MfState<D>& st) {
   constexpr int NKS = D / 32, NDB = D / 16, VPASS = D / 64, PITCH = MF_TS + 4;
   const int g = lane >> 4, c16 = lane & 15, qa = lane & 7;
@@ -241,14 +241,36 @@ __device__ __forceinline__ void mf_compute(const AttnArgs& a, const MfCtx& x, in
     sv[i] = oka ? sa[i] * sc2 : -INFINITY;
     sv[4 + i] = okb ? sb[i] * sc2 : -INFINITY;
   }
-  if (lg_row != nullptr) {
+  if (lg_base != nullptr) {
+    // the tile's [head][slot] logits go through the wave's LDS tile (free until the V
+    // transpose below), so that each head's 32 slots leave as one contiguous run
+    constexpr int LP = MF_TS + 4;
+    float* lt = reinterpret_cast<float*>(vt);
+    f32x4 la, lb;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool oka = (va >> (4 * g + i)) & 1, okb = (vb >> (4 * g + i)) & 1;
-      const int sla = base + 4 * g + i, slb = base + 16 + 4 * g + i;
-      if (sla < x.s1 && sla < a.logit_cap) lg_row[sla] = oka ? sa[i] * a.scale : -INFINITY;
-      if (slb < x.s1 && slb < a.logit_cap) lg_row[slb] = okb ? sb[i] * a.scale : -INFINITY;
+      la[i] = ((va >> (4 * g + i)) & 1) ? sa[i] * a.scale : -INFINITY;
+      lb[i] = ((vb >> (4 * g + i)) & 1) ? sb[i] * a.scale : -INFINITY;
     }
+    *reinterpret_cast<f32x4*>(lt + c16 * LP + 4 * g) = la;
+    *reinterpret_cast<f32x4*>(lt + c16 * LP + 16 + 4 * g) = lb;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int sl = base + (lane & 31);
+    const bool sok = sl < x.s1 && sl < a.logit_cap;
+    // offsets within the group's rows (G * logit_cap < 2^31): one per-lane term, the
+    // head pair's part uniform, so no per-head pointer stays live across tiles
+    const uint32_t loff = uint32_t(lane >> 5) * uint32_t(a.logit_cap) + uint32_t(sl);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {   // heads 2k and 2k + 1
+      if (2 * k >= a.G) break;
+      const int h = 2 * k + (lane >> 5);
+      if (h < a.G && sok) lg_base[loff + uint32_t(2 * k) * uint32_t(a.logit_cap)] = lt[h * LP + (lane & 31)];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
   // ---- online softmax; head c16 lives in lanes c16, c16+16, c16+32, c16+48
   float tmax = sv[0];
@@ -325,14 +347,14 @@ __device__ __forceinline__ void mf_fetch(const MfCtx& x, int base, int lane, MfR
 
 template <int D, bool F8>
 __device__ __forceinline__ void mf_step(const AttnArgs& a, const MfCtx& x, int base, int lane, const u32x4* qv,
-                                        float sc2, float* lg_row, uint16_t* vt, const MfRaw<D, F8>& T,
+                                        float sc2, float* lg_base, uint16_t* vt, const MfRaw<D, F8>& T,
                                         MfState<D>& st) {
   if constexpr (F8) {
     MfTile<D> B;
     mf_convert<D>(T, B);
-    mf_compute<D>(a, x, base, lane, qv, sc2, lg_row, vt, B, st);
+    mf_compute<D>(a, x, base, lane, qv, sc2, lg_base, vt, B, st);
   } else {
-    mf_compute<D>(a, x, base, lane, qv, sc2, lg_row, vt, T, st);
+    mf_compute<D>(a, x, base, lane, qv, sc2, lg_base, vt, T, st);
   }
 }
 
@@ -441,9 +463,8 @@ void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < NDB; ++i) st.o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   uint16_t* vt = vt_lds[w];   // row pitch PITCH, D rows
-  float* lg_row = (a.logits != nullptr && c16 < G)
-                      ? a.logits + (size_t(b) * a.Hq + size_t(kvh) * G + c16) * a.logit_cap
-                      : nullptr;
+  // the group's first logits row (head h at + h * logit_cap), or null: wave-uniform
+  float* lg_base = a.logits != nullptr ? a.logits + (size_t(b) * a.Hq + size_t(kvh) * G) * a.logit_cap : nullptr;
 
   // This wave's tiles are w, w + 4, ...  The steady-state loop runs only while
   // every tile it prefetches exists: its loads are unconditional and an
@@ -459,7 +480,7 @@ void attn_mfma_kernel(AttnArgs a) {
     MfRaw<D, F8> T0, T1, T2;               // two tiles in flight while a third is computed
     if (nmine == 1) {
       mf_fetch<D, VC, F8, APP>(x, first, lane, T0);
-      mf_step<D, F8>(a, x, first, lane, qv, sc2, lg_row, vt, T0, st);
+      mf_step<D, F8>(a, x, first, lane, qv, sc2, lg_base, vt, T0, st);
     } else if (nmine > 1) {
       mf_fetch<D, VC, F8, APP>(x, first, lane, T0);
       mf_fetch<D, VC, F8, APP>(x, first + STEP, lane, T1);
@@ -467,20 +488,20 @@ void attn_mfma_kernel(AttnArgs a) {
       for (; i + 4 < nmine; i += 3) {      // T0 = tile i, T1 = tile i + 1 in flight
         const int b0 = first + i * STEP;
         mf_fetch<D, VC, F8, APP>(x, b0 + 2 * STEP, lane, T2);
-        mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_row, vt, T0, st);
+        mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_base, vt, T0, st);
         mf_fetch<D, VC, F8, APP>(x, b0 + 3 * STEP, lane, T0);
-        mf_step<D, F8>(a, x, b0 + STEP, lane, qv, sc2, lg_row, vt, T1, st);
+        mf_step<D, F8>(a, x, b0 + STEP, lane, qv, sc2, lg_base, vt, T1, st);
         mf_fetch<D, VC, F8, APP>(x, b0 + 4 * STEP, lane, T1);
-        mf_step<D, F8>(a, x, b0 + 2 * STEP, lane, qv, sc2, lg_row, vt, T2, st);
+        mf_step<D, F8>(a, x, b0 + 2 * STEP, lane, qv, sc2, lg_base, vt, T2, st);
       }
       const int r = nmine - i;             // 2, 3 or 4 tiles left
       const int b0 = first + i * STEP;
       if (r >= 3) mf_fetch<D, VC, F8, APP>(x, b0 + 2 * STEP, lane, T2);
-      mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_row, vt, T0, st);
+      mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_base, vt, T0, st);
       if (r == 4) mf_fetch<D, VC, F8, APP>(x, b0 + 3 * STEP, lane, T0);
-      mf_step<D, F8>(a, x, b0 + STEP, lane, qv, sc2, lg_row, vt, T1, st);
-      if (r >= 3) mf_step<D, F8>(a, x, b0 + 2 * STEP, lane, qv, sc2, lg_row, vt, T2, st);
-      if (r == 4) mf_step<D, F8>(a, x, b0 + 3 * STEP, lane, qv, sc2, lg_row, vt, T0, st);
+      mf_step<D, F8>(a, x, b0 + STEP, lane, qv, sc2, lg_base, vt, T1, st);
+      if (r >= 3) mf_step<D, F8>(a, x, b0 + 2 * STEP, lane, qv, sc2, lg_base, vt, T2, st);
+      if (r == 4) mf_step<D, F8>(a, x, b0 + 3 * STEP, lane, qv, sc2, lg_base, vt, T0, st);
     }
   } else {
     MfRaw<D, F8> T0, T1;                   // one tile in flight while the other is computed
@@ -490,17 +511,17 @@ void attn_mfma_kernel(AttnArgs a) {
       for (; i + 2 < nmine; i += 2) {      // T0 = tile i in flight
         const int b0 = first + i * STEP;
         mf_fetch<D, VC, F8, APP>(x, b0 + STEP, lane, T1);
-        mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_row, vt, T0, st);
+        mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_base, vt, T0, st);
         mf_fetch<D, VC, F8, APP>(x, b0 + 2 * STEP, lane, T0);
-        mf_step<D, F8>(a, x, b0 + STEP, lane, qv, sc2, lg_row, vt, T1, st);
+        mf_step<D, F8>(a, x, b0 + STEP, lane, qv, sc2, lg_base, vt, T1, st);
       }
       const int b0 = first + i * STEP;     // one or two tiles left
       if (i + 1 < nmine) {
         mf_fetch<D, VC, F8, APP>(x, b0 + STEP, lane, T1);
-        mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_row, vt, T0, st);
-        mf_step<D, F8>(a, x, b0 + STEP, lane, qv, sc2, lg_row, vt, T1, st);
+        mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_base, vt, T0, st);
+        mf_step<D, F8>(a, x, b0 + STEP, lane, qv, sc2, lg_base, vt, T1, st);
       } else {
-        mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_row, vt, T0, st);
+        mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_base, vt, T0, st);
       }
     }
   }
