@@ -75,6 +75,7 @@ def test_attention_argument_errors(lib):
     assert call_attn(lib, c, view=FAKE, vlen=None, cap=4, g=16) == -1
     assert call_attn(lib, c, view=FAKE, vlen=FAKE, cap=0, g=16) == -2
     assert call_attn(lib, c, logits=FAKE, logit_cap=0) == -2
+    assert call_attn(lib, c, logits=FAKE, logit_cap=(1 << 31) // 4 + 1) == -2   # G * logit_cap past 2^31 - 1
     assert call_attn(lib, c, scale=0.0) == -2
     assert call_attn(lib, c, ws=None) == -6
     assert call_attn(lib, c, ws=FAKE, ws_bytes=16) == -6
