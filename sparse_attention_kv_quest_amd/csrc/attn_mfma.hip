@@ -222,7 +222,7 @@ struct MfState {
 
 template <int D>
 __device__ __forceinline__ void mf_compute(const AttnArgs& a, const MfCtx& x, int base, int lane, const u32x4* qv,
-                                           float sc2, float* lg_base, uint16_t* vt, const MfTile<D>& T,
+                                           float sc2, float* lg_base, float* lgs, uint16_t* vt, const MfTile<D>& T,
                                            MfState<D>& st) {
   constexpr int NKS = D / 32, NDB = D / 16, VPASS = D / 64, PITCH = MF_TS + 4;
   const int g = lane >> 4, c16 = lane & 15, qa = lane & 7;
@@ -242,10 +242,11 @@ __device__ __forceinline__ void mf_compute(const AttnArgs& a, const MfCtx& x, in
     sv[4 + i] = okb ? sb[i] * sc2 : -INFINITY;
   }
   if (lg_base != nullptr) {
-    // the tile's [head][slot] logits go through the wave's LDS tile (free until the V
-    // transpose below), so that each head's 32 slots leave as one contiguous run
+    // the tile's [head][slot] logits go through the wave's LDS staging rows and are
+    // stored after P.V (fewer registers live there), each head's 32 slots as one
+    // contiguous run
     constexpr int LP = MF_TS + 4;
-    float* lt = reinterpret_cast<float*>(vt);
+    float* lt = lgs;
     f32x4 la, lb;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -254,23 +255,6 @@ __device__ __forceinline__ void mf_compute(const AttnArgs& a, const MfCtx& x, in
     }
     *reinterpret_cast<f32x4*>(lt + c16 * LP + 4 * g) = la;
     *reinterpret_cast<f32x4*>(lt + c16 * LP + 16 + 4 * g) = lb;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int sl = base + (lane & 31);
-    const bool sok = sl < x.s1 && sl < a.logit_cap;
-    // offsets within the group's rows (G * logit_cap < 2^31): one per-lane term, the
-    // head pair's part uniform, so no per-head pointer stays live across tiles
-    const uint32_t loff = uint32_t(lane >> 5) * uint32_t(a.logit_cap) + uint32_t(sl);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {   // heads 2k and 2k + 1
-      if (2 * k >= a.G) break;
-      const int h = 2 * k + (lane >> 5);
-      if (h < a.G && sok) lg_base[loff + uint32_t(2 * k) * uint32_t(a.logit_cap)] = lt[h * LP + (lane & 31)];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
   // ---- online softmax; head c16 lives in lanes c16, c16+16, c16+32, c16+48
   float tmax = sv[0];
@@ -337,6 +321,21 @@ __device__ __forceinline__ void mf_compute(const AttnArgs& a, const MfCtx& x, in
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lg_base != nullptr) {   // this tile's logits, staged above (the barriers above ordered them)
+    constexpr int LP = MF_TS + 4;
+    const float* lt = lgs;
+    const int sl = base + (lane & 31);
+    const bool sok = sl < x.s1 && sl < a.logit_cap;
+    // offsets within the group's rows (G * logit_cap < 2^31): one per-lane term, the
+    // head pair's part uniform, so no per-head pointer stays live across tiles
+    const uint32_t loff = uint32_t(lane >> 5) * uint32_t(a.logit_cap) + uint32_t(sl);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {   // heads 2k and 2k + 1
+      if (2 * k >= a.G) break;
+      const int h = 2 * k + (lane >> 5);
+      if (h < a.G && sok) lg_base[loff + uint32_t(2 * k) * uint32_t(a.logit_cap)] = lt[h * LP + (lane & 31)];
+    }
+  }
 }
 
 template <int D, bool VC, bool F8, bool APP>
@@ -347,18 +346,20 @@ __device__ __forceinline__ void mf_fetch(const MfCtx& x, int base, int lane, MfR
 
 template <int D, bool F8>
 __device__ __forceinline__ void mf_step(const AttnArgs& a, const MfCtx& x, int base, int lane, const u32x4* qv,
-                                        float sc2, float* lg_base, uint16_t* vt, const MfRaw<D, F8>& T,
+                                        float sc2, float* lg_base, float* lgs, uint16_t* vt, const MfRaw<D, F8>& T,
                                         MfState<D>& st) {
   if constexpr (F8) {
     MfTile<D> B;
     mf_convert<D>(T, B);
-    mf_compute<D>(a, x, base, lane, qv, sc2, lg_base, vt, B, st);
+    mf_compute<D>(a, x, base, lane, qv, sc2, lg_base, lgs, vt, B, st);
   } else {
-    mf_compute<D>(a, x, base, lane, qv, sc2, lg_base, vt, T, st);
+    mf_compute<D>(a, x, base, lane, qv, sc2, lg_base, lgs, vt, T, st);
   }
 }
 
-template <int D, bool VC, int OCC, bool F8, bool APP>
+// LG: logits requested.  Launches without them compile the logits path out, which
+// keeps the register budget (a spill here costs far more than its few bytes).
+template <int D, bool VC, int OCC, bool F8, bool APP, bool LG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void attn_mfma_kernel(AttnArgs a) {
   static_assert(!(APP && F8), "the fused append writes bf16 rows");
@@ -367,6 +368,8 @@ void attn_mfma_kernel(AttnArgs a) {
   constexpr int NKS = D / 32;
   static_assert(D == 64 || D == 128, "head width");
   __shared__ __align__(16) uint16_t vt_lds[MF_WAVES][D * PITCH];   // V tiles, then the wave merge
+  __shared__ __align__(16) float lg_lds[LG ? MF_WAVES : 1][16 * (MF_TS + 4)];   // logits staging
+  __shared__ u32x4 app_lds[APP ? 2 * (D / 8) : 1];   // the new row, parked during the tiles
   __shared__ float red_m[MF_WAVES][16], red_l[MF_WAVES][16];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -463,8 +466,9 @@ void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < NDB; ++i) st.o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   uint16_t* vt = vt_lds[w];   // row pitch PITCH, D rows
+  float* lgs = LG ? lg_lds[w] : nullptr;
   // the group's first logits row (head h at + h * logit_cap), or null: wave-uniform
-  float* lg_base = a.logits != nullptr ? a.logits + (size_t(b) * a.Hq + size_t(kvh) * G) * a.logit_cap : nullptr;
+  float* lg_base = LG ? a.logits + (size_t(b) * a.Hq + size_t(kvh) * G) * a.logit_cap : nullptr;
 
   // This wave's tiles are w, w + 4, ...  The steady-state loop runs only while
   // every tile it prefetches exists: its loads are unconditional and an
@@ -476,52 +480,65 @@ void attn_mfma_kernel(AttnArgs a) {
   const int nmine = w < ntiles ? (ntiles - w + MF_WAVES - 1) / MF_WAVES : 0;
   constexpr int STEP = MF_WAVES * MF_TS;   // slots between this wave's consecutive tiles
   const int first = s0 + w * MF_TS;
+  // the new row's 16 bytes per thread wait in LDS while the tiles run (written once
+  // the first tile's loads are out, so that its wait delays none of them): four
+  // fewer registers held across the loop
+  const bool app_mine = APP && split == 0 && tgt >= 0 && threadIdx.x < 2 * (D / 8);
+  auto park_app_row = [&]() {
+    if (app_mine) app_lds[threadIdx.x] = app_row;
+  };
   if (OCC == 1) {
     MfRaw<D, F8> T0, T1, T2;               // two tiles in flight while a third is computed
-    if (nmine == 1) {
+    if (nmine == 0) {
+      park_app_row();
+    } else if (nmine == 1) {
       mf_fetch<D, VC, F8, APP>(x, first, lane, T0);
-      mf_step<D, F8>(a, x, first, lane, qv, sc2, lg_base, vt, T0, st);
-    } else if (nmine > 1) {
+      park_app_row();
+      mf_step<D, F8>(a, x, first, lane, qv, sc2, lg_base, lgs, vt, T0, st);
+    } else {
       mf_fetch<D, VC, F8, APP>(x, first, lane, T0);
       mf_fetch<D, VC, F8, APP>(x, first + STEP, lane, T1);
+      park_app_row();
       int i = 0;
       for (; i + 4 < nmine; i += 3) {      // T0 = tile i, T1 = tile i + 1 in flight
         const int b0 = first + i * STEP;
         mf_fetch<D, VC, F8, APP>(x, b0 + 2 * STEP, lane, T2);
-        mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_base, vt, T0, st);
+        mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_base, lgs, vt, T0, st);
         mf_fetch<D, VC, F8, APP>(x, b0 + 3 * STEP, lane, T0);
-        mf_step<D, F8>(a, x, b0 + STEP, lane, qv, sc2, lg_base, vt, T1, st);
+        mf_step<D, F8>(a, x, b0 + STEP, lane, qv, sc2, lg_base, lgs, vt, T1, st);
         mf_fetch<D, VC, F8, APP>(x, b0 + 4 * STEP, lane, T1);
-        mf_step<D, F8>(a, x, b0 + 2 * STEP, lane, qv, sc2, lg_base, vt, T2, st);
+        mf_step<D, F8>(a, x, b0 + 2 * STEP, lane, qv, sc2, lg_base, lgs, vt, T2, st);
       }
       const int r = nmine - i;             // 2, 3 or 4 tiles left
       const int b0 = first + i * STEP;
       if (r >= 3) mf_fetch<D, VC, F8, APP>(x, b0 + 2 * STEP, lane, T2);
-      mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_base, vt, T0, st);
+      mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_base, lgs, vt, T0, st);
       if (r == 4) mf_fetch<D, VC, F8, APP>(x, b0 + 3 * STEP, lane, T0);
-      mf_step<D, F8>(a, x, b0 + STEP, lane, qv, sc2, lg_base, vt, T1, st);
-      if (r >= 3) mf_step<D, F8>(a, x, b0 + 2 * STEP, lane, qv, sc2, lg_base, vt, T2, st);
-      if (r == 4) mf_step<D, F8>(a, x, b0 + 3 * STEP, lane, qv, sc2, lg_base, vt, T0, st);
+      mf_step<D, F8>(a, x, b0 + STEP, lane, qv, sc2, lg_base, lgs, vt, T1, st);
+      if (r >= 3) mf_step<D, F8>(a, x, b0 + 2 * STEP, lane, qv, sc2, lg_base, lgs, vt, T2, st);
+      if (r == 4) mf_step<D, F8>(a, x, b0 + 3 * STEP, lane, qv, sc2, lg_base, lgs, vt, T0, st);
     }
   } else {
     MfRaw<D, F8> T0, T1;                   // one tile in flight while the other is computed
+    if (nmine == 0) park_app_row();
     if (nmine > 0) {
       mf_fetch<D, VC, F8, APP>(x, first, lane, T0);
+      park_app_row();
       int i = 0;
       for (; i + 2 < nmine; i += 2) {      // T0 = tile i in flight
         const int b0 = first + i * STEP;
         mf_fetch<D, VC, F8, APP>(x, b0 + STEP, lane, T1);
-        mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_base, vt, T0, st);
+        mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_base, lgs, vt, T0, st);
         mf_fetch<D, VC, F8, APP>(x, b0 + 2 * STEP, lane, T0);
-        mf_step<D, F8>(a, x, b0 + STEP, lane, qv, sc2, lg_base, vt, T1, st);
+        mf_step<D, F8>(a, x, b0 + STEP, lane, qv, sc2, lg_base, lgs, vt, T1, st);
       }
       const int b0 = first + i * STEP;     // one or two tiles left
       if (i + 1 < nmine) {
         mf_fetch<D, VC, F8, APP>(x, b0 + STEP, lane, T1);
-        mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_base, vt, T0, st);
-        mf_step<D, F8>(a, x, b0 + STEP, lane, qv, sc2, lg_base, vt, T1, st);
+        mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_base, lgs, vt, T0, st);
+        mf_step<D, F8>(a, x, b0 + STEP, lane, qv, sc2, lg_base, lgs, vt, T1, st);
       } else {
-        mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_base, vt, T0, st);
+        mf_step<D, F8>(a, x, b0, lane, qv, sc2, lg_base, lgs, vt, T0, st);
       }
     }
   }
@@ -532,11 +549,11 @@ void attn_mfma_kernel(AttnArgs a) {
     // last one stores the new length at the end
     row_ticket = __hip_atomic_fetch_add(a.row_ctr + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (APP && split == 0 && tgt >= 0 && threadIdx.x < 2 * (D / 8)) {   // its load went out before the tiles
+  if (app_mine) {   // its load went out before the tiles
     const bool isv = threadIdx.x >= D / 8;
     const int o = 8 * (isv ? threadIdx.x - D / 8 : threadIdx.x);
     *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(isv ? a.v_w : a.k_w) + (size_t(unit) * a.cap + tgt) * D + o) =
-        app_row;
+        app_lds[threadIdx.x];
   }
   // ---- merge the waves of the block: per head, the waves' (max, sum) and
   // outputs [wave][head][dim] (row pitch D + 4) go through LDS; a thread then
@@ -614,6 +631,14 @@ int attn_mfma_auto_splits(int units, int slots) {
   return std::min(s, 256);
 }
 
+template <int D, bool VC, int OCC, bool F8, bool APP>
+static void mf_launch(const AttnArgs& a, dim3 grid, hipStream_t s) {
+  if (a.logits != nullptr)
+    hipLaunchKernelGGL((attn_mfma_kernel<D, VC, OCC, F8, APP, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<D, VC, OCC, F8, APP, false>), grid, dim3(256), 0, s, a);
+}
+
 se_status launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.splits, a.B * a.Hkv);
   // entries one block reads: its chunk of slots divided by the granularity (+2 for straddled entries)
@@ -621,8 +646,7 @@ se_status launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
   int chunk = (slots + a.splits - 1) / a.splits;
   chunk = (chunk + MF_TS - 1) / MF_TS * MF_TS;
   const bool vc = a.view_idx != nullptr && chunk / a.gran + 2 <= MF_VCACHE;
-#define SE_MF_LAUNCH(DD, VV, OO, FF, AA) \
-  hipLaunchKernelGGL((attn_mfma_kernel<DD, VV, OO, FF, AA>), grid, dim3(256), 0, s, a)
+#define SE_MF_LAUNCH(DD, VV, OO, FF, AA) mf_launch<DD, VV, OO, FF, AA>(a, grid, s)
 #define SE_MF_D(FF, AA)                                                                              \
   if (a.Dk == 128) {                                                                                 \
     if (vc) SE_MF_LAUNCH(128, true, 2, FF, AA); else SE_MF_LAUNCH(128, false, 2, FF, AA);            \
