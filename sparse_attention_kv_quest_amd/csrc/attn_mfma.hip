@@ -329,8 +329,8 @@ __device__ __forceinline__ void mf_compute(const AttnArgs& a, const MfCtx& x, in
     // offsets within the group's rows (G * logit_cap < 2^31): one per-lane term, the
     // head pair's part uniform, so no per-head pointer stays live across tiles
     const uint32_t loff = uint32_t(lane >> 5) * uint32_t(a.logit_cap) + uint32_t(sl);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {   // heads 2k and 2k + 1
+#pragma unroll 1
+    for (int k = 0; k < 8; ++k) {   // heads 2k and 2k + 1 (not unrolled: fewer live registers)
       if (2 * k >= a.G) break;
       const int h = 2 * k + (lane >> 5);
       if (h < a.G && sok) lg_base[loff + uint32_t(2 * k) * uint32_t(a.logit_cap)] = lt[h * LP + (lane & 31)];
