@@ -432,19 +432,21 @@ __global__ __launch_bounds__(BLOCK) void quest_topk_reg_kernel(
   const int len = min(seq_len[b], cap);
   const int new_len = (APP && len < cap) ? len + 1 : len;
   const int n = min((new_len + P - 1) / P, n_cap_pages);
-  // APP: the row ticket is taken as soon as the old length has been read and its
-  // value is looked at only at the end, so the atomic's round trip overlaps the
-  // selection instead of following it
+  // APP: the row ticket is taken right after the score loads have been issued --
+  // their addresses depend on the old length, so it has been read -- and its value
+  // is looked at only at the end: the atomic's round trip overlaps the scores'
+  // (the compiler waits for its return at once: the wave-aggregated atomic needs it)
   int ticket = 0;
-  if (APP && threadIdx.x == 0) {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);   // the old length has been read
-    ticket = __hip_atomic_fetch_add(counters + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  }
+  auto take_ticket = [&]() {
+    if (APP && threadIdx.x == 0) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      ticket = __hip_atomic_fetch_add(counters + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    }
+  };
   const float* su = score + size_t(unit) * n_cap_pages;
   const int kk = block_topk_reg<BLOCK, E>([&](int i) { return su[i]; }, n, top_pages,
-                                          view_idx + size_t(unit) * top_pages, sh);
+                                          view_idx + size_t(unit) * top_pages, sh, take_ticket);
   if (threadIdx.x == 0) view_len[unit] = kk;
   if (APP && threadIdx.x == 0 && ticket == Hkv - 1) {   // every block of the row has read the old length
     if (new_len != len) seq_len[b] = new_len;

@@ -321,16 +321,30 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
   return int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
 }
 
-template <int BLOCK, int E, class LoadFn>
-__device__ int block_topk_reg(LoadFn load, int n, int k, int32_t* out, TopkRegShared& sh) {
+struct TopkNoHook {
+  __device__ void operator()() const {}
+};
+
+// after_loads() runs once every key load has been issued (its own memory operations
+// then overlap those loads' return)
+template <int BLOCK, int E, class LoadFn, class AfterLoads = TopkNoHook>
+__device__ int block_topk_reg(LoadFn load, int n, int k, int32_t* out, TopkRegShared& sh,
+                              AfterLoads after_loads = AfterLoads{}) {
   static_assert(BLOCK >= 64 && BLOCK <= 1024 && BLOCK % WAVE == 0, "block size");
   constexpr int NW = BLOCK / WAVE;
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
   const int kk = k < n ? k : n;
   const int base = w * WAVE * E + lane;
   uint32_t key[E];
+  // unconditional loads at a clamped index (element 0 always exists), masked after:
+  // all E loads go out together instead of one guarded round trip each
 #pragma unroll
-  for (int j = 0; j < E; ++j) key[j] = (base + j * WAVE < n) ? ordered_bits(load(base + j * WAVE)) : 0u;
+  for (int j = 0; j < E; ++j) {
+    const int i = base + j * WAVE;
+    const uint32_t v = ordered_bits(load(max(min(i, n - 1), 0)));
+    key[j] = i < n ? v : 0u;
+  }
+  after_loads();
   uint32_t mask = 0u, prefix = 0u;   // resolved top bits and their value
   int r = kk;                        // keys still to take from the bucket (key & mask) == prefix
   if (kk > 0 && kk < n) {
