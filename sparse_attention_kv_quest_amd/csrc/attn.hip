@@ -145,6 +145,40 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const float* pml = a.part_ml + size_t(unit) * S * G * 2;
   const float* po = a.part_o + size_t(unit) * S * G * Dv;
+  const size_t row = size_t(b) * a.Hq + size_t(kvh) * G + h;
+  constexpr int CS = 8, CD = 4;
+  if (S <= CS && Dv == CD * 128) {
+    // every load of the block at once (clamped split index, weight 0 past S): the
+    // partial outputs, then each split's (max, sum), one round trip in all
+    float pv[CS][CD];
+#pragma unroll
+    for (int sx = 0; sx < CS; ++sx)
+#pragma unroll
+      for (int j = 0; j < CD; ++j) pv[sx][j] = po[(size_t(min(sx, S - 1)) * G + h) * Dv + threadIdx.x + 128 * j];
+    float2 ml[CS];
+#pragma unroll
+    for (int sx = 0; sx < CS; ++sx) ml[sx] = *reinterpret_cast<const float2*>(pml + (min(sx, S - 1) * G + h) * 2);
+    float M = -INFINITY;
+#pragma unroll
+    for (int sx = 0; sx < CS; ++sx)
+      if (sx < S) M = fmaxf(M, ml[sx].x);
+    float f[CS], L = 0.f;
+#pragma unroll
+    for (int sx = 0; sx < CS; ++sx) {
+      f[sx] = (sx < S && ml[sx].x != -INFINITY) ? ex2((ml[sx].x - M) * LOG2E) : 0.f;
+      L += f[sx] * ml[sx].y;
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+    for (int j = 0; j < CD; ++j) {
+      float o = 0.f;
+#pragma unroll
+      for (int sx = 0; sx < CS; ++sx) o += f[sx] * pv[sx][j];
+      a.out[row * Dv + threadIdx.x + 128 * j] = o * inv;
+    }
+    if (threadIdx.x == 0 && a.lse != nullptr) a.lse[row] = L > 0.f ? M + logf(L) : -INFINITY;
+    return;
+  }
   float mloc = -INFINITY;
   for (int s = threadIdx.x; s < S; s += 128) {
     const float ms = pml[(s * G + h) * 2];
@@ -167,7 +201,6 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   if (lane == 0) red[w] = lloc;
   __syncthreads();
   const float L = red[0] + red[1];
-  const size_t row = size_t(b) * a.Hq + size_t(kvh) * G + h;
   const float inv = L > 0.f ? 1.f / L : 0.f;
   for (int d = threadIdx.x; d < Dv; d += 128) {
     float o = 0.f;
