@@ -107,23 +107,22 @@ __global__ __launch_bounds__(256) void h2o_reg_kernel(
   const int in = evict_slot[unit];
   const int ns = in >= 0 ? in : n - 1;   // the slot that received the token at cur_pos
   if (threadIdx.x == 0 && ns >= n && ns < cap) { pos[ns] = cur_pos; a[ns] = 0.f; }   // outside the attended slots
+  // the slot state and the first HC heads' logits go out together (unconditional
+  // loads at clamped indices, masked after): one memory round trip before the
+  // accumulation instead of two
   int p[E];
   float sc[E];
 #pragma unroll
   for (int j = 0; j < E; ++j) {
-    const int s = j * 256 + threadIdx.x;
-    const bool ok = s < n;
-    p[j] = ok ? pos[s] : -1;
-    sc[j] = ok ? a[s] : 0.f;
-    if (s == ns) { p[j] = cur_pos; sc[j] = 0.f; }
+    const int s = max(min(j * 256 + int(threadIdx.x), n - 1), 0);
+    p[j] = pos[s];
+    sc[j] = a[s];
   }
   // accumulate: every occupied slot adds the group's softmax weight on it, heads in
   // ascending order; the logit loads of HC heads go out together (one memory round
   // trip per HC heads, not per head)
   constexpr int HC = E <= 8 ? 8 : 4;
-  int cnt = 0;
-  for (int h0 = 0; h0 < G; h0 += HC) {
-    float l[HC], x[HC][E];
+  auto load_heads = [&](int h0, float (&l)[HC], float (&x)[HC][E]) {
 #pragma unroll
     for (int hh = 0; hh < HC; ++hh) {
       const int h = min(h0 + hh, G - 1);
@@ -131,6 +130,8 @@ __global__ __launch_bounds__(256) void h2o_reg_kernel(
 #pragma unroll
       for (int j = 0; j < E; ++j) x[hh][j] = lg[size_t(h) * logit_cap + min(j * 256 + int(threadIdx.x), logit_cap - 1)];
     }
+  };
+  auto add_heads = [&](const float (&l)[HC], const float (&x)[HC][E]) {
 #pragma unroll
     for (int hh = 0; hh < HC; ++hh) {
       if (l[hh] == -INFINITY) continue;
@@ -138,7 +139,24 @@ __global__ __launch_bounds__(256) void h2o_reg_kernel(
       for (int j = 0; j < E; ++j)
         if (p[j] >= 0) sc[j] += expf(x[hh][j] - l[hh]);
     }
+  };
+  {
+    float l[HC], x[HC][E];
+    load_heads(0, l, x);
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int s = j * 256 + threadIdx.x;
+      if (s >= n) { p[j] = -1; sc[j] = 0.f; }
+      if (s == ns) { p[j] = cur_pos; sc[j] = 0.f; }
+    }
+    add_heads(l, x);
   }
+  for (int h0 = HC; h0 < G; h0 += HC) {
+    float l[HC], x[HC][E];
+    load_heads(h0, l, x);
+    add_heads(l, x);
+  }
+  int cnt = 0;
 #pragma unroll
   for (int j = 0; j < E; ++j) {
     const int s = j * 256 + threadIdx.x;
