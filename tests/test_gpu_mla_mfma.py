@@ -48,7 +48,7 @@ def check(got, ref, lens_or_counts, logit_cap):
             np.testing.assert_allclose(lg[b, :, :n], rlg[b, :, :n], rtol=0, atol=tol)
 
 
-@pytest.mark.parametrize("heads", [16, 32, 48, 64])
+@pytest.mark.parametrize("heads", [16, 17, 24, 32, 48, 64])   # 17, 24: partial second head block of a group
 @pytest.mark.parametrize("splits", [0, 1, 2, 3])
 def test_mla_identity_view_head_groups(se, heads, splits):
     banner(f"mla mfma identity heads={heads} splits={splits}")
