@@ -215,11 +215,11 @@ def run_quest(se, torch, args):
     for i in range(args.warmup):
         step(layers[i % nL])
     torch.cuda.synchronize()
-    t_step = Timer(torch, lambda: [step(L) for L in layers], use_graph)
+    # one replay = exactly --steps decode steps, rotating over the layer caches
+    n_steps = max(1, args.steps)
+    t_step = Timer(torch, lambda: [step(layers[i % nL]) for i in range(n_steps)], use_graph)
     t_attn = Timer(torch, lambda: [attn_only(L) for L in layers], use_graph)
-    reps = max(1, args.steps // nL)
-    n_steps = reps * nL
-    ms_step = t_step.ms_per_replay(reps) / nL
+    ms_step = t_step.ms_per_replay(1) / n_steps
     us_attn = t_attn.ms_per_replay(args.attn_reps) * 1e3 / nL
     # the step's first stage replayed alone over the same layers (it appends a row per replay)
     t_sel = Timer(torch, lambda: [append_select(L) for L in layers], use_graph)
