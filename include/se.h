@@ -283,6 +283,26 @@ se_status se_sparse_decode_attn(const se_cache* c, const void* q, const void* k,
                                 int32_t logit_cap, int32_t num_splits,
                                 void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* se_sparse_decode_attn for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without a workspace, and the same results,
+ * bit for bit.  Its split partials and ticket counters live in a static device
+ * array of SE_NOALLOC_SCRATCH_BYTES bytes that each GPU the library runs on
+ * holds until the process ends; the call allocates nothing.  Calls whose
+ * workspace (se_workspace_bytes(SE_OP_ATTN, c, view_cap * granularity,
+ * num_splits)) would exceed that size return SE_ERR_WORKSPACE and enqueue
+ * nothing.  Every call on one GPU shares that GPU's array: calls that may run
+ * concurrently on one GPU (different streams without ordering between them)
+ * race and give undefined results.  Each call first clears the array's
+ * counters with a fill kernel on `stream` (no memset node).  SE_ERR_HIP if the
+ * array's device address cannot be obtained. */
+#define SE_NOALLOC_SCRATCH_BYTES (32u << 20)
+se_status se_sparse_decode_attn_noalloc(const se_cache* c, const void* q, const void* k, const void* v,
+                                        const int32_t* seq_len, const int32_t* view_idx,
+                                        const int32_t* view_len, int32_t view_cap, int32_t granularity,
+                                        float scale, float* out, float* lse, float* logits,
+                                        int32_t logit_cap, int32_t num_splits, hipStream_t stream);
+
 /* A decode step's append and attention in one launch (the hooks' append-then-
  * attend, as for a SnapKV-compacted or H2O cache): the same results, bit for
  * bit, as

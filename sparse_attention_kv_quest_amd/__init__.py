@@ -22,7 +22,7 @@ STATUS = {0: "SE_OK", -1: "SE_ERR_NULL", -2: "SE_ERR_SHAPE", -3: "SE_ERR_DTYPE",
           -5: "SE_ERR_BUDGET", -6: "SE_ERR_WORKSPACE", -7: "SE_ERR_UNSUPPORTED", -8: "SE_ERR_HIP"}
 
 EXPORTS = ("se_kv_append", "se_kv_append_meta", "se_page_meta_update", "se_quest_select", "se_quest_append_select",
-           "se_sparse_decode_attn", "se_kv_append_decode_attn", "se_streaming_view", "se_pyramid_budgets",
+           "se_sparse_decode_attn", "se_sparse_decode_attn_noalloc", "se_kv_append_decode_attn", "se_streaming_view", "se_pyramid_budgets",
            "se_kv_quantize_fp8", "se_kv_append_fp8", "se_sparse_decode_attn_fp8",
            "se_chain_match", "se_chain_remap", "se_chain_append_positions", "se_h2o_prefill_init",
            "se_snapkv_score_compact", "se_h2o_accumulate_evict", "se_omnikv_topk",
@@ -51,6 +51,7 @@ _SIGS = {
     "se_quest_select": [_C, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _SZ, _P],
     "se_quest_append_select": [_C, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _SZ, _P],
     "se_sparse_decode_attn": [_C, _P, _P, _P, _P, _P, _P, _I32, _I32, _F32, _P, _P, _P, _I32, _I32, _P, _SZ, _P],
+    "se_sparse_decode_attn_noalloc": [_C, _P, _P, _P, _P, _P, _P, _I32, _I32, _F32, _P, _P, _P, _I32, _I32, _P],
     "se_kv_append_decode_attn": [_C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _F32, _P, _P, _P, _I32, _I32, _P,
                                  _SZ, _P],
     "se_streaming_view": [_C, _P, _I32, _I32, _P, _P, _I32, _I32, _P],
@@ -255,6 +256,13 @@ def se_sparse_decode_attn(c, q, k, v, seq_len, view_idx, view_len, view_cap, gra
         ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(seq_len), _ptr(view_idx), _ptr(view_len), view_cap,
         granularity, scale, _ptr(out), _ptr(lse), _ptr(logits), logit_cap, num_splits, _ptr(ws), _nbytes(ws),
         _stream(stream)))
+
+
+def se_sparse_decode_attn_noalloc(c, q, k, v, seq_len, view_idx, view_len, view_cap, granularity, scale, out,
+                                  lse=None, logits=None, logit_cap=0, num_splits=0, stream=None):
+    _check("se_sparse_decode_attn_noalloc", load().se_sparse_decode_attn_noalloc(
+        ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(seq_len), _ptr(view_idx), _ptr(view_len), view_cap,
+        granularity, scale, _ptr(out), _ptr(lse), _ptr(logits), logit_cap, num_splits, _stream(stream)))
 
 
 def se_kv_append_decode_attn(c, q, k, v, k_new, v_new, slot, seq_len, view_idx, view_len, view_cap, granularity,

@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 using namespace se;
 
 namespace {
@@ -44,12 +46,12 @@ se_status check_cache(const se_cache* c) {
   return SE_OK;
 }
 
-// Shared validation and launch of the attention calls (cache already checked);
-// k_scale / v_scale non-null for FP8 rows.
-se_status attn_impl(const se_cache* c, const void* q, const void* k, const void* v, const int32_t* seq_len,
-                    const int32_t* view_idx, const int32_t* view_len, int32_t view_cap, int32_t granularity,
-                    float scale, float* out, float* lse, float* logits, int32_t logit_cap, int32_t num_splits,
-                    void* ws, size_t ws_bytes, hipStream_t stream, const uint8_t* k_scale, const uint8_t* v_scale) {
+// Argument checks of the attention calls (cache already checked), up to the
+// workspace size, which the caller compares: *need receives it.
+se_status attn_validate(const se_cache* c, const void* q, const void* k, const void* v, const int32_t* seq_len,
+                        const int32_t* view_idx, const int32_t* view_len, int32_t view_cap, int32_t granularity,
+                        float scale, float* out, float* logits, int32_t logit_cap, int32_t num_splits,
+                        size_t* need) {
   if (!q || !k || !seq_len || !out || (!c->latent && !v)) return SE_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || (!c->latent && !aligned16(v)) || !aligned16(out)) return SE_ERR_ALIGN;
   if (view_idx) {
@@ -63,7 +65,20 @@ se_status attn_impl(const se_cache* c, const void* q, const void* k, const void*
   if (num_splits < 0 || num_splits > 256) return SE_ERR_SHAPE;
   if (!(scale > 0.f) || !(scale < 1e30f)) return SE_ERR_SHAPE;
   const int slots = view_idx ? view_cap * granularity : c->capacity;
-  const size_t need = attn_ws_bytes(*c, slots, num_splits);
+  *need = attn_ws_bytes(*c, slots, num_splits);
+  return SE_OK;
+}
+
+// Shared validation and launch of the attention calls (cache already checked);
+// k_scale / v_scale non-null for FP8 rows.
+se_status attn_impl(const se_cache* c, const void* q, const void* k, const void* v, const int32_t* seq_len,
+                    const int32_t* view_idx, const int32_t* view_len, int32_t view_cap, int32_t granularity,
+                    float scale, float* out, float* lse, float* logits, int32_t logit_cap, int32_t num_splits,
+                    void* ws, size_t ws_bytes, hipStream_t stream, const uint8_t* k_scale, const uint8_t* v_scale) {
+  size_t need = 0;
+  se_status st = attn_validate(c, q, k, v, seq_len, view_idx, view_len, view_cap, granularity, scale, out, logits,
+                               logit_cap, num_splits, &need);
+  if (st != SE_OK) return st;
   if (!ws || ws_bytes < need) return SE_ERR_WORKSPACE;
   SE_TRACE_CALL("sparse_decode_attn%s B=%d Hq=%d Hkv=%d d_k=%d d_v=%d view=%s cap=%d g=%d splits=%d logits=%d",
                 k_scale ? "_fp8" : "", c->batch, c->n_q_heads, c->n_kv_heads, c->d_k, c->d_v, view_idx ? "idx" : "identity",
@@ -71,6 +86,30 @@ se_status attn_impl(const se_cache* c, const void* q, const void* k, const void*
   clear_stale_error();
   return launch_attn(*c, q, k, v, seq_len, view_idx, view_len, view_cap, granularity, scale, out, lse, logits,
                      logit_cap, num_splits, ws, stream, k_scale, v_scale);
+}
+
+// Device memory of se_sparse_decode_attn_noalloc: one array per GPU the library
+// runs on, held until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device array: kernels and fills get the address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[SE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's device address on the current device, looked up once per device.
+se_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return SE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SE_OK;
 }
 
 }  // namespace
@@ -327,6 +366,33 @@ se_status se_sparse_decode_attn(const se_cache* c, const void* q, const void* k,
   if (st != SE_OK) return st;
   return attn_impl(c, q, k, v, seq_len, view_idx, view_len, view_cap, granularity, scale, out, lse, logits, logit_cap,
                    num_splits, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+se_status se_sparse_decode_attn_noalloc(const se_cache* c, const void* q, const void* k, const void* v,
+                                        const int32_t* seq_len, const int32_t* view_idx,
+                                        const int32_t* view_len, int32_t view_cap, int32_t granularity,
+                                        float scale, float* out, float* lse, float* logits,
+                                        int32_t logit_cap, int32_t num_splits, hipStream_t stream) {
+  se_status st = check_cache(c);
+  if (st != SE_OK) return st;
+  size_t need = 0;
+  st = attn_validate(c, q, k, v, seq_len, view_idx, view_len, view_cap, granularity, scale, out, logits, logit_cap,
+                     num_splits, &need);
+  if (st != SE_OK) return st;
+  if (need > SE_NOALLOC_SCRATCH_BYTES) return SE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  clear_stale_error();
+  st = scratch_of_current_device(&ws);
+  if (st != SE_OK) return st;
+  SE_TRACE_CALL("sparse_decode_attn_noalloc B=%d Hq=%d Hkv=%d d_k=%d view=%s cap=%d g=%d splits=%d scratch=%zu",
+                c->batch, c->n_q_heads, c->n_kv_heads, c->d_k, view_idx ? "idx" : "identity", view_cap, granularity,
+                num_splits, need);
+  // the ticket counters start at zero: cleared by a fill kernel (capturable) on the
+  // caller's stream, ahead of the attention, whatever an earlier call left there
+  st = launch_zero_fill(ws, attn_counter_bytes(*c), stream);
+  if (st != SE_OK) return st;
+  return launch_attn(*c, q, k, v, seq_len, view_idx, view_len, view_cap, granularity, scale, out, lse, logits,
+                     logit_cap, num_splits, ws, stream, nullptr, nullptr);
 }
 
 se_status se_kv_append_decode_attn(const se_cache* c, const void* q, void* k, void* v, const void* k_new,

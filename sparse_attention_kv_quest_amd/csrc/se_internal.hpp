@@ -485,6 +485,7 @@ se_status launch_quest(const se_cache& c, const void* q, const void* kmin, const
                        const int32_t* seq_len, int page_size, int top_pages, int32_t* view_idx,
                        int32_t* view_len, float* page_score, void* ws, hipStream_t s);
 int attn_auto_splits(const se_cache& c, int slots);
+size_t attn_counter_bytes(const se_cache& c);   // leading ticket-counter bytes of an attention workspace
 size_t attn_ws_bytes(const se_cache& c, int slots, int num_splits);
 // k_scale / v_scale non-null: K / V hold FP8 rows with one scale byte per row.
 size_t attn_append_ws_bytes(const se_cache& c, int slots, int num_splits);

@@ -132,3 +132,27 @@ def test_product_path_does_not_import_the_oracle():
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f), errors="ignore").read()
                 assert "oracle" not in text.lower(), f
+
+
+def call_attn_noalloc(lib, c, q=FAKE, k=FAKE, v=FAKE, seq=FAKE, view=None, vlen=None, cap=0, g=1, scale=0.1,
+                      out=FAKE, logits=None, logit_cap=0, splits=0):
+    return lib.se_sparse_decode_attn_noalloc(ctypes.byref(c), q, k, v, seq, view, vlen, cap, g, scale, out, None,
+                                             logits, logit_cap, splits, None)
+
+
+def test_noalloc_attention_argument_errors(lib):
+    """The workspace-free attention checks its arguments as se_sparse_decode_attn does and
+    rejects calls whose workspace would not fit its fixed scratch, before any HIP call."""
+    c = se.cache(2, 8, 2, 128, 128, 1024, "bf16")
+    assert call_attn_noalloc(lib, c, q=None) == -1
+    assert call_attn_noalloc(lib, c, out=MIS) == -4
+    assert call_attn_noalloc(lib, c, view=FAKE, vlen=None, cap=4, g=16) == -1
+    assert call_attn_noalloc(lib, c, scale=float("nan")) == -2
+    assert call_attn_noalloc(lib, c, splits=300) == -2
+    assert call_attn_noalloc(lib, se.cache(2, 8, 3, 128, 128, 1024, "bf16")) == -2
+    big = se.cache(64, 32, 4, 128, 128, 16384, "bf16")
+    assert se.se_workspace_bytes(se.SE_OP_ATTN, big, 16384, 256) > (32 << 20)
+    assert call_attn_noalloc(lib, big, splits=256) == -6
+    # the headline shape fits
+    quest = se.cache(16, 32, 4, 128, 128, 32832, "bf16")
+    assert se.se_workspace_bytes(se.SE_OP_ATTN, quest, 2048, 0) <= (32 << 20)
