@@ -1,137 +1,233 @@
 """Finds, with the CPU oracle only, the seeded query draws that keep every
-selection decision of the full-size parity cases clear of near-ties, and writes
-them to attempts.json beside this script.
+selection decision of the parity cases clear of near-ties, and writes them to
+attempts.json beside this script.
 
 A decision (top-k boundary, H2O argmin) is accepted when the oracle's float64
 scores put at least GAP relative distance between the kept side and the rest;
 otherwise the unit's query of that step is redrawn with attempt + 1.  float32
 rounding of the GPU scores (a few ulp of accumulated error) cannot reorder such
-decisions.  Run: python tests/golden/make_attempts.py
+decisions.  The searches are independent per unit and run in a process pool.
+Run: python tests/golden/make_attempts.py
 """
 import json
 import os
 import sys
+import time
 
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(os.path.dirname(HERE))
-sys.path.insert(0, ROOT)
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
 
+from oracle import boundary_gap  # noqa: E402
 from oracle import h2o as oh2o  # noqa: E402
 from oracle import omnikv as oomni  # noqa: E402
 from oracle import snapkv as osnap  # noqa: E402
-from oracle import boundary_gap  # noqa: E402
 from oracle.attention import unit_attention  # noqa: E402
-from tests.h2o_omni_cases import h2o_config, h2o_step_inputs, h2o_unit_start, omni_config  # noqa: E402
-from tests.sampled_units import H2O_UNITS, OMNI_STEPS, OMNI_UNITS, SNAP_UNITS  # noqa: E402
+from tests.h2o_omni_cases import (OMNI_STEPS, OMNI_UNITS, PREFILL_CASES, PREFILL_DECODE_CFG,  # noqa: E402
+                                  PREFILL_DECODE_LAYER, PREFILL_KV_LAYER, PYRAMID_CASES, PYRAMID_LAYERS,
+                                  h2o_config, omni_config, prefill_unit_queries)
 from workloads import generator as gen  # noqa: E402
 from workloads import get_config  # noqa: E402
 
 GAP = 1e-4
+MAX_ATTEMPTS = 64
 OUT = os.path.join(HERE, "attempts.json")
 
 
-def key(layer, step, unit):
-    return f"{layer},{step},{unit}"
+def key(*parts):
+    return ",".join(str(int(p)) for p in parts)
 
 
-def h2o_attempts(cfg, units):
-    """Sequential per unit: redraw the step's query until the eviction gap clears GAP."""
+def h2o_steps_from(cfg, layer, unit, k, v, pos, acc, t_steps, cur0):
+    """Attempt per step of one unit's H2O decode from the given slot state: the step's
+    query is redrawn until its eviction decision clears GAP.  Returns {step: attempt}."""
+    b, h = divmod(unit, cfg.n_kv_heads)
+    acc = np.asarray(acc, np.float64)
+    n, free = k.shape[0], k.shape[0] - 1
     found = {}
-    G = cfg.group
-    for unit in units:
-        b, h = divmod(unit, cfg.n_kv_heads)
-        k, v, pos, acc = h2o_unit_start(cfg, unit)
-        acc = acc.astype(np.float64)
-        n, free = k.shape[0], k.shape[0] - 1
-        for t in range(cfg.decode_steps):
-            _, kn, vn = h2o_step_inputs(cfg, t)
-            for attempt in range(64):
-                qg = gen.unit_query(cfg, 0, t, unit, attempt)
-                k2, v2 = k.copy(), v.copy()
-                gaps = []
-                res = oh2o.h2o_step(k2, v2, pos, acc, n, free, qg, kn[b, h], vn[b, h], cfg.context + t,
-                                    cfg.h2o_heavy, cfg.h2o_recent, cfg.softmax_scale, gaps)
-                if not gaps or gaps[0] >= GAP:
-                    break
-            else:
-                raise RuntimeError(f"no clear draw for h2o unit {unit} step {t}")
-            if attempt:
-                found[key(0, t, unit)] = attempt
-            k, v = k2, v2
-            _, _, pos, acc, n, free = res
-    return found
-
-
-def omni_attempts(cfg, units, steps):
-    """Per (unit, step): redraw the filter layers' queries until every boundary gap clears GAP."""
-    found = {}
-    G = cfg.group
-    cap = cfg.context + cfg.extra["omni_steps"]
-    last_filter = max(cfg.omni_filters)
-    for unit in units:
-        b, h = divmod(unit, cfg.n_kv_heads)
-        Ks, Vs = [], []
-        for layer in range(last_filter + 1):
-            k, v = gen.unit_kv(cfg, layer, unit, cap)
-            k[cfg.context:] = 0
-            v[cfg.context:] = 0
-            Ks.append(k)
-            Vs.append(v)
-        for s in range(max(steps) + 1):
-            for layer in range(last_filter + 1):
-                kn, vn = gen.decode_kv_new(cfg, layer, s)
-                Ks[layer][cfg.context + s], Vs[layer][cfg.context + s] = kn[b, h], vn[b, h]
-            if s not in steps:
-                continue
-            n = cfg.context + s + 1
-            for f in cfg.omni_filters:
-                for attempt in range(64):
-                    qg = gen.unit_query(cfg, f, s, unit, attempt)
-                    _, lse, logits = unit_attention(qg, Ks[f][:n], Vs[f][:n], cfg.softmax_scale)
-                    if boundary_gap(oomni.omnikv_scores(logits, lse, n), cfg.omni_top_k) >= GAP:
-                        break
-                else:
-                    raise RuntimeError(f"no clear draw for omnikv unit {unit} step {s} layer {f}")
-                if attempt:
-                    found[key(f, s, unit)] = attempt
-    return found
-
-
-def snap_attempts(cfg, units):
-    found = {}
-    L, W = cfg.context, cfg.snap_window
-    for unit in units:
-        k, _ = gen.unit_kv(cfg, 0, unit, L)
-        for attempt in range(64):
-            qo = gen.unit_obs_queries(cfg, 0, unit, attempt)
-            votes = osnap.unit_votes(qo, k, L, W, cfg.softmax_scale)
-            pooled = osnap.snapkv_pool(votes, cfg.snap_pool)
-            if cfg.snap_budget >= L or boundary_gap(pooled, cfg.snap_budget - W) >= GAP:
+    for t in range(t_steps):
+        kn, vn = gen.decode_kv_new(cfg, layer, t)
+        for attempt in range(MAX_ATTEMPTS):
+            qg = gen.unit_query(cfg, layer, t, unit, attempt)
+            k2, v2 = k.copy(), v.copy()
+            gaps = []
+            res = oh2o.h2o_step(k2, v2, pos, acc, n, free, qg, kn[b, h], vn[b, h], cur0 + t, cfg.h2o_heavy,
+                                cfg.h2o_recent, cfg.softmax_scale, gaps)
+            if not gaps or gaps[0] >= GAP:
                 break
         else:
-            raise RuntimeError(f"no clear draw for snapkv unit {unit}")
+            raise RuntimeError(f"no clear draw for h2o unit {unit} step {t}")
         if attempt:
-            found[key(0, 0, unit)] = attempt
-        print(f"snapkv unit {unit}: attempt {attempt}", flush=True)
+            found[t] = attempt
+        k, v = k2, v2
+        _, _, pos, acc, n, free = res
     return found
+
+
+def h2o_unit_job(unit):
+    """The 16K H2O workload, one unit, every decode step from the synthetic prefill state."""
+    cfg = h2o_config(True)
+    cap = cfg.h2o_heavy + cfg.h2o_recent + 1
+    k = gen.unit_rows(cfg, 0, gen.T_K, unit, cap, cfg.d_k)
+    v = gen.unit_rows(cfg, 0, gen.T_V, unit, cap, cfg.d_v)
+    pos, acc = gen.h2o_initial_state(cfg, 0, unit)
+    found = h2o_steps_from(cfg, 0, unit, k, v, pos, acc, cfg.decode_steps, cfg.context)
+    return {key(0, t, unit): a for t, a in found.items()}
+
+
+def omni_unit_job(unit):
+    """The 16K OmniKV workload, one unit: per checked step and filter layer, the query
+    draw whose top-k boundary clears GAP (a filter layer's view depends on its own
+    query and rows only)."""
+    cfg = omni_config(True)
+    b, h = divmod(unit, cfg.n_kv_heads)
+    cap = cfg.context + max(OMNI_STEPS) + 1
+    layers = {}
+    for f in cfg.omni_filters:
+        kk, vv = gen.unit_kv(cfg, f, unit, cfg.context)
+        K = np.zeros((cap, cfg.d_k), np.float32)
+        V = np.zeros((cap, cfg.d_v), np.float32)
+        K[:cfg.context], V[:cfg.context] = kk, vv
+        for s in range(cap - cfg.context):
+            kn, vn = gen.decode_kv_new(cfg, f, s)
+            K[cfg.context + s], V[cfg.context + s] = kn[b, h], vn[b, h]
+        layers[f] = (K, V)
+    found = {}
+    for s in OMNI_STEPS:
+        n = cfg.context + s + 1
+        for f in cfg.omni_filters:
+            K, V = layers[f]
+            for attempt in range(MAX_ATTEMPTS):
+                qg = gen.unit_query(cfg, f, s, unit, attempt)
+                _, lse, logits = unit_attention(qg, K[:n], V[:n], cfg.softmax_scale)
+                if boundary_gap(oomni.omnikv_scores(logits, lse, n), cfg.omni_top_k) >= GAP:
+                    break
+            else:
+                raise RuntimeError(f"no clear draw for omnikv unit {unit} step {s} layer {f}")
+            if attempt:
+                found[key(f, s, unit)] = attempt
+    return found
+
+
+def snap_unit_job(args):
+    """A SnapKV eviction, one unit: the window-query draw whose kept-set boundary clears GAP."""
+    cfg_id, kw, layer, unit, budget = args
+    cfg = get_config(cfg_id, **kw)
+    L, W = cfg.context, cfg.snap_window
+    k, _ = gen.unit_kv(cfg, layer, unit, L)
+    for attempt in range(MAX_ATTEMPTS):
+        qo = gen.unit_obs_queries(cfg, layer, unit, attempt)
+        votes = osnap.unit_votes(qo, k, L, W, cfg.softmax_scale)
+        pooled = osnap.snapkv_pool(votes, cfg.snap_pool)
+        if budget >= L or boundary_gap(pooled, budget - W) >= GAP:
+            return {key(layer, 0, unit): attempt} if attempt else {}
+    raise RuntimeError(f"no clear draw for snapkv unit {unit} layer {layer}")
+
+
+def prefill_unit_job(args):
+    """The prefill-end H2O state, one unit: the prompt-query draw whose heavy-hitter
+    boundary clears GAP."""
+    name, unit = args
+    cfg, L, heavy, recent = PREFILL_CASES[name]
+    tag = list(PREFILL_CASES).index(name)
+    K, _ = gen.cache_kv(cfg, PREFILL_KV_LAYER, L + 7, length=L + 7)
+    b, h = divmod(unit, cfg.n_kv_heads)
+    scale = 1.0 / np.sqrt(cfg.d_k)
+    if heavy + recent >= L:
+        return name, unit, 0
+    for attempt in range(MAX_ATTEMPTS):
+        q = prefill_unit_queries(cfg, tag, L, unit, attempt)
+        acc0 = oh2o.prefill_scores(q, K[b, h], L, scale)
+        if boundary_gap(acc0[:L - recent], heavy) >= GAP:
+            return name, unit, attempt
+    raise RuntimeError(f"no clear draw for prefill case {name} unit {unit}")
+
+
+def prefill_decode_unit_job(unit):
+    """The prefill-end state continued by H2O decode steps, one unit: first the prompt
+    draw, then each step's query draw, all from the oracle's own state."""
+    cfg = PREFILL_DECODE_CFG
+    L, heavy, recent = cfg.context, cfg.h2o_heavy, cfg.h2o_recent
+    cap = heavy + recent + 1
+    b, h = divmod(unit, cfg.n_kv_heads)
+    K, V = gen.cache_kv(cfg, PREFILL_DECODE_LAYER, L, length=L)
+    for attempt in range(MAX_ATTEMPTS):
+        q = prefill_unit_queries(cfg, 99, L, unit, attempt)
+        acc0 = oh2o.prefill_scores(q, K[b, h], L, cfg.softmax_scale)
+        if boundary_gap(acc0[:L - recent], heavy) >= GAP:
+            break
+    else:
+        raise RuntimeError(f"no clear prompt draw for unit {unit}")
+    kept, pos, acc = oh2o.prefill_state(acc0, L, heavy, recent, cap)
+    k = np.zeros((cap, cfg.d_k))
+    v = np.zeros((cap, cfg.d_v))
+    k[:len(kept)], v[:len(kept)] = K[b, h][kept], V[b, h][kept]
+    steps = h2o_steps_from(cfg, PREFILL_DECODE_LAYER, unit, k, v, pos, acc, cfg.decode_steps, L)
+    return unit, attempt, steps
 
 
 def main():
-    out = {}
-    out["h2o_16k"] = h2o_attempts(h2o_config(True), H2O_UNITS)
-    print("h2o", out["h2o_16k"], flush=True)
-    out["omnikv_16k"] = omni_attempts(omni_config(True), OMNI_UNITS, OMNI_STEPS)
-    print("omnikv", out["omnikv_16k"], flush=True)
-    out["snapkv_128k"] = snap_attempts(get_config(2), SNAP_UNITS)
-    out["snapkv_tiny"] = snap_attempts(get_config(0), range(get_config(0).units))
-    print("snapkv", out["snapkv_128k"], flush=True)
-    out["gap"] = GAP
+    from tests import oracle_pool
+    t0 = time.time()
+    pool = oracle_pool.pool()
+    out = {"gap": GAP}
+
+    cfg = h2o_config(True)
+    out["h2o_16k"] = {}
+    for d in pool.map(h2o_unit_job, range(cfg.units)):
+        out["h2o_16k"].update(d)
+    print(f"h2o_16k: {len(out['h2o_16k'])} redraws ({time.time() - t0:.0f}s)", flush=True)
+
+    out["omnikv_16k"] = {}
+    for d in pool.map(omni_unit_job, OMNI_UNITS):
+        out["omnikv_16k"].update(d)
+    print(f"omnikv_16k: {len(out['omnikv_16k'])} redraws ({time.time() - t0:.0f}s)", flush=True)
+
+    for name, cfg_id in (("snapkv_128k", 2), ("snapkv_tiny", 0)):
+        c = get_config(cfg_id)
+        out[name] = {}
+        for d in pool.map(snap_unit_job, [(cfg_id, {}, 0, u, c.snap_budget) for u in range(c.units)]):
+            out[name].update(d)
+        print(f"{name}: {len(out[name])} redraws ({time.time() - t0:.0f}s)", flush=True)
+
+    out["pyramid"] = {}
+    from oracle import variants as ov
+    for name, (c, avg, bmin) in PYRAMID_CASES.items():
+        budgets = ov.pyramid_budgets(PYRAMID_LAYERS, avg, bmin)
+        kw = {f: getattr(c, f) for f in ("dtype", "batch", "n_q_heads", "n_kv_heads", "d_k", "d_v", "context",
+                                         "snap_window", "snap_pool", "snap_budget", "snap_peaks", "snap_peak_spacing",
+                                         "snap_peak_levels")}
+        jobs = [(c.cfg_id, kw, layer, u, budgets[layer]) for layer in range(PYRAMID_LAYERS) for u in range(c.units)]
+        out["pyramid"][name] = {}
+        for d in pool.map(snap_unit_job, jobs):
+            out["pyramid"][name].update(d)
+        print(f"pyramid {name}: {len(out['pyramid'][name])} redraws ({time.time() - t0:.0f}s)", flush=True)
+
+    out["h2o_prefill"] = {name: {} for name in PREFILL_CASES}
+    jobs = [(name, u) for name, (c, _, _, _) in PREFILL_CASES.items() for u in range(c.units)]
+    for name, unit, attempt in pool.map(prefill_unit_job, jobs):
+        if attempt:
+            out["h2o_prefill"][name][str(unit)] = attempt
+    print(f"h2o_prefill: {out['h2o_prefill']} ({time.time() - t0:.0f}s)", flush=True)
+
+    dec = {"prompt": {}, "steps": {}}
+    for unit, attempt, steps in pool.map(prefill_decode_unit_job, range(PREFILL_DECODE_CFG.units)):
+        if attempt:
+            dec["prompt"][str(unit)] = attempt
+        for t, a in steps.items():
+            dec["steps"][key(t, unit)] = a
+    out["h2o_prefill_decode"] = dec
+    print(f"h2o_prefill_decode: {dec} ({time.time() - t0:.0f}s)", flush=True)
+
+    oracle_pool.shutdown()
     with open(OUT, "w") as f:
         json.dump(out, f, indent=1, sort_keys=True)
     print("wrote", OUT)
 
 
 if __name__ == "__main__":
-    main()
+    from tests.golden.make_attempts import main as _main   # jobs pickled by this module's name
+    _main()

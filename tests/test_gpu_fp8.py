@@ -216,3 +216,76 @@ def test_fp8_quest_decode(se):
         ref, ref_lse, _ = oatt.decode_attention(q, Kh, Vh, lens, cfg.softmax_scale, rv, rl, P)
         np.testing.assert_allclose(host(out), ref, atol=TOL["bf16"], rtol=0)
         np.testing.assert_allclose(host(lse), ref_lse, atol=TOL["bf16"], rtol=0)
+
+
+def test_fp8_quest_32k_all_units(se):
+    """The 32K Quest workload over FP8 rows at full size, through the bench's calls
+    (se_kv_quantize_fp8 once, then per step se_kv_append_fp8, se_quest_select,
+    se_sparse_decode_attn_fp8): at the first, a middle and the last of 64 steps, every
+    unit's codes, scale bytes and page metadata are compared by digest, its page scores
+    and view exactly, and its attention at the bf16 tolerance, with the oracle's."""
+    from tests import oracle_pool
+    from tests.parity_jobs import digest, fp8_quest_unit
+    cfg = get_config(1)
+    B, H, Hq, D, P, k, G = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.d_k, cfg.page_size, cfg.top_pages, cfg.group
+    checks = (0, 31, cfg.decode_steps - 1)
+    jobs = [oracle_pool.pool().submit(fp8_quest_unit, ((1, {}), u, checks)) for u in range(cfg.units)]
+    banner("fp8 quest 32K: building caches")
+    cap = cfg.context + cfg.decode_steps
+    c = se.cache(B, Hq, H, D, D, cap, "bf16")
+    K, V = gen.cache_kv(cfg, 0, cap)
+    kq = torch.full((B, H, cap, D), 0x55, dtype=torch.uint8, device="cuda")
+    vq = torch.full_like(kq, 0x55)
+    ks = torch.full((B, H, cap), 0x55, dtype=torch.uint8, device="cuda")
+    vs = torch.full_like(ks, 0x55)
+    ncp = (cap + P - 1) // P
+    kmin = torch.zeros((B, H, ncp, D), dtype=torch.bfloat16, device="cuda")
+    kmax = torch.zeros_like(kmin)
+    seq = torch.full((B,), cfg.context, dtype=torch.int32, device="cuda")
+    se.se_kv_quantize_fp8(c, dev(K, torch.bfloat16), dev(V, torch.bfloat16), seq, kq, vq, ks, vs, kmin, kmax, P)
+    del K, V
+    view = torch.zeros((B, H, k), dtype=torch.int32, device="cuda")
+    vlen = torch.zeros((B, H), dtype=torch.int32, device="cuda")
+    score = torch.zeros((B, H, ncp), device="cuda")
+    out, lse = zeros((B, Hq, D)), zeros((B, Hq))
+    ws_q = se.workspace(se.SE_OP_QUEST, c, P, k)
+    ws_a = se.workspace(se.SE_OP_ATTN, c, k * P, 0)
+    got = {}
+    for step in range(cfg.decode_steps):
+        kn, vn = gen.decode_kv_new(cfg, 0, step)
+        qd = dev(gen.decode_query(cfg, 0, step), torch.bfloat16)
+        se.se_kv_append_fp8(c, kq, vq, ks, vs, dev(kn, torch.bfloat16), dev(vn, torch.bfloat16), seq, kmin, kmax, P)
+        se.se_quest_select(c, qd, kmin, kmax, seq, P, k, view, vlen, score, ws_q)
+        se.se_sparse_decode_attn_fp8(c, qd, kq, vq, ks, vs, seq, view, vlen, k, P, cfg.softmax_scale, out, lse,
+                                     ws=ws_a)
+        if step in checks:
+            torch.cuda.synchronize()
+            L = cfg.context + step + 1
+            assert np.all(host(seq) == L)
+            npv = (L + P - 1) // P
+            hk, hv, hks, hvs = kq.cpu().numpy(), vq.cpu().numpy(), ks.cpu().numpy(), vs.cpu().numpy()
+            mn, mx = host(kmin), host(kmax)
+            got[step] = dict(
+                codes=[digest(np.stack([hk[u // H, u % H, :L], hv[u // H, u % H, :L]])) for u in range(cfg.units)],
+                scales=[digest(np.stack([hks[u // H, u % H, :L], hvs[u // H, u % H, :L]])) for u in range(cfg.units)],
+                meta=[digest(np.stack([mn[u // H, u % H, :npv], mx[u // H, u % H, :npv]])) for u in range(cfg.units)],
+                score=host(score), view=host(view), vlen=host(vlen), out=host(out), lse=host(lse))
+            banner(f"fp8 quest 32K: step {step} captured")
+    for u, job in enumerate(jobs):
+        ref = job.result()
+        b, h = divmod(u, H)
+        for step in checks:
+            g, r = got[step], ref[step]
+            L = cfg.context + step + 1
+            npv = (L + P - 1) // P
+            where = f"unit {u} step {step}"
+            assert g["codes"][u] == r["codes"], f"{where}: FP8 codes differ"
+            assert g["scales"][u] == r["scales"], f"{where}: scale bytes differ"
+            assert g["meta"][u] == r["meta"], f"{where}: page metadata differs"
+            np.testing.assert_array_equal(g["score"][b, h, :npv], r["score"].astype(np.float32), err_msg=where)
+            assert g["vlen"][b, h] == r["vlen"]
+            np.testing.assert_array_equal(g["view"][b, h], r["view"], err_msg=where)
+            np.testing.assert_allclose(g["out"][b, h * G:(h + 1) * G], r["out"], atol=TOL["bf16"], rtol=0,
+                                       err_msg=where)
+            np.testing.assert_allclose(g["lse"][b, h * G:(h + 1) * G], r["lse"], atol=TOL["bf16"], rtol=0,
+                                       err_msg=where)

@@ -71,8 +71,62 @@ def test_mla_small_all_units(se, fused):
     run_mla(se, cfg, range(cfg.batch), steps=3, fused=fused)
 
 
-def test_mla_128k_sampled_units(se):
-    """The bench's calls: the fused append + selection, then the attention."""
+def test_mla_128k_all_rows(se):
+    """The 128K MLA workload at full size through the bench's calls (the fused append +
+    selection, then the latent attention): 64 decode steps, every batch row compared
+    with the oracle at steps 0, 1, 31 and 63 (metadata by digest, page scores and views
+    exactly, output and lse at the bf16 tolerance)."""
+    from concurrent.futures import ThreadPoolExecutor
+    from tests import oracle_pool
+    from tests.parity_jobs import digest, mla_row
     cfg = get_config(4)
+    B, Hq, D, Dv, P, k = cfg.batch, cfg.n_q_heads, cfg.d_k, cfg.d_v, cfg.page_size, cfg.top_pages
+    checks = (0, 1, 31, cfg.decode_steps - 1)
+    jobs = [oracle_pool.pool().submit(mla_row, ((4, {}), b, checks)) for b in range(B)]
     banner("mla 128K: 32 x 131072 latent rows, top-64 pages")
-    run_mla(se, cfg, (0, 19, 31), fused=True)
+    cap = cfg.context + cfg.decode_steps
+    c = se.cache(B, Hq, 1, D, Dv, cap, "bf16", latent=True)
+    cd = torch.zeros((B, 1, cap, D), dtype=torch.bfloat16, device="cuda")
+    with ThreadPoolExecutor(oracle_pool.n_workers()) as ex:
+        for b, (rows, _) in enumerate(ex.map(lambda b: gen.unit_kv(cfg, 0, b, cfg.context), range(B))):
+            cd[b, 0, :cfg.context] = torch.from_numpy(rows).to("cuda", torch.bfloat16)
+    seq = torch.full((B,), cfg.context, dtype=torch.int32, device="cuda")
+    ncp = (cap + P - 1) // P
+    kmin = torch.zeros((B, 1, ncp, D), dtype=torch.bfloat16, device="cuda")
+    kmax = torch.zeros_like(kmin)
+    view = torch.zeros((B, 1, k), dtype=torch.int32, device="cuda")
+    vlen = torch.zeros((B, 1), dtype=torch.int32, device="cuda")
+    score = torch.zeros((B, 1, ncp), device="cuda")
+    out, lse = zeros((B, Hq, Dv)), zeros((B, Hq))
+    ws_qa = se.workspace(se.SE_OP_QUEST_APPEND, c, P, 0)
+    ws_a = se.workspace(se.SE_OP_ATTN, c, k * P, 0)
+    se.se_page_meta_update(c, cd, kmin, kmax, seq, P, 0)
+    got = {}
+    for s in range(cfg.decode_steps):
+        qd = dev(gen.decode_query(cfg, 0, s), torch.bfloat16)
+        kn, _ = gen.decode_kv_new(cfg, 0, s)
+        se.se_quest_append_select(c, qd, cd, None, dev(kn, torch.bfloat16), None, seq, kmin, kmax, P, k, view, vlen,
+                                  score, ws_qa)
+        se.se_sparse_decode_attn(c, qd, cd, None, seq, view, vlen, k, P, cfg.softmax_scale, out, lse, ws=ws_a)
+        if s in checks:
+            torch.cuda.synchronize()
+            L = cfg.context + s + 1
+            assert np.all(host(seq) == L)
+            npv = (L + P - 1) // P
+            mn, mx = host(kmin), host(kmax)
+            got[s] = dict(meta=[digest(np.stack([mn[b, 0, :npv], mx[b, 0, :npv]])) for b in range(B)],
+                          score=host(score), view=host(view), vlen=host(vlen), out=host(out), lse=host(lse))
+            banner(f"mla 128K: step {s} captured")
+    for b, job in enumerate(jobs):
+        r = job.result()
+        for s in checks:
+            g = got[s]
+            L = cfg.context + s + 1
+            npv = (L + P - 1) // P
+            where = f"row {b} step {s}"
+            assert g["meta"][b] == r[s]["meta"], f"{where}: page metadata differs"
+            np.testing.assert_array_equal(g["score"][b, 0, :npv], r[s]["score"].astype(np.float32), err_msg=where)
+            assert g["vlen"][b, 0] == r[s]["vlen"]
+            np.testing.assert_array_equal(g["view"][b, 0], r[s]["view"], err_msg=where)
+            np.testing.assert_allclose(g["out"][b], r[s]["out"], rtol=0, atol=TOL["bf16"], err_msg=where)
+            np.testing.assert_allclose(g["lse"][b], r[s]["lse"], rtol=0, atol=TOL["bf16"], err_msg=where)

@@ -11,7 +11,6 @@ from oracle import attention as oatt
 from oracle import boundary_gap
 from oracle import snapkv as osnap
 from tests.gpu_util import TOL, banner, dev, host, zeros
-from tests.sampled_units import SNAP_UNITS
 from workloads import generator as gen
 from workloads import get_config
 
@@ -123,7 +122,62 @@ def test_snapkv_budget_covers_prompt_and_window_only(se):
     assert np.all(kept[:, :, :cfg.snap_window] == np.arange(300 - cfg.snap_window, 300))
 
 
-def test_snapkv_128k_sampled_units(se):
+def test_snapkv_128k_all_units(se):
+    """The 128K SnapKV workload at full size through the bench's calls: the eviction of
+    every unit's 131072-token prompt to 8192 tokens (votes, kept set, compacted rows),
+    then 128 decode steps over the compacted cache (append and attention in one launch),
+    every unit compared with the oracle at the first, a middle and the last step."""
+    from tests import oracle_pool
+    from tests.parity_jobs import snap_unit
     cfg = get_config(2)
-    banner("snapkv 128K: 8 x 4 units, 131072 -> 8192, then a decode step")
-    run_snap(se, cfg, SNAP_UNITS, attempts_of("snapkv_128k"), decode=True)
+    B, H, Hq, D, G = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.d_k, cfg.group
+    L, W, pool, budget = cfg.context, cfg.snap_window, cfg.snap_pool, cfg.snap_budget
+    attempts = attempts_of("snapkv_128k")
+    checks = (0, 63, cfg.decode_steps - 1)
+    jobs = [oracle_pool.pool().submit(snap_unit, ((2, {}), u, attempts.get((0, 0, u), 0), budget, checks))
+            for u in range(cfg.units)]
+    banner("snapkv 128K: 8 x 4 units, 131072 -> 8192, then 128 decode steps")
+    K, V = gen.cache_kv(cfg, 0, L)
+    qo = gen.obs_queries(cfg, 0, attempts)
+    c = se.cache(B, Hq, H, D, D, L, "bf16")
+    cap_out = budget + cfg.decode_steps + 3
+    oc = se.cache(B, Hq, H, D, D, cap_out, "bf16")
+    k_out = torch.zeros((B, H, cap_out, D), dtype=torch.bfloat16, device="cuda")
+    v_out = torch.zeros_like(k_out)
+    kept = torch.zeros((B, H, budget), dtype=torch.int32, device="cuda")
+    votes = torch.zeros((B, H, L - W), device="cuda")
+    olen = torch.zeros((B,), dtype=torch.int32, device="cuda")
+    se.se_snapkv_score_compact(c, dev(qo, torch.bfloat16), dev(K, torch.bfloat16), dev(V, torch.bfloat16), L, W, pool,
+                               budget, cfg.softmax_scale, oc, k_out, v_out, kept, votes, olen,
+                               se.workspace(se.SE_OP_SNAPKV, c, L, W))
+    torch.cuda.synchronize()
+    assert np.all(host(olen) == budget)
+    g_kept, g_votes, g_k, g_v = host(kept), host(votes), host(k_out), host(v_out)
+    out, lse = zeros((B, Hq, D)), zeros((B, Hq))
+    ws = se.workspace(se.SE_OP_APPEND_ATTN, oc, cap_out, 0)
+    dec = {}
+    for s in range(cfg.decode_steps):
+        q = gen.decode_query(cfg, 0, s)
+        kn, vn = gen.decode_kv_new(cfg, 0, s)
+        se.se_kv_append_decode_attn(oc, dev(q, torch.bfloat16), k_out, v_out, dev(kn, torch.bfloat16),
+                                    dev(vn, torch.bfloat16), None, olen, None, None, 0, 1, cfg.softmax_scale, out, lse,
+                                    ws=ws)
+        if s in checks:
+            torch.cuda.synchronize()
+            assert np.all(host(olen) == budget + s + 1)
+            dec[s] = (host(out), host(lse))
+    banner("snapkv 128K: comparing with the oracle")
+    for u, job in enumerate(jobs):
+        r = job.result()
+        b, h = divmod(u, H)
+        assert r["gap"] >= GAP, f"unit {u}: generated input has a near-tie ({r['gap']:.2e})"
+        np.testing.assert_allclose(g_votes[b, h], r["votes"], rtol=1e-4, atol=1e-30, err_msg=f"unit {u} votes")
+        np.testing.assert_array_equal(g_kept[b, h], r["kept"], err_msg=f"unit {u} kept")
+        np.testing.assert_array_equal(g_k[b, h, :budget], K[b, h][r["kept"]], err_msg=f"unit {u} K rows")
+        np.testing.assert_array_equal(g_v[b, h, :budget], V[b, h][r["kept"]], err_msg=f"unit {u} V rows")
+        for s in checks:
+            ro, rl = r["decode"][s]
+            np.testing.assert_allclose(dec[s][0][b, h * G:(h + 1) * G], ro, atol=TOL["bf16"], rtol=0,
+                                       err_msg=f"unit {u} step {s} out")
+            np.testing.assert_allclose(dec[s][1][b, h * G:(h + 1) * G], rl, atol=TOL["bf16"], rtol=0,
+                                       err_msg=f"unit {u} step {s} lse")
