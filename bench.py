@@ -62,7 +62,6 @@ def parse():
     ap.add_argument("--attn-reps", type=int, default=20, help="graph replays for the attention-call timing")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--splits", type=int, default=0, help="split-K factor of the attention (0 = library choice)")
     ap.add_argument("--workloads", default=",".join(ALL_WORKLOADS),
                     help="comma-separated subset of " + ",".join(ALL_WORKLOADS))
@@ -192,12 +191,6 @@ def run_quest(se, torch, args):
     lse = torch.empty((B, Hq), device="cuda")
     torch.cuda.synchronize()
     log(f"quest_32k: caches ready in {time.time() - t0:.1f}s")
-    # a plain 256 MiB device copy of known size: counter-based traffic figures are
-    # scaled by what the counters report for it
-    calib = torch.empty(128 << 20, dtype=torch.bfloat16, device="cuda")
-    calib_copy = calib.clone()
-    del calib, calib_copy
-    torch.cuda.synchronize()
 
     def append_select(L):
         se.se_quest_append_select(c, q, L.k, L.v, kn, vn, L.seq, L.kmin, L.kmax, P, k, L.view, L.vlen, None, ws_q)
@@ -687,10 +680,22 @@ def main():
     if bad:
         print(f"unknown workloads {bad}; choose from {ALL_WORKLOADS}", file=sys.stderr)
         sys.exit(2)
+    if "quest_32k" in wanted and not args.no_cpu_baseline:
+        # the CPU baseline's process pool forks from a forkserver started before the GPU is used
+        import multiprocessing as mp
+        import multiprocessing.forkserver as mpfs
+        mp.get_context("forkserver").set_forkserver_preload(["numpy"])
+        mpfs.ensure_running()
     import torch
     import sparse_attention_kv_quest_amd as se
 
     se.load()
+    # the run's first device copy: a plain 256 MiB clone of known size, by which the
+    # rocprofv3 FETCH_SIZE / WRITE_SIZE counts of the kernels are scaled to bytes
+    calib = torch.zeros(128 << 20, dtype=torch.bfloat16, device="cuda")
+    calib_copy = calib.clone()
+    torch.cuda.synchronize()
+    del calib, calib_copy
     result = {
         "metric": "sparse decode tokens/s per layer-step (Quest, 32K ctx) + achieved HBM GB/s of the attention kernel",
         "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": 0, "warmup": args.warmup, "ms_per_step": None,
@@ -720,40 +725,197 @@ def main():
     if extra:
         result["workloads"] = extra
     if "quest_32k" in wanted and not args.no_cpu_baseline:
-        from workloads import get_config
-        result["cpu_baseline"] = cpu_baseline(get_config(1), args.cpu_seconds)
+        log("cpu baseline: the oracle over the host cores")
+        result["cpu_baseline"] = cpu_baseline()
+        log(f"cpu baseline: {json.dumps(result['cpu_baseline'])}")
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(cfg, budget_s):
-    """The CPU oracle, single-threaded, on a bounded sample of the headline decode
-    step: per unit, page metadata, the Quest page view and the attention over it."""
+# ---------------------------------------------------------------- CPU oracle baseline
+#
+# The oracle as it stands (plain single-threaded NumPy per unit), run over the
+# host's cores in a process pool: every job rebuilds one unit's inputs from the
+# seeded generator (untimed), then times the same per-step work the GPU path
+# does -- for Quest / MLA the appended row, the last page's min / max (the other
+# pages' metadata carried over), page scores, top-k and attention; for H2O one
+# full step; for OmniKV one 48-layer sweep -- and returns the timed seconds.
+
+CPU_MAX_WORKERS = 16
+
+
+def _cpu_init():
     from threadpoolctl import threadpool_limits
-    import oracle
+    threadpool_limits(1)
+
+
+def _cpu_quest_unit(job):
+    """Quest decode steps of one unit (GQA or latent): seconds spent in the steps."""
+    cfg_id, unit, steps = job
+    from oracle import attention as oatt
     from oracle import quest as oquest
     from workloads import generator as gen
+    from workloads import get_config
+    cfg = get_config(cfg_id)
+    P, k, L = cfg.page_size, cfg.top_pages, cfg.context
+    K0, V0 = gen.unit_kv(cfg, 0, unit, L)
+    K = np.zeros((L + steps, cfg.d_k), np.float32)
+    K[:L] = K0
+    V = None
+    if V0 is not None:
+        V = np.zeros((L + steps, cfg.d_v), np.float32)
+        V[:L] = V0
+    kmin, kmax = oquest.page_meta(K[None, None], [L], P)
+    b, h = divmod(unit, cfg.n_kv_heads)
+    spent = 0.0
+    for s in range(steps):
+        qg = gen.unit_query(cfg, 0, s, unit)[None]
+        kn, vn = gen.decode_kv_new(cfg, 0, s)
+        t0 = time.perf_counter()
+        K[L] = kn[b, h]
+        if V is not None:
+            V[L] = vn[b, h]
+        L += 1
+        p0 = (L - 1) // P * P
+        mn, mx = oquest.page_meta(K[None, None, p0:L], [L - p0], P)
+        kmin[0, 0, p0 // P], kmax[0, 0, p0 // P] = mn[0, 0, 0], mx[0, 0, 0]
+        view, vlen, _ = oquest.quest_select(qg, kmin, kmax, [L], P, k)
+        oatt.decode_attention(qg, K[None, None], None if V is None else V[None, None], [L], cfg.softmax_scale, view,
+                              vlen, P, latent_dv=cfg.d_v if V is None else None)
+        spent += time.perf_counter() - t0
+    return spent
 
-    P, k, G = cfg.page_size, cfg.top_pages, cfg.group
-    L = cfg.context + 1
-    q = gen.decode_query(cfg, 0, 0)
-    done, spent = 0, 0.0
-    with threadpool_limits(1):
-        for unit in range(cfg.units):
-            Ku, Vu = gen.unit_kv(cfg, 0, unit, L)
-            b, h = divmod(unit, cfg.n_kv_heads)
-            qu = q[b:b + 1, h * G:(h + 1) * G]
-            t0 = time.perf_counter()
-            kmin, kmax = oquest.page_meta(Ku[None, None], [L], P)
-            view, vlen, _ = oquest.quest_select(qu, kmin, kmax, [L], P, k)
-            oracle.decode_attention(qu, Ku[None, None], Vu[None, None], [L], cfg.softmax_scale, view, vlen, P)
-            spent += time.perf_counter() - t0
-            done += 1
-            if spent >= budget_s and done >= 4:
-                break
-    step_s = spent / done * cfg.units
-    return {"value": round(cfg.batch / step_s, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {cfg.units} KV-head units of one quest_32k decode step "
-                      f"(page metadata + page view + attention), scaled to the full step"}
+
+def _cpu_snap_unit(job):
+    """SnapKV on one unit: (seconds of the eviction -- votes, pool, keep, compaction --,
+    seconds of the decode steps over the compacted cache)."""
+    unit, steps = job
+    import oracle
+    from oracle import snapkv as osnap
+    from workloads import generator as gen
+    from workloads import get_config
+    cfg = get_config(2)
+    L, W = cfg.context, cfg.snap_window
+    K, V = gen.unit_kv(cfg, 0, unit, L)
+    qo = gen.unit_obs_queries(cfg, 0, unit)
+    t0 = time.perf_counter()
+    pooled = osnap.snapkv_pool(osnap.unit_votes(qo, K, L, W, cfg.softmax_scale), cfg.snap_pool)
+    kept = osnap.snapkv_keep(pooled, L, W, cfg.snap_budget)
+    Kc, Vc = osnap.snapkv_compact(K, kept), osnap.snapkv_compact(V, kept)
+    t_compact = time.perf_counter() - t0
+    b, h = divmod(unit, cfg.n_kv_heads)
+    t_dec = 0.0
+    for s in range(steps):
+        qg = gen.unit_query(cfg, 0, s, unit)
+        kn, vn = gen.decode_kv_new(cfg, 0, s)
+        t0 = time.perf_counter()
+        Kc, Vc = np.concatenate([Kc, kn[b, h][None]]), np.concatenate([Vc, vn[b, h][None]])
+        oracle.unit_attention(qg, Kc, Vc, cfg.softmax_scale)
+        t_dec += time.perf_counter() - t0
+    return t_compact, t_dec
+
+
+def _cpu_h2o_unit(job):
+    """H2O decode steps of one unit from its post-prefill state."""
+    unit, steps = job
+    from oracle import h2o as oh2o
+    from workloads import generator as gen
+    from workloads import get_config
+    cfg = get_config(3)
+    cap = cfg.h2o_heavy + cfg.h2o_recent + 1
+    k = gen.unit_rows(cfg, 0, gen.T_K, unit, cap, cfg.d_k)
+    v = gen.unit_rows(cfg, 0, gen.T_V, unit, cap, cfg.d_v)
+    pos, acc = gen.h2o_initial_state(cfg, 0, unit)
+    acc = acc.astype(np.float64)
+    n, free = cap, cap - 1
+    b, h = divmod(unit, cfg.n_kv_heads)
+    spent = 0.0
+    for t in range(steps):
+        qg = gen.unit_query(cfg, 0, t, unit)
+        kn, vn = gen.decode_kv_new(cfg, 0, t)
+        t0 = time.perf_counter()
+        _, _, pos, acc, n, free = oh2o.h2o_step(k, v, pos, acc, n, free, qg, kn[b, h], vn[b, h], cfg.context + t,
+                                                cfg.h2o_heavy, cfg.h2o_recent, cfg.softmax_scale)
+        spent += time.perf_counter() - t0
+    return spent
+
+
+def _cpu_omni_unit(job):
+    """OmniKV 48-layer sweeps of one unit (appends, dense / filter / reused-view layers)."""
+    unit, steps = job
+    from oracle import omnikv as oomni
+    from workloads import generator as gen
+    from workloads import get_config
+    cfg = get_config(3)
+    b, h = divmod(unit, cfg.n_kv_heads)
+    cap = cfg.context + steps
+    Ks, Vs = [], []
+    for layer in range(cfg.omni_layers):
+        kk, vv = gen.unit_kv(cfg, layer, unit, cfg.context)
+        Kl, Vl = np.zeros((cap, cfg.d_k), np.float32), np.zeros((cap, cfg.d_v), np.float32)
+        Kl[:cfg.context], Vl[:cfg.context] = kk, vv
+        Ks.append(Kl)
+        Vs.append(Vl)
+    spent = 0.0
+    for s in range(steps):
+        qs = [gen.unit_query(cfg, layer, s, unit) for layer in range(cfg.omni_layers)]
+        new = [gen.decode_kv_new(cfg, layer, s) for layer in range(cfg.omni_layers)]
+        t0 = time.perf_counter()
+        for layer in range(cfg.omni_layers):
+            Ks[layer][cfg.context + s], Vs[layer][cfg.context + s] = new[layer][0][b, h], new[layer][1][b, h]
+        oomni.unit_sweep(qs, Ks, Vs, cfg.context + s + 1, cfg.omni_filters, cfg.omni_top_k, cfg.softmax_scale)
+        spent += time.perf_counter() - t0
+    return spent
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(steps=2, omni_units=32):
+    """Decode tokens/s of the CPU oracle on every workload, from the seeded inputs of the
+    same shapes: per workload, the timed seconds of every unit's steps are summed and
+    divided by the worker count (units are independent, one per worker at a time)."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    from workloads import get_config
+
+    n = max(1, min(CPU_MAX_WORKERS, len(os.sched_getaffinity(0))))
+    ex = cf.ProcessPoolExecutor(n, mp_context=mp.get_context("forkserver"), initializer=_cpu_init)
+    t_wall = time.time()
+    q1, q4, c2, c3 = get_config(1), get_config(4), get_config(2), get_config(3)
+    quest = list(ex.map(_cpu_quest_unit, [(1, u, steps) for u in range(q1.units)]))
+    mla = list(ex.map(_cpu_quest_unit, [(4, u, steps) for u in range(q4.units)]))
+    snap = list(ex.map(_cpu_snap_unit, [(u, steps) for u in range(c2.units)]))
+    h2o = list(ex.map(_cpu_h2o_unit, [(u, steps) for u in range(c3.units)]))
+    omni_sample = list(range(0, c3.units, c3.units // omni_units))[:omni_units]
+    omni = list(ex.map(_cpu_omni_unit, [(u, steps) for u in omni_sample]))
+    ex.shutdown()
+
+    def tok_s(batch, secs, scale=1.0):
+        step_wall = sum(secs) * scale / steps / n
+        return round(batch / step_wall, 3)
+
+    per = {
+        "quest_32k": {"tokens_per_s": tok_s(q1.batch, quest)},
+        "mla_128k": {"tokens_per_s": tok_s(q4.batch, mla)},
+        "snapkv_128k": {"compaction_ms_per_call": round(sum(t for t, _ in snap) / n * 1e3, 1),
+                        "decode_tokens_per_s": tok_s(c2.batch, [d for _, d in snap])},
+        "h2o_16k": {"tokens_per_s": tok_s(c3.batch, h2o)},
+        "omnikv_16k": {"tokens_per_s_per_48_layer_step": tok_s(c3.batch, omni, c3.units / len(omni_sample)),
+                       "units_sampled": len(omni_sample)},
+    }
+    return {"value": per["quest_32k"]["tokens_per_s"], "unit": "tokens/s", "cores": n, "kind": "oracle",
+            "sample": f"{steps} decode steps of every unit of quest_32k (the headline), with the same work per step "
+                      f"as the GPU path (append, last-page min/max, page scores, top-k, attention); "
+                      f"per-unit step seconds summed over units and divided by the {n} worker processes",
+            "cpu_model": cpu_model(), "threads_per_worker": 1, "workloads": per,
+            "wall_s": round(time.time() - t_wall, 1)}
 
 
 if __name__ == "__main__":

@@ -26,9 +26,10 @@ from oracle import h2o as oh2o  # noqa: E402
 from oracle import omnikv as oomni  # noqa: E402
 from oracle import snapkv as osnap  # noqa: E402
 from oracle.attention import unit_attention  # noqa: E402
-from tests.h2o_omni_cases import (OMNI_STEPS, OMNI_UNITS, PREFILL_CASES, PREFILL_DECODE_CFG,  # noqa: E402
-                                  PREFILL_DECODE_LAYER, PREFILL_KV_LAYER, PYRAMID_CASES, PYRAMID_LAYERS,
-                                  h2o_config, omni_config, prefill_unit_queries)
+from tests.h2o_omni_cases import (CHAIN_BUDGET2, CHAIN_CASES, CHAIN_TAGS, CHAIN_TURN2, OMNI_STEPS,  # noqa: E402
+                                  OMNI_UNITS, PREFILL_CASES, PREFILL_DECODE_CFG, PREFILL_DECODE_LAYER,
+                                  PREFILL_KV_LAYER, PYRAMID_CASES, PYRAMID_LAYERS, h2o_config, omni_config,
+                                  prefill_unit_queries)
 from workloads import generator as gen  # noqa: E402
 from workloads import get_config  # noqa: E402
 
@@ -169,6 +170,33 @@ def prefill_decode_unit_job(unit):
     return unit, attempt, steps
 
 
+def chain_unit_job(args):
+    """Chain Cache over two turns, one unit: the window-query draw of the turn-1
+    compaction, then (over the oracle's chained rows: the kept prompt rows and the
+    turn-2 rows) the draw of the turn-2 compaction, each clearing GAP."""
+    name, unit = args
+    cfg = CHAIN_CASES[name]
+    b, h = divmod(unit, cfg.n_kv_heads)
+    L1, W = cfg.context, cfg.snap_window
+    Klog, _ = gen.cache_kv(cfg, CHAIN_TAGS[0], L1 + CHAIN_TURN2, length=L1 + CHAIN_TURN2)
+    found = {}
+
+    def search(tag, rows, n, budget):
+        for attempt in range(MAX_ATTEMPTS):
+            qo = gen.unit_obs_queries(cfg, tag, unit, attempt)
+            pooled = osnap.snapkv_pool(osnap.unit_votes(qo, rows, n, W, cfg.softmax_scale), cfg.snap_pool)
+            if boundary_gap(pooled, budget - W) >= GAP:
+                if attempt:
+                    found[key(tag, 0, unit)] = attempt
+                return osnap.snapkv_keep(pooled, n, W, budget)
+        raise RuntimeError(f"no clear draw for chain {name} unit {unit} tag {tag}")
+
+    kept = search(CHAIN_TAGS[0], Klog[b, h], L1, cfg.snap_budget)
+    pos = np.concatenate([kept, np.arange(L1, L1 + CHAIN_TURN2)])
+    search(CHAIN_TAGS[1], Klog[b, h][pos], len(pos), CHAIN_BUDGET2)
+    return name, found
+
+
 def main():
     from tests import oracle_pool
     t0 = time.time()
@@ -221,6 +249,11 @@ def main():
             dec["steps"][key(t, unit)] = a
     out["h2o_prefill_decode"] = dec
     print(f"h2o_prefill_decode: {dec} ({time.time() - t0:.0f}s)", flush=True)
+
+    out["chain"] = {name: {} for name in CHAIN_CASES}
+    for name, found in pool.map(chain_unit_job, [(n, u) for n, c in CHAIN_CASES.items() for u in range(c.units)]):
+        out["chain"][name].update(found)
+    print(f"chain: {out['chain']} ({time.time() - t0:.0f}s)", flush=True)
 
     oracle_pool.shutdown()
     with open(OUT, "w") as f:

@@ -100,3 +100,12 @@ PYRAMID_CASES = {
                             snap_peak_spacing=40, snap_peak_levels=10), 400, 200),
 }
 PYRAMID_LAYERS = 4
+
+
+# ------------------------------------------------------------------ Chain Cache over two turns
+
+# dtype -> config: SnapKV at the end of turn 1 (window queries of layer tag 31), turn 2
+# appends CHAIN_TURN2 tokens, a second SnapKV (layer tag 32) keeps CHAIN_BUDGET2 rows
+CHAIN_CASES = {"f32": get_config(0),
+               "bf16": get_config(0, dtype="bf16", batch=2, n_q_heads=16, n_kv_heads=2, d_k=128, d_v=128)}
+CHAIN_TURN2, CHAIN_BUDGET2, CHAIN_TAGS = 40, 64, (31, 32)

@@ -1,16 +1,14 @@
 """GPU checks of the Quest scoring of 576-column latent rows at grid shapes that
 select each groups-per-wave variant of its kernel (1 to 4 groups of 16 pages per
-wave, two blocks per CU): page bounds of sampled units against the CPU oracle's
-bounds over the stored metadata, the views against the oracle's top-k of the
-kernel's own scores (the decision taken in the kernel's precision), and the fused
-decode call (append, fold into the last page, score, select) against the separate
-calls, bit for bit, for every unit."""
+wave, two blocks per CU): on grid-valued rows and queries (every bound exact in
+fp32), page bounds and views of sampled units against the CPU oracle's, bit for
+bit, and the fused decode call (append, fold into the last page, score, select)
+against the separate calls, bit for bit, for every unit."""
 import numpy as np
 import pytest
 import torch
 
 from oracle import quest as oquest
-from oracle.selection import top_k_ascending
 from tests.gpu_util import banner
 
 pytestmark = pytest.mark.gpu
@@ -35,10 +33,17 @@ def same_bits(x, y):
     return torch.equal(x.contiguous().view(dt), y.contiguous().view(dt))
 
 
+def grid_randn(shape, g):
+    """round(32 x) / 32 clipped to +-255/32, x ~ N(0, 1), drawn on the device: exact in
+    bf16, and every sum of products of two such values below 2^14 is exact in fp32."""
+    x = torch.randn(shape, generator=g, device="cuda")
+    return x.mul_(32.0).round_().clamp_(-255.0, 255.0).div_(32.0).add_(0.0).to(torch.bfloat16)
+
+
 def make(se, units, cap, lens, seed):
     g = torch.Generator(device="cuda").manual_seed(seed)
     c = se.cache(units, HQ, 1, D, DV, cap, "bf16", latent=True)
-    k = torch.randn((units, 1, cap, D), generator=g, device="cuda").to(torch.bfloat16)
+    k = grid_randn((units, 1, cap, D), g)
     ncp = -(-cap // P)
     kmin = torch.zeros((units, 1, ncp, D), dtype=torch.bfloat16, device="cuda")
     kmax = torch.zeros_like(kmin)
@@ -57,8 +62,8 @@ def test_wide_scoring_grid_variants(se, name):
     lens = rng.integers(1, cap - 1, size=units)
     lens[:5] = [cap - 1, 1, P, 5 * P, cap]
     g = torch.Generator(device="cuda").manual_seed(7)
-    q = torch.randn((units, HQ, D), generator=g, device="cuda").to(torch.bfloat16)
-    kn = torch.randn((units, 1, D), generator=g, device="cuda").to(torch.bfloat16)
+    q = grid_randn((units, HQ, D), g)
+    kn = grid_randn((units, 1, D), g)
     sample = sorted({0, 1, 2, 3, 4, units // 2, units - 1, int(rng.integers(units))})
 
     # the selection alone
@@ -69,16 +74,18 @@ def test_wide_scoring_grid_variants(se, name):
     se.se_quest_select(c, q, kmin, kmax, seq, P, TOP, view, vlen, score, se.workspace(se.SE_OP_QUEST, c, P, TOP))
     torch.cuda.synchronize()
     qh = q.float().cpu().numpy()[sample]
-    mn = kmin.float().cpu().numpy()[sample]
-    mx = kmax.float().cpu().numpy()[sample]
-    _, S = oquest.quest_bounds(qh, mn, mx, lens[sample], P)
+    kh = k.float().cpu().numpy()[sample]
+    mn, mx = oquest.page_meta(kh, lens[sample], P)
+    np.testing.assert_array_equal(kmin.float().cpu().numpy()[sample][:, :, :mn.shape[2]][~np.isnan(mn)],
+                                  mn[~np.isnan(mn)])
+    assert float((np.abs(qh).sum(-1).max()) * np.abs(kh).max()) < 2 ** 14     # the exactness precondition
+    rview, rlen, S = oquest.quest_select(qh, mn, mx, lens[sample], P, TOP)
     got = score.cpu().numpy()[sample]
     for i, u in enumerate(sample):
         npv = -(-int(lens[u]) // P)
-        np.testing.assert_allclose(got[i, 0, :npv], S[i, 0, :npv], rtol=1e-5, atol=1e-3, err_msg=f"unit {u}")
-        ref = top_k_ascending(got[i, 0, :npv], TOP)
-        np.testing.assert_array_equal(view.cpu().numpy()[u, 0, :ref.size], ref, err_msg=f"view unit {u}")
-        assert vlen.cpu().numpy()[u, 0] == ref.size
+        np.testing.assert_array_equal(got[i, 0, :npv], S[i, 0, :npv].astype(np.float32), err_msg=f"unit {u}")
+        np.testing.assert_array_equal(view.cpu().numpy()[u, 0], rview[i, 0], err_msg=f"view unit {u}")
+        assert vlen.cpu().numpy()[u, 0] == rlen[i, 0]
     del k, kmin, kmax, score
 
     # the fused decode call against the separate calls, every unit
