@@ -2,9 +2,11 @@
 
 Headline: the Quest path on the 32K workload (16 x 32q/4kv x d128, pages of 16,
 top-128 pages).  A step is one decode token for every batch row through one
-layer: one launch appends the new K/V row, rebuilds the last page's min/max,
-scores every page and selects the top pages (se_quest_append_select), then
-split-K decode attention runs over the selected pages.  Steps rotate over
+layer, one se_quest_decode_step call: a first launch appends the new K/V row,
+folds it into the last page's min/max and scores every page; a second launch
+selects each unit's top pages and runs split-K decode attention over them.
+The roofline is that of the sparse decode attention kernel, timed alone over
+the step's views (se_sparse_decode_attn).  Steps rotate over
 --layers distinct layer caches so that each step's working set has left the
 256 MB Infinity Cache before it is read again.  Inputs are resident in HBM
 before timing starts; steps are replayed from HIP graphs.
@@ -171,7 +173,7 @@ def run_quest(se, torch, args):
     B, H, Hq, D, P, k = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.d_k, cfg.page_size, cfg.top_pages
     nL = args.layers
     # appends per layer: warm-up and timed steps, the append + select stage timing, slack
-    steps_per_layer = -(-(args.warmup + args.steps) // nL) + 2 * args.attn_reps + 4
+    steps_per_layer = -(-(args.warmup + args.steps) // nL) + 3 * args.attn_reps + 4
     cap = cfg.context + steps_per_layer
     c = se.cache(B, Hq, H, D, D, cap, "bf16")
     log(f"quest_32k: B={B} Hq={Hq} Hkv={H} D={D} ctx={cfg.context} P={P} top={k} cap={cap} layers={nL}")
@@ -188,35 +190,47 @@ def run_quest(se, torch, args):
     del K0, V0
     ws_q = se.workspace(se.SE_OP_QUEST_APPEND, c, P, 0)
     ws_a = se.workspace(se.SE_OP_ATTN, c, k * P, args.splits)
+    ws_s = se.workspace(se.SE_OP_QUEST_STEP, c, P, k)
     lse = torch.empty((B, Hq), device="cuda")
     torch.cuda.synchronize()
     log(f"quest_32k: caches ready in {time.time() - t0:.1f}s")
 
+    def step(L, view=False):
+        """One decode step: se_quest_decode_step (launch 1: the new rows, the appended
+        page's min / max, every page's score; launch 2: per unit the top pages and the
+        attention over them).  view: also write the step's view (for the timings below)."""
+        se.se_quest_decode_step(c, q, L.k, L.v, kn, vn, L.seq, L.kmin, L.kmax, P, k, cfg.softmax_scale, L.out, lse,
+                                L.view if view else None, L.vlen if view else None, None, ws_s)
+
     def append_select(L):
         se.se_quest_append_select(c, q, L.k, L.v, kn, vn, L.seq, L.kmin, L.kmax, P, k, L.view, L.vlen, None, ws_q)
-
-    def step(L):
-        append_select(L)
-        se.se_sparse_decode_attn(c, q, L.k, L.v, L.seq, L.view, L.vlen, k, P, cfg.softmax_scale, L.out, lse,
-                                 num_splits=args.splits, ws=ws_a)
 
     def attn_only(L):
         se.se_sparse_decode_attn(c, q, L.k, L.v, L.seq, L.view, L.vlen, k, P, cfg.softmax_scale, L.out, lse,
                                  num_splits=args.splits, ws=ws_a)
 
+    def two_calls(L):   # the same step as the separate calls: append + selection, then attention
+        append_select(L)
+        attn_only(L)
+
     use_graph = not args.no_graph
     for i in range(args.warmup):
-        step(layers[i % nL])
+        step(layers[i % nL], view=True)
     torch.cuda.synchronize()
     # one replay = exactly --steps decode steps, rotating over the layer caches
     n_steps = max(1, args.steps)
     t_step = Timer(torch, lambda: [step(layers[i % nL]) for i in range(n_steps)], use_graph)
-    t_attn = Timer(torch, lambda: [attn_only(L) for L in layers], use_graph)
     ms_step = t_step.ms_per_replay(1) / n_steps
+    # the sparse decode attention alone over each layer's current view
+    for L in layers:
+        step(L, view=True)
+    t_attn = Timer(torch, lambda: [attn_only(L) for L in layers], use_graph)
     us_attn = t_attn.ms_per_replay(args.attn_reps) * 1e3 / nL
-    # the step's first stage replayed alone over the same layers (it appends a row per replay)
+    # for reference: the append + selection call alone, and the step as the two separate calls
     t_sel = Timer(torch, lambda: [append_select(L) for L in layers], use_graph)
     us_sel = t_sel.ms_per_replay(args.attn_reps) * 1e3 / nL
+    t_two = Timer(torch, lambda: [two_calls(L) for L in layers], use_graph)
+    us_two = t_two.ms_per_replay(max(1, args.attn_reps // 2)) * 1e3 / nL
 
     # algorithmic bytes of one attention call: K and V rows of the selected tokens,
     # plus q, the views and the fp32 outputs
@@ -235,7 +249,8 @@ def run_quest(se, torch, args):
     free(torch)
     return cfg, {
         "tokens_per_s": B / (ms_step * 1e-3), "ms_per_step": ms_step, "steps": n_steps,
-        "stages_us": {"append_select": round(us_sel, 3), "attention": round(us_attn, 3)},
+        "stages_us": {"step": round(ms_step * 1e3, 3), "attention": round(us_attn, 3),
+                      "append_select": round(us_sel, 3), "two_call_step": round(us_two, 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "attn_mfma_kernel (se_sparse_decode_attn: split-K, splits merged in-kernel)", "us_per_launch": round(us_attn, 3),

@@ -91,7 +91,8 @@ typedef enum {
   SE_OP_OMNIKV = 4,     /* a0 = logit_cap, a1 = top_k */
   SE_OP_QUEST_APPEND = 5, /* a0 = page_size (a1 unused) */
   SE_OP_H2O_PREFILL = 6,  /* a0 = prompt_len, a1 = recent_window */
-  SE_OP_APPEND_ATTN = 7   /* a0 = view_cap * granularity (slots per unit), a1 = num_splits (0 = auto) */
+  SE_OP_APPEND_ATTN = 7,  /* a0 = view_cap * granularity (slots per unit), a1 = num_splits (0 = auto) */
+  SE_OP_QUEST_STEP = 8    /* a0 = page_size, a1 = top_pages */
 } se_op;
 
 /* Append one decode token's K/V row to every unit (helper of the hooks: the
@@ -163,6 +164,31 @@ se_status se_quest_append_select(const se_cache* c, const void* q, void* k, void
                                  const void* v_new, int32_t* seq_len, void* kmin, void* kmax, int32_t page_size,
                                  int32_t top_pages, int32_t* view_idx, int32_t* view_len, float* page_score,
                                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* A whole Quest decode step (tokendh.com explainer, section "历史太长,会撑爆什么":
+ * pages chosen per query from the summary index; section "把边界划在'生命周期'上":
+ * attention over the chosen view): the same results, bit for bit, as
+ *   se_quest_append_select(c, q, k, v, k_new, v_new, seq_len, kmin, kmax,
+ *                          page_size, top_pages, view_idx, view_len, page_score, ...)
+ * followed by
+ *   se_sparse_decode_attn(c, q, k, v, seq_len, view_idx, view_len, top_pages,
+ *                         page_size, scale, out, lse, NULL, 0, 0, ...)
+ * (K / V rows, metadata, seq_len, out, lse, and the view and scores where
+ * requested).  For bf16 GQA caches with d_k 64 / 128, G <= 16, a power-of-two
+ * page size, at most 4096 pages and top_pages <= 2048 it runs in two launches:
+ * the append and page scoring, then one launch in which every block selects its
+ * unit's top pages from the scores and attends over its share of them (the view
+ * never goes through memory); other shapes run the two calls' kernels.
+ * view_idx int32 [B][Hkv][top_pages] / view_len int32 [B][Hkv]: NULL (both) or
+ * the step's view; page_score: NULL or float [B][Hkv][ceil(capacity/page_size)].
+ * Other arguments as for the two calls.
+ * ws: se_workspace_bytes(SE_OP_QUEST_STEP, c, page_size, top_pages) bytes,
+ * 16-byte aligned, zero-filled once before first use (se_workspace_init); the
+ * call leaves its counters at zero. */
+se_status se_quest_decode_step(const se_cache* c, const void* q, void* k, void* v, const void* k_new,
+                               const void* v_new, int32_t* seq_len, void* kmin, void* kmax, int32_t page_size,
+                               int32_t top_pages, float scale, float* out, float* lse, int32_t* view_idx,
+                               int32_t* view_len, float* page_score, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* FP8 KV rows (tokendh.com explainer, section "历史太长,会撑爆什么": KV
  * quantization keeps the history at lower precision with what is needed to

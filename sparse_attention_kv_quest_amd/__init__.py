@@ -18,10 +18,12 @@ LIB_PATH = os.path.join(HERE, "libse.so")
 SE_F32, SE_BF16 = 0, 1
 SE_OP_QUEST, SE_OP_ATTN, SE_OP_SNAPKV, SE_OP_OMNIKV, SE_OP_QUEST_APPEND, SE_OP_H2O_PREFILL, SE_OP_APPEND_ATTN = \
     1, 2, 3, 4, 5, 6, 7
+SE_OP_QUEST_STEP = 8
 STATUS = {0: "SE_OK", -1: "SE_ERR_NULL", -2: "SE_ERR_SHAPE", -3: "SE_ERR_DTYPE", -4: "SE_ERR_ALIGN",
           -5: "SE_ERR_BUDGET", -6: "SE_ERR_WORKSPACE", -7: "SE_ERR_UNSUPPORTED", -8: "SE_ERR_HIP"}
 
 EXPORTS = ("se_kv_append", "se_kv_append_meta", "se_page_meta_update", "se_quest_select", "se_quest_append_select",
+           "se_quest_decode_step",
            "se_sparse_decode_attn", "se_sparse_decode_attn_noalloc", "se_kv_append_decode_attn", "se_streaming_view", "se_pyramid_budgets",
            "se_kv_quantize_fp8", "se_kv_append_fp8", "se_sparse_decode_attn_fp8",
            "se_chain_match", "se_chain_remap", "se_chain_append_positions", "se_h2o_prefill_init",
@@ -50,6 +52,7 @@ _SIGS = {
     "se_kv_append_meta": [_C, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P],
     "se_quest_select": [_C, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _SZ, _P],
     "se_quest_append_select": [_C, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _P, _P, _P, _P, _SZ, _P],
+    "se_quest_decode_step": [_C, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _F32, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "se_sparse_decode_attn": [_C, _P, _P, _P, _P, _P, _P, _I32, _I32, _F32, _P, _P, _P, _I32, _I32, _P, _SZ, _P],
     "se_sparse_decode_attn_noalloc": [_C, _P, _P, _P, _P, _P, _P, _I32, _I32, _F32, _P, _P, _P, _I32, _I32, _P],
     "se_kv_append_decode_attn": [_C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _F32, _P, _P, _P, _I32, _I32, _P,
@@ -184,6 +187,14 @@ def se_quest_append_select(c, q, k, v, k_new, v_new, seq_len, kmin, kmax, page_s
         ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(k_new), _ptr(v_new), _ptr(seq_len), _ptr(kmin), _ptr(kmax),
         page_size, top_pages, _ptr(view_idx), _ptr(view_len), _ptr(page_score), _ptr(ws), _nbytes(ws),
         _stream(stream)))
+
+
+def se_quest_decode_step(c, q, k, v, k_new, v_new, seq_len, kmin, kmax, page_size, top_pages, scale, out, lse=None,
+                         view_idx=None, view_len=None, page_score=None, ws=None, stream=None):
+    _check("se_quest_decode_step", load().se_quest_decode_step(
+        ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(k_new), _ptr(v_new), _ptr(seq_len), _ptr(kmin), _ptr(kmax),
+        page_size, top_pages, scale, _ptr(out), _ptr(lse), _ptr(view_idx), _ptr(view_len), _ptr(page_score), _ptr(ws),
+        _nbytes(ws), _stream(stream)))
 
 
 def se_kv_quantize_fp8(c, k, v, seq_len, k_q, v_q, k_scale, v_scale, kmin=None, kmax=None, page_size=0,

@@ -143,6 +143,7 @@ size_t se_workspace_bytes(int32_t op, const se_cache* c, int32_t a0, int32_t a1)
     case SE_OP_QUEST_APPEND: return a0 > 0 ? quest_append_ws_bytes(*c, a0) : 0;
     case SE_OP_H2O_PREFILL: return (a0 > a1 && a1 > 0) ? h2o_prefill_ws_bytes(*c, a0, a1) : 0;
     case SE_OP_APPEND_ATTN: return attn_append_ws_bytes(*c, a0 > 0 ? a0 : c->capacity, a1);
+    case SE_OP_QUEST_STEP: return (a0 > 0 && a1 > 0) ? quest_step_ws_bytes(*c, a0, a1) : 0;
     default: return 0;
   }
 }
@@ -240,6 +241,30 @@ se_status se_quest_append_select(const se_cache* c, const void* q, void* k, void
   clear_stale_error();
   return launch_quest_append(*c, q, k, v, k_new, v_new, seq_len, kmin, kmax, page_size, top_pages, view_idx,
                              view_len, page_score, ws, stream);
+}
+
+se_status se_quest_decode_step(const se_cache* c, const void* q, void* k, void* v, const void* k_new,
+                               const void* v_new, int32_t* seq_len, void* kmin, void* kmax, int32_t page_size,
+                               int32_t top_pages, float scale, float* out, float* lse, int32_t* view_idx,
+                               int32_t* view_len, float* page_score, void* ws, size_t ws_bytes, hipStream_t stream) {
+  se_status st = check_cache(c);
+  if (st != SE_OK) return st;
+  if (!q || !k || !k_new || !seq_len || !kmin || !kmax || !out || !ws || (!c->latent && (!v || !v_new)))
+    return SE_ERR_NULL;
+  if ((view_idx == nullptr) != (view_len == nullptr)) return SE_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(k_new) || !aligned16(kmin) || !aligned16(kmax) || !aligned16(ws) ||
+      !aligned16(out) || (!c->latent && (!aligned16(v) || !aligned16(v_new))))
+    return SE_ERR_ALIGN;
+  if (page_size <= 0 || page_size > c->capacity) return SE_ERR_SHAPE;
+  if (top_pages < 1) return SE_ERR_BUDGET;
+  if (int64_t(top_pages) * page_size > (int64_t(1) << 30)) return SE_ERR_SHAPE;
+  if (!(scale > 0.f) || !(scale < 1e30f)) return SE_ERR_SHAPE;
+  if (ws_bytes < quest_step_ws_bytes(*c, page_size, top_pages)) return SE_ERR_WORKSPACE;
+  SE_TRACE_CALL("quest_decode_step B=%d Hq=%d Hkv=%d d_k=%d P=%d k=%d", c->batch, c->n_q_heads, c->n_kv_heads,
+                c->d_k, page_size, top_pages);
+  clear_stale_error();
+  return launch_quest_step(*c, q, k, v, k_new, v_new, seq_len, kmin, kmax, page_size, top_pages, scale, out, lse,
+                           view_idx, view_len, page_score, ws, stream);
 }
 
 // FP8 caches: bf16 q / metadata / source rows, GQA with d_k 64 or 128.

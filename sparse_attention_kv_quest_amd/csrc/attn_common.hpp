@@ -33,6 +33,13 @@ struct AttnArgs {
   // the old length) stores the new length into seq_len_w.
   const void* k_new; const void* v_new; void* k_w; void* v_w;
   const int32_t* slot; int32_t* seq_len_w; int* row_ctr; int app;
+  // In-launch page selection (sel != 0, the Quest decode step): the row at slot
+  // seq_len[b] was appended by the preceding scoring launch, so the attention runs
+  // over seq_len[b] + 1 slots (capped at the capacity); every block selects its
+  // unit's top view_cap pages from sel_score [units][sel_ncp] into its LDS view
+  // cache (the rule of the separate top-k launch); split 0 writes the view to
+  // sel_view / sel_vlen when they are given; the new length is stored as for app.
+  const float* sel_score; int sel_ncp; int32_t* sel_view; int32_t* sel_vlen; int sel;
 };
 
 // Number of view slots of a unit: view entries times granularity, or seq_len for the identity view.
@@ -159,6 +166,7 @@ int attn_mla_auto_splits(int units, int G, int slots);
 se_status launch_attn_mla(const AttnArgs& a, hipStream_t s);
 int attn_mfma_auto_splits(int units, int slots);
 se_status launch_attn_mfma(const AttnArgs& a, hipStream_t s);
+int attn_mfma_sel_keys(int ncp);
 
 inline bool attn_mfma_eligible(const se_cache& c) {
   return c.dtype == SE_BF16 && !c.latent && (c.d_k == 128 || c.d_k == 64) && c.d_v == c.d_k &&

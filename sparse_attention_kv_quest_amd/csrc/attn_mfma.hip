@@ -359,10 +359,13 @@ __device__ __forceinline__ void mf_step(const AttnArgs& a, const MfCtx& x, int b
 
 // LG: logits requested.  Launches without them compile the logits path out, which
 // keeps the register budget (a spill here costs far more than its few bytes).
-template <int D, bool VC, int OCC, bool F8, bool APP, bool LG>
+// SEL > 0: the page view is selected in the launch (AttnArgs::sel), SEL keys per
+// thread (up to 256 SEL pages).
+template <int D, bool VC, int OCC, bool F8, bool APP, bool LG, int SEL = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void attn_mfma_kernel(AttnArgs a) {
   static_assert(!(APP && F8), "the fused append writes bf16 rows");
+  static_assert(SEL == 0 || (VC && !APP && !F8 && !LG), "in-launch selection: page views over bf16 rows");
   constexpr int PITCH = MF_TS + 4;          // u16 per transposed V row (72 bytes)
   constexpr int NDB = D / 16;
   constexpr int NKS = D / 32;
@@ -392,17 +395,22 @@ void attn_mfma_kernel(AttnArgs a) {
     chunk = (chunk + MF_TS - 1) / MF_TS * MF_TS;
     s0 = min(n_slots, split * chunk);
     s1 = min(n_slots, s0 + chunk);
-    e0 = s0 >> a.gshift;
-    const int e1 = s1 > s0 ? ((s1 - 1) >> a.gshift) + 1 : e0;
-    const int32_t* vrow = a.view_idx + size_t(unit) * a.view_cap;
+    if constexpr (SEL == 0) {
+      e0 = s0 >> a.gshift;
+      const int e1 = s1 > s0 ? ((s1 - 1) >> a.gshift) + 1 : e0;
+      const int32_t* vrow = a.view_idx + size_t(unit) * a.view_cap;
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int e = e0 + threadIdx.x + 256 * j;
-      ventry[j] = e < e1 ? vrow[e] : -1;
+      for (int j = 0; j < VPT; ++j) {
+        const int e = e0 + threadIdx.x + 256 * j;
+        ventry[j] = e < e1 ? vrow[e] : -1;
+      }
     }
   }
   const int len0 = min(a.seq_len[b], a.cap);
   int len = len0, tgt = -2, row_ticket = 0;
+  if constexpr (SEL > 0) {   // the row the scoring launch appended
+    if (len0 < a.cap) len = len0 + 1;
+  }
   u32x4 app_row = {0, 0, 0, 0};   // this thread's 16 bytes of the new row, stored after the tiles
   if constexpr (APP) {
     // se_kv_append's rule, per unit
@@ -424,7 +432,9 @@ void attn_mfma_kernel(AttnArgs a) {
     s0 = min(n_slots, split * chunk);
     s1 = min(n_slots, s0 + chunk);
   }
-  const int s_valid = identity ? len : min(a.view_len[unit], a.view_cap) * a.gran;
+
+  // the view's slot count (selected in the launch: known after the selection)
+  int s_valid = identity ? len : (SEL > 0 ? 0 : min(a.view_len[unit], a.view_cap) * a.gran);
 
   MfCtx x;
   const size_t ebytes = F8 ? 1 : 2;   // bytes per stored element
@@ -440,7 +450,7 @@ void attn_mfma_kernel(AttnArgs a) {
   x.tgt = tgt;
   x.knew = APP ? static_cast<const uint16_t*>(a.k_new) + size_t(unit) * D : nullptr;
   x.vnew = APP ? static_cast<const uint16_t*>(a.v_new) + size_t(unit) * D : nullptr;
-  x.vglob = identity ? nullptr : a.view_idx + size_t(unit) * a.view_cap;
+  x.vglob = (identity || SEL > 0) ? nullptr : a.view_idx + size_t(unit) * a.view_cap;
 
   // Q as the B operand: lane holds head c16, dims 32c + 8g .. 32c + 8g + 7 of k-step c
   u32x4 qv[NKS];
@@ -452,12 +462,29 @@ void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int c = 0; c < NKS; ++c) qv[c] = u32x4{0, 0, 0, 0};
   }
-  if (VC) {
+  int sel_len = 0;
+  if constexpr (SEL > 0) {
+    // the unit's top pages by score, ascending, straight into the view cache (the
+    // V staging tiles are not in use yet and hold the selection's histograms)
+    TopkRegShared& tsh = *reinterpret_cast<TopkRegShared*>(&vt_lds[0][0]);
+    static_assert(sizeof(TopkRegShared) <= sizeof(vt_lds), "selection scratch");
+    const float* srow = a.sel_score + size_t(unit) * a.sel_ncp;
+    const int npages = min((len + a.gran - 1) >> a.gshift, a.sel_ncp);
+    sel_len = block_topk_reg<256, SEL>([&](int i) { return srow[i]; }, npages, a.view_cap, mf_vcache, tsh);
+  } else if (VC) {
 #pragma unroll
     for (int j = 0; j < VPT; ++j)
       if (threadIdx.x + 256 * j < MF_VCACHE) mf_vcache[threadIdx.x + 256 * j] = ventry[j];
   }
   __syncthreads();   // view cache ready
+  if constexpr (SEL > 0) {
+    s_valid = min(sel_len, a.view_cap) * a.gran;
+    x.s1 = min(s1, s_valid);
+  }
+  if (SEL > 0 && split == 0 && a.sel_view != nullptr) {
+    for (int i = threadIdx.x; i < a.view_cap; i += 256) a.sel_view[size_t(unit) * a.view_cap + i] = mf_vcache[i];
+    if (threadIdx.x == 0) a.sel_vlen[unit] = sel_len;
+  }
 
   const float sc2 = a.scale * LOG2E;
   MfState<D> st;
@@ -543,7 +570,7 @@ void attn_mfma_kernel(AttnArgs a) {
     }
   }
 
-  if (APP && threadIdx.x == 0) {
+  if ((APP || SEL > 0) && threadIdx.x == 0) {
     // every block of the batch row takes a ticket, long after it read the old length
     // (issued here, not up front, so that no tile's loads wait for its return); the
     // last one stores the new length at the end
@@ -610,7 +637,7 @@ void attn_mfma_kernel(AttnArgs a) {
     int* ctr = a.counters + unit * ATTN_MAX_HG;
     if (attn_split_done(ctr, a.splits)) attn_merge_splits<256>(a, unit, 0, G, ctr);
   }
-  if (APP && threadIdx.x == 0 && row_ticket == a.Hkv * a.splits - 1) {   // every block of the row has read it
+  if ((APP || SEL > 0) && threadIdx.x == 0 && row_ticket == a.Hkv * a.splits - 1) {   // every block of the row has read it
     if (len != len0) a.seq_len_w[b] = len;
     ticket_reset(a.row_ctr + b);
   }
@@ -639,8 +666,25 @@ static void mf_launch(const AttnArgs& a, dim3 grid, hipStream_t s) {
     hipLaunchKernelGGL((attn_mfma_kernel<D, VC, OCC, F8, APP, false>), grid, dim3(256), 0, s, a);
 }
 
+// Keys per thread of the in-launch page selection for sel_ncp pages (0: too many).
+int attn_mfma_sel_keys(int ncp) { return ncp <= 256 * 4 ? 4 : ncp <= 256 * 9 ? 9 : ncp <= 256 * 16 ? 16 : 0; }
+
 se_status launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.splits, a.B * a.Hkv);
+  if (a.sel) {   // page views selected in the launch (the Quest decode step)
+#define SE_SEL(DD, OO, EE) hipLaunchKernelGGL((attn_mfma_kernel<DD, true, OO, false, false, false, EE>), grid, dim3(256), \
+                                              0, s, a)
+    const int e = attn_mfma_sel_keys(a.sel_ncp);
+    if (a.Dk == 128) {
+      if (e == 4) SE_SEL(128, 2, 4); else if (e == 9) SE_SEL(128, 2, 9); else if (e == 16) SE_SEL(128, 2, 16);
+      else return SE_ERR_UNSUPPORTED;
+    } else {
+      if (e == 4) SE_SEL(64, 1, 4); else if (e == 9) SE_SEL(64, 1, 9); else if (e == 16) SE_SEL(64, 1, 16);
+      else return SE_ERR_UNSUPPORTED;
+    }
+#undef SE_SEL
+    return launch_status();
+  }
   // entries one block reads: its chunk of slots divided by the granularity (+2 for straddled entries)
   const int slots = a.view_idx ? a.view_cap * a.gran : 0;
   int chunk = (slots + a.splits - 1) / a.splits;

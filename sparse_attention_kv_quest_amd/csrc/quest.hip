@@ -540,6 +540,34 @@ size_t quest_append_ws_bytes(const se_cache& c, int page_size) {
   return (ctr + 255) / 256 * 256 + quest_ws_bytes(c, page_size, 0);
 }
 
+// The first launch of the fused Quest decode step (bf16 GQA, d_k 64 / 128, G <= 16):
+// the new rows, the appended page's min / max and every page's score (into
+// page_score, else the workspace, after its batch-row counters); seq_len is left
+// for the step's attention launch to update.
+se_status launch_quest_append_scores(const se_cache& c, const void* q, void* k, void* v, const void* k_new,
+                                     const void* v_new, const int32_t* seq_len, void* kmin, void* kmax, int page_size,
+                                     float* page_score, void* ws, float** score_out, hipStream_t s) {
+  const int units = c.batch * c.n_kv_heads, G = c.n_q_heads / c.n_kv_heads;
+  const int ncp = ceil_div(c.capacity, page_size);
+  const size_t ctr_bytes = (size_t(c.batch) * sizeof(int) + 255) / 256 * 256;
+  float* score = page_score ? page_score : (float*)((char*)ws + ctr_bytes);
+  QuestAppendArgs ap{};
+  ap.k = (uint16_t*)k; ap.v = (uint16_t*)v;
+  ap.k_new = (const uint16_t*)k_new; ap.v_new = (const uint16_t*)v_new;
+  ap.kmin_w = (uint16_t*)kmin; ap.kmax_w = (uint16_t*)kmax;
+  const dim3 grid(ceil_div(ncp, 64), units);
+#define SE_AP(DD) hipLaunchKernelGGL((quest_score_mfma_kernel<DD, 1, true>), grid, dim3(256), 0, s, (const uint16_t*)q, \
+                                     (const uint16_t*)kmin, (const uint16_t*)kmax, seq_len, score, c.n_kv_heads, G,  \
+                                     page_size, ncp, c.capacity, ap)
+  if (c.dtype != SE_BF16 || c.latent || G > 16) return SE_ERR_UNSUPPORTED;
+  if (c.d_k == 128) SE_AP(128);
+  else if (c.d_k == 64) SE_AP(64);
+  else return SE_ERR_UNSUPPORTED;
+#undef SE_AP
+  *score_out = score;
+  return launch_status();
+}
+
 // Two launches: append + page scores, then top-k + the new seq_len.
 se_status launch_quest_append(const se_cache& c, const void* q, void* k, void* v, const void* k_new,
                               const void* v_new, int32_t* seq_len, void* kmin, void* kmax, int page_size,

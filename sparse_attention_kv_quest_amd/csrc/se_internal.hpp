@@ -460,6 +460,14 @@ se_status launch_kv_append_meta(const se_cache& c, void* k, void* v, const void*
                                 hipStream_t s);
 size_t quest_ws_bytes(const se_cache& c, int page_size, int top_pages);
 size_t quest_append_ws_bytes(const se_cache& c, int page_size);
+size_t quest_step_ws_bytes(const se_cache& c, int page_size, int top_pages);
+se_status launch_quest_append_scores(const se_cache& c, const void* q, void* k, void* v, const void* k_new,
+                                     const void* v_new, const int32_t* seq_len, void* kmin, void* kmax, int page_size,
+                                     float* page_score, void* ws, float** score_out, hipStream_t s);
+se_status launch_quest_step(const se_cache& c, const void* q, void* k, void* v, const void* k_new,
+                            const void* v_new, int32_t* seq_len, void* kmin, void* kmax, int page_size,
+                            int top_pages, float scale, float* out, float* lse, int32_t* view_idx,
+                            int32_t* view_len, float* page_score, void* ws, hipStream_t s);
 se_status launch_streaming_view(const se_cache& c, const int32_t* seq_len, int sink, int recent,
                                 int32_t* view_idx, int32_t* view_len, int view_cap, int pending, hipStream_t s);
 void pyramid_budgets(int n, int avg, int bmin, int32_t* out);

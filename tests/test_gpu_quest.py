@@ -35,17 +35,24 @@ class QuestState:
         self.ws_q = se.workspace(se.SE_OP_QUEST, self.c, P, cfg.top_pages)
         self.ws_qa = se.workspace(se.SE_OP_QUEST_APPEND, self.c, P, 0)
         self.ws_a = se.workspace(se.SE_OP_ATTN, self.c, cfg.top_pages * P, 0)
+        self.ws_step = se.workspace(se.SE_OP_QUEST_STEP, self.c, P, cfg.top_pages)
         se.se_page_meta_update(self.c, self.k, self.kmin, self.kmax, self.seq, P, 0)
 
-    def step(self, se, step, splits=0, fused=False):
-        """fused: append, metadata, scores and view through se_quest_append_select (the
-        bench's call) instead of se_kv_append, se_page_meta_update, se_quest_select."""
+    def step(self, se, step, splits=0, fused=False, whole=False):
+        """fused: append, metadata, scores and view through se_quest_append_select instead
+        of se_kv_append, se_page_meta_update, se_quest_select; whole: the whole step
+        through se_quest_decode_step (the bench's call)."""
         cfg, dt, P = self.cfg, tdtype(self.cfg), self.cfg.page_size
         q = gen.decode_query(cfg, 0, step)
         kn, vn = gen.decode_kv_new(cfg, 0, step)
         L = cfg.context + step
         self.K[:, :, L], self.V[:, :, L] = kn, vn
         qd = dev(q, dt)
+        if whole:
+            se.se_quest_decode_step(self.c, qd, self.k, self.v, dev(kn, dt), dev(vn, dt), self.seq, self.kmin,
+                                    self.kmax, P, cfg.top_pages, cfg.softmax_scale, self.out, self.lse, self.view,
+                                    self.vlen, self.score, self.ws_step)
+            return q, L + 1
         if fused:
             se.se_quest_append_select(self.c, qd, self.k, self.v, dev(kn, dt), dev(vn, dt), self.seq, self.kmin,
                                       self.kmax, P, cfg.top_pages, self.view, self.vlen, self.score, self.ws_qa)
@@ -100,14 +107,14 @@ def test_tiny_f32_quest_decode_all_units_all_steps(se):
             check_unit(cfg, st, q, L, unit, got)
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_tiny_bf16_quest_decode_with_partial_pages(se, fused):
+@pytest.mark.parametrize("mode", ["separate", "fused", "whole"])
+def test_tiny_bf16_quest_decode_with_partial_pages(se, mode):
     cfg = get_config(0, dtype="bf16", batch=3, n_q_heads=8, n_kv_heads=2, d_k=128, d_v=128, context=300,
                       top_pages=5, decode_steps=20)
-    banner(f"tiny bf16 quest pipeline, ragged pages, fused={fused}")
+    banner(f"tiny bf16 quest pipeline, ragged pages, {mode}")
     st = QuestState(se, cfg, cfg.context + cfg.decode_steps)
     for step in range(cfg.decode_steps):
-        q, L = st.step(se, step, fused=fused)
+        q, L = st.step(se, step, fused=mode == "fused", whole=mode == "whole")
         torch.cuda.synchronize()
         got = snapshot(st)
         for unit in range(cfg.units):
@@ -130,9 +137,10 @@ def test_quest_top_k_edges(se, k_pages):
 
 
 def test_quest_32k_decode(se):
-    """The 32K Quest workload at full size through the bench's calls (the fused append +
-    selection, then the attention): every step runs on the GPU; every unit is compared
-    with the oracle at the first, a middle and the last step."""
+    """The 32K Quest workload at full size through the bench's call (se_quest_decode_step:
+    the append and page scores, then the page selection and attention in one launch):
+    every step runs on the GPU; every unit is compared with the oracle at the first, a
+    middle and the last step."""
     cfg = get_config(1)
     banner("quest 32K: building caches")
     st = QuestState(se, cfg, cfg.context + cfg.decode_steps)
@@ -140,7 +148,7 @@ def test_quest_32k_decode(se):
     sample_steps = {0: every, 31: every, cfg.decode_steps - 1: every}
     recall = []
     for step in range(cfg.decode_steps):
-        q, L = st.step(se, step, fused=True)
+        q, L = st.step(se, step, whole=True)
         if step in sample_steps:
             torch.cuda.synchronize()
             banner(f"quest 32K: checking step {step}")
@@ -169,7 +177,7 @@ def test_quest_32k_step_deterministic_and_resumable(se):
     banner("quest 32K determinism: building caches")
     st = QuestState(se, cfg, cfg.context + 4)
     for step in range(3):
-        st.step(se, step, fused=True)
+        st.step(se, step, whole=True)
     torch.cuda.synchronize()
     saved = [t.cpu() for t in quest_32k_state_buffers(st)]
     results = []
@@ -177,7 +185,7 @@ def test_quest_32k_step_deterministic_and_resumable(se):
         banner(f"quest 32K determinism: run {rep}")
         for t, h in zip(quest_32k_state_buffers(st), saved):
             t.copy_(h)
-        st.step(se, 3, fused=True)
+        st.step(se, 3, whole=True)
         torch.cuda.synchronize()
         results.append([t.cpu() for t in quest_32k_state_buffers(st)])
     for a, b, name in zip(results[0], results[1], ("k", "v", "kmin", "kmax", "seq", "view", "vlen", "score", "out",
