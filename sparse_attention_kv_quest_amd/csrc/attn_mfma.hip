@@ -389,6 +389,15 @@ void attn_mfma_kernel(AttnArgs a) {
   constexpr int VPT = MF_VCACHE / 256;   // cached view entries per thread
   int ventry[VPT];
   int e0 = 0, s0, s1;
+  // in-launch selection: the unit's page scores, loaded first (their addresses depend
+  // on kernel arguments alone, so they overlap the length load), masked by the page
+  // count once it is known
+  float sraw[SEL > 0 ? SEL : 1];
+  if constexpr (SEL > 0) {
+    const float* srow = a.sel_score + size_t(unit) * a.sel_ncp;
+#pragma unroll
+    for (int j = 0; j < SEL; ++j) sraw[j] = srow[min(topk_reg_index<256, SEL>(j), a.sel_ncp - 1)];
+  }
   if (VC) {
     const int n_slots = a.view_cap * a.gran;
     int chunk = (n_slots + a.splits - 1) / a.splits;
@@ -466,11 +475,14 @@ void attn_mfma_kernel(AttnArgs a) {
   if constexpr (SEL > 0) {
     // the unit's top pages by score, ascending, straight into the view cache (the
     // V staging tiles are not in use yet and hold the selection's histograms)
-    TopkRegShared& tsh = *reinterpret_cast<TopkRegShared*>(&vt_lds[0][0]);
-    static_assert(sizeof(TopkRegShared) <= sizeof(vt_lds), "selection scratch");
-    const float* srow = a.sel_score + size_t(unit) * a.sel_ncp;
+    using SelShared = TopkRegSharedN<MF_WAVES>;
+    SelShared& tsh = *reinterpret_cast<SelShared*>(&vt_lds[0][0]);
+    static_assert(sizeof(SelShared) <= sizeof(vt_lds), "selection scratch");
     const int npages = min((len + a.gran - 1) >> a.gshift, a.sel_ncp);
-    sel_len = block_topk_reg<256, SEL>([&](int i) { return srow[i]; }, npages, a.view_cap, mf_vcache, tsh);
+    uint32_t key[SEL > 0 ? SEL : 1];
+#pragma unroll
+    for (int j = 0; j < SEL; ++j) key[j] = topk_reg_index<256, SEL>(j) < npages ? ordered_bits(sraw[j]) : 0u;
+    sel_len = block_topk_keys<256, SEL, SelShared>(key, npages, a.view_cap, mf_vcache, tsh);
   } else if (VC) {
 #pragma unroll
     for (int j = 0; j < VPT; ++j)

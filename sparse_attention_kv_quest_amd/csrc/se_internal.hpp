@@ -310,12 +310,14 @@ __device__ int block_topk_ascending(ScoreFn score, int n, int k, int32_t* out, T
 // of the prefix's bucket in index order (the lower-index tie rule); per-wave
 // counts give each wave its output offset and ballot prefix counts place each
 // kept candidate, so the view comes out in ascending index order.
-struct TopkRegShared {
-  uint32_t hist[16][256];     // one histogram per wave (BLOCK <= 1024)
-  uint32_t red_or[16], red_and[16];
-  int cnt_a[16], cnt_b[16];
+template <int NWAVES>
+struct TopkRegSharedN {
+  uint32_t hist[NWAVES][256];     // one histogram per wave
+  uint32_t red_or[NWAVES], red_and[NWAVES];
+  int cnt_a[NWAVES], cnt_b[NWAVES];
   int digit, rem, cnt;
 };
+using TopkRegShared = TopkRegSharedN<16>;   // blocks of up to 1024 threads
 
 __device__ __forceinline__ int lanes_below(uint64_t m) {
   return int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
@@ -325,26 +327,43 @@ struct TopkNoHook {
   __device__ void operator()() const {}
 };
 
+// The candidate this thread's key j stands for in block_topk_reg / block_topk_keys.
+template <int BLOCK, int E>
+__device__ __forceinline__ int topk_reg_index(int j) {
+  return (int(threadIdx.x) / WAVE) * WAVE * E + (int(threadIdx.x) & (WAVE - 1)) + j * WAVE;
+}
+
+template <int BLOCK, int E, class SH>
+__device__ int block_topk_keys(uint32_t (&key)[E], int n, int k, int32_t* out, SH& sh);
+
 // after_loads() runs once every key load has been issued (its own memory operations
 // then overlap those loads' return)
-template <int BLOCK, int E, class LoadFn, class AfterLoads = TopkNoHook>
-__device__ int block_topk_reg(LoadFn load, int n, int k, int32_t* out, TopkRegShared& sh,
+template <int BLOCK, int E, class LoadFn, class SH, class AfterLoads = TopkNoHook>
+__device__ int block_topk_reg(LoadFn load, int n, int k, int32_t* out, SH& sh,
                               AfterLoads after_loads = AfterLoads{}) {
-  static_assert(BLOCK >= 64 && BLOCK <= 1024 && BLOCK % WAVE == 0, "block size");
-  constexpr int NW = BLOCK / WAVE;
-  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
-  const int kk = k < n ? k : n;
-  const int base = w * WAVE * E + lane;
   uint32_t key[E];
   // unconditional loads at a clamped index (element 0 always exists), masked after:
   // all E loads go out together instead of one guarded round trip each
 #pragma unroll
   for (int j = 0; j < E; ++j) {
-    const int i = base + j * WAVE;
+    const int i = topk_reg_index<BLOCK, E>(j);
     const uint32_t v = ordered_bits(load(max(min(i, n - 1), 0)));
     key[j] = i < n ? v : 0u;
   }
   after_loads();
+  return block_topk_keys<BLOCK, E, SH>(key, n, k, out, sh);
+}
+
+// The selection itself, on keys already in registers: key[j] is ordered_bits of the
+// score of candidate topk_reg_index(j), or 0 where that index is not a candidate.
+template <int BLOCK, int E, class SH>
+__device__ int block_topk_keys(uint32_t (&key)[E], int n, int k, int32_t* out, SH& sh) {
+  static_assert(BLOCK >= 64 && BLOCK <= 1024 && BLOCK % WAVE == 0, "block size");
+  constexpr int NW = BLOCK / WAVE;
+  static_assert(sizeof(sh.red_or) / sizeof(sh.red_or[0]) >= NW, "shared state for every wave");
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+  const int kk = k < n ? k : n;
+  const int base = w * WAVE * E + lane;
   uint32_t mask = 0u, prefix = 0u;   // resolved top bits and their value
   int r = kk;                        // keys still to take from the bucket (key & mask) == prefix
   if (kk > 0 && kk < n) {
