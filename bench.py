@@ -363,27 +363,30 @@ def run_h2o(se, torch, args):
                         v=dev_grid(torch, (B, H, cap, D), 32 + 2 * i, torch.bfloat16),
                         pos=pos_d.clone(), acc=acc_d.clone(),
                         seq=torch.full((B,), cap, dtype=torch.int32, device="cuda"),
-                        evict=torch.full((B, H), cap - 1, dtype=torch.int32, device="cuda"),
-                        out=torch.empty((B, Hq, D), device="cuda"), cur=cfg.context + i))
+                        ev=(torch.full((B, H), cap - 1, dtype=torch.int32, device="cuda"),
+                            torch.full((B, H), -1, dtype=torch.int32, device="cuda")),
+                        out=torch.empty((B, Hq, D), device="cuda"), cur=cfg.context + 2 * i))
     q = dev_grid(torch, (B, Hq, D), 30, torch.bfloat16)
     kn = dev_grid(torch, (B, H, D), 29, torch.bfloat16)
     vn = dev_grid(torch, (B, H, D), 28, torch.bfloat16)
     lse = torch.empty((B, Hq), device="cuda")
-    logits = torch.empty((B, Hq, cap), device="cuda")
-    ws_aa = se.workspace(se.SE_OP_APPEND_ATTN, c, cap, 0)
+    ws_h = se.workspace(se.SE_OP_H2O_STEP, c, 0, 0)
 
-    # each captured layer slot runs at its own position; replays repeat the same work
-    def step(Ly):   # the new row into the freed slot + attention with logits in one launch, then H2O
-        se.se_kv_append_decode_attn(c, q, Ly["k"], Ly["v"], kn, vn, Ly["evict"], Ly["seq"], None, None, 0, 1,
-                                    cfg.softmax_scale, Ly["out"], lse, logits, cap, 0, ws_aa)
-        se.se_h2o_accumulate_evict(c, logits, lse, cap, Ly["seq"], Ly["pos"], Ly["acc"], Ly["cur"], heavy, recent,
-                                   Ly["evict"])
+    # one H2O decode step, se_h2o_decode_step: the new row into the slot the previous
+    # step freed, attention over every slot, accumulate + evict, in one launch; a layer's
+    # two steps alternate the slot arrays, so replays continue the eviction sequence
+    def step(Ly, t):
+        se.se_h2o_decode_step(c, q, Ly["k"], Ly["v"], kn, vn, Ly["ev"][t], Ly["seq"], Ly["pos"], Ly["acc"],
+                              Ly["cur"] + t, heavy, recent, cfg.softmax_scale, Ly["out"], lse, Ly["ev"][1 - t], ws_h)
 
     for Ly in lay:
-        step(Ly)
-    t_s = Timer(torch, lambda: [step(Ly) for Ly in lay], not args.no_graph)
-    ms_step = t_s.ms_per_replay(steps // nL) / nL
-    step_bytes = B * H * cap * (2 * D * 2 + 2 * G * 4 + 4 * 3) + B * Hq * D * (2 + 4)
+        step(Ly, 0)
+        step(Ly, 1)
+    t_s = Timer(torch, lambda: [step(Ly, t) for Ly in lay for t in (0, 1)], not args.no_graph)
+    ms_step = t_s.ms_per_replay(max(1, steps // (2 * nL))) / (2 * nL)
+    steps = max(1, steps // (2 * nL)) * 2 * nL
+    # K and V rows of every slot, the slot's score (read, written) and position, q and out
+    step_bytes = B * H * cap * (2 * D * 2 + 4 * 3) + B * Hq * D * (2 + 4)
     del lay, t_s
     free(torch)
     pre = h2o_prefill_timing(se, torch, cfg, c)

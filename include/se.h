@@ -92,7 +92,8 @@ typedef enum {
   SE_OP_QUEST_APPEND = 5, /* a0 = page_size (a1 unused) */
   SE_OP_H2O_PREFILL = 6,  /* a0 = prompt_len, a1 = recent_window */
   SE_OP_APPEND_ATTN = 7,  /* a0 = view_cap * granularity (slots per unit), a1 = num_splits (0 = auto) */
-  SE_OP_QUEST_STEP = 8    /* a0 = page_size, a1 = top_pages */
+  SE_OP_QUEST_STEP = 8,   /* a0 = page_size, a1 = top_pages */
+  SE_OP_H2O_STEP = 9      /* a0, a1 unused */
 } se_op;
 
 /* Append one decode token's K/V row to every unit (helper of the hooks: the
@@ -397,6 +398,32 @@ se_status se_h2o_accumulate_evict(const se_cache* c, const float* logits, const 
                                   int32_t logit_cap, const int32_t* seq_len, int32_t* slot_pos,
                                   float* acc, int32_t cur_pos, int32_t heavy_budget,
                                   int32_t recent_window, int32_t* evict_slot, hipStream_t stream);
+
+/* A whole H2O decode step (tokendh.com explainer, section "把边界划在'生命周期'上":
+ * the scores are updated at every decode step, then the victim is chosen): the
+ * same results, bit for bit, as
+ *   se_kv_append(c, k, v, k_new, v_new, slot_in, seq_len)
+ *   se_sparse_decode_attn(c, q, k, v, seq_len, NULL, NULL, 0, 1, scale, out, lse,
+ *                         logits, capacity, 1, ...)
+ *   se_h2o_accumulate_evict(c, logits, lse, capacity, seq_len, slot_pos, acc,
+ *                           cur_pos, heavy_budget, recent_window, evict)
+ * where evict holds slot_in on entry (-1 everywhere when slot_in is NULL) and is
+ * copied to evict_out on exit: slot_in int32 [B][Hkv] (or NULL) is the slot each
+ * unit's new token goes to (the slot the previous step evicted), evict_out int32
+ * [B][Hkv] receives the slot this step evicts (or -1).  slot_in and evict_out
+ * must be different arrays (SE_ERR_SHAPE): every block of a batch row reads the
+ * row's first slot_in entry.  Steps alternate the two arrays.  For bf16 GQA
+ * caches with d_k 64 / 128, G <= 16, capacity <= 2048 and G * capacity <= 12288
+ * it is one launch, in which the logits never leave the chip; other shapes run
+ * the three calls' kernels.  lse: NULL or float [B][Hq].
+ * ws: se_workspace_bytes(SE_OP_H2O_STEP, c, 0, 0) bytes, 16-byte aligned,
+ * zero-filled once before first use (se_workspace_init); the call leaves its
+ * counters at zero. */
+se_status se_h2o_decode_step(const se_cache* c, const void* q, void* k, void* v, const void* k_new,
+                             const void* v_new, const int32_t* slot_in, int32_t* seq_len, int32_t* slot_pos,
+                             float* acc, int32_t cur_pos, int32_t heavy_budget, int32_t recent_window, float scale,
+                             float* out, float* lse, int32_t* evict_out, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
 
 /* H2O state at the end of a prefill (tokendh.com explainer, sections
  * "历史太长,会撑爆什么" and "把边界划在'生命周期'上": H2O's table accumulates the

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libse.so")
 SE_F32, SE_BF16 = 0, 1
 SE_OP_QUEST, SE_OP_ATTN, SE_OP_SNAPKV, SE_OP_OMNIKV, SE_OP_QUEST_APPEND, SE_OP_H2O_PREFILL, SE_OP_APPEND_ATTN = \
     1, 2, 3, 4, 5, 6, 7
-SE_OP_QUEST_STEP = 8
+SE_OP_QUEST_STEP, SE_OP_H2O_STEP = 8, 9
 STATUS = {0: "SE_OK", -1: "SE_ERR_NULL", -2: "SE_ERR_SHAPE", -3: "SE_ERR_DTYPE", -4: "SE_ERR_ALIGN",
           -5: "SE_ERR_BUDGET", -6: "SE_ERR_WORKSPACE", -7: "SE_ERR_UNSUPPORTED", -8: "SE_ERR_HIP"}
 
@@ -26,7 +26,7 @@ EXPORTS = ("se_kv_append", "se_kv_append_meta", "se_page_meta_update", "se_quest
            "se_quest_decode_step",
            "se_sparse_decode_attn", "se_sparse_decode_attn_noalloc", "se_kv_append_decode_attn", "se_streaming_view", "se_pyramid_budgets",
            "se_kv_quantize_fp8", "se_kv_append_fp8", "se_sparse_decode_attn_fp8",
-           "se_chain_match", "se_chain_remap", "se_chain_append_positions", "se_h2o_prefill_init",
+           "se_chain_match", "se_chain_remap", "se_chain_append_positions", "se_h2o_prefill_init", "se_h2o_decode_step",
            "se_snapkv_score_compact", "se_h2o_accumulate_evict", "se_omnikv_topk",
            "se_workspace_bytes", "se_workspace_init", "se_status_string", "se_abi_version")
 
@@ -69,6 +69,7 @@ _SIGS = {
     "se_h2o_prefill_init": [_C, _P, _P, _P, _I32, _I32, _I32, _F32, _C, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "se_snapkv_score_compact": [_C, _P, _P, _P, _I32, _I32, _I32, _I32, _F32, _C, _P, _P, _P, _P, _P, _P, _SZ,
                                 _P],
+    "se_h2o_decode_step": [_C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _F32, _P, _P, _P, _P, _SZ, _P],
     "se_h2o_accumulate_evict": [_C, _P, _P, _I32, _P, _P, _P, _I32, _I32, _I32, _P, _P],
     "se_omnikv_topk": [_C, _P, _P, _I32, _P, _I32, _P, _P, _P, _P, _SZ, _P],
 }
@@ -298,6 +299,14 @@ def se_h2o_accumulate_evict(c, logits, lse, logit_cap, seq_len, slot_pos, acc, c
     _check("se_h2o_accumulate_evict", load().se_h2o_accumulate_evict(
         ctypes.byref(c), _ptr(logits), _ptr(lse), logit_cap, _ptr(seq_len), _ptr(slot_pos), _ptr(acc), cur_pos,
         heavy_budget, recent_window, _ptr(evict_slot), _stream(stream)))
+
+
+def se_h2o_decode_step(c, q, k, v, k_new, v_new, slot_in, seq_len, slot_pos, acc, cur_pos, heavy_budget, recent_window,
+                       scale, out, lse, evict_out, ws=None, stream=None):
+    _check("se_h2o_decode_step", load().se_h2o_decode_step(
+        ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(k_new), _ptr(v_new), _ptr(slot_in), _ptr(seq_len),
+        _ptr(slot_pos), _ptr(acc), cur_pos, heavy_budget, recent_window, scale, _ptr(out), _ptr(lse), _ptr(evict_out),
+        _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def se_omnikv_topk(c, logits, lse, logit_cap, seq_len, top_k, view_idx, view_len, scores=None, ws=None,

@@ -144,6 +144,7 @@ size_t se_workspace_bytes(int32_t op, const se_cache* c, int32_t a0, int32_t a1)
     case SE_OP_H2O_PREFILL: return (a0 > a1 && a1 > 0) ? h2o_prefill_ws_bytes(*c, a0, a1) : 0;
     case SE_OP_APPEND_ATTN: return attn_append_ws_bytes(*c, a0 > 0 ? a0 : c->capacity, a1);
     case SE_OP_QUEST_STEP: return (a0 > 0 && a1 > 0) ? quest_step_ws_bytes(*c, a0, a1) : 0;
+    case SE_OP_H2O_STEP: return h2o_step_ws_bytes(*c);
     default: return 0;
   }
 }
@@ -501,6 +502,33 @@ se_status se_h2o_accumulate_evict(const se_cache* c, const float* logits, const 
   clear_stale_error();
   return launch_h2o(*c, logits, lse, logit_cap, seq_len, slot_pos, acc, cur_pos, heavy_budget, recent_window,
                     evict_slot, stream);
+}
+
+se_status se_h2o_decode_step(const se_cache* c, const void* q, void* k, void* v, const void* k_new,
+                             const void* v_new, const int32_t* slot_in, int32_t* seq_len, int32_t* slot_pos,
+                             float* acc, int32_t cur_pos, int32_t heavy_budget, int32_t recent_window, float scale,
+                             float* out, float* lse, int32_t* evict_out, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  se_status st = check_cache(c);
+  if (st != SE_OK) return st;
+  if (!q || !k || !k_new || !seq_len || !slot_pos || !acc || !out || !evict_out || !ws ||
+      (!c->latent && (!v || !v_new)))
+    return SE_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(k_new) || !aligned16(out) || !aligned16(ws) ||
+      (!c->latent && (!aligned16(v) || !aligned16(v_new))))
+    return SE_ERR_ALIGN;
+  if (slot_in != nullptr && slot_in == evict_out) return SE_ERR_SHAPE;   // read by every block of a row
+  if (heavy_budget < 0 || recent_window < 0) return SE_ERR_BUDGET;
+  if (int64_t(heavy_budget) + recent_window + 1 > c->capacity) return SE_ERR_BUDGET;
+  if (cur_pos < 0) return SE_ERR_SHAPE;
+  if (!(scale > 0.f) || !(scale < 1e30f)) return SE_ERR_SHAPE;
+  if (int64_t(c->n_q_heads / c->n_kv_heads) * c->capacity > INT32_MAX) return SE_ERR_SHAPE;
+  if (ws_bytes < h2o_step_ws_bytes(*c)) return SE_ERR_WORKSPACE;
+  SE_TRACE_CALL("h2o_decode_step B=%d Hq=%d Hkv=%d cap=%d pos=%d heavy=%d recent=%d", c->batch, c->n_q_heads,
+                c->n_kv_heads, c->capacity, cur_pos, heavy_budget, recent_window);
+  clear_stale_error();
+  return launch_h2o_step(*c, q, k, v, k_new, v_new, slot_in, seq_len, slot_pos, acc, cur_pos, heavy_budget,
+                         recent_window, scale, out, lse, evict_out, ws, stream);
 }
 
 se_status se_h2o_prefill_init(const se_cache* c, const void* q_prompt, const void* k, const void* v,

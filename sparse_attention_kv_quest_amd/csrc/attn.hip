@@ -359,6 +359,56 @@ se_status launch_quest_step(const se_cache& c, const void* q, void* k, void* v, 
   return launch_status();
 }
 
+// The H2O decode step: [the fused attention's batch-row tickets and counters][logits
+// and lse scratch for shapes that run the separate kernels].
+size_t h2o_step_ws_bytes(const se_cache& c) {
+  const size_t rows = size_t(c.batch) * c.n_q_heads;
+  return r256(attn_append_ws_bytes(c, c.capacity, 1)) + r256(rows * size_t(c.capacity) * sizeof(float)) +
+         r256(rows * sizeof(float));
+}
+
+__global__ void copy_or_fill_i32_kernel(int32_t* __restrict__ dst, const int32_t* __restrict__ src, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src != nullptr ? src[i] : -1;
+}
+
+se_status launch_h2o_step(const se_cache& c, const void* q, void* k, void* v, const void* k_new, const void* v_new,
+                          const int32_t* slot_in, int32_t* seq_len, int32_t* slot_pos, float* acc, int cur_pos,
+                          int heavy, int recent, float scale, float* out, float* lse, int32_t* evict_out, void* ws,
+                          hipStream_t s) {
+  const int units = c.batch * c.n_kv_heads, G = c.n_q_heads / c.n_kv_heads;
+  char* ws_att = (char*)ws;
+  float* lg_ws = (float*)(ws_att + r256(attn_append_ws_bytes(c, c.capacity, 1)));
+  float* lse_ws = (float*)((char*)lg_ws + r256(size_t(c.batch) * c.n_q_heads * c.capacity * sizeof(float)));
+  float* lse_o = lse ? lse : lse_ws;
+  AttnArgs a = make_attn_args(c, q, k, v, seq_len, nullptr, nullptr, 0, 1, scale, out, lse_o, nullptr, 0);
+  const bool fused = attn_mfma_supported(a) && int64_t(G) * c.capacity <= ATTN_H2O_LDS_LOGITS &&
+                     c.capacity <= 256 * ATTN_H2O_SLOTS_PER_THREAD;
+  if (!fused) {   // other shapes: append, attention with logits, accumulate + evict (the same results)
+    se_status st = launch_kv_append(c, k, v, k_new, v_new, slot_in, seq_len, s);
+    if (st != SE_OK) return st;
+    st = launch_attn(c, q, k, v, seq_len, nullptr, nullptr, 0, 1, scale, out, lse_o, lg_ws, c.capacity, 1,
+                     ws_att + attn_row_ctr_bytes(c), s, nullptr, nullptr);
+    if (st != SE_OK) return st;
+    hipLaunchKernelGGL(copy_or_fill_i32_kernel, dim3(ceil_div(units, 256)), dim3(256), 0, s, evict_out, slot_in, units);
+    if (hipGetLastError() != hipSuccess) return SE_ERR_HIP;
+    return launch_h2o(c, lg_ws, lse_o, c.capacity, seq_len, slot_pos, acc, cur_pos, heavy, recent, evict_out, s);
+  }
+  a.splits = 1;
+  a.counters = (int*)(ws_att + attn_row_ctr_bytes(c));
+  a.part_ml = (float*)((char*)a.counters + attn_counter_bytes(c));
+  a.part_o = a.part_ml + size_t(units) * G * 2;
+  a.fused = 0;
+  a.logit_cap = c.capacity;
+  a.app = 1;
+  a.k_new = k_new; a.v_new = v_new; a.k_w = k; a.v_w = v;
+  a.slot = slot_in; a.seq_len_w = seq_len; a.row_ctr = (int*)ws_att;
+  a.h2o = 1;
+  a.h2o_pos = slot_pos; a.h2o_acc = acc; a.h2o_evict = evict_out;
+  a.h2o_cur = cur_pos; a.h2o_heavy = heavy; a.h2o_recent = recent;
+  return launch_attn_mfma(a, s);
+}
+
 se_status launch_attn(const se_cache& c, const void* q, const void* k, const void* v,
                       const int32_t* seq_len, const int32_t* view_idx, const int32_t* view_len,
                       int view_cap, int granularity, float scale, float* out, float* lse,

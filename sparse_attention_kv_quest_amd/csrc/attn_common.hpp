@@ -40,7 +40,15 @@ struct AttnArgs {
   // cache (the rule of the separate top-k launch); split 0 writes the view to
   // sel_view / sel_vlen when they are given; the new length is stored as for app.
   const float* sel_score; int sel_ncp; int32_t* sel_view; int32_t* sel_vlen; int sel;
+  // H2O decode step (h2o != 0, with app, the identity view and one split): the
+  // logits stay in LDS and, after the attention, the block runs the unit's
+  // accumulate-then-evict (se_h2o_accumulate_evict's rule) on h2o_pos / h2o_acc,
+  // the slot that received the token being slot[unit] (or seq_len - 1), and
+  // writes the evicted slot (or -1) to h2o_evict.
+  int32_t* h2o_pos; float* h2o_acc; int32_t* h2o_evict; int h2o_cur, h2o_heavy, h2o_recent, h2o;
 };
+constexpr int ATTN_H2O_LDS_LOGITS = 12288;   // G * capacity logits held in LDS by the H2O step
+constexpr int ATTN_H2O_SLOTS_PER_THREAD = 8;   // capacity <= 256 * this
 
 // Number of view slots of a unit: view entries times granularity, or seq_len for the identity view.
 __device__ __forceinline__ int view_slot_count(const AttnArgs& a, int unit, int b) {

@@ -360,12 +360,16 @@ __device__ __forceinline__ void mf_step(const AttnArgs& a, const MfCtx& x, int b
 // LG: logits requested.  Launches without them compile the logits path out, which
 // keeps the register budget (a spill here costs far more than its few bytes).
 // SEL > 0: the page view is selected in the launch (AttnArgs::sel), SEL keys per
-// thread (up to 256 SEL pages).
-template <int D, bool VC, int OCC, bool F8, bool APP, bool LG, int SEL = 0>
+// thread (up to 256 SEL pages).  H2O: the H2O decode step (AttnArgs::h2o): the
+// logits go to LDS, then the unit's accumulate-then-evict runs in the block.
+template <int D, bool VC, int OCC, bool F8, bool APP, bool LG, int SEL = 0, bool H2O = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void attn_mfma_kernel(AttnArgs a) {
   static_assert(!(APP && F8), "the fused append writes bf16 rows");
   static_assert(SEL == 0 || (VC && !APP && !F8 && !LG), "in-launch selection: page views over bf16 rows");
+  static_assert(!H2O || (APP && LG && !VC && SEL == 0), "the H2O step: fused append, identity view, logits");
+  __shared__ float lg_unit[H2O ? ATTN_H2O_LDS_LOGITS : 1];   // [head][slot], row pitch logit_cap
+  __shared__ float h2o_lse[H2O ? 16 : 1];
   constexpr int PITCH = MF_TS + 4;          // u16 per transposed V row (72 bytes)
   constexpr int NDB = D / 16;
   constexpr int NKS = D / 32;
@@ -507,7 +511,7 @@ void attn_mfma_kernel(AttnArgs a) {
   uint16_t* vt = vt_lds[w];   // row pitch PITCH, D rows
   float* lgs = LG ? lg_lds[w] : nullptr;
   // the group's first logits row (head h at + h * logit_cap), or null: wave-uniform
-  float* lg_base = LG ? a.logits + (size_t(b) * a.Hq + size_t(kvh) * G) * a.logit_cap : nullptr;
+  float* lg_base = H2O ? lg_unit : LG ? a.logits + (size_t(b) * a.Hq + size_t(kvh) * G) * a.logit_cap : nullptr;
 
   // This wave's tiles are w, w + 4, ...  The steady-state loop runs only while
   // every tile it prefetches exists: its loads are unconditional and an
@@ -635,6 +639,7 @@ void attn_mfma_kernel(AttnArgs a) {
       const float inv = L > 0.f ? 1.f / L : 0.f;
       *reinterpret_cast<f32x4*>(a.out + row * D + d0) = O * inv;
       if (d0 == 0 && a.lse != nullptr) a.lse[row] = L > 0.f ? Mn + logf(L) : -INFINITY;
+      if (H2O && d0 == 0) h2o_lse[h] = L > 0.f ? Mn + logf(L) : -INFINITY;
     } else if (a.fused) {
       st_dev2(po + h * D + d0, O[0], O[1]);
       st_dev2(po + h * D + d0 + 2, O[2], O[3]);
@@ -648,6 +653,91 @@ void attn_mfma_kernel(AttnArgs a) {
   if (a.fused) {
     int* ctr = a.counters + unit * ATTN_MAX_HG;
     if (attn_split_done(ctr, a.splits)) attn_merge_splits<256>(a, unit, 0, G, ctr);
+  }
+  if constexpr (H2O) {
+    // the H2O accumulate-then-evict of this unit, as se_h2o_accumulate_evict (h2o_reg_kernel)
+    // computes it from the logits and lse of the attention: the same operations in the same
+    // order, with the logits read from LDS instead of memory
+    __syncthreads();   // every tile's logits and the heads' lse are in LDS
+    constexpr int HE = ATTN_H2O_SLOTS_PER_THREAD;
+    __shared__ int h2o_cnt[MF_WAVES], h2o_slot[MF_WAVES];
+    __shared__ uint32_t h2o_hi[MF_WAVES], h2o_lo[MF_WAVES];
+    const int n = len;
+    int32_t* pos = a.h2o_pos + size_t(unit) * a.cap;
+    float* acc = a.h2o_acc + size_t(unit) * a.cap;
+    const int in = a.slot != nullptr ? a.slot[unit] : -1;
+    const int ns = in >= 0 ? in : n - 1;   // the slot that received the token at cur_pos
+    if (threadIdx.x == 0 && ns >= n && ns < a.cap) { pos[ns] = a.h2o_cur; acc[ns] = 0.f; }
+    int p[HE];
+    float sc[HE];
+#pragma unroll
+    for (int j = 0; j < HE; ++j) {
+      const int sl = max(min(j * 256 + int(threadIdx.x), n - 1), 0);
+      p[j] = pos[sl];
+      sc[j] = acc[sl];
+    }
+#pragma unroll
+    for (int j = 0; j < HE; ++j) {
+      const int sl = j * 256 + threadIdx.x;
+      if (sl >= n) { p[j] = -1; sc[j] = 0.f; }
+      if (sl == ns) { p[j] = a.h2o_cur; sc[j] = 0.f; }
+    }
+    for (int hh = 0; hh < G; ++hh) {   // heads in ascending order
+      const float l = h2o_lse[hh];
+      if (l == -INFINITY) continue;
+#pragma unroll
+      for (int j = 0; j < HE; ++j) {
+        const int sl = min(j * 256 + int(threadIdx.x), a.logit_cap - 1);
+        if (p[j] >= 0) sc[j] += expf(lg_unit[hh * a.logit_cap + sl] - l);
+      }
+    }
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < HE; ++j) {
+      const int sl = j * 256 + threadIdx.x;
+      if (sl < n) {
+        if (sl == ns) pos[sl] = a.h2o_cur;
+        if (p[j] >= 0) acc[sl] = sc[j];
+        else if (sl == ns) acc[sl] = 0.f;
+        cnt += p[j] >= 0;
+      }
+    }
+    cnt = wave_sum_i(cnt);
+    if (lane == 0) h2o_cnt[w] = cnt;
+    __syncthreads();
+    const int occupied = h2o_cnt[0] + h2o_cnt[1] + h2o_cnt[2] + h2o_cnt[3];
+    if (occupied <= a.h2o_heavy + a.h2o_recent) {
+      if (threadIdx.x == 0) a.h2o_evict[unit] = -1;
+    } else {
+      // argmin of (score, position) over the slots outside the recent window
+      uint32_t bh = ~0u, bl = ~0u;
+      int bs = -1;
+#pragma unroll
+      for (int j = 0; j < HE; ++j) {
+        const int sl = j * 256 + threadIdx.x;
+        if (sl < n && p[j] >= 0 && p[j] <= a.h2o_cur - a.h2o_recent) {
+          const uint32_t hkey = ordered_bits(sc[j]), lkey = uint32_t(p[j]);
+          if (hkey < bh || (hkey == bh && lkey < bl)) { bh = hkey; bl = lkey; bs = sl; }
+        }
+      }
+      const uint32_t wh = wave_last(wave_incl_scan_dpp(bh, ~0u, [](uint32_t x, uint32_t y) { return x < y ? x : y; }));
+      const uint32_t wl = wave_last(wave_incl_scan_dpp(bh == wh ? bl : ~0u, ~0u,
+                                                       [](uint32_t x, uint32_t y) { return x < y ? x : y; }));
+      const uint64_t hit = __ballot(bh == wh && bl == wl && bs >= 0);
+      const int wsl = hit ? __builtin_amdgcn_readlane(bs, __ffsll((unsigned long long)hit) - 1) : -1;
+      if (lane == 0) { h2o_hi[w] = wh; h2o_lo[w] = wl; h2o_slot[w] = wsl; }
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        uint32_t kh = h2o_hi[0], kl = h2o_lo[0];
+        int ev = h2o_slot[0];
+        for (int i = 1; i < MF_WAVES; ++i)
+          if (h2o_slot[i] >= 0 && (ev < 0 || h2o_hi[i] < kh || (h2o_hi[i] == kh && h2o_lo[i] < kl))) {
+            kh = h2o_hi[i]; kl = h2o_lo[i]; ev = h2o_slot[i];
+          }
+        if (ev >= 0) { pos[ev] = -1; acc[ev] = 0.f; }
+        a.h2o_evict[unit] = ev;
+      }
+    }
   }
   if ((APP || SEL > 0) && threadIdx.x == 0 && row_ticket == a.Hkv * a.splits - 1) {   // every block of the row has read it
     if (len != len0) a.seq_len_w[b] = len;
@@ -683,6 +773,14 @@ int attn_mfma_sel_keys(int ncp) { return ncp <= 256 * 4 ? 4 : ncp <= 256 * 9 ? 9
 
 se_status launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.splits, a.B * a.Hkv);
+  if (a.h2o) {   // the H2O decode step: fused append, identity view, logits in LDS, one split
+    if (a.splits != 1 || !a.app || a.view_idx != nullptr) return SE_ERR_UNSUPPORTED;
+    if (a.Dk == 128)
+      hipLaunchKernelGGL((attn_mfma_kernel<128, false, 2, false, true, true, 0, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_mfma_kernel<64, false, 1, false, true, true, 0, true>), grid, dim3(256), 0, s, a);
+    return launch_status();
+  }
   if (a.sel) {   // page views selected in the launch (the Quest decode step)
 #define SE_SEL(DD, OO, EE) hipLaunchKernelGGL((attn_mfma_kernel<DD, true, OO, false, false, false, EE>), grid, dim3(256), \
                                               0, s, a)

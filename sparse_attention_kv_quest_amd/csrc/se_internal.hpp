@@ -480,6 +480,11 @@ se_status launch_kv_append_meta(const se_cache& c, void* k, void* v, const void*
 size_t quest_ws_bytes(const se_cache& c, int page_size, int top_pages);
 size_t quest_append_ws_bytes(const se_cache& c, int page_size);
 size_t quest_step_ws_bytes(const se_cache& c, int page_size, int top_pages);
+size_t h2o_step_ws_bytes(const se_cache& c);
+se_status launch_h2o_step(const se_cache& c, const void* q, void* k, void* v, const void* k_new, const void* v_new,
+                          const int32_t* slot_in, int32_t* seq_len, int32_t* slot_pos, float* acc, int cur_pos,
+                          int heavy, int recent, float scale, float* out, float* lse, int32_t* evict_out, void* ws,
+                          hipStream_t s);
 se_status launch_quest_append_scores(const se_cache& c, const void* q, void* k, void* v, const void* k_new,
                                      const void* v_new, const int32_t* seq_len, void* kmin, void* kmax, int page_size,
                                      float* page_score, void* ws, float** score_out, hipStream_t s);

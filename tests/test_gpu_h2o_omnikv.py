@@ -91,10 +91,10 @@ def test_h2o_tiny_all_units_all_steps(se, fused):
 
 
 def test_h2o_16k_all_units(se):
-    """The 16K H2O workload at full size through the bench's step (the append into the
-    freed slot and the attention with logits in one launch, then accumulate + evict):
-    every unit's evicted slot, slot positions, scores and output compared with the
-    oracle at every one of the 128 steps."""
+    """The 16K H2O workload at full size through the bench's call (se_h2o_decode_step:
+    the append into the freed slot, the attention and the accumulate + evict in one
+    launch): every unit's evicted slot, slot positions, scores and output compared
+    with the oracle at every one of the 128 steps."""
     from tests import oracle_pool
     from tests.parity_jobs import h2o_unit
     cfg = h2o_config(True)
@@ -115,20 +115,20 @@ def test_h2o_16k_all_units(se):
     k, v = dev(K, torch.bfloat16), dev(V, torch.bfloat16)
     slot_pos, acc_d = dev(pos, torch.int32), dev(acc)
     seq = torch.full((B,), cap, dtype=torch.int32, device="cuda")
-    evict = torch.full((B, H), cap - 1, dtype=torch.int32, device="cuda")
-    out, lse, logits = zeros((B, Hq, D)), zeros((B, Hq)), zeros((B, Hq, cap))
-    ws = se.workspace(se.SE_OP_APPEND_ATTN, c, cap, 0)
+    ev = [torch.full((B, H), cap - 1, dtype=torch.int32, device="cuda"),
+          torch.full((B, H), -1, dtype=torch.int32, device="cuda")]
+    out, lse = zeros((B, Hq, D)), zeros((B, Hq))
+    ws = se.workspace(se.SE_OP_H2O_STEP, c, 0, 0)
     g_ev = np.zeros((T, B, H), np.int32)
     g_pos = np.zeros((T, B, H, cap), np.int32)
     g_acc = np.zeros((T, B, H, cap), np.float32)
     g_out = np.zeros((T, B, Hq, D), np.float32)
     for t in range(T):
         q, kn, vn = h2o_step_inputs(cfg, t, att)
-        se.se_kv_append_decode_attn(c, dev(q, torch.bfloat16), k, v, dev(kn, torch.bfloat16), dev(vn, torch.bfloat16),
-                                    evict, seq, None, None, 0, 1, cfg.softmax_scale, out, lse, logits, cap, 0, ws)
-        se.se_h2o_accumulate_evict(c, logits, lse, cap, seq, slot_pos, acc_d, cfg.context + t, cfg.h2o_heavy,
-                                   cfg.h2o_recent, evict)
-        g_ev[t], g_pos[t], g_acc[t], g_out[t] = host(evict), host(slot_pos), host(acc_d), host(out)
+        se.se_h2o_decode_step(c, dev(q, torch.bfloat16), k, v, dev(kn, torch.bfloat16), dev(vn, torch.bfloat16),
+                              ev[t % 2], seq, slot_pos, acc_d, cfg.context + t, cfg.h2o_heavy, cfg.h2o_recent,
+                              cfg.softmax_scale, out, lse, ev[(t + 1) % 2], ws)
+        g_ev[t], g_pos[t], g_acc[t], g_out[t] = host(ev[(t + 1) % 2]), host(slot_pos), host(acc_d), host(out)
     banner("h2o 16K: comparing with the oracle")
     for u, job in enumerate(jobs):
         r = job.result()
@@ -166,21 +166,22 @@ def test_h2o_16k_resume_from_saved_state(se):
     c = se.cache(B, Hq, H, D, D, cap, "bf16")
     state = dict(k=dev(K, torch.bfloat16), v=dev(V, torch.bfloat16), slot_pos=dev(pos, torch.int32), acc=dev(acc),
                  seq=torch.full((B,), cap, dtype=torch.int32, device="cuda"),
-                 evict=torch.full((B, H), cap - 1, dtype=torch.int32, device="cuda"))
-    ws = se.workspace(se.SE_OP_APPEND_ATTN, c, cap, 0)
+                 ev0=torch.full((B, H), cap - 1, dtype=torch.int32, device="cuda"),
+                 ev1=torch.full((B, H), -1, dtype=torch.int32, device="cuda"))
+    ws = se.workspace(se.SE_OP_H2O_STEP, c, 0, 0)
 
     def run(st, steps):
         outs = []
-        out, lse, logits = zeros((B, Hq, D)), zeros((B, Hq)), zeros((B, Hq, cap))
+        out, lse = zeros((B, Hq, D)), zeros((B, Hq))
         for t in steps:
             q, kn, vn = h2o_step_inputs(cfg, t)
-            se.se_kv_append_decode_attn(c, dev(q, torch.bfloat16), st["k"], st["v"], dev(kn, torch.bfloat16),
-                                        dev(vn, torch.bfloat16), st["evict"], st["seq"], None, None, 0, 1,
-                                        cfg.softmax_scale, out, lse, logits, cap, 0, ws)
-            se.se_h2o_accumulate_evict(c, logits, lse, cap, st["seq"], st["slot_pos"], st["acc"], cfg.context + t,
-                                       cfg.h2o_heavy, cfg.h2o_recent, st["evict"])
+            ev_in, ev_out = (st["ev0"], st["ev1"]) if t % 2 == 0 else (st["ev1"], st["ev0"])
+            se.se_h2o_decode_step(c, dev(q, torch.bfloat16), st["k"], st["v"], dev(kn, torch.bfloat16),
+                                  dev(vn, torch.bfloat16), ev_in, st["seq"], st["slot_pos"], st["acc"],
+                                  cfg.context + t, cfg.h2o_heavy, cfg.h2o_recent, cfg.softmax_scale, out, lse, ev_out,
+                                  ws)
             outs.append(torch.cat([out.flatten().view(torch.int32), lse.flatten().view(torch.int32),
-                                   st["evict"].flatten()]).cpu())
+                                   ev_out.flatten()]).cpu())
         torch.cuda.synchronize()
         return outs, {n: t.cpu() for n, t in st.items()}
 
