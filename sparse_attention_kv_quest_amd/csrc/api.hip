@@ -5,6 +5,7 @@
 #include <stdlib.h>
 
 #include <mutex>
+#include <vector>
 
 using namespace se;
 
@@ -24,6 +25,40 @@ bool trace_on() {
     on = (e && e[0] && e[0] != '0') ? 1 : 0;
   }
   return on == 1;
+}
+
+// Debug mode (SE_CHECK_VIEWS=1 in the environment, read once): the attention calls
+// synchronise the stream, copy the view and its lengths to the host and check every
+// entry in use (view_len within [0, view_cap], each entry >= 0 with its first slot
+// inside the cache's capacity; entries past seq_len are allowed, their slots are
+// skipped) before launching; a bad view returns SE_ERR_SHAPE and launches nothing.
+// Not for graph capture.
+bool check_views_on() {
+  static int on = -1;
+  if (on < 0) {
+    const char* e = getenv("SE_CHECK_VIEWS");
+    on = (e && e[0] && e[0] != '0') ? 1 : 0;
+  }
+  return on == 1;
+}
+
+se_status check_view_host(const se_cache* c, const int32_t* view_idx, const int32_t* view_len, int32_t view_cap,
+                          int32_t granularity, hipStream_t stream) {
+  const int units = c->batch * c->n_kv_heads;
+  std::vector<int32_t> v(size_t(units) * view_cap), vl(units);
+  if (hipStreamSynchronize(stream) != hipSuccess ||
+      hipMemcpy(v.data(), view_idx, v.size() * sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(vl.data(), view_len, vl.size() * sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess)
+    return SE_ERR_HIP;
+  for (int u = 0; u < units; ++u) {
+    const int n = vl[u];
+    if (n < 0 || n > view_cap) return SE_ERR_SHAPE;
+    for (int e = 0; e < n; ++e) {
+      const int32_t x = v[size_t(u) * view_cap + e];
+      if (x < 0 || int64_t(x) * granularity >= c->capacity) return SE_ERR_SHAPE;
+    }
+  }
+  return SE_OK;
 }
 
 #define SE_TRACE_CALL(...)                                  \
@@ -80,6 +115,10 @@ se_status attn_impl(const se_cache* c, const void* q, const void* k, const void*
                                logit_cap, num_splits, &need);
   if (st != SE_OK) return st;
   if (!ws || ws_bytes < need) return SE_ERR_WORKSPACE;
+  if (view_idx && check_views_on()) {
+    st = check_view_host(c, view_idx, view_len, view_cap, granularity, stream);
+    if (st != SE_OK) return st;
+  }
   SE_TRACE_CALL("sparse_decode_attn%s B=%d Hq=%d Hkv=%d d_k=%d d_v=%d view=%s cap=%d g=%d splits=%d logits=%d",
                 k_scale ? "_fp8" : "", c->batch, c->n_q_heads, c->n_kv_heads, c->d_k, c->d_v, view_idx ? "idx" : "identity",
                 view_cap, granularity, num_splits, logits ? logit_cap : 0);
