@@ -652,11 +652,11 @@ def run_quest_fp8(se, torch, args):
     vn = dev_grid(torch, (B, H, D), 5102, torch.bfloat16)
     lse = torch.empty((B, Hq), device="cuda")
     ws_q = se.workspace(se.SE_OP_QUEST, c, P, k)
-    ws_a = se.workspace(se.SE_OP_ATTN, c, k * P, 0)
+    ws_a = se.workspace(se.SE_OP_ATTN, c, k * P, args.splits)
 
     def attn(Ly):
         se.se_sparse_decode_attn_fp8(c, q, Ly["kq"], Ly["vq"], Ly["ks"], Ly["vs"], Ly["seq"], Ly["view"], Ly["vlen"], k,
-                                     P, cfg.softmax_scale, Ly["out"], lse, ws=ws_a)
+                                     P, cfg.softmax_scale, Ly["out"], lse, num_splits=args.splits, ws=ws_a)
 
     def step(Ly):
         se.se_kv_append_fp8(c, Ly["kq"], Ly["vq"], Ly["ks"], Ly["vs"], kn, vn, Ly["seq"], Ly["kmin"], Ly["kmax"], P)
