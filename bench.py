@@ -526,14 +526,16 @@ def run_mla(se, torch, args):
     q = dev_grid(torch, (B, Hq, D), 3900, torch.bfloat16)
     kn = dev_grid(torch, (B, 1, D), 3901, torch.bfloat16)
     lse = torch.empty((B, Hq), device="cuda")
-    ws_q = se.workspace(se.SE_OP_QUEST_APPEND, c, P, 0)
+    ws_s = se.workspace(se.SE_OP_QUEST_STEP, c, P, k)
     ws_a = se.workspace(se.SE_OP_ATTN, c, k * P, 0)
 
     def step(Ly):
-        se.se_quest_append_select(c, q, Ly["c"], None, kn, None, Ly["seq"], Ly["kmin"], Ly["kmax"], P, k, Ly["view"],
-                                  Ly["vlen"], None, ws_q)
-        se.se_sparse_decode_attn(c, q, Ly["c"], None, Ly["seq"], Ly["view"], Ly["vlen"], k, P, cfg.softmax_scale,
-                                 Ly["out"], lse, ws=ws_a)
+        """One decode step (se_quest_decode_step: launch 1 appends the latent row, folds it
+        into its page's min / max and scores every page; launch 2 selects each row's top
+        pages and attends over them; the split combine).  The view is written for the
+        attention-alone timing below."""
+        se.se_quest_decode_step(c, q, Ly["c"], None, kn, None, Ly["seq"], Ly["kmin"], Ly["kmax"], P, k,
+                                cfg.softmax_scale, Ly["out"], lse, Ly["view"], Ly["vlen"], None, ws_s)
 
     def attn(Ly):
         se.se_sparse_decode_attn(c, q, Ly["c"], None, Ly["seq"], Ly["view"], Ly["vlen"], k, P, cfg.softmax_scale,

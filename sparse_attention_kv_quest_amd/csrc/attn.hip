@@ -322,9 +322,12 @@ se_status launch_quest_step(const se_cache& c, const void* q, void* k, void* v, 
   a.gshift = -1;
   for (int sh = 0; sh < 31; ++sh)
     if ((1 << sh) == page_size) { a.gshift = sh; break; }
-  const bool fused = c.dtype == SE_BF16 && !c.latent && (c.d_k == 128 || c.d_k == 64) && G <= 16 &&
-                     attn_mfma_sel_keys(ncp) > 0 && top_pages <= 2048 &&
-                     a.gshift >= 0 && attn_mfma_supported(a);
+  // GQA: attn_mfma_kernel; latent rows: attn_mla_pf_kernel (groups of 17..32 heads)
+  const bool gqa = c.dtype == SE_BF16 && !c.latent && (c.d_k == 128 || c.d_k == 64) && G <= 16 &&
+                   attn_mfma_sel_keys(ncp) > 0 && top_pages <= 2048 && a.gshift >= 0 && attn_mfma_supported(a);
+  const bool mla = c.dtype == SE_BF16 && c.latent && c.d_k == 576 && c.d_v == 512 && G > 16 && G <= 32 &&
+                   attn_mla_sel_keys(ncp) > 0 && top_pages <= 1024 && a.gshift >= 0 && attn_mla_supported(a);
+  const bool fused = gqa || mla;
   if (!fused) {   // other shapes: the append + selection call, then the attention call (same results)
     int32_t* vi = view_idx ? view_idx : (int32_t*)ws_view;
     int32_t* vl = view_len ? view_len : (int32_t*)ws_view + size_t(units) * top_pages;
@@ -348,12 +351,12 @@ se_status launch_quest_step(const se_cache& c, const void* q, void* k, void* v, 
   a.fused = a.splits > 1 && size_t(a.splits) * std::min(a.G, 32) * a.Dv * sizeof(float) <= ATTN_FUSED_MERGE_BYTES;
   a.row_ctr = (int*)ws_att;
   a.seq_len_w = seq_len;
-  a.sel = attn_mfma_sel_keys(ncp);
+  a.sel = gqa ? attn_mfma_sel_keys(ncp) : attn_mla_sel_keys(ncp);
   a.sel_score = score;
   a.sel_ncp = ncp;
   a.sel_view = view_idx;
   a.sel_vlen = view_len;
-  st = launch_attn_mfma(a, s);
+  st = gqa ? launch_attn_mfma(a, s) : launch_attn_mla(a, s);
   if (st != SE_OK || a.splits == 1 || a.fused) return st;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(a.G, a.B * a.Hkv), dim3(128), 0, s, a);
   return launch_status();

@@ -175,6 +175,7 @@ se_status launch_attn_mla(const AttnArgs& a, hipStream_t s);
 int attn_mfma_auto_splits(int units, int slots);
 se_status launch_attn_mfma(const AttnArgs& a, hipStream_t s);
 int attn_mfma_sel_keys(int ncp);
+int attn_mla_sel_keys(int ncp);
 
 inline bool attn_mfma_eligible(const se_cache& c) {
   return c.dtype == SE_BF16 && !c.latent && (c.d_k == 128 || c.d_k == 64) && c.d_v == c.d_k &&

@@ -27,6 +27,13 @@
 //
 // Each split stores a partial (max, sum, output), which the combine kernel
 // merges (or, for small partials, the block finishing the last split).
+//
+// SEL > 0 (attn_mla_pf_kernel, the fused Quest decode step over latent rows):
+// the page view is selected inside the launch from the page scores the scoring
+// launch wrote (every block of a unit selects the same pages: the register
+// top-k of block_topk_keys, SEL keys per thread), the scores' loads going out
+// with q's; the row appended by the scoring launch is counted, and the last
+// block of a batch row stores the new length.
 #include "attn_common.hpp"
 #include "mfma_util.hpp"
 
@@ -407,6 +414,7 @@ __device__ __forceinline__ int mp_load(const MlCtx& x, const int32_t* vcache, in
   return tk;
 }
 
+template <int SEL>
 __global__ __launch_bounds__(ML_THREADS) void attn_mla_pf_kernel(AttnArgs a) {
   __shared__ __align__(16) unsigned char lds[MP_LDS_BYTES];
   __shared__ float wmax[4][32];
@@ -423,10 +431,19 @@ __global__ __launch_bounds__(ML_THREADS) void attn_mla_pf_kernel(AttnArgs a) {
   const int unit = blockIdx.y, split = blockIdx.x, hg = blockIdx.z;
   const int b = unit / a.Hkv, kvh = unit % a.Hkv;
   const int G = a.G, h0 = 32 * hg;
-  const bool identity = a.view_idx == nullptr;
-  const int len = min(a.seq_len[b], a.cap);
+  const bool identity = SEL == 0 && a.view_idx == nullptr;
+  // in-launch selection: the unit's page scores, loaded first (their addresses depend
+  // on kernel arguments alone), masked by the page count once the length is known
+  float sraw[SEL > 0 ? SEL : 1];
+  if constexpr (SEL > 0) {
+    const float* srow = a.sel_score + size_t(unit) * a.sel_ncp;
+#pragma unroll
+    for (int j = 0; j < SEL; ++j) sraw[j] = srow[min(topk_reg_index<ML_THREADS, SEL>(j), a.sel_ncp - 1)];
+  }
+  const int len0 = min(a.seq_len[b], a.cap);
+  const int len = (SEL > 0 && len0 < a.cap) ? len0 + 1 : len0;   // the row the scoring launch appended
   const int n_slots = identity ? len : a.view_cap * a.gran;
-  const int s_valid = identity ? len : min(a.view_len[unit], a.view_cap) * a.gran;
+  const int s_valid = identity ? len : (SEL > 0 ? 0 : min(a.view_len[unit], a.view_cap) * a.gran);
   int chunk = (n_slots + a.splits - 1) / a.splits;
   chunk = (chunk + MP_TS - 1) / MP_TS * MP_TS;
   const int s0 = min(n_slots, split * chunk), s1 = min(n_slots, s0 + chunk);
@@ -457,7 +474,7 @@ __global__ __launch_bounds__(ML_THREADS) void attn_mla_pf_kernel(AttnArgs a) {
   constexpr int VR = ML_VCACHE / ML_THREADS;
   int32_t ve[VR];
   int e0 = 0, e1 = 0;
-  if (!identity) {
+  if (!identity && SEL == 0) {
     const int32_t* vrow = a.view_idx + size_t(unit) * a.view_cap;
     e0 = s0 >> a.gshift;
     e1 = s1 > s0 ? ((s1 - 1) >> a.gshift) + 1 : e0;
@@ -473,14 +490,34 @@ __global__ __launch_bounds__(ML_THREADS) void attn_mla_pf_kernel(AttnArgs a) {
     const int i = threadIdx.x + r * ML_THREADS;
     if (i < QN) reinterpret_cast<u32x4*>(lds)[i] = qv[r];
   }
-  if (!identity) {
+  if (!identity && SEL == 0) {
 #pragma unroll
     for (int r = 0; r < VR; ++r) {
       const int e = e0 + threadIdx.x + r * ML_THREADS;
       if (e < e1) vcache[e - e0] = ve[r];
     }
   }
+  int sel_len = 0;
+  if constexpr (SEL > 0) {
+    // the unit's top pages by score, ascending, straight into the view cache (the
+    // value tile is not in use yet and holds the selection's histograms)
+    using SelShared = TopkRegSharedN<ML_WAVES>;
+    static_assert(sizeof(SelShared) <= MP_V_BYTES, "selection scratch");
+    SelShared& tsh = *reinterpret_cast<SelShared*>(lds + ML_Q_BYTES);
+    const int npages = min((len + a.gran - 1) >> a.gshift, a.sel_ncp);
+    uint32_t key[SEL > 0 ? SEL : 1];
+#pragma unroll
+    for (int j = 0; j < SEL; ++j) key[j] = topk_reg_index<ML_THREADS, SEL>(j) < npages ? ordered_bits(sraw[j]) : 0u;
+    sel_len = block_topk_keys<ML_THREADS, SEL, SelShared>(key, npages, a.view_cap, vcache, tsh);
+  }
   __syncthreads();
+  if constexpr (SEL > 0) {
+    x.s1 = min(s1, min(sel_len, a.view_cap) * a.gran);
+    if (split == 0 && hg == 0 && a.sel_view != nullptr) {
+      for (int i = threadIdx.x; i < a.view_cap; i += ML_THREADS) a.sel_view[size_t(unit) * a.view_cap + i] = vcache[i];
+      if (threadIdx.x == 0) a.sel_vlen[unit] = sel_len;
+    }
+  }
   u32x4 kb0[MP_KH], kb1[MP_KH];
   // unconditional (slots past the split read row 0): the loop's wait counts stay exact
   int tk0 = mp_load(x, vcache, s0, sg, ch, lane, kb0), tk1 = -1;
@@ -612,6 +649,12 @@ __global__ __launch_bounds__(ML_THREADS) void attn_mla_pf_kernel(AttnArgs a) {
     step(kb0, tk0, kb1, tk1, it, NoPf{});
   }
 
+  int row_ticket = 0;
+  if (SEL > 0 && threadIdx.x == 0) {
+    // every block of the batch row takes a ticket, long after it read the old length;
+    // the last one stores the new length at the end
+    row_ticket = __hip_atomic_fetch_add(a.row_ctr + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   // ---- sums over lanes and slot groups (every wave shares the same running max)
   {
     const float s = rows4_sum(lsum);
@@ -674,6 +717,15 @@ __global__ __launch_bounds__(ML_THREADS) void attn_mla_pf_kernel(AttnArgs a) {
     int* ctr = a.counters + unit * ATTN_MAX_HG + hg;
     if (attn_split_done(ctr, a.splits)) attn_merge_splits<ML_THREADS>(a, unit, h0, min(32, G - h0), ctr);
   }
+  if (SEL > 0 && threadIdx.x == 0 && row_ticket == a.Hkv * a.splits * int(gridDim.z) - 1) {   // all have read it
+    if (len != len0) a.seq_len_w[b] = len;
+    ticket_reset(a.row_ctr + b);
+  }
+}
+
+// Keys per thread of the in-launch page selection for sel_ncp pages (0: too many).
+int attn_mla_sel_keys(int ncp) {
+  return ncp <= ML_THREADS * 4 ? 4 : ncp <= ML_THREADS * 8 ? 8 : ncp <= ML_THREADS * 16 ? 16 : 0;
 }
 
 bool attn_mla_supported(const AttnArgs& a) {
@@ -699,10 +751,17 @@ int attn_mla_auto_splits(int units, int G, int slots) {
 
 se_status launch_attn_mla(const AttnArgs& a, hipStream_t s) {
   dim3 grid(a.splits, a.B * a.Hkv, (a.G + 31) / 32);
-  if (a.G <= 16)
+  if (a.sel) {   // the fused decode step: groups of 17..32 heads, a view that fits the view cache
+    const int e = attn_mla_sel_keys(a.sel_ncp);
+    if (a.G <= 16 || a.G > 32 || a.view_cap > ML_VCACHE || a.gshift < 0 || e == 0) return SE_ERR_UNSUPPORTED;
+    if (e == 4) hipLaunchKernelGGL((attn_mla_pf_kernel<4>), grid, dim3(ML_THREADS), 0, s, a);
+    else if (e == 8) hipLaunchKernelGGL((attn_mla_pf_kernel<8>), grid, dim3(ML_THREADS), 0, s, a);
+    else hipLaunchKernelGGL((attn_mla_pf_kernel<16>), grid, dim3(ML_THREADS), 0, s, a);
+  } else if (a.G <= 16) {
     hipLaunchKernelGGL((attn_mla_kernel<1>), grid, dim3(ML_THREADS), 0, s, a);
-  else
-    hipLaunchKernelGGL(attn_mla_pf_kernel, grid, dim3(ML_THREADS), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((attn_mla_pf_kernel<0>), grid, dim3(ML_THREADS), 0, s, a);
+  }
   return launch_status();
 }
 

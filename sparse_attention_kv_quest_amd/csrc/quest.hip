@@ -252,12 +252,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // w, w + 4, ..  (its group gi starts at page p_blk + 16 (w + 4 gi))
   const int p_blk = blockIdx.x * ppb, p_end = min(ncp, p_blk + ppb);
   auto grp_page = [&](int gi) { return p_blk + 16 * (w + 4 * gi); };
-  // chunk r of group gi; pages past the valid ones (and groups past the block's)
-  // read page 0: unconditional loads keep the wait counts exact; their bounds are
-  // masked or not stored
+  // chunk r of group gi; pages past the valid ones or past the block's own (the
+  // next block's) read page 0, which stays in cache: unconditional loads keep the
+  // wait counts exact; their bounds are masked or not stored
+  const int p_load = min(npages, p_end);
   auto chunk_ptr = [&](int gi, int r) -> const uint16_t* {
     const int pg = grp_page(gi) + c16;
-    const size_t row = size_t(unit) * ncp + (pg < npages ? pg : 0);
+    const size_t row = size_t(unit) * ncp + (pg < p_load ? pg : 0);
     return (r < NKS ? kmax : kmin) + row * D + 8 * g + 32 * (r % NKS);
   };
   // q first (each 16-byte piece feeds both the q+ and the q- entry), then the
@@ -540,10 +541,11 @@ size_t quest_append_ws_bytes(const se_cache& c, int page_size) {
   return (ctr + 255) / 256 * 256 + quest_ws_bytes(c, page_size, 0);
 }
 
-// The first launch of the fused Quest decode step (bf16 GQA, d_k 64 / 128, G <= 16):
-// the new rows, the appended page's min / max and every page's score (into
-// page_score, else the workspace, after its batch-row counters); seq_len is left
-// for the step's attention launch to update.
+// The first launch of the fused Quest decode step (bf16 GQA with d_k 64 / 128 and
+// G <= 16, or bf16 latent rows of 576 with G <= 32): the new rows, the appended
+// page's min / max and every page's score (into page_score, else the workspace,
+// after its batch-row counters); seq_len is left for the step's attention launch
+// to update.
 se_status launch_quest_append_scores(const se_cache& c, const void* q, void* k, void* v, const void* k_new,
                                      const void* v_new, const int32_t* seq_len, void* kmin, void* kmax, int page_size,
                                      float* page_score, void* ws, float** score_out, hipStream_t s) {
@@ -552,9 +554,14 @@ se_status launch_quest_append_scores(const se_cache& c, const void* q, void* k, 
   const size_t ctr_bytes = (size_t(c.batch) * sizeof(int) + 255) / 256 * 256;
   float* score = page_score ? page_score : (float*)((char*)ws + ctr_bytes);
   QuestAppendArgs ap{};
-  ap.k = (uint16_t*)k; ap.v = (uint16_t*)v;
-  ap.k_new = (const uint16_t*)k_new; ap.v_new = (const uint16_t*)v_new;
+  ap.k = (uint16_t*)k; ap.v = c.latent ? nullptr : (uint16_t*)v;
+  ap.k_new = (const uint16_t*)k_new; ap.v_new = c.latent ? nullptr : (const uint16_t*)v_new;
   ap.kmin_w = (uint16_t*)kmin; ap.kmax_w = (uint16_t*)kmax;
+  if (c.dtype == SE_BF16 && c.latent && c.d_k == 576 && G <= 32) {
+    launch_score_ring576<true>(c, q, kmin, kmax, seq_len, score, page_size, ncp, ap, s);
+    *score_out = score;
+    return launch_status();
+  }
   const dim3 grid(ceil_div(ncp, 64), units);
 #define SE_AP(DD) hipLaunchKernelGGL((quest_score_mfma_kernel<DD, 1, true>), grid, dim3(256), 0, s, (const uint16_t*)q, \
                                      (const uint16_t*)kmin, (const uint16_t*)kmax, seq_len, score, c.n_kv_heads, G,  \

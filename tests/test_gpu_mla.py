@@ -13,9 +13,10 @@ from workloads import get_config
 pytestmark = pytest.mark.gpu
 
 
-def run_mla(se, cfg, units, steps=1, fused=False):
-    """fused: append, metadata, scores and view through se_quest_append_select (the
-    bench's call) instead of se_kv_append, se_page_meta_update, se_quest_select."""
+def run_mla(se, cfg, units, steps=1, mode="separate"):
+    """mode "separate": se_kv_append, se_page_meta_update, se_quest_select, then the
+    attention; "fused": se_quest_append_select, then the attention; "step": the whole
+    decode step in se_quest_decode_step (the bench's call)."""
     B, Hq, D, Dv, P, k = cfg.batch, cfg.n_q_heads, cfg.d_k, cfg.d_v, cfg.page_size, cfg.top_pages
     cap = cfg.context + steps
     C, _ = gen.cache_kv(cfg, 0, cap)                       # [B][1][cap][576]
@@ -32,13 +33,18 @@ def run_mla(se, cfg, units, steps=1, fused=False):
     ws_q = se.workspace(se.SE_OP_QUEST, c, P, k)
     ws_qa = se.workspace(se.SE_OP_QUEST_APPEND, c, P, 0)
     ws_a = se.workspace(se.SE_OP_ATTN, c, k * P, 0)
+    ws_s = se.workspace(se.SE_OP_QUEST_STEP, c, P, k)
     se.se_page_meta_update(c, cd, kmin, kmax, seq, P, 0)
     for s in range(steps):
         q = gen.decode_query(cfg, 0, s)                     # [B][32][576]
         kn, _ = gen.decode_kv_new(cfg, 0, s)
         C[:, :, cfg.context + s] = kn
         qd = dev(q, torch.bfloat16)
-        if fused:
+        if mode == "step":
+            se.se_quest_decode_step(c, qd, cd, None, dev(kn, torch.bfloat16), None, seq, kmin, kmax, P, k,
+                                    cfg.softmax_scale, out, lse, view, vlen, score, ws_s)
+            continue
+        if mode == "fused":
             se.se_quest_append_select(c, qd, cd, None, dev(kn, torch.bfloat16), None, seq, kmin, kmax, P, k, view,
                                       vlen, score, ws_qa)
         else:
@@ -64,18 +70,19 @@ def run_mla(se, cfg, units, steps=1, fused=False):
         np.testing.assert_allclose(g["lse"][b], rlse[0], rtol=0, atol=TOL["bf16"])
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_mla_small_all_units(se, fused):
+@pytest.mark.parametrize("mode", ["separate", "fused", "step"])
+def test_mla_small_all_units(se, mode):
     cfg = get_config(4, batch=3, context=3000, top_pages=8)
-    banner(f"mla small fused={fused}")
-    run_mla(se, cfg, range(cfg.batch), steps=3, fused=fused)
+    banner(f"mla small {mode}")
+    run_mla(se, cfg, range(cfg.batch), steps=3, mode=mode)
 
 
 def test_mla_128k_all_rows(se):
-    """The 128K MLA workload at full size through the bench's calls (the fused append +
-    selection, then the latent attention): 64 decode steps, every batch row compared
-    with the oracle at steps 0, 1, 31 and 63 (metadata by digest, page scores and views
-    exactly, output and lse at the bf16 tolerance)."""
+    """The 128K MLA workload at full size through the bench's call (se_quest_decode_step:
+    the scoring launch with the append, then the attention launch that selects the
+    pages itself): 64 decode steps, every batch row compared with the oracle at steps
+    0, 1, 31 and 63 (metadata by digest, page scores and views exactly, output and lse
+    at the bf16 tolerance)."""
     from concurrent.futures import ThreadPoolExecutor
     from tests import oracle_pool
     from tests.parity_jobs import digest, mla_row
@@ -98,16 +105,14 @@ def test_mla_128k_all_rows(se):
     vlen = torch.zeros((B, 1), dtype=torch.int32, device="cuda")
     score = torch.zeros((B, 1, ncp), device="cuda")
     out, lse = zeros((B, Hq, Dv)), zeros((B, Hq))
-    ws_qa = se.workspace(se.SE_OP_QUEST_APPEND, c, P, 0)
-    ws_a = se.workspace(se.SE_OP_ATTN, c, k * P, 0)
+    ws_s = se.workspace(se.SE_OP_QUEST_STEP, c, P, k)
     se.se_page_meta_update(c, cd, kmin, kmax, seq, P, 0)
     got = {}
     for s in range(cfg.decode_steps):
         qd = dev(gen.decode_query(cfg, 0, s), torch.bfloat16)
         kn, _ = gen.decode_kv_new(cfg, 0, s)
-        se.se_quest_append_select(c, qd, cd, None, dev(kn, torch.bfloat16), None, seq, kmin, kmax, P, k, view, vlen,
-                                  score, ws_qa)
-        se.se_sparse_decode_attn(c, qd, cd, None, seq, view, vlen, k, P, cfg.softmax_scale, out, lse, ws=ws_a)
+        se.se_quest_decode_step(c, qd, cd, None, dev(kn, torch.bfloat16), None, seq, kmin, kmax, P, k,
+                                cfg.softmax_scale, out, lse, view, vlen, score, ws_s)
         if s in checks:
             torch.cuda.synchronize()
             L = cfg.context + s + 1
