@@ -193,25 +193,21 @@ __device__ __forceinline__ void mf_load_f8(const MfCtx& x, int base, int lane, M
   }
 }
 
-// FP8 tile -> the bf16 operands of the MFMA tile (stored values, exact).
+// The MFMA operands of a tile: bf16 tiles as loaded; FP8 tiles converted at their use
+// (K per k-step, V per pass), so no converted copy of a whole tile is held.
 template <int D>
-__device__ __forceinline__ void mf_convert(const MfTileF8<D>& T, MfTile<D>& B) {
-  constexpr int NKS = D / 32, VPASS = D / 64;
-  const float s0 = mf_scale(T.ks0), s1 = mf_scale(T.ks1);
-#pragma unroll
-  for (int c = 0; c < NKS; ++c) {   // k-step c: bytes 8c .. 8c + 7 of the lane's span
-    const int j = c / 2, w = 2 * (c % 2);
-    B.k0[c] = mf_cvt8(T.k0[j][w], T.k0[j][w + 1], s0);
-    B.k1[c] = mf_cvt8(T.k1[j][w], T.k1[j][w + 1], s1);
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float sv = mf_scale(T.vs[r]);
-#pragma unroll
-    for (int p = 0; p < VPASS; ++p) B.v[p][r] = mf_cvt8(T.v[p][r].x, T.v[p][r].y, sv);
-  }
-  B.tk0 = T.tk0;
-  B.tk1 = T.tk1;
+__device__ __forceinline__ u32x4 mf_kop(const MfTile<D>& T, int half, int c) { return half ? T.k1[c] : T.k0[c]; }
+template <int D>
+__device__ __forceinline__ u32x4 mf_kop(const MfTileF8<D>& T, int half, int c) {
+  const int j = c / 2, w = 2 * (c % 2);   // k-step c: bytes 8c .. 8c + 7 of the lane's span
+  const u32x4& src = half ? T.k1[j] : T.k0[j];
+  return mf_cvt8(src[w], src[w + 1], mf_scale(half ? T.ks1 : T.ks0));
+}
+template <int D>
+__device__ __forceinline__ u32x4 mf_vop(const MfTile<D>& T, int pp, int r) { return T.v[pp][r]; }
+template <int D>
+__device__ __forceinline__ u32x4 mf_vop(const MfTileF8<D>& T, int pp, int r) {
+  return mf_cvt8(T.v[pp][r].x, T.v[pp][r].y, mf_scale(T.vs[r]));
 }
 
 template <int D>
@@ -220,9 +216,9 @@ struct MfState {
   float m2, lsum;
 };
 
-template <int D>
+template <int D, class TT>
 __device__ __forceinline__ void mf_compute(const AttnArgs& a, const MfCtx& x, int base, int lane, const u32x4* qv,
-                                           float sc2, float* lg_base, float* lgs, uint16_t* vt, const MfTile<D>& T,
+                                           float sc2, float* lg_base, float* lgs, uint16_t* vt, const TT& T,
                                            MfState<D>& st) {
   constexpr int NKS = D / 32, NDB = D / 16, VPASS = D / 64, PITCH = MF_TS + 4;
   const int g = lane >> 4, c16 = lane & 15, qa = lane & 7;
@@ -230,8 +226,8 @@ __device__ __forceinline__ void mf_compute(const AttnArgs& a, const MfCtx& x, in
   f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < NKS; ++c) {
-    sa = mfma_bf16_16x16x32(T.k0[c], qv[c], sa);
-    sb = mfma_bf16_16x16x32(T.k1[c], qv[c], sb);
+    sa = mfma_bf16_16x16x32(mf_kop<D>(T, 0, c), qv[c], sa);
+    sb = mfma_bf16_16x16x32(mf_kop<D>(T, 1, c), qv[c], sb);
   }
   const uint64_t va = __ballot(T.tk0 >= 0), vb = __ballot(T.tk1 >= 0);
   float sv[8];
@@ -293,9 +289,12 @@ __device__ __forceinline__ void mf_compute(const AttnArgs& a, const MfCtx& x, in
 #pragma unroll
   for (int pp = 0; pp < VPASS; ++pp) {
     const int ch = (lane >> 3) + 8 * pp;
+    u32x4 vv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vv[r] = mf_vop<D>(T, pp, r);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const uint32_t w0 = T.v[pp][0][m], w1 = T.v[pp][1][m], w2 = T.v[pp][2][m], w3 = T.v[pp][3][m];
+      const uint32_t w0 = vv[0][m], w1 = vv[1][m], w2 = vv[2][m], w3 = vv[3][m];
       uint2 lo, hi;
       lo.x = lo16_pair(w0, w1);
       lo.y = lo16_pair(w2, w3);
@@ -348,13 +347,7 @@ template <int D, bool F8>
 __device__ __forceinline__ void mf_step(const AttnArgs& a, const MfCtx& x, int base, int lane, const u32x4* qv,
                                         float sc2, float* lg_base, float* lgs, uint16_t* vt, const MfRaw<D, F8>& T,
                                         MfState<D>& st) {
-  if constexpr (F8) {
-    MfTile<D> B;
-    mf_convert<D>(T, B);
-    mf_compute<D>(a, x, base, lane, qv, sc2, lg_base, lgs, vt, B, st);
-  } else {
-    mf_compute<D>(a, x, base, lane, qv, sc2, lg_base, lgs, vt, T, st);
-  }
+  mf_compute<D>(a, x, base, lane, qv, sc2, lg_base, lgs, vt, T, st);
 }
 
 // LG: logits requested.  Launches without them compile the logits path out, which
