@@ -87,8 +87,10 @@ __device__ __forceinline__ uint32_t bf16x2_fmin(uint32_t acc, uint32_t x, bool m
   return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
 }
 
+// Eight blocks per CU for one head block: a Quest 32K grid (2112 blocks) then takes
+// one round of the GPU but for 64 blocks, where seven per CU left 320 for a second.
 template <int D, int HB, bool APP>
-__global__ __launch_bounds__(256) void quest_score_mfma_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HB == 1 ? 8 : 1, 8))) void quest_score_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* kmin, const uint16_t* kmax,
     const int32_t* seq_len, float* score, int Hkv, int G, int P, int ncp, int cap, QuestAppendArgs ap) {
   constexpr int NKS = D / 32;
