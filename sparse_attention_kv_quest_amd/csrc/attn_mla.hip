@@ -485,11 +485,14 @@ __global__ __launch_bounds__(ML_THREADS) void attn_mla_pf_kernel(AttnArgs a) {
     }
     x.e0 = e0;
   }
+  auto stage_q = [&]() {
 #pragma unroll
-  for (int r = 0; r < QR; ++r) {
-    const int i = threadIdx.x + r * ML_THREADS;
-    if (i < QN) reinterpret_cast<u32x4*>(lds)[i] = qv[r];
-  }
+    for (int r = 0; r < QR; ++r) {
+      const int i = threadIdx.x + r * ML_THREADS;
+      if (i < QN) reinterpret_cast<u32x4*>(lds)[i] = qv[r];
+    }
+  };
+  if constexpr (SEL == 0) stage_q();
   if (!identity && SEL == 0) {
 #pragma unroll
     for (int r = 0; r < VR; ++r) {
@@ -509,6 +512,7 @@ __global__ __launch_bounds__(ML_THREADS) void attn_mla_pf_kernel(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < SEL; ++j) key[j] = topk_reg_index<ML_THREADS, SEL>(j) < npages ? ordered_bits(sraw[j]) : 0u;
     sel_len = block_topk_keys<ML_THREADS, SEL, SelShared>(key, npages, a.view_cap, vcache, tsh);
+    stage_q();   // after the selection: q's loads return while it runs
   }
   __syncthreads();
   if constexpr (SEL > 0) {

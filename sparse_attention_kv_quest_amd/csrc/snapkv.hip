@@ -115,25 +115,33 @@ __global__ __launch_bounds__(256) void snap_mfma_kernel(SnapArgs a) {
           f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int c = 0; c < NKS; ++c) s = mfma_bf16_16x16x32(kc[c], qv[rb][c], s);
-          float v[4];
           if (blk < plain) {
+            // no mask: the block max scaled once (sc2 > 0 and rounding is monotonic, so
+            // it equals the max of the scaled logits) and each term as one fma
+            const float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])) * a.sc2;
+            if (bm > m[rb] + SK_MARGIN) {
+              l[rb] *= (m[rb] == -INFINITY) ? 0.f : ex2(m[rb] - bm);
+              m[rb] = bm;
+            }
+            const float nref = m[rb] == -INFINITY ? 0.f : -m[rb];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = s[i] * a.sc2;
+            for (int i = 0; i < 4; ++i) l[rb] += ex2(fmaf(s[i], a.sc2, nref));
           } else {
+            float v[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int key = kb + 4 * g + i;
               v[i] = key < k1 && key <= rowpos[rb] ? s[i] * a.sc2 : -INFINITY;
             }
-          }
-          const float bm = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
-          if (bm > m[rb] + SK_MARGIN) {
-            l[rb] *= (m[rb] == -INFINITY) ? 0.f : ex2(m[rb] - bm);
-            m[rb] = bm;
-          }
-          const float mref = m[rb] == -INFINITY ? 0.f : m[rb];
+            const float bm = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+            if (bm > m[rb] + SK_MARGIN) {
+              l[rb] *= (m[rb] == -INFINITY) ? 0.f : ex2(m[rb] - bm);
+              m[rb] = bm;
+            }
+            const float mref = m[rb] == -INFINITY ? 0.f : m[rb];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) l[rb] += ex2(v[i] - mref);
+            for (int i = 0; i < 4; ++i) l[rb] += ex2(v[i] - mref);
+          }
         }
       } else {
         // S[row][key]: lane (g, c16) holds rows 4g + i of key kb + c16, so a key's sum
