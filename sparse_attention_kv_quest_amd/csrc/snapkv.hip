@@ -13,6 +13,8 @@
 // bf16 caches score them on MFMA in two passes over K: pass A forms each row's
 // log-sum-exp (split over key chunks, then merged), pass B sums the softmax
 // weights per key.  fp32 caches use vector kernels.
+#include <type_traits>
+
 #include "se_internal.hpp"
 #include "mfma_util.hpp"
 
@@ -33,6 +35,19 @@ struct SnapArgs {
   int B, Hq, Hkv, G, D, cap, out_cap, L, W, R, pool, budget, nchunks, dtype;
   float sc2;   // scale * log2(e)
 };
+
+// The lazy running max of pass A: moved (and the sum rescaled) only when a block's
+// max exceeds it by more than the margin.  The branch is taken by the whole wave when
+// any lane moves (rare once the rows' maxima settle), so no lane's registers are
+// shuffled through divergent control flow; lanes that do not move keep m and l.
+__device__ __forceinline__ void sk_grow(float bm, float& m, float& l) {
+  const bool grow = bm > m + SK_MARGIN;
+  if (__ballot(grow) != 0) {
+    const float f = (m == -INFINITY) ? 0.f : ex2(m - bm);
+    l = grow ? l * f : l;
+    m = grow ? bm : m;
+  }
+}
 
 // ------------------------------------------------------------------ MFMA passes (bf16)
 // grid (chunks, units); 4 waves, each owning NRB 16-row blocks of the R = 64 * NRB rows.
@@ -97,67 +112,77 @@ __global__ __launch_bounds__(256) void snap_mfma_kernel(SnapArgs a) {
   fetch(0);
   put(0);
   __syncthreads();
+  // One 16-key block of a tile.  PLAIN (pass A): no key of the block is past k1 or
+  // past any row's position, so no mask is formed.
+  auto key_block = [&](int buf, int sb, int blk, auto plain_c) {
+    constexpr bool PLAIN = decltype(plain_c)::value;
+    u32x4 kc[NKS];
+#pragma unroll
+    for (int c = 0; c < NKS; ++c) kc[c] = *reinterpret_cast<const u32x4*>(&kt[buf][16 * sb + c16][8 * g + 32 * c]);
+    const int kb = k0 + blk * 16;
+    if constexpr (!PASS_B) {
+      // S^T[key][row]: lane (g, c16) holds keys kb + 4g + i of row c16
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NKS; ++c) s = mfma_bf16_16x16x32(kc[c], qv[rb][c], s);
+        if constexpr (PLAIN) {
+          // the block max scaled once (sc2 > 0 and rounding is monotonic, so it equals
+          // the max of the scaled logits) and each term as one fma
+          const float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])) * a.sc2;
+          sk_grow(bm, m[rb], l[rb]);
+          const float nref = m[rb] == -INFINITY ? 0.f : -m[rb];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) l[rb] += ex2(fmaf(s[i], a.sc2, nref));
+        } else {
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kb + 4 * g + i;
+            v[i] = key < k1 && key <= rowpos[rb] ? s[i] * a.sc2 : -INFINITY;
+          }
+          const float bm = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+          sk_grow(bm, m[rb], l[rb]);
+          const float mref = m[rb] == -INFINITY ? 0.f : m[rb];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) l[rb] += ex2(v[i] - mref);
+        }
+      }
+    } else {
+      // S[row][key]: lane (g, c16) holds rows 4g + i of key kb + c16, so a key's sum
+      // over the wave's rows stays in its lane until two exchanges across g.
+      // History keys precede every window row: only keys past k1 are dropped.
+      float vote = 0.f;
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NKS; ++c) s = mfma_bf16_16x16x32(qv[rb][c], kc[c], s);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vote += ex2(fmaf(s[i], a.sc2, nlse[rb][i]));
+      }
+      vote = rows4_sum(vote);
+      if (g == 0) vsum[w][blk][c16] = kb + c16 < k1 ? vote : 0.f;
+    }
+  };
+  using Plain = std::integral_constant<bool, true>;
+  using Masked = std::integral_constant<bool, false>;
   for (int t = 0; t < ntile; ++t) {
     const int buf = t & 1;
     if (t + 1 < ntile) fetch(t + 1);
+    // tiles whose four blocks all need no mask (and exist) take one straight-line body;
+    // the chunk's last tiles take the general one (uniform across the block)
+    if ((t + 1) * (SK_KT / 16) <= (PASS_B ? nblk : plain)) {
 #pragma unroll
-    for (int sb = 0; sb < SK_KT / 16; ++sb) {
-      const int blk = t * (SK_KT / 16) + sb;
-      if (blk >= nblk) break;                          // uniform across the block
-      u32x4 kc[NKS];
+      for (int sb = 0; sb < SK_KT / 16; ++sb) key_block(buf, sb, t * (SK_KT / 16) + sb, Plain{});
+    } else {
 #pragma unroll
-      for (int c = 0; c < NKS; ++c) kc[c] = *reinterpret_cast<const u32x4*>(&kt[buf][16 * sb + c16][8 * g + 32 * c]);
-      const int kb = k0 + blk * 16;
-      if (!PASS_B) {
-        // S^T[key][row]: lane (g, c16) holds keys kb + 4g + i of row c16
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-          f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int c = 0; c < NKS; ++c) s = mfma_bf16_16x16x32(kc[c], qv[rb][c], s);
-          if (blk < plain) {
-            // no mask: the block max scaled once (sc2 > 0 and rounding is monotonic, so
-            // it equals the max of the scaled logits) and each term as one fma
-            const float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])) * a.sc2;
-            if (bm > m[rb] + SK_MARGIN) {
-              l[rb] *= (m[rb] == -INFINITY) ? 0.f : ex2(m[rb] - bm);
-              m[rb] = bm;
-            }
-            const float nref = m[rb] == -INFINITY ? 0.f : -m[rb];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) l[rb] += ex2(fmaf(s[i], a.sc2, nref));
-          } else {
-            float v[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = kb + 4 * g + i;
-              v[i] = key < k1 && key <= rowpos[rb] ? s[i] * a.sc2 : -INFINITY;
-            }
-            const float bm = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
-            if (bm > m[rb] + SK_MARGIN) {
-              l[rb] *= (m[rb] == -INFINITY) ? 0.f : ex2(m[rb] - bm);
-              m[rb] = bm;
-            }
-            const float mref = m[rb] == -INFINITY ? 0.f : m[rb];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) l[rb] += ex2(v[i] - mref);
-          }
-        }
-      } else {
-        // S[row][key]: lane (g, c16) holds rows 4g + i of key kb + c16, so a key's sum
-        // over the wave's rows stays in its lane until two exchanges across g.
-        // History keys precede every window row: only keys past k1 are dropped.
-        float vote = 0.f;
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-          f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int c = 0; c < NKS; ++c) s = mfma_bf16_16x16x32(qv[rb][c], kc[c], s);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) vote += ex2(fmaf(s[i], a.sc2, nlse[rb][i]));
-        }
-        vote = rows4_sum(vote);
-        if (g == 0) vsum[w][blk][c16] = kb + c16 < k1 ? vote : 0.f;
+      for (int sb = 0; sb < SK_KT / 16; ++sb) {
+        const int blk = t * (SK_KT / 16) + sb;
+        if (blk >= nblk) break;
+        if (PASS_B || blk < plain) key_block(buf, sb, blk, Plain{});
+        else key_block(buf, sb, blk, Masked{});
       }
     }
     if (t + 1 < ntile) put(buf ^ 1);
