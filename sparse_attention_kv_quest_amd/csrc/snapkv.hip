@@ -60,7 +60,7 @@ template <int D, int NRB, bool PASS_B>
 __global__ __launch_bounds__(256) void snap_mfma_kernel(SnapArgs a) {
   constexpr int NKS = D / 32, PITCH = D + 8, CH = D / 8, TPT = SK_KT * CH / 256;
   __shared__ __align__(16) uint16_t kt[2][SK_KT][PITCH];
-  __shared__ float vsum[4][SK_CHUNK / 16][16];   // pass B: per-wave key sums of each 16-key block
+  __shared__ float vsum[PASS_B ? 4 : 1][SK_CHUNK / 16][16];   // pass B: per-wave key sums of each 16-key block
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
   const int unit = blockIdx.y, chunk = blockIdx.x;
   const int b = unit / a.Hkv, kvh = unit % a.Hkv;

@@ -5,8 +5,8 @@ metadata, seq_len, page scores, views, outputs and lse.  Shapes that run the
 in-launch selection (d_k 128 and 64, ragged and fresh pages, a full cache, page
 counts across the selection's key-per-thread variants; MLA latent rows with 32
 heads, including more pages than the view holds and a view longer than the
-pages) and shapes that run the two calls' kernels (fp32, latent rows with 16
-heads, a non-power-of-two page size).  The
+pages, and a group of 24 heads) and shapes that run the two calls' kernels
+(fp32, latent rows with 16 heads, a non-power-of-two page size).  The
 step call's results against the oracle are checked at full size in
 test_gpu_quest.py."""
 import numpy as np
@@ -35,6 +35,7 @@ CASES = {
     "mla_latent": (get_config(4, batch=2, context=1000, page_size=64, top_pages=5), 3),
     "mla_latent_2200_pages": (get_config(4, batch=1, context=140700, page_size=64, top_pages=64), 2),
     "mla_latent_ragged_view": (get_config(4, batch=3, context=900, page_size=64, top_pages=40), 3),
+    "mla_g24_latent": (get_config(4, batch=2, n_q_heads=24, context=2000, page_size=64, top_pages=9), 3),
     "mla_g16_fallback": (get_config(4, batch=2, n_q_heads=16, context=1000, page_size=64, top_pages=5), 3),
     "page_12_fallback": (get_config(0, dtype="bf16", batch=2, n_q_heads=8, n_kv_heads=2, d_k=128, d_v=128,
                                     context=300, page_size=12, top_pages=6), 3),
