@@ -653,7 +653,7 @@ def run_quest_fp8(se, torch, args):
     kn = dev_grid(torch, (B, H, D), 5101, torch.bfloat16)
     vn = dev_grid(torch, (B, H, D), 5102, torch.bfloat16)
     lse = torch.empty((B, Hq), device="cuda")
-    ws_q = se.workspace(se.SE_OP_QUEST, c, P, k)
+    ws_s = se.workspace(se.SE_OP_QUEST_STEP, c, P, k)
     ws_a = se.workspace(se.SE_OP_ATTN, c, k * P, args.splits)
 
     def attn(Ly):
@@ -661,9 +661,13 @@ def run_quest_fp8(se, torch, args):
                                      P, cfg.softmax_scale, Ly["out"], lse, num_splits=args.splits, ws=ws_a)
 
     def step(Ly):
-        se.se_kv_append_fp8(c, Ly["kq"], Ly["vq"], Ly["ks"], Ly["vs"], kn, vn, Ly["seq"], Ly["kmin"], Ly["kmax"], P)
-        se.se_quest_select(c, q, Ly["kmin"], Ly["kmax"], Ly["seq"], P, k, Ly["view"], Ly["vlen"], None, ws_q)
-        attn(Ly)
+        """One decode step over FP8 rows (se_quest_decode_step_fp8: launch 1 quantizes the
+        new rows, folds their stored K values into the page's min / max and scores every
+        page; launch 2 selects the pages and attends over the FP8 rows).  The view is
+        written for the attention-alone timing."""
+        se.se_quest_decode_step_fp8(c, q, Ly["kq"], Ly["vq"], Ly["ks"], Ly["vs"], kn, vn, Ly["seq"], Ly["kmin"],
+                                    Ly["kmax"], P, k, cfg.softmax_scale, Ly["out"], lse, Ly["view"], Ly["vlen"], None,
+                                    ws_s)
 
     for Ly in lay:
         step(Ly)

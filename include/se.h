@@ -230,6 +230,21 @@ se_status se_sparse_decode_attn_fp8(const se_cache* c, const void* q, const void
                                     int32_t logit_cap, int32_t num_splits, void* ws, size_t ws_bytes,
                                     hipStream_t stream);
 
+/* The Quest decode step over FP8 rows: se_kv_append_fp8, se_quest_select (over
+ * the stored values' page metadata) and se_sparse_decode_attn_fp8 in one call,
+ * with bit-identical results (codes, scale bytes, kmin / kmax, seq_len, page
+ * scores, views, out, lse).  Arguments as in those calls; view_idx / view_len
+ * (both or neither) and page_score are optional outputs.  Workspace:
+ * se_workspace_bytes(SE_OP_QUEST_STEP, c, page_size, top_pages), 16-byte aligned,
+ * zero-filled once before first use; the call leaves its counters at zero.  GQA
+ * with d_k 64 or 128, G <= 16 and a power-of-two page size, as the FP8 attention
+ * (SE_ERR_UNSUPPORTED otherwise, before anything is written). */
+se_status se_quest_decode_step_fp8(const se_cache* c, const void* q, void* k_q, void* v_q, uint8_t* k_scale,
+                                   uint8_t* v_scale, const void* k_new, const void* v_new, int32_t* seq_len,
+                                   void* kmin, void* kmax, int32_t page_size, int32_t top_pages, float scale,
+                                   float* out, float* lse, int32_t* view_idx, int32_t* view_len, float* page_score,
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* StreamingLLM view (Netics blog "SparseEngine 统一接入十五种稀疏注意力", section
  * "哪些情况下加速幅度会缩小": named there beside PyramidKV and SnapKV).  Unit
  * (b, h) attends over the first `sink` and the last `recent` positions below

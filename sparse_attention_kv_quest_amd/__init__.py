@@ -25,7 +25,7 @@ STATUS = {0: "SE_OK", -1: "SE_ERR_NULL", -2: "SE_ERR_SHAPE", -3: "SE_ERR_DTYPE",
 EXPORTS = ("se_kv_append", "se_kv_append_meta", "se_page_meta_update", "se_quest_select", "se_quest_append_select",
            "se_quest_decode_step",
            "se_sparse_decode_attn", "se_sparse_decode_attn_noalloc", "se_kv_append_decode_attn", "se_streaming_view", "se_pyramid_budgets",
-           "se_kv_quantize_fp8", "se_kv_append_fp8", "se_sparse_decode_attn_fp8",
+           "se_kv_quantize_fp8", "se_kv_append_fp8", "se_sparse_decode_attn_fp8", "se_quest_decode_step_fp8",
            "se_chain_match", "se_chain_remap", "se_chain_append_positions", "se_h2o_prefill_init", "se_h2o_decode_step",
            "se_snapkv_score_compact", "se_h2o_accumulate_evict", "se_omnikv_topk",
            "se_workspace_bytes", "se_workspace_init", "se_status_string", "se_abi_version")
@@ -60,6 +60,8 @@ _SIGS = {
     "se_streaming_view": [_C, _P, _I32, _I32, _P, _P, _I32, _I32, _P],
     "se_kv_quantize_fp8": [_C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P],
     "se_kv_append_fp8": [_C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P],
+    "se_quest_decode_step_fp8": [_C, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _F32, _P, _P, _P, _P, _P, _P,
+                                 _SZ, _P],
     "se_sparse_decode_attn_fp8": [_C, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _F32, _P, _P, _P, _I32, _I32, _P, _SZ,
                                   _P],
     "se_pyramid_budgets": [_I32, _I32, _I32, _P],
@@ -196,6 +198,14 @@ def se_quest_decode_step(c, q, k, v, k_new, v_new, seq_len, kmin, kmax, page_siz
         ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(k_new), _ptr(v_new), _ptr(seq_len), _ptr(kmin), _ptr(kmax),
         page_size, top_pages, scale, _ptr(out), _ptr(lse), _ptr(view_idx), _ptr(view_len), _ptr(page_score), _ptr(ws),
         _nbytes(ws), _stream(stream)))
+
+
+def se_quest_decode_step_fp8(c, q, k_q, v_q, k_scale, v_scale, k_new, v_new, seq_len, kmin, kmax, page_size, top_pages,
+                             scale, out, lse=None, view_idx=None, view_len=None, page_score=None, ws=None, stream=None):
+    _check("se_quest_decode_step_fp8", load().se_quest_decode_step_fp8(
+        ctypes.byref(c), _ptr(q), _ptr(k_q), _ptr(v_q), _ptr(k_scale), _ptr(v_scale), _ptr(k_new), _ptr(v_new),
+        _ptr(seq_len), _ptr(kmin), _ptr(kmax), page_size, top_pages, scale, _ptr(out), _ptr(lse), _ptr(view_idx),
+        _ptr(view_len), _ptr(page_score), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def se_kv_quantize_fp8(c, k, v, seq_len, k_q, v_q, k_scale, v_scale, kmin=None, kmax=None, page_size=0,

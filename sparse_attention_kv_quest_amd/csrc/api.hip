@@ -316,6 +316,32 @@ se_status check_fp8_cache(const se_cache* c) {
   return SE_OK;
 }
 
+se_status se_quest_decode_step_fp8(const se_cache* c, const void* q, void* k_q, void* v_q, uint8_t* k_scale,
+                                   uint8_t* v_scale, const void* k_new, const void* v_new, int32_t* seq_len,
+                                   void* kmin, void* kmax, int32_t page_size, int32_t top_pages, float scale,
+                                   float* out, float* lse, int32_t* view_idx, int32_t* view_len, float* page_score,
+                                   void* ws, size_t ws_bytes, hipStream_t stream) {
+  se_status st = check_fp8_cache(c);
+  if (st != SE_OK) return st;
+  if (c->n_q_heads / c->n_kv_heads > 16) return SE_ERR_UNSUPPORTED;
+  if (!q || !k_q || !v_q || !k_scale || !v_scale || !k_new || !v_new || !seq_len || !kmin || !kmax || !out || !ws)
+    return SE_ERR_NULL;
+  if ((view_idx == nullptr) != (view_len == nullptr)) return SE_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_q) || !aligned16(v_q) || !aligned16(k_new) || !aligned16(v_new) ||
+      !aligned16(kmin) || !aligned16(kmax) || !aligned16(ws) || !aligned16(out))
+    return SE_ERR_ALIGN;
+  if (page_size <= 0 || page_size > c->capacity) return SE_ERR_SHAPE;
+  if (top_pages < 1) return SE_ERR_BUDGET;
+  if (int64_t(top_pages) * page_size > (int64_t(1) << 30)) return SE_ERR_SHAPE;
+  if (!(scale > 0.f) || !(scale < 1e30f)) return SE_ERR_SHAPE;
+  if (ws_bytes < quest_step_ws_bytes(*c, page_size, top_pages)) return SE_ERR_WORKSPACE;
+  SE_TRACE_CALL("quest_decode_step_fp8 B=%d Hq=%d Hkv=%d d_k=%d P=%d k=%d", c->batch, c->n_q_heads, c->n_kv_heads,
+                c->d_k, page_size, top_pages);
+  clear_stale_error();
+  return launch_quest_step_fp8(*c, q, k_q, v_q, k_scale, v_scale, k_new, v_new, seq_len, kmin, kmax, page_size,
+                               top_pages, scale, out, lse, view_idx, view_len, page_score, ws, stream);
+}
+
 se_status se_kv_quantize_fp8(const se_cache* c, const void* k, const void* v, const int32_t* seq_len, void* k_q,
                              void* v_q, uint8_t* k_scale, uint8_t* v_scale, void* kmin, void* kmax, int32_t page_size,
                              hipStream_t stream) {

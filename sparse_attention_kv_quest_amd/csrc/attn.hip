@@ -362,6 +362,67 @@ se_status launch_quest_step(const se_cache& c, const void* q, void* k, void* v, 
   return launch_status();
 }
 
+// The Quest decode step over FP8 rows, in the same two launches and workspace as
+// launch_quest_step: launch 1 quantizes the new rows, folds the stored K values into
+// the appended page's min / max and scores every page; launch 2 selects each unit's
+// pages and attends over the FP8 rows; other shapes run the separate calls' kernels.
+se_status launch_quest_step_fp8(const se_cache& c, const void* q, void* kq, void* vq, uint8_t* ks, uint8_t* vs,
+                                const void* k_new, const void* v_new, int32_t* seq_len, void* kmin, void* kmax,
+                                int page_size, int top_pages, float scale, float* out, float* lse, int32_t* view_idx,
+                                int32_t* view_len, float* page_score, void* ws, hipStream_t s) {
+  const int units = c.batch * c.n_kv_heads, G = c.n_q_heads / c.n_kv_heads;
+  const int ncp = ceil_div(c.capacity, page_size);
+  char* ws_sel = (char*)ws;
+  char* ws_att = ws_sel + r256(quest_append_ws_bytes(c, page_size));
+  char* ws_view = ws_att + r256(attn_append_ws_bytes(c, top_pages * page_size, 0));
+  AttnArgs a = make_attn_args(c, q, kq, vq, seq_len, nullptr, nullptr, 0, 1, scale, out, lse, nullptr, 0);
+  a.k_scale = ks;
+  a.v_scale = vs;
+  a.fp8 = true;
+  a.view_cap = top_pages;
+  a.gran = page_size;
+  a.gshift = -1;
+  for (int sh = 0; sh < 31; ++sh)
+    if ((1 << sh) == page_size) { a.gshift = sh; break; }
+  // the attention over FP8 rows runs on the MFMA kernel only, over power-of-two page
+  // views: reject anything else before anything is written
+  if (a.gshift < 0 || !attn_mfma_supported(a)) return SE_ERR_UNSUPPORTED;
+  const bool fused = c.dtype == SE_BF16 && !c.latent && (c.d_k == 128 || c.d_k == 64) && G <= 16 &&
+                     attn_mfma_sel_keys(ncp) > 0 && top_pages <= 2048 && a.gshift >= 0;
+  if (!fused) {   // other shapes: the three calls' kernels (same results)
+    int32_t* vi = view_idx ? view_idx : (int32_t*)ws_view;
+    int32_t* vl = view_len ? view_len : (int32_t*)ws_view + size_t(units) * top_pages;
+    se_status st = launch_fp8_append(c, kq, vq, ks, vs, k_new, v_new, seq_len, kmin, kmax, page_size, s);
+    if (st != SE_OK) return st;
+    const size_t ctr_bytes = r256(size_t(c.batch) * sizeof(int));
+    st = launch_quest(c, q, kmin, kmax, seq_len, page_size, top_pages, vi, vl, page_score, ws_sel + ctr_bytes, s);
+    if (st != SE_OK) return st;
+    return launch_attn(c, q, kq, vq, seq_len, vi, vl, top_pages, page_size, scale, out, lse, nullptr, 0, 0,
+                       ws_att + attn_row_ctr_bytes(c), s, ks, vs);
+  }
+  float* score = nullptr;
+  se_status st = launch_quest_fp8_append_scores(c, q, kq, vq, ks, vs, k_new, v_new, seq_len, kmin, kmax, page_size,
+                                                page_score, ws_sel, &score, s);
+  if (st != SE_OK) return st;
+  a.splits = attn_auto_splits(c, top_pages * page_size);
+  void* aws = ws_att + attn_row_ctr_bytes(c);
+  a.counters = (int*)aws;
+  a.part_ml = (float*)((char*)aws + attn_counter_bytes(c));
+  a.part_o = a.part_ml + size_t(a.B) * a.Hkv * a.splits * a.G * 2;
+  a.fused = a.splits > 1 && size_t(a.splits) * std::min(a.G, 32) * a.Dv * sizeof(float) <= ATTN_FUSED_MERGE_BYTES;
+  a.row_ctr = (int*)ws_att;
+  a.seq_len_w = seq_len;
+  a.sel = attn_mfma_sel_keys(ncp);
+  a.sel_score = score;
+  a.sel_ncp = ncp;
+  a.sel_view = view_idx;
+  a.sel_vlen = view_len;
+  st = launch_attn_mfma(a, s);
+  if (st != SE_OK || a.splits == 1 || a.fused) return st;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(a.G, a.B * a.Hkv), dim3(128), 0, s, a);
+  return launch_status();
+}
+
 // The H2O decode step: [the fused attention's batch-row tickets and counters][logits
 // and lse scratch for shapes that run the separate kernels].
 size_t h2o_step_ws_bytes(const se_cache& c) {

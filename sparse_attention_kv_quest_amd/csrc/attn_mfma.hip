@@ -359,7 +359,7 @@ template <int D, bool VC, int OCC, bool F8, bool APP, bool LG, int SEL = 0, bool
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void attn_mfma_kernel(AttnArgs a) {
   static_assert(!(APP && F8), "the fused append writes bf16 rows");
-  static_assert(SEL == 0 || (VC && !APP && !F8 && !LG), "in-launch selection: page views over bf16 rows");
+  static_assert(SEL == 0 || (VC && !APP && !LG), "in-launch selection: page views, no fused append, no logits");
   static_assert(!H2O || (APP && LG && !VC && SEL == 0), "the H2O step: fused append, identity view, logits");
   __shared__ float lg_unit[H2O ? ATTN_H2O_LDS_LOGITS : 1];   // [head][slot], row pitch logit_cap
   __shared__ float h2o_lse[H2O ? 16 : 1];
@@ -774,17 +774,19 @@ se_status launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((attn_mfma_kernel<64, false, 1, false, true, true, 0, true>), grid, dim3(256), 0, s, a);
     return launch_status();
   }
-  if (a.sel) {   // page views selected in the launch (the Quest decode step)
-#define SE_SEL(DD, OO, EE) hipLaunchKernelGGL((attn_mfma_kernel<DD, true, OO, false, false, false, EE>), grid, dim3(256), \
-                                              0, s, a)
+  if (a.sel) {   // page views selected in the launch (the Quest decode step, bf16 or FP8 rows)
+#define SE_SEL(DD, OO, FF, EE) hipLaunchKernelGGL((attn_mfma_kernel<DD, true, OO, FF, false, false, EE>), grid, \
+                                                  dim3(256), 0, s, a)
+#define SE_SEL_E(DD, OO, FF)                                                                                   \
+  if (e == 4) SE_SEL(DD, OO, FF, 4); else if (e == 9) SE_SEL(DD, OO, FF, 9); else if (e == 16) SE_SEL(DD, OO, FF, 16); \
+  else return SE_ERR_UNSUPPORTED;
     const int e = attn_mfma_sel_keys(a.sel_ncp);
     if (a.Dk == 128) {
-      if (e == 4) SE_SEL(128, 2, 4); else if (e == 9) SE_SEL(128, 2, 9); else if (e == 16) SE_SEL(128, 2, 16);
-      else return SE_ERR_UNSUPPORTED;
+      if (a.fp8) { SE_SEL_E(128, 2, true) } else { SE_SEL_E(128, 2, false) }
     } else {
-      if (e == 4) SE_SEL(64, 1, 4); else if (e == 9) SE_SEL(64, 1, 9); else if (e == 16) SE_SEL(64, 1, 16);
-      else return SE_ERR_UNSUPPORTED;
+      if (a.fp8) { SE_SEL_E(64, 1, true) } else { SE_SEL_E(64, 1, false) }
     }
+#undef SE_SEL_E
 #undef SE_SEL
     return launch_status();
   }

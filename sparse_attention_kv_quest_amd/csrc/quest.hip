@@ -12,7 +12,7 @@
 // contraction S^T = [max | min] . [q+ | q-]^T over 2 d_k terms, whose partial
 // sums are exact in fp32 for the grid-valued inputs the tests use.  fp32 caches
 // use the vector kernel.
-#include "se_internal.hpp"
+#include "fp8_row.hpp"
 #include "mfma_util.hpp"
 
 namespace se {
@@ -75,10 +75,15 @@ __global__ __launch_bounds__(256) void quest_score_vector_kernel(
 // call here leaves them, so this equals the separate call's rebuild bit for
 // bit).  Pages are counted with the new length; seq_len itself is left for the
 // top-k launch to update, after every block of the batch row has read it.
+//
+// APP == 2 (the fused FP8 decode step): the new rows are stored as FP8 codes and
+// scale bytes (the encoding of fp8_row.hpp, as se_kv_append_fp8 writes them), and the
+// stored values of the new K row are folded into the page's min / max.
 struct QuestAppendArgs {
   uint16_t* k; uint16_t* v;                      // cache rows [units][cap][D]; v null for a latent cache
   const uint16_t* k_new; const uint16_t* v_new;  // [units][D]
   uint16_t* kmin_w; uint16_t* kmax_w;            // the metadata, written for the appended page
+  uint8_t* kq; uint8_t* vq; uint8_t* ks; uint8_t* vs;   // APP == 2: codes [units][cap][D], scales [units][cap]
 };
 
 __device__ __forceinline__ uint32_t bf16x2_fmin(uint32_t acc, uint32_t x, bool mx) {
@@ -89,12 +94,13 @@ __device__ __forceinline__ uint32_t bf16x2_fmin(uint32_t acc, uint32_t x, bool m
 
 // Eight blocks per CU for one head block: a Quest 32K grid (2112 blocks) then takes
 // one round of the GPU but for 64 blocks, where seven per CU left 320 for a second.
-template <int D, int HB, bool APP>
+template <int D, int HB, int APP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HB == 1 ? 8 : 1, 8))) void quest_score_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* kmin, const uint16_t* kmax,
     const int32_t* seq_len, float* score, int Hkv, int G, int P, int ncp, int cap, QuestAppendArgs ap) {
   constexpr int NKS = D / 32;
   __shared__ u32x4 qb[2 * NKS][HB][64];
+  __shared__ __align__(16) uint16_t frow[APP == 2 ? D : 8];   // FP8 append: the new K row as stored (bf16)
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
   const int unit = blockIdx.y, b = unit / Hkv, kvh = unit % Hkv;
   const int len = min(seq_len[b], cap);
@@ -129,42 +135,72 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HB == 1 ? 8
       amn[c] = ld16(mnp + 32 * c);
     }
   }
+  // folds a new K row (bf16 values, this lane's dims 8g + 32c) into the min / max of
+  // page plast: the page's stored values with the new row folded in (the last step of
+  // the in-order rebuild the separate calls run, so bit-identical), or the new row
+  // alone on a fresh page; the page is then scored from the folded rows
+  auto fold_new_row = [&](const u32x4 (&xk)[NKS], int plast) {
+    const bool fresh = len % P == 0;
+    const size_t mo = (size_t(unit) * ncp + plast) * D + 8 * g;
+#pragma unroll
+    for (int c = 0; c < NKS; ++c) {
+      const u32x4 x = xk[c];
+      u32x4 mn, mx;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        mn[j] = bf16x2_fmin(fresh ? 0x7f807f80u : amn[c][j], x[j], false);   // +inf pair on a fresh page
+        mx[j] = bf16x2_fmin(fresh ? 0xff80ff80u : amx[c][j], x[j], true);    // -inf pair
+      }
+      *reinterpret_cast<u32x4*>(ap.kmin_w + mo + 32 * c) = mn;
+      *reinterpret_cast<u32x4*>(ap.kmax_w + mo + 32 * c) = mx;
+      amn[c] = mn;
+      amx[c] = mx;
+    }
+  };
   if (APP && app) {
     const int plast = len / P;
     const size_t urow = size_t(unit) * cap;
     if (blockIdx.x == plast / 64) {   // this block writes the new K / V rows
-      for (int i = threadIdx.x; i < 2 * (D / 8); i += 256) {
-        const bool isv = i >= D / 8;
-        const int o = 8 * (isv ? i - D / 8 : i);
-        if (!isv) *reinterpret_cast<u32x4*>(ap.k + (urow + len) * D + o) = ld16(ap.k_new + size_t(unit) * D + o);
-        else if (ap.v != nullptr)
-          *reinterpret_cast<u32x4*>(ap.v + (urow + len) * D + o) = ld16(ap.v_new + size_t(unit) * D + o);
+      if constexpr (APP == 2) {
+        constexpr int TPR = D / 8;        // threads per row: K's first, then V's
+        if (threadIdx.x < 2 * TPR) {
+          const bool isv = threadIdx.x >= TPR;
+          const int part = threadIdx.x % TPR;
+          int e;
+          const uint2 cw = fp8_quantize8<TPR>(ld16((isv ? ap.v_new : ap.k_new) + size_t(unit) * D + 8 * part), e);
+          *reinterpret_cast<uint2*>((isv ? ap.vq : ap.kq) + (urow + len) * D + 8 * part) = cw;
+          if (part == 0) (isv ? ap.vs : ap.ks)[urow + len] = uint8_t(e + 127);
+          if (!isv) {   // the stored K values (exact in bf16) for the page's min / max below
+            u32x4 sv;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const uint32_t wd = j < 2 ? cw.x : cw.y;
+              const float lo = (j & 1) ? fp8_value<2>(wd, e) : fp8_value<0>(wd, e);
+              const float hi = (j & 1) ? fp8_value<3>(wd, e) : fp8_value<1>(wd, e);
+              sv[j] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+            }
+            *reinterpret_cast<u32x4*>(&frow[8 * part]) = sv;
+          }
+        }
+      } else {
+        for (int i = threadIdx.x; i < 2 * (D / 8); i += 256) {
+          const bool isv = i >= D / 8;
+          const int o = 8 * (isv ? i - D / 8 : i);
+          if (!isv) *reinterpret_cast<u32x4*>(ap.k + (urow + len) * D + o) = ld16(ap.k_new + size_t(unit) * D + o);
+          else if (ap.v != nullptr)
+            *reinterpret_cast<u32x4*>(ap.v + (urow + len) * D + o) = ld16(ap.v_new + size_t(unit) * D + o);
+        }
       }
     }
-    if (pg == plast) {
+    if (APP == 1 && pg == plast) {
       // this lane's dims of the appended page's min / max: the page's stored values
       // with the new row folded in (the last step of the in-order rebuild the
       // separate call runs, so bit-identical), or the new row alone on a fresh page
-      const bool fresh = len % P == 0;
       const uint16_t* kn = ap.k_new + size_t(unit) * D + 8 * g;
-      const size_t mo = (size_t(unit) * ncp + plast) * D + 8 * g;
       u32x4 xk[NKS];   // all of the new row's pieces in flight before the stores
 #pragma unroll
       for (int c = 0; c < NKS; ++c) xk[c] = ld16(kn + 32 * c);
-#pragma unroll
-      for (int c = 0; c < NKS; ++c) {
-        const u32x4 x = xk[c];
-        u32x4 mn, mx;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          mn[j] = bf16x2_fmin(fresh ? 0x7f807f80u : amn[c][j], x[j], false);   // +inf pair on a fresh page
-          mx[j] = bf16x2_fmin(fresh ? 0xff80ff80u : amx[c][j], x[j], true);    // -inf pair
-        }
-        *reinterpret_cast<u32x4*>(ap.kmin_w + mo + 32 * c) = mn;
-        *reinterpret_cast<u32x4*>(ap.kmax_w + mo + 32 * c) = mx;
-        amn[c] = mn;
-        amx[c] = mx;
-      }
+      fold_new_row(xk, plast);
     }
   }
   // threads past the last entry store that entry again (the same values): no branch
@@ -187,6 +223,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HB == 1 ? 8
     qb[NKS + c][hb][ln] = xn;
   }
   __syncthreads();
+  if constexpr (APP == 2) {
+    // FP8 append: the new K row as stored (written to LDS by the block's row writers)
+    if (app && pg == len / P) {
+      u32x4 xk[NKS];
+#pragma unroll
+      for (int c = 0; c < NKS; ++c) xk[c] = *reinterpret_cast<const u32x4*>(&frow[8 * g + 32 * c]);
+      fold_new_row(xk, len / P);
+    }
+  }
   const int p0 = (blockIdx.x * 4 + w) * 16;
   if (p0 < ncp) {
     float best[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
@@ -569,6 +614,35 @@ se_status launch_quest_append_scores(const se_cache& c, const void* q, void* k, 
                                      (const uint16_t*)kmin, (const uint16_t*)kmax, seq_len, score, c.n_kv_heads, G,  \
                                      page_size, ncp, c.capacity, ap)
   if (c.dtype != SE_BF16 || c.latent || G > 16) return SE_ERR_UNSUPPORTED;
+  if (c.d_k == 128) SE_AP(128);
+  else if (c.d_k == 64) SE_AP(64);
+  else return SE_ERR_UNSUPPORTED;
+#undef SE_AP
+  *score_out = score;
+  return launch_status();
+}
+
+// The first launch of the fused Quest decode step over FP8 rows (GQA, d_k 64 / 128,
+// G <= 16): the new rows quantized into codes and scale bytes, the stored K values
+// folded into the appended page's min / max, and every page's score; seq_len is
+// left for the step's attention launch to update.
+se_status launch_quest_fp8_append_scores(const se_cache& c, const void* q, void* kq, void* vq, void* ks, void* vs,
+                                         const void* k_new, const void* v_new, const int32_t* seq_len, void* kmin,
+                                         void* kmax, int page_size, float* page_score, void* ws, float** score_out,
+                                         hipStream_t s) {
+  const int units = c.batch * c.n_kv_heads, G = c.n_q_heads / c.n_kv_heads;
+  const int ncp = ceil_div(c.capacity, page_size);
+  const size_t ctr_bytes = (size_t(c.batch) * sizeof(int) + 255) / 256 * 256;
+  float* score = page_score ? page_score : (float*)((char*)ws + ctr_bytes);
+  QuestAppendArgs ap{};
+  ap.k_new = (const uint16_t*)k_new; ap.v_new = (const uint16_t*)v_new;
+  ap.kmin_w = (uint16_t*)kmin; ap.kmax_w = (uint16_t*)kmax;
+  ap.kq = (uint8_t*)kq; ap.vq = (uint8_t*)vq; ap.ks = (uint8_t*)ks; ap.vs = (uint8_t*)vs;
+  if (c.dtype != SE_BF16 || c.latent || G > 16) return SE_ERR_UNSUPPORTED;
+  const dim3 grid(ceil_div(ncp, 64), units);
+#define SE_AP(DD) hipLaunchKernelGGL((quest_score_mfma_kernel<DD, 1, 2>), grid, dim3(256), 0, s, (const uint16_t*)q, \
+                                     (const uint16_t*)kmin, (const uint16_t*)kmax, seq_len, score, c.n_kv_heads, G, \
+                                     page_size, ncp, c.capacity, ap)
   if (c.d_k == 128) SE_AP(128);
   else if (c.d_k == 64) SE_AP(64);
   else return SE_ERR_UNSUPPORTED;

@@ -492,6 +492,14 @@ se_status launch_quest_step(const se_cache& c, const void* q, void* k, void* v, 
                             const void* v_new, int32_t* seq_len, void* kmin, void* kmax, int page_size,
                             int top_pages, float scale, float* out, float* lse, int32_t* view_idx,
                             int32_t* view_len, float* page_score, void* ws, hipStream_t s);
+se_status launch_quest_fp8_append_scores(const se_cache& c, const void* q, void* kq, void* vq, void* ks, void* vs,
+                                         const void* k_new, const void* v_new, const int32_t* seq_len, void* kmin,
+                                         void* kmax, int page_size, float* page_score, void* ws, float** score_out,
+                                         hipStream_t s);
+se_status launch_quest_step_fp8(const se_cache& c, const void* q, void* kq, void* vq, uint8_t* ks, uint8_t* vs,
+                                const void* k_new, const void* v_new, int32_t* seq_len, void* kmin, void* kmax,
+                                int page_size, int top_pages, float scale, float* out, float* lse, int32_t* view_idx,
+                                int32_t* view_len, float* page_score, void* ws, hipStream_t s);
 se_status launch_streaming_view(const se_cache& c, const int32_t* seq_len, int sink, int recent,
                                 int32_t* view_idx, int32_t* view_len, int view_cap, int pending, hipStream_t s);
 void pyramid_budgets(int n, int avg, int bmin, int32_t* out);

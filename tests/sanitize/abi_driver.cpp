@@ -75,6 +75,20 @@ static void entry_point_checks() {
                               nullptr), SE_ERR_SHAPE);
   EXPECT(se_quest_decode_step(&c, A, A, A, A, A, I, A, A, 16, 8, 0.1f, F, F, nullptr, nullptr, nullptr, A, 16,
                               nullptr), SE_ERR_WORKSPACE);
+  // the FP8 decode step
+  EXPECT(se_quest_decode_step_fp8(&c, A, A, A, U, nullptr, A, A, I, A, A, 16, 8, 0.1f, F, F, nullptr, nullptr,
+                                  nullptr, A, 1 << 24, nullptr), SE_ERR_NULL);   // no V scales
+  EXPECT(se_quest_decode_step_fp8(&c, A, A, A, U, U, A, A, I, A, A, 16, 0, 0.1f, F, F, nullptr, nullptr, nullptr, A,
+                                  1 << 24, nullptr), SE_ERR_BUDGET);
+  EXPECT(se_quest_decode_step_fp8(&c, A, A, A, U, U, A, A, I, A, A, 16, 8, 0.f, F, F, nullptr, nullptr, nullptr, A,
+                                  1 << 24, nullptr), SE_ERR_SHAPE);
+  EXPECT(se_quest_decode_step_fp8(&c, A, A, A, U, U, A, A, I, A, A, 16, 8, 0.1f, F, F, nullptr, nullptr, nullptr, A,
+                                  16, nullptr), SE_ERR_WORKSPACE);
+  {
+    const se_cache wide = cache(2, 64, 2, 128, 128, 1024);   // 32 heads per KV head
+    EXPECT(se_quest_decode_step_fp8(&wide, A, A, A, U, U, A, A, I, A, A, 16, 8, 0.1f, F, F, nullptr, nullptr,
+                                    nullptr, A, 1 << 26, nullptr), SE_ERR_UNSUPPORTED);
+  }
   // attention
   EXPECT(se_sparse_decode_attn(&c, A, A, A, I, I, nullptr, 8, 16, 0.1f, F, nullptr, nullptr, 0, 0, A, 1 << 20,
                                nullptr), SE_ERR_NULL);

@@ -220,10 +220,10 @@ def test_fp8_quest_decode(se):
 
 def test_fp8_quest_32k_all_units(se):
     """The 32K Quest workload over FP8 rows at full size, through the bench's calls
-    (se_kv_quantize_fp8 once, then per step se_kv_append_fp8, se_quest_select,
-    se_sparse_decode_attn_fp8): at the first, a middle and the last of 64 steps, every
-    unit's codes, scale bytes and page metadata are compared by digest, its page scores
-    and view exactly, and its attention at the bf16 tolerance, with the oracle's."""
+    (se_kv_quantize_fp8 once, then per step se_quest_decode_step_fp8): at the first, a
+    middle and the last of 64 steps, every unit's codes, scale bytes and page metadata
+    are compared by digest, its page scores and view exactly, and its attention at the
+    bf16 tolerance, with the oracle's."""
     from tests import oracle_pool
     from tests.parity_jobs import digest, fp8_quest_unit
     cfg = get_config(1)
@@ -248,16 +248,13 @@ def test_fp8_quest_32k_all_units(se):
     vlen = torch.zeros((B, H), dtype=torch.int32, device="cuda")
     score = torch.zeros((B, H, ncp), device="cuda")
     out, lse = zeros((B, Hq, D)), zeros((B, Hq))
-    ws_q = se.workspace(se.SE_OP_QUEST, c, P, k)
-    ws_a = se.workspace(se.SE_OP_ATTN, c, k * P, 0)
+    ws_s = se.workspace(se.SE_OP_QUEST_STEP, c, P, k)
     got = {}
     for step in range(cfg.decode_steps):
         kn, vn = gen.decode_kv_new(cfg, 0, step)
         qd = dev(gen.decode_query(cfg, 0, step), torch.bfloat16)
-        se.se_kv_append_fp8(c, kq, vq, ks, vs, dev(kn, torch.bfloat16), dev(vn, torch.bfloat16), seq, kmin, kmax, P)
-        se.se_quest_select(c, qd, kmin, kmax, seq, P, k, view, vlen, score, ws_q)
-        se.se_sparse_decode_attn_fp8(c, qd, kq, vq, ks, vs, seq, view, vlen, k, P, cfg.softmax_scale, out, lse,
-                                     ws=ws_a)
+        se.se_quest_decode_step_fp8(c, qd, kq, vq, ks, vs, dev(kn, torch.bfloat16), dev(vn, torch.bfloat16), seq,
+                                    kmin, kmax, P, k, cfg.softmax_scale, out, lse, view, vlen, score, ws_s)
         if step in checks:
             torch.cuda.synchronize()
             L = cfg.context + step + 1
