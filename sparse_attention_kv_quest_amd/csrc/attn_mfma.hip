@@ -591,6 +591,22 @@ void attn_mfma_kernel(AttnArgs a) {
     *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(isv ? a.v_w : a.k_w) + (size_t(unit) * a.cap + tgt) * D + o) =
         app_lds[threadIdx.x];
   }
+  // H2O: the slots' positions and scores, loaded now so that their round trip overlaps
+  // the wave and head merges below (nothing in this launch writes them before they are
+  // used, but for the slot past the occupied ones, which no thread loads)
+  constexpr int HE = ATTN_H2O_SLOTS_PER_THREAD;
+  int h2o_p[H2O ? HE : 1];
+  float h2o_sc[H2O ? HE : 1];
+  if constexpr (H2O) {
+    const int32_t* pos = a.h2o_pos + size_t(unit) * a.cap;
+    const float* acc = a.h2o_acc + size_t(unit) * a.cap;
+#pragma unroll
+    for (int j = 0; j < HE; ++j) {
+      const int sl = max(min(j * 256 + int(threadIdx.x), len - 1), 0);
+      h2o_p[j] = pos[sl];
+      h2o_sc[j] = acc[sl];
+    }
+  }
   // ---- merge the waves of the block: per head, the waves' (max, sum) and
   // outputs [wave][head][dim] (row pitch D + 4) go through LDS; a thread then
   // owns four consecutive dims of one head.
@@ -652,7 +668,6 @@ void attn_mfma_kernel(AttnArgs a) {
     // computes it from the logits and lse of the attention: the same operations in the same
     // order, with the logits read from LDS instead of memory
     __syncthreads();   // every tile's logits and the heads' lse are in LDS
-    constexpr int HE = ATTN_H2O_SLOTS_PER_THREAD;
     __shared__ int h2o_cnt[MF_WAVES], h2o_slot[MF_WAVES];
     __shared__ uint32_t h2o_hi[MF_WAVES], h2o_lo[MF_WAVES];
     const int n = len;
@@ -661,14 +676,8 @@ void attn_mfma_kernel(AttnArgs a) {
     const int in = a.slot != nullptr ? a.slot[unit] : -1;
     const int ns = in >= 0 ? in : n - 1;   // the slot that received the token at cur_pos
     if (threadIdx.x == 0 && ns >= n && ns < a.cap) { pos[ns] = a.h2o_cur; acc[ns] = 0.f; }
-    int p[HE];
-    float sc[HE];
-#pragma unroll
-    for (int j = 0; j < HE; ++j) {
-      const int sl = max(min(j * 256 + int(threadIdx.x), n - 1), 0);
-      p[j] = pos[sl];
-      sc[j] = acc[sl];
-    }
+    int (&p)[HE] = h2o_p;
+    float (&sc)[HE] = h2o_sc;
 #pragma unroll
     for (int j = 0; j < HE; ++j) {
       const int sl = j * 256 + threadIdx.x;
