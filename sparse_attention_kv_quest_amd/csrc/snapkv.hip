@@ -83,6 +83,10 @@ __global__ __launch_bounds__(256) void snap_mfma_kernel(SnapArgs a) {
     for (int i = 0; i < 4; ++i)
       nlse[rb][i] = PASS_B ? -a.lse2[size_t(unit) * a.R + (w * NRB + rb) * 16 + 4 * g + i] : 0.f;
   }
+  // q's and lse's loads stay ahead of the first K tile's: the wait that tile's LDS
+  // store takes then covers them, and no wait inside the tile loop is left waiting for
+  // them (or, behind them in the in-order count, for the next tile's prefetch)
+  __builtin_amdgcn_sched_barrier(0);
   float m[NRB], l[NRB];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) { m[rb] = -INFINITY; l[rb] = 0.f; }
