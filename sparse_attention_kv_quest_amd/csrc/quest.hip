@@ -192,10 +192,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HB == 1 ? 8
         }
       }
     }
-    if (APP == 1 && pg == plast) {
-      // this lane's dims of the appended page's min / max: the page's stored values
-      // with the new row folded in (the last step of the in-order rebuild the
-      // separate call runs, so bit-identical), or the new row alone on a fresh page
+    if (APP == 1 && pg == plast) {   // this lane's dims of the new row, folded into the page
       const uint16_t* kn = ap.k_new + size_t(unit) * D + 8 * g;
       u32x4 xk[NKS];   // all of the new row's pieces in flight before the stores
 #pragma unroll
