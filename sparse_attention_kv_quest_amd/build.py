@@ -22,6 +22,10 @@ FLAGS = [
     "-I" + os.path.join(ROOT, "include"),
     # packed fp32 VALU forms stay off in every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: without this the compiler parks the SnapKV scoring passes'
+    # score tiles in AGPRs and copies each one back (one v_accvgpr_read per element)
+    # before the exps; no kernel of the library needs the AGPR file for capacity
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 
