@@ -472,7 +472,7 @@ void attn_mfma_kernel(AttnArgs a) {
   if constexpr (SEL > 0) {
     // the unit's top pages by score, ascending, straight into the view cache (the
     // V staging tiles are not in use yet and hold the selection's histograms)
-    using SelShared = TopkRegSharedN<MF_WAVES>;
+    using SelShared = TopkRegSharedN<MF_WAVES, 2>;
     SelShared& tsh = *reinterpret_cast<SelShared*>(&vt_lds[0][0]);
     static_assert(sizeof(SelShared) <= sizeof(vt_lds), "selection scratch");
     const int npages = min((len + a.gran - 1) >> a.gshift, a.sel_ncp);

@@ -504,7 +504,7 @@ __global__ __launch_bounds__(ML_THREADS) void attn_mla_pf_kernel(AttnArgs a) {
   if constexpr (SEL > 0) {
     // the unit's top pages by score, ascending, straight into the view cache (the
     // value tile is not in use yet and holds the selection's histograms)
-    using SelShared = TopkRegSharedN<ML_WAVES>;
+    using SelShared = TopkRegSharedN<ML_WAVES, 2>;
     static_assert(sizeof(SelShared) <= MP_V_BYTES, "selection scratch");
     SelShared& tsh = *reinterpret_cast<SelShared*>(lds + ML_Q_BYTES);
     const int npages = min((len + a.gran - 1) >> a.gshift, a.sel_ncp);

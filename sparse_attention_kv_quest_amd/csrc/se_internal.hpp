@@ -302,17 +302,22 @@ __device__ int block_topk_ascending(ScoreFn score, int n, int k, int32_t* out, T
 // key 0, which is below every real key (ordered_bits of a non-NaN float is
 // never 0), so they never enter the kept set and need no masks.  Radix select
 // on the score bits: the bits every candidate shares are skipped, then 8-bit
-// digits are counted in one LDS histogram per wave (zeroed by that wave), and
-// wave 0 alone scans the digit counts (DPP) and posts the crossing digit, so a
-// digit pass costs two block barriers.  The search stops when one digit bucket
+// digits are counted in LDS histograms private to each wave (zeroed by that wave),
+// COPIES of them per wave with lane l counting into copy l % COPIES: scores cluster
+// in few digits, and LDS atomics to one address from the lanes of an instruction
+// are serialized, so copies divide that serialization, while each copy adds to the
+// clearing and to the scan (two copies measured best in the in-launch selections of
+// the decode attention; four and eight were slower).  Wave 0 alone scans the digit
+// counts (DPP) and posts the crossing digit, so a digit pass costs two block barriers.  The search stops when one digit bucket
 // holds exactly the keys still to choose, or when all 32 bits are resolved.
 // The kept set is every key above the resolved prefix plus the first `r` keys
 // of the prefix's bucket in index order (the lower-index tie rule); per-wave
 // counts give each wave its output offset and ballot prefix counts place each
 // kept candidate, so the view comes out in ascending index order.
-template <int NWAVES>
+template <int NWAVES, int COPIES = 1>
 struct TopkRegSharedN {
-  uint32_t hist[NWAVES][256];     // one histogram per wave
+  static constexpr int copies = COPIES;
+  uint32_t hist[NWAVES][COPIES][256];   // per wave, lane l counting into copy l % COPIES
   uint32_t red_or[NWAVES], red_and[NWAVES];
   int cnt_a[NWAVES], cnt_b[NWAVES];
   int digit, rem, cnt;
@@ -388,11 +393,14 @@ __device__ int block_topk_keys(uint32_t (&key)[E], int n, int k, int32_t* out, S
       const int top = 31 - __clz(diff);
       mask = top == 31 ? 0u : (~0u << (top + 1));
       prefix = kand & mask;
-      uint32_t* hist = sh.hist[w];
+      constexpr int NC = SH::copies;
+      uint32_t* hist = sh.hist[w][lane % NC];
       for (int hb = top; hb >= 0; hb -= 8) {
         const int shift = hb >= 7 ? hb - 7 : 0;
         const uint32_t dmask = (1u << (hb - shift + 1)) - 1u;
-        reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);   // in LDS order before the atomics
+#pragma unroll
+        for (int c = 0; c < NC; ++c)   // in LDS order before this wave's atomics
+          reinterpret_cast<uint4*>(sh.hist[w][c])[lane] = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
         for (int j = 0; j < E; ++j)
           if ((key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
@@ -402,10 +410,12 @@ __device__ int block_topk_keys(uint32_t (&key)[E], int n, int k, int32_t* out, S
           // lanes counts the keys whose digit is >= the lane's lowest
           int c0 = 0, c1 = 0, c2 = 0, c3 = 0;
 #pragma unroll
-          for (int i = 0; i < NW; ++i) {
-            const uint4 h4 = reinterpret_cast<const uint4*>(sh.hist[i])[63 - lane];
-            c0 += int(h4.w); c1 += int(h4.z); c2 += int(h4.y); c3 += int(h4.x);
-          }
+          for (int i = 0; i < NW; ++i)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+              const uint4 h4 = reinterpret_cast<const uint4*>(sh.hist[i][c])[63 - lane];
+              c0 += int(h4.w); c1 += int(h4.z); c2 += int(h4.y); c3 += int(h4.x);
+            }
           const int own = c0 + c1 + c2 + c3;
           const int incl = wave_incl_scan(own);
           int above = incl - own;
