@@ -684,13 +684,23 @@ void attn_mfma_kernel(AttnArgs a) {
       if (sl >= n) { p[j] = -1; sc[j] = 0.f; }
       if (sl == ns) { p[j] = a.h2o_cur; sc[j] = 0.f; }
     }
-    for (int hh = 0; hh < G; ++hh) {   // heads in ascending order
+    // heads in ascending order.  A head's logits are read unconditionally (clamped
+    // slot) and together, so one LDS wait covers them, and each sum takes its term only
+    // for an occupied slot (a per-lane branch around each read had made every read a
+    // waited LDS round trip of its own)
+    static_assert(sizeof(h2o_lse) / sizeof(h2o_lse[0]) == 16, "at most 16 heads per KV head");
+#pragma unroll
+    for (int hh = 0; hh < 16; ++hh) {
+      if (hh >= G) break;
       const float l = h2o_lse[hh];
       if (l == -INFINITY) continue;
+      float lv[HE];
+#pragma unroll
+      for (int j = 0; j < HE; ++j) lv[j] = lg_unit[hh * a.logit_cap + min(j * 256 + int(threadIdx.x), a.logit_cap - 1)];
 #pragma unroll
       for (int j = 0; j < HE; ++j) {
-        const int sl = min(j * 256 + int(threadIdx.x), a.logit_cap - 1);
-        if (p[j] >= 0) sc[j] += expf(lg_unit[hh * a.logit_cap + sl] - l);
+        const float e = expf(lv[j] - l);
+        sc[j] = p[j] >= 0 ? sc[j] + e : sc[j];
       }
     }
     int cnt = 0;
