@@ -308,8 +308,9 @@ __device__ int block_topk_ascending(ScoreFn score, int n, int k, int32_t* out, T
 // are serialized, so copies divide that serialization, while each copy adds to the
 // clearing and to the scan (two copies measured best in the in-launch selections of
 // the decode attention; four and eight were slower).  Wave 0 alone scans the digit
-// counts (DPP) and posts the crossing digit, so a digit pass costs two block barriers.  The search stops when one digit bucket
-// holds exactly the keys still to choose, or when all 32 bits are resolved.
+// counts (DPP) and posts the crossing digit, so a digit pass costs two block
+// barriers.  The search stops when one digit bucket holds exactly the keys still
+// to choose, or when all 32 bits are resolved.
 // The kept set is every key above the resolved prefix plus the first `r` keys
 // of the prefix's bucket in index order (the lower-index tie rule); per-wave
 // counts give each wave its output offset and ballot prefix counts place each
