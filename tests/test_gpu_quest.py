@@ -121,6 +121,35 @@ def test_tiny_bf16_quest_decode_with_partial_pages(se, mode):
             check_unit(cfg, st, q, L, unit, got)
 
 
+PAGE_CASES = {   # page size: (context, top pages, decode steps, d_k); steps cross page boundaries
+    1: (200, 24, 3, 128),
+    2: (150, 20, 5, 64),
+    4: (201, 10, 6, 128),
+    8: (250, 8, 10, 128),
+    32: (700, 5, 40, 128),
+}
+
+
+@pytest.mark.parametrize("mode", ["separate", "whole"])
+@pytest.mark.parametrize("page", list(PAGE_CASES))
+def test_bf16_quest_decode_page_sizes(se, page, mode):
+    """Quest over pages of 1 to 32 tokens (token views, slot quads split across
+    entries below 4 tokens, within one entry from 4 on), every unit against the
+    oracle at every step, through the separate calls and through the whole step."""
+    ctx, k, steps, d = PAGE_CASES[page]
+    cfg = get_config(0, dtype="bf16", batch=2, n_q_heads=8, n_kv_heads=2, d_k=d, d_v=d, context=ctx,
+                      page_size=page, top_pages=k, decode_steps=steps)
+    banner(f"bf16 quest page={page} {mode}")
+    st = QuestState(se, cfg, cfg.context + cfg.decode_steps)
+    for step in range(cfg.decode_steps):
+        q, L = st.step(se, step, whole=mode == "whole")
+        torch.cuda.synchronize()
+        got = snapshot(st)
+        assert np.all(host(st.seq) == L)
+        for unit in range(cfg.units):
+            check_unit(cfg, st, q, L, unit, got)
+
+
 @pytest.mark.parametrize("k_pages", [1, 19, 40])
 def test_quest_top_k_edges(se, k_pages):
     # k = 1, k just below the page count, k above the page count (every page selected)
