@@ -33,6 +33,13 @@ CASES = {
                                  top_pages=9), 3),
     "ncp_above_selection": (get_config(0, dtype="bf16", batch=1, n_q_heads=8, n_kv_heads=1, d_k=64, d_v=64,
                                        context=70000, top_pages=40), 2),
+    # other page sizes: slot quads split across view entries (2) and within one (4, 32)
+    "page2_d64": (get_config(0, dtype="bf16", batch=2, n_q_heads=8, n_kv_heads=2, context=150, page_size=2,
+                             top_pages=20), 5),
+    "page4": (get_config(0, dtype="bf16", batch=2, n_q_heads=8, n_kv_heads=2, d_k=128, d_v=128, context=201,
+                         page_size=4, top_pages=10), 6),
+    "page32": (get_config(0, dtype="bf16", batch=2, n_q_heads=16, n_kv_heads=2, d_k=128, d_v=128, context=700,
+                          page_size=32, top_pages=5), 4),
 }
 
 

@@ -37,6 +37,10 @@ CASES = {
     "mla_latent_ragged_view": (get_config(4, batch=3, context=900, page_size=64, top_pages=40), 3),
     "mla_g24_latent": (get_config(4, batch=2, n_q_heads=24, context=2000, page_size=64, top_pages=9), 3),
     "mla_g16_fallback": (get_config(4, batch=2, n_q_heads=16, context=1000, page_size=64, top_pages=5), 3),
+    "mla_latent_page16": (get_config(4, batch=2, context=1000, page_size=16, top_pages=20), 3),
+    "mla_latent_page32": (get_config(4, batch=3, context=1300, page_size=32, top_pages=9), 3),
+    "d128_g8_page8": (get_config(0, dtype="bf16", batch=2, n_q_heads=16, n_kv_heads=2, d_k=128, d_v=128,
+                                 context=250, page_size=8, top_pages=8), 9),
     "page_12_fallback": (get_config(0, dtype="bf16", batch=2, n_q_heads=8, n_kv_heads=2, d_k=128, d_v=128,
                                     context=300, page_size=12, top_pages=6), 3),
 }
