@@ -77,6 +77,16 @@ def test_mla_small_all_units(se, mode):
     run_mla(se, cfg, range(cfg.batch), steps=3, mode=mode)
 
 
+@pytest.mark.parametrize("mode", ["separate", "step"])
+@pytest.mark.parametrize("page", [16, 32])
+def test_mla_small_page_sizes(se, page, mode):
+    """Latent rows over 16- and 32-token pages, every batch row against the oracle after
+    steps that cross a page boundary."""
+    cfg = get_config(4, batch=2, context=1000 + page - 3, page_size=page, top_pages=12)
+    banner(f"mla small page={page} {mode}")
+    run_mla(se, cfg, range(cfg.batch), steps=5, mode=mode)
+
+
 def test_mla_128k_all_rows(se):
     """The 128K MLA workload at full size through the bench's call (se_quest_decode_step:
     the scoring launch with the append, then the attention launch that selects the
