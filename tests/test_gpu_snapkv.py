@@ -113,6 +113,16 @@ def test_snapkv_bf16_rows_128_and_256(se):
         run_snap(se, cfg, range(cfg.units), {})
 
 
+def test_snapkv_bf16_rows_192_and_d64(se):
+    """The MFMA passes with three 16-row blocks per wave (192 window rows) and with
+    64-wide heads (128 rows)."""
+    for W, d in ((24, 128), (16, 64)):
+        cfg = get_config(2, batch=1, context=3000, d_k=d, d_v=d, snap_window=W, snap_budget=300, snap_peaks=60,
+                          snap_peak_spacing=40, snap_peak_levels=8)
+        banner(f"snapkv bf16 rows {cfg.group * W} d {d}")
+        run_snap(se, cfg, range(cfg.units), {})
+
+
 def test_snapkv_budget_covers_prompt_and_window_only(se):
     cfg = get_config(0, context=300)
     banner("snapkv edges")
