@@ -452,8 +452,9 @@ se_status se_h2o_decode_step(const se_cache* c, const void* q, void* k, void* v,
  * int32 [B][Hkv][slots.capacity] gets their positions (-1 after them) and acc
  * float [B][Hkv][slots.capacity] their scores (0 after them) — the state
  * se_h2o_accumulate_evict continues from.  scores: NULL or float
- * [B][Hkv][prompt_len].  bf16, d_k 64 / 128, G <= 16, prompt_len * G <= 2^30
- * (SE_ERR_SHAPE beyond).
+ * [B][Hkv][prompt_len].  bf16, d_k 64 / 128, G <= 16, prompt_len * G <= 2^30 and
+ * B * Hkv * max(ceil(prompt_len * G / 1024), ceil(prompt_len / 512)) < 2^31 (SE_ERR_SHAPE
+ * beyond, before any launch).
  * ws: se_workspace_bytes(SE_OP_H2O_PREFILL, c, prompt_len, recent_window) bytes,
  * zero-filled once before first use (its selection counters return to zero). */
 se_status se_h2o_prefill_init(const se_cache* c, const void* q_prompt, const void* k, const void* v,

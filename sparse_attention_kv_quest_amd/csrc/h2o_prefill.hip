@@ -35,6 +35,7 @@ struct HpArgs {
   float* acc0;          // [units][L]
   float* votes;         // [units][L - recent]: acc0 of the candidates of the keep rule
   int Hq, Hkv, G, cap, L, n_cand;
+  int units;            // batch * Hkv
   float sc2;            // scale * log2(e)
 };
 
@@ -49,9 +50,9 @@ __global__ __launch_bounds__(512) void hp_rowlse_kernel(HpArgs a) {
   __shared__ __align__(16) uint16_t kt[2][HP_KT][PITCH];
   const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int unit = blockIdx.y, b = unit / a.Hkv, kvh = unit % a.Hkv;
+  const int unit = blockIdx.x % a.units, b = unit / a.Hkv, kvh = unit % a.Hkv;
   const int L = a.L, G = a.G, nrows = L * G;
-  const int r_blk = blockIdx.x * HP_ROWS;
+  const int r_blk = ((nrows + HP_ROWS - 1) / HP_ROWS - 1 - int(blockIdx.x / a.units)) * HP_ROWS;   // latest rows first
   if (r_blk >= nrows) return;                          // uniform per block
   const int r_w = r_blk + w * HP_RPW;
   const uint16_t* ku = a.k + size_t(unit) * a.cap * D;
@@ -153,8 +154,9 @@ __global__ __launch_bounds__(512) void hp_colsum_kernel(HpArgs a) {
   __shared__ float lt[2][HP_QR];
   const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int unit = blockIdx.y, b = unit / a.Hkv, kvh = unit % a.Hkv;
-  const int L = a.L, G = a.G, nrows = L * G, j_blk = blockIdx.x * HP_KEYS;
+  const int unit = blockIdx.x % a.units, b = unit / a.Hkv, kvh = unit % a.Hkv;
+  const int L = a.L, G = a.G, nrows = L * G;
+  const int j_blk = int(blockIdx.x / a.units) * HP_KEYS;   // the earliest keys (most rows) first
   if (j_blk >= L) return;                               // uniform per block
   const uint16_t* ku = a.k + size_t(unit) * a.cap * D;
   const uint16_t* qu = a.q + (size_t(b) * a.Hq + size_t(kvh) * G) * size_t(L) * D;
@@ -203,7 +205,48 @@ __global__ __launch_bounds__(512) void hp_colsum_kernel(HpArgs a) {
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1, r0 = r_beg + t * HP_QR;
     if (t + 1 < ntiles) fetch(t + 1);
-    if (r0 >= r_full) {                                 // no causal test anywhere in the tile
+    if (r0 >= r_full && r0 + HP_QR <= nrows) {         // a whole tile, no causal test anywhere
+      // software pipeline over the tile's 16-row groups: the scores of group j + 1 go
+      // through the matrix cores while group j's exps run, and group j + 2's operands
+      // are read from LDS meanwhile
+      u32x4 bq[NQG][NKS];
+      float nl[NQG];
+      f32x4 s[NQG][HP_KB];
+      auto rd = [&](int j) {
+#pragma unroll
+        for (int c = 0; c < NKS; ++c) bq[j][c] = *reinterpret_cast<const u32x4*>(&qt[buf][16 * j + c16][8 * g + 32 * c]);
+        nl[j] = -lt[buf][16 * j + c16];
+      };
+      auto mm = [&](int j) {
+#pragma unroll
+        for (int kb = 0; kb < HP_KB; ++kb) s[j][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NKS; ++c)
+#pragma unroll
+          for (int kb = 0; kb < HP_KB; ++kb) s[j][kb] = mfma_bf16_16x16x32(ak[kb][c], bq[j][c], s[j][kb]);
+      };
+      rd(0);
+      rd(1);
+      mm(0);
+#pragma unroll
+      for (int j = 0; j < NQG; ++j) {
+        if (j + 2 < NQG) rd(j + 2);
+        if (j + 1 < NQG) mm(j + 1);
+#pragma unroll
+        for (int kb = 0; kb < HP_KB; ++kb)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) col[kb][ii] += ex2(fmaf(s[j][kb][ii], a.sc2, nl[j]));
+        if (j + 1 < NQG) {
+          if (j + 2 < NQG) __builtin_amdgcn_sched_group_barrier(0x100, NKS + 1, 0);
+#pragma unroll
+          for (int i = 0; i < NKS * HP_KB; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);             // one scheduling region per group
+      }
+    } else if (r0 >= r_full) {                          // the partial last tile
 #pragma unroll
       for (int j = 0; j < NQG; ++j) {
         if (r0 + 16 * j >= nrows) break;                // uniform across the block
@@ -292,7 +335,15 @@ se_status launch_h2o_prefill_scores(const se_cache& c, const void* q, const void
   a.n_cand = n_cand;
   a.sc2 = scale * 1.4426950408889634f;
   const int units = c.batch * c.n_kv_heads;
-  const dim3 ga(ceil_div(L * a.G, HP_ROWS), units), gb(ceil_div(L, HP_KEYS), units);
+  // Block b takes unit b % units: a block fills a CU, and the dispatcher then deals
+  // consecutive blocks to the CUs in a fixed rotation, so consecutive blocks should cost
+  // the same (one causal row / key block of every unit) and each CU should see every
+  // block index.  With the units outermost, each CU had received the same block index
+  // of every unit, from the cheapest to the costliest, and the launch ran twice as long
+  // as the average CU's work.
+  a.units = units;
+  if (int64_t(units) * std::max(ceil_div(L * a.G, HP_ROWS), ceil_div(L, HP_KEYS)) > INT32_MAX) return SE_ERR_SHAPE;
+  const dim3 ga(units * ceil_div(L * a.G, HP_ROWS)), gb(units * ceil_div(L, HP_KEYS));
   if (c.d_k == 128) {
     hipLaunchKernelGGL(hp_rowlse_kernel<128>, ga, dim3(512), 0, s, a);
     hipLaunchKernelGGL(hp_colsum_kernel<128>, gb, dim3(512), 0, s, a);

@@ -7,7 +7,7 @@ scores put at least GAP relative distance between the kept side and the rest;
 otherwise the unit's query of that step is redrawn with attempt + 1.  float32
 rounding of the GPU scores (a few ulp of accumulated error) cannot reorder such
 decisions.  The searches are independent per unit and run in a process pool.
-Run: python tests/golden/make_attempts.py
+Run: python tests/golden/make_attempts.py [--only SECTION[,SECTION..]]
 """
 import json
 import os
@@ -197,23 +197,22 @@ def chain_unit_job(args):
     return name, found
 
 
-def main():
-    from tests import oracle_pool
-    t0 = time.time()
-    pool = oracle_pool.pool()
-    out = {"gap": GAP}
-
+def section_h2o_16k(pool, out, t0):
     cfg = h2o_config(True)
     out["h2o_16k"] = {}
     for d in pool.map(h2o_unit_job, range(cfg.units)):
         out["h2o_16k"].update(d)
     print(f"h2o_16k: {len(out['h2o_16k'])} redraws ({time.time() - t0:.0f}s)", flush=True)
 
+
+def section_omnikv_16k(pool, out, t0):
     out["omnikv_16k"] = {}
     for d in pool.map(omni_unit_job, OMNI_UNITS):
         out["omnikv_16k"].update(d)
     print(f"omnikv_16k: {len(out['omnikv_16k'])} redraws ({time.time() - t0:.0f}s)", flush=True)
 
+
+def section_snapkv(pool, out, t0):
     for name, cfg_id in (("snapkv_128k", 2), ("snapkv_tiny", 0)):
         c = get_config(cfg_id)
         out[name] = {}
@@ -221,6 +220,8 @@ def main():
             out[name].update(d)
         print(f"{name}: {len(out[name])} redraws ({time.time() - t0:.0f}s)", flush=True)
 
+
+def section_pyramid(pool, out, t0):
     out["pyramid"] = {}
     from oracle import variants as ov
     for name, (c, avg, bmin) in PYRAMID_CASES.items():
@@ -234,6 +235,8 @@ def main():
             out["pyramid"][name].update(d)
         print(f"pyramid {name}: {len(out['pyramid'][name])} redraws ({time.time() - t0:.0f}s)", flush=True)
 
+
+def section_h2o_prefill(pool, out, t0):
     out["h2o_prefill"] = {name: {} for name in PREFILL_CASES}
     jobs = [(name, u) for name, (c, _, _, _) in PREFILL_CASES.items() for u in range(c.units)]
     for name, unit, attempt in pool.map(prefill_unit_job, jobs):
@@ -241,6 +244,8 @@ def main():
             out["h2o_prefill"][name][str(unit)] = attempt
     print(f"h2o_prefill: {out['h2o_prefill']} ({time.time() - t0:.0f}s)", flush=True)
 
+
+def section_h2o_prefill_decode(pool, out, t0):
     dec = {"prompt": {}, "steps": {}}
     for unit, attempt, steps in pool.map(prefill_decode_unit_job, range(PREFILL_DECODE_CFG.units)):
         if attempt:
@@ -250,11 +255,42 @@ def main():
     out["h2o_prefill_decode"] = dec
     print(f"h2o_prefill_decode: {dec} ({time.time() - t0:.0f}s)", flush=True)
 
+
+def section_chain(pool, out, t0):
     out["chain"] = {name: {} for name in CHAIN_CASES}
     for name, found in pool.map(chain_unit_job, [(n, u) for n, c in CHAIN_CASES.items() for u in range(c.units)]):
         out["chain"][name].update(found)
     print(f"chain: {out['chain']} ({time.time() - t0:.0f}s)", flush=True)
 
+
+SECTIONS = {"h2o_16k": section_h2o_16k, "omnikv_16k": section_omnikv_16k, "snapkv": section_snapkv,
+            "pyramid": section_pyramid, "h2o_prefill": section_h2o_prefill,
+            "h2o_prefill_decode": section_h2o_prefill_decode, "chain": section_chain}
+
+
+def main(argv=None):
+    """Every section, or with --only NAME[,NAME..] those sections recomputed into the
+    existing attempts.json (the others kept as they are)."""
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--only", default="", help="comma-separated sections: " + ", ".join(SECTIONS))
+    args = ap.parse_args(argv)
+    only = [n for n in args.only.split(",") if n]
+    for n in only:
+        if n not in SECTIONS:
+            raise SystemExit(f"unknown section {n}; sections: {', '.join(SECTIONS)}")
+    from tests import oracle_pool
+    t0 = time.time()
+    pool = oracle_pool.pool()
+    if only:
+        with open(OUT) as f:
+            out = json.load(f)
+        assert out["gap"] == GAP, "the stored draws were searched with another gap"
+    else:
+        out = {"gap": GAP}
+    for name, fn in SECTIONS.items():
+        if not only or name in only:
+            fn(pool, out, t0)
     oracle_pool.shutdown()
     with open(OUT, "w") as f:
         json.dump(out, f, indent=1, sort_keys=True)

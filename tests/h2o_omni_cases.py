@@ -68,6 +68,8 @@ PREFILL_CASES = {
     "d128_g6_ragged": (get_config(0, dtype="bf16", batch=2, n_q_heads=12, n_kv_heads=2, d_k=128, d_v=128), 1111, 90,
                        33),
     "keep_all": (get_config(0, dtype="bf16", batch=1, n_q_heads=8, n_kv_heads=2), 90, 64, 32),
+    # past one 512-key column block: the column pass's whole-tile path with 64-wide heads
+    "d64_g4_long": (get_config(0, dtype="bf16", batch=2, n_q_heads=8, n_kv_heads=2), 900, 60, 24),
 }
 PREFILL_KV_LAYER = 41
 
