@@ -10,21 +10,27 @@
 //   B: per key, the sum of exp2(sc2 * q . k - lse2) over the later queries.
 // Both compute S^T[key][row] = K . Q^T on 16x16x32 MFMA: A = 16 keys (lane: key
 // c16, dims 32c + 8g ..), B = 16 consecutive (position, head) query rows (lane:
-// row c16, the same dims).  K tiles (pass A) and Q tiles (pass B) go through
-// double-buffered LDS shared by the block's 8 waves.
+// row c16, the same dims).  K tiles (pass A, 12-wave blocks at three waves per
+// SIMD) and Q tiles (pass B, 8-wave blocks) go through double-buffered LDS shared
+// by the block's waves.  Both passes are bound by the vector ALU (one exp2 and two
+// to five other operations per score), so the MFMAs of the next 16x16 score tile
+// are issued before the exps of the current one.
 // The kept set then follows the SnapKV keep rule on acc0 (no pooling).
 #include "se_internal.hpp"
 #include "mfma_util.hpp"
 
 namespace se {
 
-constexpr int HP_WAVES = 8;
-constexpr int HP_NG = 8;                        // pass A: 16-row groups per wave
+constexpr int HPA_WAVES = 12;                   // pass A: waves per block
+constexpr int HPA_THREADS = 64 * HPA_WAVES;
+constexpr int HP_NG = 4;                        // pass A: 16-row groups per wave
 constexpr int HP_RPW = HP_NG * 16;              // pass A: (position, head) rows per wave
-constexpr int HP_ROWS = HP_WAVES * HP_RPW;      // pass A: 1024 rows per block
+constexpr int HP_ROWS = HPA_WAVES * HP_RPW;     // pass A: 768 rows per block
 constexpr int HP_KT = 64;                       // pass A: keys per K tile
+constexpr int HPB_WAVES = 8;                    // pass B: waves per block
+constexpr int HPB_THREADS = 64 * HPB_WAVES;
 constexpr int HP_KB = 4;                        // pass B: 16-key blocks per wave
-constexpr int HP_KEYS = HP_WAVES * HP_KB * 16;  // pass B: 512 keys per block
+constexpr int HP_KEYS = HPB_WAVES * HP_KB * 16; // pass B: 512 keys per block
 constexpr int HP_QR = 128;                      // pass B: (position, head) rows per Q tile
 constexpr float HP_MARGIN = 8.f;                // pass A: log2 headroom before the running max moves
 
@@ -39,14 +45,27 @@ struct HpArgs {
   float sc2;            // scale * log2(e)
 };
 
+// Eight floats as separate fields, indexed only by unrolled constants.  An array
+// indexed that way becomes one 8-wide vector value after unrolling, and the
+// compiler then copies the whole register tuple at every branch join.
+struct F8 {
+  float v0, v1, v2, v3, v4, v5, v6, v7;
+  __device__ __forceinline__ float& operator[](int i) {
+    switch (i) {
+      case 0: return v0; case 1: return v1; case 2: return v2; case 3: return v3;
+      case 4: return v4; case 5: return v5; case 6: return v6; default: return v7;
+    }
+  }
+};
+
 // The group's queries are taken as L * G rows (position-major, head-minor) and go
 // sixteen at a time into the MFMA N dimension, so no column is spent on padding
 // whatever G is.
 
 template <int D>
-__global__ __launch_bounds__(512) void hp_rowlse_kernel(HpArgs a) {
+__global__ __launch_bounds__(HPA_THREADS) void hp_rowlse_kernel(HpArgs a) {
   constexpr int NKS = D / 32, PITCH = D + 8, CH = D / 8;   // CH 16-byte chunks per row
-  constexpr int TPT = HP_KT * CH / 512;                     // K tile chunks per thread
+  constexpr int NCH = HP_KT * CH, TPT = (NCH + HPA_THREADS - 1) / HPA_THREADS;   // K tile chunks (per thread)
   __shared__ __align__(16) uint16_t kt[2][HP_KT][PITCH];
   const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -70,7 +89,8 @@ __global__ __launch_bounds__(512) void hp_rowlse_kernel(HpArgs a) {
 #pragma unroll
     for (int c = 0; c < NKS; ++c) qv[j][c] = ok ? ld16(qp + 8 * g + 32 * c) : u32x4{0, 0, 0, 0};
   }
-  float m[HP_NG], l[HP_NG];
+  static_assert(HP_NG <= 8, "one F8 field per row group");
+  F8 m, l;
 #pragma unroll
   for (int j = 0; j < HP_NG; ++j) { m[j] = -INFINITY; l[j] = 0.f; }
   const int last_pos = (min(nrows, r_blk + HP_ROWS) - 1) / G;
@@ -79,16 +99,16 @@ __global__ __launch_bounds__(512) void hp_rowlse_kernel(HpArgs a) {
   auto fetch = [&](int t) {
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
-      const int e = threadIdx.x + 512 * i;
+      const int e = threadIdx.x + HPA_THREADS * i;
       const int key = min(t * HP_KT + e / CH, L - 1);
-      stage[i] = ld16(ku + size_t(key) * D + 8 * (e % CH));
+      if (NCH % HPA_THREADS == 0 || e < NCH) stage[i] = ld16(ku + size_t(key) * D + 8 * (e % CH));
     }
   };
   auto put = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
-      const int e = threadIdx.x + 512 * i;
-      *reinterpret_cast<u32x4*>(&kt[buf][e / CH][8 * (e % CH)]) = stage[i];
+      const int e = threadIdx.x + HPA_THREADS * i;
+      if (NCH % HPA_THREADS == 0 || e < NCH) *reinterpret_cast<u32x4*>(&kt[buf][e / CH][8 * (e % CH)]) = stage[i];
     }
   };
   fetch(0);
@@ -97,6 +117,58 @@ __global__ __launch_bounds__(512) void hp_rowlse_kernel(HpArgs a) {
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     if (t + 1 < ntiles) fetch(t + 1);
+    if (t * HP_KT + HP_KT - 1 <= pmin[0]) {            // every key of the tile precedes every row of the wave
+      // software pipeline over the tile's (16-key block, row group) pairs: the next
+      // pair's scores go through the matrix cores while this pair's max test and exps
+      // run; the next key block's operands are read from LDS a block ahead
+      constexpr int NSB = HP_KT / 16, NP = NSB * HP_NG;
+      u32x4 ak[2][NKS];
+      auto rd = [&](int sb) {
+#pragma unroll
+        for (int c = 0; c < NKS; ++c)
+          ak[sb & 1][c] = *reinterpret_cast<const u32x4*>(&kt[buf][16 * sb + c16][8 * g + 32 * c]);
+      };
+      auto mm = [&](int p) {
+        const int sb = p / HP_NG, j = p % HP_NG;
+        f32x4 r = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NKS; ++c) r = mfma_bf16_16x16x32(ak[sb & 1][c], qv[j][c], r);
+        return r;
+      };
+      // raw score above which a key moves the running max: (m + margin) / sc2
+      const float inv_sc2 = 1.f / a.sc2;
+      F8 thr;
+#pragma unroll
+      for (int j = 0; j < HP_NG; ++j) thr[j] = (m[j] + HP_MARGIN) * inv_sc2;
+      rd(0);
+      f32x4 sc = mm(0);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int sb = p / HP_NG, j = p % HP_NG;
+        if (j == 0 && sb + 1 < NSB) rd(sb + 1);
+        f32x4 sn = sc;
+        if (p + 1 < NP) sn = mm(p + 1);
+        // the running max moves only when a key beats it by more than 2^8, which is
+        // rare once a row has seen a few keys: the raw scores are compared with that
+        // bound in raw units, and one wave-uniform test per pair takes the update
+        const bool up = (sc[0] > thr[j]) | (sc[1] > thr[j]) | (sc[2] > thr[j]) | (sc[3] > thr[j]);
+        if (__builtin_amdgcn_ballot_w64(up)) {
+          const float hm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) * a.sc2;
+          l[j] = up ? (m[j] == -INFINITY ? 0.f : l[j] * ex2(m[j] - hm)) : l[j];
+          thr[j] = up ? (hm + HP_MARGIN) * inv_sc2 : thr[j];
+          m[j] = up ? hm : m[j];
+        }
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) l[j] += ex2(fmaf(sc[ii], a.sc2, -m[j]));
+        // keeps the sum here: left free, the compiler sinks it to the row group's next
+        // pair and holds eight pairs' scores in registers meanwhile
+        asm volatile("" : "+v"(l[j]));
+        sc = sn;
+      }
+      if (t + 1 < ntiles) put(buf ^ 1);
+      __syncthreads();
+      continue;
+    }
 #pragma unroll
     for (int sb = 0; sb < HP_KT / 16; ++sb) {
       const int key0 = t * HP_KT + 16 * sb;
@@ -146,9 +218,9 @@ __global__ __launch_bounds__(512) void hp_rowlse_kernel(HpArgs a) {
 }
 
 template <int D>
-__global__ __launch_bounds__(512) void hp_colsum_kernel(HpArgs a) {
+__global__ __launch_bounds__(HPB_THREADS) void hp_colsum_kernel(HpArgs a) {
   constexpr int NKS = D / 32, PITCH = D + 8, CH = D / 8;
-  constexpr int TPT = HP_QR * CH / 512;                 // Q tile chunks per thread
+  constexpr int TPT = HP_QR * CH / HPB_THREADS;         // Q tile chunks per thread
   constexpr int NQG = HP_QR / 16;                       // 16-row groups per Q tile
   __shared__ __align__(16) uint16_t qt[2][HP_QR][PITCH];
   __shared__ float lt[2][HP_QR];
@@ -185,7 +257,7 @@ __global__ __launch_bounds__(512) void hp_colsum_kernel(HpArgs a) {
     const int r0 = r_beg + t * HP_QR;
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
-      const int e = threadIdx.x + 512 * i;
+      const int e = threadIdx.x + HPB_THREADS * i;
       const int r = r0 + e / CH;
       stage[i] = r < nrows ? ld16(qu + (size_t(r % G) * L + r / G) * D + 8 * (e % CH)) : u32x4{0, 0, 0, 0};
     }
@@ -194,7 +266,7 @@ __global__ __launch_bounds__(512) void hp_colsum_kernel(HpArgs a) {
   auto put = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
-      const int e = threadIdx.x + 512 * i;
+      const int e = threadIdx.x + HPB_THREADS * i;
       *reinterpret_cast<u32x4*>(&qt[buf][e / CH][8 * (e % CH)]) = stage[i];
     }
     if (threadIdx.x < HP_QR) lt[buf][threadIdx.x] = lstage;
@@ -345,11 +417,11 @@ se_status launch_h2o_prefill_scores(const se_cache& c, const void* q, const void
   if (int64_t(units) * std::max(ceil_div(L * a.G, HP_ROWS), ceil_div(L, HP_KEYS)) > INT32_MAX) return SE_ERR_SHAPE;
   const dim3 ga(units * ceil_div(L * a.G, HP_ROWS)), gb(units * ceil_div(L, HP_KEYS));
   if (c.d_k == 128) {
-    hipLaunchKernelGGL(hp_rowlse_kernel<128>, ga, dim3(512), 0, s, a);
-    hipLaunchKernelGGL(hp_colsum_kernel<128>, gb, dim3(512), 0, s, a);
+    hipLaunchKernelGGL(hp_rowlse_kernel<128>, ga, dim3(HPA_THREADS), 0, s, a);
+    hipLaunchKernelGGL(hp_colsum_kernel<128>, gb, dim3(HPB_THREADS), 0, s, a);
   } else {
-    hipLaunchKernelGGL(hp_rowlse_kernel<64>, ga, dim3(512), 0, s, a);
-    hipLaunchKernelGGL(hp_colsum_kernel<64>, gb, dim3(512), 0, s, a);
+    hipLaunchKernelGGL(hp_rowlse_kernel<64>, ga, dim3(HPA_THREADS), 0, s, a);
+    hipLaunchKernelGGL(hp_colsum_kernel<64>, gb, dim3(HPB_THREADS), 0, s, a);
   }
   return launch_status();
 }
