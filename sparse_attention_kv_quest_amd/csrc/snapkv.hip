@@ -21,7 +21,10 @@
 namespace se {
 
 constexpr float SK_LOG2E = 1.4426950408889634f;
-constexpr int SK_CHUNK = 1024;        // keys per block in the MFMA passes
+// keys per block in the MFMA passes: chosen per call (snap_chunk_keys) between these;
+// the maximum is what pass B's per-wave key sums leave of the LDS at three blocks per CU
+constexpr int SK_CHUNK_MAX = 1104;
+constexpr int SK_CHUNK_MIN = 512;
 constexpr float SK_MARGIN = 8.f;      // lazy running-max margin (log2 units)
 constexpr int SK_KT = 64;             // keys per LDS tile in the MFMA passes
 
@@ -32,7 +35,7 @@ struct SnapArgs {
   void* k_out; void* v_out;
   int32_t* kept; float* votes; float* pooled; float* part; float* lse2; int32_t* out_len;
   uint32_t* sel_hist; SelState* sel_state; int32_t* sel_counts;   // multi-block select
-  int B, Hq, Hkv, G, D, cap, out_cap, L, W, R, pool, budget, nchunks, dtype;
+  int B, Hq, Hkv, G, D, cap, out_cap, L, W, R, pool, budget, nchunks, chunk, dtype;
   float sc2;   // scale * log2(e)
 };
 
@@ -57,16 +60,18 @@ __device__ __forceinline__ void sk_grow(float bm, float& m, float& l) {
 // four lanes.  Pass B swaps the operands: lane (g, c16) holds rows 4g..4g+3 of
 // key c16, and a key's vote stays in four lanes.
 template <int D, int NRB, bool PASS_B>
-__global__ __launch_bounds__(256) void snap_mfma_kernel(SnapArgs a) {
+// three waves per SIMD (three blocks per CU): pass A's pipelined body needs 176
+// registers left free and so would run two, for four spilled registers at three
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void snap_mfma_kernel(SnapArgs a) {
   constexpr int NKS = D / 32, PITCH = D + 8, CH = D / 8, TPT = SK_KT * CH / 256;
   __shared__ __align__(16) uint16_t kt[2][SK_KT][PITCH];
-  __shared__ float vsum[PASS_B ? 4 : 1][SK_CHUNK / 16][16];   // pass B: per-wave key sums of each 16-key block
+  __shared__ float vsum[PASS_B ? 4 : 1][SK_CHUNK_MAX / 16][16];   // pass B: per-wave key sums of each 16-key block
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
   const int unit = blockIdx.y, chunk = blockIdx.x;
   const int b = unit / a.Hkv, kvh = unit % a.Hkv;
   const int n_hist = a.L - a.W;
   const int kend = PASS_B ? n_hist : a.L;          // pass B scores history keys only
-  const int k0 = chunk * SK_CHUNK, k1 = min(kend, k0 + SK_CHUNK);
+  const int k0 = chunk * a.chunk, k1 = min(kend, k0 + a.chunk);
   const uint16_t* ku = (const uint16_t*)a.k + size_t(unit) * a.cap * D;
   const uint16_t* qu = (const uint16_t*)a.q + (size_t(b) * a.Hq + size_t(kvh) * a.G) * a.W * D;
   // Q operand of this wave's row blocks
@@ -170,16 +175,76 @@ __global__ __launch_bounds__(256) void snap_mfma_kernel(SnapArgs a) {
       if (g == 0) vsum[w][blk][c16] = kb + c16 < k1 ? vote : 0.f;
     }
   };
+  // A tile whose four blocks all need no mask (and exist): one straight-line software
+  // pipeline over its (16-key block, row block) pairs, the next pair's MFMAs issued
+  // before this pair's exps (the passes are bound by the vector ALU: one exp2 and two
+  // to three other operations per score), the next key block's operands read from
+  // LDS a block ahead.
+  auto plain_tile = [&](int buf, int t) {
+    constexpr int NSB = SK_KT / 16, NP = NSB * NRB;
+    u32x4 kc[2][NKS];
+    auto rd = [&](int sb) {
+#pragma unroll
+      for (int c = 0; c < NKS; ++c)
+        kc[sb & 1][c] = *reinterpret_cast<const u32x4*>(&kt[buf][16 * sb + c16][8 * g + 32 * c]);
+    };
+    auto mm = [&](int p) {
+      const int sb = p / NRB, rb = p % NRB;
+      f32x4 r = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NKS; ++c)
+        r = PASS_B ? mfma_bf16_16x16x32(qv[rb][c], kc[sb & 1][c], r) : mfma_bf16_16x16x32(kc[sb & 1][c], qv[rb][c], r);
+      return r;
+    };
+    // pass A: raw score above which a key moves a row's running max, (m + margin) / sc2
+    float thr[NRB];
+    const float inv_sc2 = 1.f / a.sc2;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) thr[rb] = (m[rb] + SK_MARGIN) * inv_sc2;
+    float vote = 0.f;
+    rd(0);
+    f32x4 sc = mm(0);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int sb = p / NRB, rb = p % NRB;
+      if (rb == 0 && sb + 1 < NSB) rd(sb + 1);
+      f32x4 sn = sc;
+      if (p + 1 < NP) sn = mm(p + 1);
+      if constexpr (!PASS_B) {
+        // the lazy running max (the rule sk_grow applies), tested on the raw scores
+        const bool up = (sc[0] > thr[rb]) | (sc[1] > thr[rb]) | (sc[2] > thr[rb]) | (sc[3] > thr[rb]);
+        if (__ballot(up) != 0) {
+          const float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])) * a.sc2;
+          l[rb] = up ? (m[rb] == -INFINITY ? 0.f : l[rb] * ex2(m[rb] - bm)) : l[rb];
+          thr[rb] = up ? (bm + SK_MARGIN) * inv_sc2 : thr[rb];
+          m[rb] = up ? bm : m[rb];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) l[rb] += ex2(fmaf(sc[i], a.sc2, -m[rb]));
+        // keeps the sum here: left free, the compiler sinks it to the row block's next
+        // pair and holds the scores of the pairs between in registers
+        asm volatile("" : "+v"(l[rb]));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vote += ex2(fmaf(sc[i], a.sc2, nlse[rb][i]));
+        if (rb == NRB - 1) {
+          const float v = rows4_sum(vote);
+          if (g == 0) vsum[w][t * NSB + sb][c16] = v;
+          vote = 0.f;
+        }
+      }
+      sc = sn;
+    }
+  };
   using Plain = std::integral_constant<bool, true>;
   using Masked = std::integral_constant<bool, false>;
   for (int t = 0; t < ntile; ++t) {
     const int buf = t & 1;
     if (t + 1 < ntile) fetch(t + 1);
-    // tiles whose four blocks all need no mask (and exist) take one straight-line body;
+    // tiles whose four blocks all need no mask (and exist) take the pipelined body;
     // the chunk's last tiles take the general one (uniform across the block)
     if ((t + 1) * (SK_KT / 16) <= (PASS_B ? nblk : plain)) {
-#pragma unroll
-      for (int sb = 0; sb < SK_KT / 16; ++sb) key_block(buf, sb, t * (SK_KT / 16) + sb, Plain{});
+      plain_tile(buf, t);
     } else {
 #pragma unroll
       for (int sb = 0; sb < SK_KT / 16; ++sb) {
@@ -548,7 +613,38 @@ static bool snap_mfma_ok(const se_cache& c, int W) {
   return c.dtype == SE_BF16 && (c.d_k == 128 || c.d_k == 64) && R % 64 == 0 && R <= 256;
 }
 
-static int snap_chunks(int L) { return ceil_div(L, SK_CHUNK); }
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return cus[dev];
+}
+
+// Keys per block of the MFMA passes.  Three of their blocks fill a CU, and the
+// dispatcher deals blocks to the CUs in a fixed rotation, so the passes take about
+// ceil(blocks / resident blocks) rounds of one block's time: the chunk (a multiple of
+// 16 keys) minimises rounds x keys per block.  For 32 units of 128K keys on 256 CUs,
+// 1104 keys make 3808 blocks, 4.96 rounds, where 1024 keys made 4096 blocks, 5.33
+// rounds taking the time of 6.
+static int snap_chunk_keys(int L, size_t units) {
+  const long slots = 3L * device_cus();
+  int best = SK_CHUNK_MAX;
+  long best_cost = -1;
+  for (int ch = SK_CHUNK_MAX; ch >= SK_CHUNK_MIN; ch -= 16) {
+    const long blocks = long(units) * ceil_div(L, ch);
+    const long cost = (blocks + slots - 1) / slots * ch;
+    if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = ch; }
+  }
+  return best;
+}
+// chunks of pass A for a given chunk size; the workspace holds partials for the most
+// (smallest) chunks any device can be given
+static int snap_chunks(int L, int chunk) { return ceil_div(L, chunk); }
 static int sel_slices(int n) { return std::max(1, ceil_div(n, SK_SEL_CH)); }
 
 // Workspace: the select's digit histograms first (zero between calls), then its
@@ -560,7 +656,7 @@ static size_t sel_bytes(size_t units, int n) {
 size_t snapkv_ws_bytes(const se_cache& c, int prompt_len, int window) {
   const size_t units = size_t(c.batch) * c.n_kv_heads, R = size_t(c.n_q_heads / c.n_kv_heads) * window;
   const size_t n = size_t(prompt_len - window);
-  return sel_bytes(units, int(n)) + units * (size_t(snap_chunks(prompt_len)) * R * 2 + R + 2 * n) * sizeof(float);
+  return sel_bytes(units, int(n)) + units * (size_t(snap_chunks(prompt_len, SK_CHUNK_MIN)) * R * 2 + R + 2 * n) * sizeof(float);
 }
 
 // The keep rule and the compaction, from the scores in a.votes: max-pool, top
@@ -593,9 +689,11 @@ se_status launch_snapkv(const se_cache& c, const void* q_obs, const void* k, con
   a.q = q_obs; a.k = k; a.v = v; a.k_out = k_out; a.v_out = v_out;
   a.B = c.batch; a.Hq = c.n_q_heads; a.Hkv = c.n_kv_heads; a.G = c.n_q_heads / c.n_kv_heads; a.D = c.d_k;
   a.cap = c.capacity; a.out_cap = out.capacity; a.L = prompt_len; a.W = window; a.R = a.G * window;
-  a.pool = pool_kernel; a.budget = budget; a.nchunks = snap_chunks(prompt_len); a.dtype = c.dtype;
+  const size_t units = size_t(c.batch) * c.n_kv_heads, n = size_t(prompt_len - window);
+  a.pool = pool_kernel; a.budget = budget; a.dtype = c.dtype;
+  a.chunk = snap_chunk_keys(prompt_len, units);
+  a.nchunks = snap_chunks(prompt_len, a.chunk);
   a.sc2 = scale * SK_LOG2E;
-  const size_t units = size_t(a.B) * a.Hkv, n = size_t(prompt_len - window);
   a.sel_hist = (uint32_t*)ws;
   a.sel_state = (SelState*)(a.sel_hist + units * SK_SEL_BINS);
   a.sel_counts = (int32_t*)(a.sel_state + units);
@@ -609,7 +707,7 @@ se_status launch_snapkv(const se_cache& c, const void* q_obs, const void* k, con
   const dim3 vgrid(ceil_div(int(n), 256), int(units));
   if (snap_mfma_ok(c, window)) {
     const int nrb = a.R / 64;
-    const dim3 ga(a.nchunks, int(units)), gb(ceil_div(int(n), SK_CHUNK), int(units));
+    const dim3 ga(a.nchunks, int(units)), gb(ceil_div(int(n), a.chunk), int(units));
 #define SK_LAUNCH(DD, NN)                                                                          \
   do {                                                                                             \
     hipLaunchKernelGGL((snap_mfma_kernel<DD, NN, false>), ga, dim3(256), 0, s, a);                 \
