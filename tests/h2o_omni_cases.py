@@ -70,6 +70,10 @@ PREFILL_CASES = {
     "keep_all": (get_config(0, dtype="bf16", batch=1, n_q_heads=8, n_kv_heads=2), 90, 64, 32),
     # past one 512-key column block: the column pass's whole-tile path with 64-wide heads
     "d64_g4_long": (get_config(0, dtype="bf16", batch=2, n_q_heads=8, n_kv_heads=2), 900, 60, 24),
+    # one query head per KV head: the query rows are the positions themselves, two row
+    # blocks and three column blocks per unit
+    "d128_g1_long": (get_config(0, dtype="bf16", batch=2, n_q_heads=3, n_kv_heads=3, d_k=128, d_v=128), 1500, 120,
+                     40),
 }
 PREFILL_KV_LAYER = 41
 
