@@ -628,9 +628,9 @@ static int device_cus() {
 // Keys per block of the MFMA passes.  Three of their blocks fill a CU, and the
 // dispatcher deals blocks to the CUs in a fixed rotation, so the passes take about
 // ceil(blocks / resident blocks) rounds of one block's time: the chunk (a multiple of
-// 16 keys) minimises rounds x keys per block.  For 32 units of 128K keys on 256 CUs,
-// 1104 keys make 3808 blocks, 4.96 rounds, where 1024 keys made 4096 blocks, 5.33
-// rounds taking the time of 6.
+// 16 keys) minimises rounds x keys per block.  For 32 units of 128K keys on 256 CUs
+// it is 912 keys: 4608 blocks, six whole rounds, where 1024 keys made 4096 blocks,
+// 5.33 rounds taking the time of 6 (1104 keys, 4.96 rounds, measure the same).
 static int snap_chunk_keys(int L, size_t units) {
   const long slots = 3L * device_cus();
   int best = SK_CHUNK_MAX;
