@@ -699,7 +699,7 @@ void attn_mfma_kernel(AttnArgs a) {
       for (int j = 0; j < HE; ++j) lv[j] = lg_unit[hh * a.logit_cap + min(j * 256 + int(threadIdx.x), a.logit_cap - 1)];
 #pragma unroll
       for (int j = 0; j < HE; ++j) {
-        const float e = expf(lv[j] - l);
+        const float e = h2o_exp(lv[j] - l);
         sc[j] = p[j] >= 0 ? sc[j] + e : sc[j];
       }
     }

@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void h2o_kernel(
     float p = 0.f;
     for (int h = 0; h < G; ++h) {
       const float l = lse_s[h];
-      if (l != -INFINITY) p += expf(lg[size_t(h) * logit_cap + s] - l);
+      if (l != -INFINITY) p += h2o_exp(lg[size_t(h) * logit_cap + s] - l);
     }
     a[s] += p;
     ++cnt;
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256) void h2o_reg_kernel(
       if (l[hh] == -INFINITY) continue;
 #pragma unroll
       for (int j = 0; j < E; ++j)
-        if (p[j] >= 0) sc[j] += expf(x[hh][j] - l[hh]);
+        if (p[j] >= 0) sc[j] += h2o_exp(x[hh][j] - l[hh]);
     }
   };
   {

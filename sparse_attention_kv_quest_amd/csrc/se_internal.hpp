@@ -19,6 +19,10 @@ struct bf16_t { uint16_t bits; };
 // maximum's own), so a dropped term is below its rounding; a sum of
 // probabilities loses at most 2^-126 per term.
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+// e^x as one multiply and v_exp_f32 (results below 2^-126 come out as zero): the H2O
+// score accumulation, in every kernel that computes it, so that the fused decode step
+// and the separate calls agree bit for bit
+__device__ __forceinline__ float h2o_exp(float x) { return ex2(x * 1.4426950408889634f); }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float(uint32_t(x.bits) << 16); }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
