@@ -161,7 +161,7 @@ __global__ __launch_bounds__(HPA_THREADS) void hp_rowlse_kernel(HpArgs a) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) l[j] += ex2(fmaf(sc[ii], a.sc2, -m[j]));
         // keeps the sum here: left free, the compiler sinks it to the row group's next
-        // pair and holds eight pairs' scores in registers meanwhile
+        // pair and holds the scores of the pairs between in registers
         asm volatile("" : "+v"(l[j]));
         sc = sn;
       }
