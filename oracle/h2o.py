@@ -87,6 +87,23 @@ def prefill_scores(qg, Kt, L, scale):
     return acc
 
 
+def prefill_scores_tail(qg, Kt, L, scale, j0):
+    """acc0[j] of prefill_scores for the keys j0 <= j < L only, one unit (float64,
+    [L - j0]): the same definition restricted to them.  Key j receives weight only
+    from the queries i >= j, so only the rows i >= j0 are formed, each softmax
+    still running over all of its keys 0..i."""
+    qg = np.asarray(qg, np.float64)
+    Kt = np.asarray(Kt, np.float64)[:L]
+    acc = np.zeros(L - j0)
+    for h in range(qg.shape[0]):
+        for i in range(j0, L):
+            s = scale * (Kt[:i + 1] @ qg[h, i])            # keys 0..i of query i
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            acc[:i + 1 - j0] += p[j0:]
+    return acc
+
+
 def prefill_state(acc0, L, heavy, recent, cap):
     """Slot state after the prefill (reading: the SnapKV-style keep rule on the scores,
     no pooling): the `heavy` best positions below L - recent (ties to the lower

@@ -130,3 +130,56 @@ def test_h2o_decode_continues_from_prefill_state(se):
             np.testing.assert_array_equal(host(slot_pos)[b, h], s["pos"])
             np.testing.assert_allclose(host(acc)[b, h], s["acc"], rtol=2e-4, atol=1e-5)
             np.testing.assert_allclose(host(out)[b, h * G:(h + 1) * G], o, rtol=0, atol=TOL["bf16"])
+
+
+def test_h2o_prefill_init_full_size(se):
+    """The bench's prefill-end shape (64 rows x 4 KV heads x 8 query heads, 16K-token
+    prompt, 1024 heavy + 256 recent slots).  Every unit: its scores sum to G * L (each
+    query row's weights sum to one), and its kept set is the recent window plus the
+    1024 best scores below it (ties to the lower position), ascending, with those
+    scores.  Units (0, 0), (31, 2) and (63, 3): the scores of the last 48 keys against
+    the oracle's (those keys get weight only from the last 48 query rows), and the
+    kept rows as bit copies."""
+    from workloads import get_config
+    cfg = get_config(3)
+    B, H, Hq, D, G, L = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.d_k, cfg.group, cfg.context
+    heavy, recent = cfg.h2o_heavy, cfg.h2o_recent
+    banner(f"h2o prefill full size B={B} Hkv={H} G={G} L={L}")
+    scale = 1.0 / np.sqrt(D)
+    gcuda = torch.Generator(device="cuda")
+    gcuda.manual_seed(20261)
+    q = torch.randn((B, Hq, L, D), generator=gcuda, device="cuda").to(torch.bfloat16)
+    k = torch.randn((B, H, L, D), generator=gcuda, device="cuda").to(torch.bfloat16)
+    v = torch.randn((B, H, L, D), generator=gcuda, device="cuda").to(torch.bfloat16)
+    c = se.cache(B, Hq, H, D, D, L, "bf16")
+    scap = heavy + recent + 1
+    sl = se.cache(B, Hq, H, D, D, scap, "bf16")
+    k_slots = torch.zeros((B, H, scap, D), dtype=torch.bfloat16, device="cuda")
+    v_slots = torch.zeros_like(k_slots)
+    slot_pos = torch.full((B, H, scap), -9, dtype=torch.int32, device="cuda")
+    acc = torch.full((B, H, scap), -9.0, device="cuda")
+    scores = torch.zeros((B, H, L), device="cuda")
+    ws = se.workspace(se.SE_OP_H2O_PREFILL, c, L, recent)
+    se.se_h2o_prefill_init(c, q, k, v, L, heavy, recent, scale, sl, k_slots, v_slots, slot_pos, acc, scores, ws)
+    torch.cuda.synchronize()
+    g_sc, g_pos, g_acc = host(scores), host(slot_pos), host(acc)
+    np.testing.assert_allclose(g_sc.astype(np.float64).sum(axis=-1), G * L, rtol=1e-4)
+    n = heavy + recent
+    for b in range(B):
+        for h in range(H):
+            where = f"b={b} h={h}"
+            cand = g_sc[b, h, :L - recent]
+            order = np.lexsort((np.arange(L - recent), -cand))   # best first, ties to the lower position
+            kept = np.concatenate([np.sort(order[:heavy]), np.arange(L - recent, L)])
+            np.testing.assert_array_equal(g_pos[b, h, :n], kept, err_msg=f"kept positions {where}")
+            assert np.all(g_pos[b, h, n:] == -1) and np.all(g_acc[b, h, n:] == 0.0), where
+            np.testing.assert_array_equal(g_acc[b, h, :n], g_sc[b, h, kept], err_msg=f"kept scores {where}")
+    j0 = L - 48
+    for b, h in ((0, 0), (31, 2), (63, 3)):
+        qg = q[b, h * G:(h + 1) * G].float().cpu().numpy()
+        kh = k[b, h].float().cpu().numpy()
+        ref = oh2o.prefill_scores_tail(qg, kh, L, scale, j0)
+        np.testing.assert_allclose(g_sc[b, h, j0:], ref, rtol=2e-4, atol=1e-6, err_msg=f"tail scores b={b} h={h}")
+        kept = g_pos[b, h, :n]
+        np.testing.assert_array_equal(host(k_slots[b, h, :n]), host(k[b, h][torch.from_numpy(kept).long().cuda()]))
+        np.testing.assert_array_equal(host(v_slots[b, h, :n]), host(v[b, h][torch.from_numpy(kept).long().cuda()]))

@@ -66,3 +66,18 @@ def test_prefill_state_layout():
     kept, slot_pos, _ = oh2o.prefill_state(acc0[:12], 12, heavy, recent, cap)
     np.testing.assert_array_equal(kept, np.arange(12))
     assert np.all(slot_pos[12:] == -1)
+
+
+def test_tail_scores_equal_the_full_scores_past_j0():
+    """prefill_scores_tail (the keys j0.. only, for full-size parity samples) against
+    the pinned full scores, and against the harmonic closed form for equal keys."""
+    L = 37
+    q, K = rand(L, G=3, D=16, seed=5)
+    full = oh2o.prefill_scores(q, K, L, 0.35)
+    for j0 in (0, 1, 20, L - 1):
+        np.testing.assert_allclose(oh2o.prefill_scores_tail(q, K, L, 0.35, j0), full[j0:], rtol=1e-12, atol=1e-15)
+    G = 2
+    qe, _ = rand(L, G, seed=6)
+    Ke = np.tile(np.random.default_rng(7).normal(size=(1, 16)), (L, 1))
+    harmonic = np.array([G * sum(1.0 / (i + 1) for i in range(j, L)) for j in range(L)])
+    np.testing.assert_allclose(oh2o.prefill_scores_tail(qe, Ke, L, 0.5, 30), harmonic[30:], rtol=1e-12)
