@@ -42,10 +42,12 @@ struct MfTile {
   int tk0, tk1;
 };
 
-// FP8 rows as loaded: the lane's d/4 contiguous K bytes of rows tk0 / tk1 (its k
-// columns are g d/4 .. g d/4 + d/4 - 1, k-step c taking the 8 from 8c on; q is
-// staged in the same order), 8 V bytes per row and pass (the bf16 layout's
-// dims), and every row's scale byte.
+// FP8 rows as loaded: 16 K bytes of rows tk0 / tk1 per 64-byte span, lane group g
+// holding bytes 64 j + 16 g .. + 15 (so each load reads 64 contiguous bytes of 16
+// rows; k-step c takes the 8 bytes from 64 (c / 2) + 16 g + 8 (c % 2) on, and q is
+// staged in the same order), 8 V bytes per row and pass (where d is a multiple of
+// 128 a pass pair's 16 bytes are contiguous: dims 16 (lane >> 3) + 128 k on; else
+// the bf16 layout's dims), and every row's scale byte.
 template <int D>
 struct MfTileF8 {
   u32x4 k0[D / 64], k1[D / 64];
@@ -179,16 +181,27 @@ __device__ __forceinline__ void mf_load_f8(const MfCtx& x, int base, int lane, M
   const uint32_t t0 = uint32_t(max(T.tk0, 0)), t1 = uint32_t(max(T.tk1, 0));
 #pragma unroll
   for (int j = 0; j < D / 64; ++j) {
-    T.k0[j] = ld16(ku + t0 * D + g * (D / 4) + 16 * j);
-    T.k1[j] = ld16(ku + t1 * D + g * (D / 4) + 16 * j);
+    T.k0[j] = ld16(ku + t0 * D + 16 * g + 64 * j);
+    T.k1[j] = ld16(ku + t1 * D + 16 * g + 64 * j);
   }
   T.ks0 = x.ksc[t0];
   T.ks1 = x.ksc[t1];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const uint32_t tv = uint32_t(max(vtok[r], 0));
+    if constexpr (VPASS % 2 == 0) {
+      // one 16-byte load per pass pair: dims 16 (lane >> 3) + 128 k .. + 15, so each
+      // load of the wave covers eight whole 128-byte rows
 #pragma unroll
-    for (int p = 0; p < VPASS; ++p) T.v[p][r] = *reinterpret_cast<const uint2*>(vu + tv * D + 8 * (lane >> 3) + 64 * p);
+      for (int k = 0; k < VPASS / 2; ++k) {
+        const u32x4 w = ld16(vu + tv * D + 16 * (lane >> 3) + 128 * k);
+        T.v[2 * k][r] = uint2{w[0], w[1]};
+        T.v[2 * k + 1][r] = uint2{w[2], w[3]};
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < VPASS; ++p) T.v[p][r] = *reinterpret_cast<const uint2*>(vu + tv * D + 8 * (lane >> 3) + 64 * p);
+    }
     T.vs[r] = x.vsc[tv];
   }
 }
@@ -199,12 +212,20 @@ template <int D>
 __device__ __forceinline__ u32x4 mf_kop(const MfTile<D>& T, int half, int c) { return half ? T.k1[c] : T.k0[c]; }
 template <int D>
 __device__ __forceinline__ u32x4 mf_kop(const MfTileF8<D>& T, int half, int c) {
-  const int j = c / 2, w = 2 * (c % 2);   // k-step c: bytes 8c .. 8c + 7 of the lane's span
+  const int j = c / 2, w = 2 * (c % 2);   // k-step c: bytes 64 j + 16 g + 4 w .. + 7 of the row
   const u32x4& src = half ? T.k1[j] : T.k0[j];
   return mf_cvt8(src[w], src[w + 1], mf_scale(half ? T.ks1 : T.ks0));
 }
 template <int D>
 __device__ __forceinline__ u32x4 mf_vop(const MfTile<D>& T, int pp, int r) { return T.v[pp][r]; }
+// The 8-dim V chunk a lane holds in pass pp (its dims are 8 ch .. 8 ch + 7).
+template <int D>
+__device__ __forceinline__ int mf_vch(const MfTile<D>&, int lane, int pp) { return (lane >> 3) + 8 * pp; }
+template <int D>
+__device__ __forceinline__ int mf_vch(const MfTileF8<D>&, int lane, int pp) {
+  if constexpr ((D / 64) % 2 == 0) return 2 * (lane >> 3) + 16 * (pp >> 1) + (pp & 1);
+  else return (lane >> 3) + 8 * pp;
+}
 template <int D>
 __device__ __forceinline__ u32x4 mf_vop(const MfTileF8<D>& T, int pp, int r) {
   return mf_cvt8(T.v[pp][r].x, T.v[pp][r].y, mf_scale(T.vs[r]));
@@ -288,7 +309,7 @@ __device__ __forceinline__ void mf_compute(const AttnArgs& a, const MfCtx& x, in
   // ---- V quads -> transposed LDS tile: row = dim, 32 tokens per row
 #pragma unroll
   for (int pp = 0; pp < VPASS; ++pp) {
-    const int ch = (lane >> 3) + 8 * pp;
+    const int ch = mf_vch<D>(T, lane, pp);
     u32x4 vv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) vv[r] = mf_vop<D>(T, pp, r);
@@ -459,11 +480,12 @@ void attn_mfma_kernel(AttnArgs a) {
   x.vglob = (identity || SEL > 0) ? nullptr : a.view_idx + size_t(unit) * a.view_cap;
 
   // Q as the B operand: lane holds head c16, dims 32c + 8g .. 32c + 8g + 7 of k-step c
+  // (FP8 tiles: dims 64 (c / 2) + 16 g + 8 (c % 2) on, the order of their K bytes)
   u32x4 qv[NKS];
   if (c16 < G) {
     const uint16_t* qh = (const uint16_t*)a.q + (size_t(b) * a.Hq + size_t(kvh) * G + c16) * D;
 #pragma unroll
-    for (int c = 0; c < NKS; ++c) qv[c] = ld16(qh + (F8 ? g * (D / 4) + 8 * c : 8 * g + 32 * c));
+    for (int c = 0; c < NKS; ++c) qv[c] = ld16(qh + (F8 ? 64 * (c >> 1) + 16 * g + 8 * (c & 1) : 8 * g + 32 * c));
   } else {
 #pragma unroll
     for (int c = 0; c < NKS; ++c) qv[c] = u32x4{0, 0, 0, 0};
